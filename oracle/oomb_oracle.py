@@ -1,0 +1,352 @@
+"""Plain, slow CPU oracle for OOMB-style paged chunk attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may use this module; the HIP library never does. It shares no code
+with the HIP path: it builds its own page pool by scatter, gathers pages back into
+contiguous key/value arrays, and evaluates every quantity from its definition.
+
+Sources (the OOMB pages; "explainer" = the gist.science explainer of arXiv 2602.02108):
+  * chunk-recurrent training with recomputation: explainer, 2.A "Chunk-Recurrent
+    Training with Activation Recomputation"; mlsanity page, "Abstract (arXiv)".
+  * paged KV cache and paged KV gradients, in-place accumulation: explainer, 2.B
+    "Paged KV Cache and Gradient Management"; mlsanity abstract.
+  * top-K page retrieval from a representative vector: explainer, 2.D "Page-Level
+    Sparse Attention".
+The pages give no formula. Attention itself is the textbook definition (softmax of
+scaled dot products, causal), so the forward/backward below is that definition
+written out in fp64. Page selection is a heuristic the pages leave open; it is
+specified here step by step (Quest-style min/max page summaries, a fixed fp32
+summation order) and implemented in float32 exactly as specified.
+
+Precision: attention in float64 from inputs widened exactly (bf16 and fp32 are
+subsets of fp64); selection arithmetic in IEEE float32, round-to-nearest, no fused
+multiply-add, in the order documented on each function.
+
+Pins (tests marked "not gpu"): finite differences; equality of the chunk sweep with
+full-sequence causal attention from torch's SDPA; an explicitly masked SDPA call for
+sparse selections; closed forms (single visible key, all-zero keys, row sums of P,
+column sums of dK and dV); page-permutation invariance; hand-derived values for the
+summation orders (tests/golden/); brute-force order statistics for the top-k.
+No function here is parity-unpinned.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "append", "gather", "summarize", "total_order_key",
+    "query_summary", "page_scores", "top_k_pages", "select_pages",
+    "attended_pages", "key_positions", "fwd", "bwd", "sweep",
+]
+
+
+# ---------------------------------------------------------------------------
+# Paging (explainer 2.B: K/V and their gradients live in fixed-size pages).
+# A pool is [N, P, D]; a table row maps logical page j of one KV head to a
+# physical page id. Token t of head g lives at pool[table[g, t // P], t % P].
+# ---------------------------------------------------------------------------
+
+def append(pool: torch.Tensor, table: torch.Tensor, new: torch.Tensor, start: int) -> None:
+    """Scatter tokens [start, start+n) of every KV head into their pages (a copy)."""
+    P = pool.shape[1]
+    hkv, n, _ = new.shape
+    t = torch.arange(start, start + n)
+    for g in range(hkv):
+        phys = table[g].long()[t // P]
+        pool[phys, t % P] = new[g]
+
+
+def gather(pool: torch.Tensor, table: torch.Tensor, g: int, pages: Sequence[int]) -> torch.Tensor:
+    """Contiguous [len(pages) * P, D] copy of the listed logical pages of head g."""
+    idx = table[g].long()[torch.as_tensor(list(pages), dtype=torch.long)]
+    return pool[idx].reshape(-1, pool.shape[2])
+
+
+def total_order_key(x: torch.Tensor) -> torch.Tensor:
+    """Integer key that orders finite floats by value and puts -0 below +0."""
+    if x.dtype == torch.bfloat16:
+        b = x.view(torch.int16).to(torch.int32)
+        mag = b & 0x7FFF
+    elif x.dtype == torch.float32:
+        b = x.view(torch.int32).to(torch.int64)
+        mag = b & 0x7FFFFFFF
+    else:
+        raise TypeError(x.dtype)
+    return torch.where(b >= 0, b, -mag - 1)
+
+
+def summarize(k_pool, table, summary, first_page: int, n_pages: int, seq_len: int) -> None:
+    """Per-page key summary (the representative of a page for retrieval, explainer 2.D;
+    min/max form as in Quest, which the mlsanity page lists among OOMB's sources).
+
+    summary[phys, 0, d] = min over the page's tokens with position < seq_len of K[., d]
+    summary[phys, 1, d] = max over the same tokens.
+    min/max use the total order of the values in which -0 < +0 (so the result never
+    depends on evaluation order). Pages without a valid token are left unchanged."""
+    P = k_pool.shape[1]
+    for g in range(table.shape[0]):
+        for j in range(first_page, first_page + n_pages):
+            n_valid = min(P, seq_len - j * P)
+            if n_valid <= 0:
+                continue
+            phys = int(table[g, j])
+            x = k_pool[phys, :n_valid]
+            key = total_order_key(x)
+            lo = torch.gather(x, 0, key.argmin(dim=0, keepdim=True))[0]
+            hi = torch.gather(x, 0, key.argmax(dim=0, keepdim=True))[0]
+            summary[phys, 0] = lo
+            summary[phys, 1] = hi
+
+
+# ---------------------------------------------------------------------------
+# Page selection (explainer 2.D "Top-K Page Retrieval": keep the K most relevant key
+# pages, judged from a representative vector average). Float32, fixed order.
+# ---------------------------------------------------------------------------
+
+BLOCK = 64  # queries summed sequentially before the pairwise stage
+
+
+def _as_f32(x: torch.Tensor) -> np.ndarray:
+    return x.detach().to("cpu", torch.float32).numpy()
+
+
+def query_summary(q: torch.Tensor, g: int, group: int) -> np.ndarray:
+    """qbar for KV head g: the mean of the chunk's queries over its `group` heads.
+
+    q is [Hq, C, D]. Let x_m = q[g*group + m // C, m % C, :] for m in [0, group*C)
+    (head-major, then query order). Within each block of 64 consecutive m, sum
+    sequentially in float32 starting from +0. Pad the block sums with +0 to a power
+    of two and combine them by stride-halving pairs: for s = n/2, n/4, .., 1:
+    a[i] = a[i] + a[i + s] for i < s. Multiply a[0] by fp32(1 / (group*C)), where
+    the reciprocal is taken in float64 and rounded once."""
+    C = q.shape[1]
+    x = _as_f32(q[g * group:(g + 1) * group]).reshape(group * C, -1)
+    M, D = x.shape
+    nb = -(-M // BLOCK)
+    padded = np.zeros((nb * BLOCK, D), np.float32)
+    padded[:M] = x
+    blocks = padded.reshape(nb, BLOCK, D)
+    acc = np.zeros((nb, D), np.float32)
+    for j in range(BLOCK):           # sequential within every block (all blocks at once)
+        acc = acc + blocks[:, j]
+    n2 = 1
+    while n2 < nb:
+        n2 *= 2
+    a = np.zeros((n2, D), np.float32)
+    a[:nb] = acc
+    s = n2 // 2
+    while s >= 1:
+        a[:s] = a[:s] + a[s:2 * s]
+        s //= 2
+    inv = np.float32(1.0 / (group * C))
+    return (a[0] * inv).astype(np.float32)
+
+
+def page_scores(qbar: np.ndarray, summary: torch.Tensor, table: torch.Tensor, g: int,
+                n_cand: int) -> np.ndarray:
+    """score_j = sum_d max(qbar_d * kmax_jd, qbar_d * kmin_jd) for logical pages j < n_cand.
+
+    Products are rounded to float32; max keeps qbar*kmax only when it is strictly
+    greater. The sum over d is a stride-halving tree: for s = D/2, .., 1:
+    a[d] = a[d] + a[d + s] for d < s."""
+    if n_cand == 0:
+        return np.zeros(0, np.float32)
+    phys = table[g, :n_cand].long()
+    smry = _as_f32(summary[phys])            # [n, 2, D]
+    kmin, kmax = smry[:, 0], smry[:, 1]
+    qb = qbar.astype(np.float32)[None, :]
+    p_hi = qb * kmax
+    p_lo = qb * kmin
+    a = np.where(p_hi > p_lo, p_hi, p_lo).astype(np.float32)
+    s = a.shape[1] // 2
+    while s >= 1:
+        a[:, :s] = a[:, :s] + a[:, s:2 * s]
+        s //= 2
+    return a[:, 0].copy()
+
+
+def top_k_pages(scores: np.ndarray, k: int) -> List[int]:
+    """The k best pages by (score descending, logical id ascending), in ascending id
+    order. Scores compare as IEEE values (-0 equals +0). k >= n keeps every page."""
+    n = len(scores)
+    order = sorted(range(n), key=lambda j: (-float(scores[j]), j))
+    return sorted(order[:max(0, min(k, n))])
+
+
+def select_pages(q, summary, table, t0: int, page: int, group: int, top_k: int):
+    """Per KV head: (qbar, scores, selected logical ids). Candidates are the complete
+    pages strictly before the chunk, [0, t0 // page); the chunk's own pages (and a
+    page straddling t0) are attended anyway and never compete."""
+    n_cand = t0 // page
+    out = []
+    for g in range(table.shape[0]):
+        qb = query_summary(q, g, group)
+        sc = page_scores(qb, summary, table, g, n_cand)
+        out.append((qb, sc, top_k_pages(sc, top_k)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Attention of one chunk over the paged cache (explainer 2.A-2.B, 2.D).
+# Query i of the chunk sits at absolute position t0 + i and sees key t iff
+# page(t) is selected or local and t <= t0 + i.
+# ---------------------------------------------------------------------------
+
+def attended_pages(t0: int, n_q: int, page: int, sel: Optional[Sequence[int]]) -> List[int]:
+    """Selected prior pages (all of [0, t0//page) when sel is None), then local pages."""
+    first_local = t0 // page
+    last_local = (t0 + n_q - 1) // page
+    prior = list(range(first_local)) if sel is None else sorted(int(j) for j in sel)
+    return prior + list(range(first_local, last_local + 1))
+
+
+def key_positions(pages: Sequence[int], page: int, end: int) -> torch.Tensor:
+    """Absolute positions of the tokens of the listed pages that lie before `end`."""
+    pos = (torch.as_tensor(list(pages), dtype=torch.long)[:, None] * page
+           + torch.arange(page)[None, :]).reshape(-1)
+    return pos[pos < end]
+
+
+def _keys(k_pool, v_pool, table, g, pages, page, end):
+    pos_all = (torch.as_tensor(list(pages), dtype=torch.long)[:, None] * page
+               + torch.arange(page)[None, :]).reshape(-1)
+    keep = pos_all < end
+    K = gather(k_pool, table, g, pages)[keep].to(torch.float64)
+    V = gather(v_pool, table, g, pages)[keep].to(torch.float64)
+    return pos_all[keep], K, V
+
+
+def _rows(n, rb):
+    for i0 in range(0, n, rb):
+        yield i0, min(n, i0 + rb)
+
+
+def _probs(Qb, K, pos, qpos, scale):
+    """P = softmax over visible keys of scale * Q K^T, and the natural-log LSE."""
+    S = scale * torch.matmul(Qb, K.T)
+    S = S.masked_fill(pos[None, None, :] > qpos[None, :, None], -math.inf)
+    m = S.amax(dim=-1, keepdim=True)
+    E = torch.exp(S - m)
+    Z = E.sum(dim=-1, keepdim=True)
+    return E / Z, (m + torch.log(Z))[..., 0]
+
+
+def fwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, row_block: int = 256):
+    """O [Hq, C, D] and LSE [Hq, C] in float64.
+
+    sel: None for dense, else one list of selected logical pages per KV head.
+    For q head h (KV head g = h // G) and query i at p = t0 + i, over the visible
+    keys t: s_t = scale * q.k_t, LSE = log sum_t exp(s_t), P_t = exp(s_t - LSE),
+    O = sum_t P_t v_t."""
+    hq, C, D = q.shape
+    hkv = table.shape[0]
+    G = hq // hkv
+    P = k_pool.shape[1]
+    O = torch.zeros(hq, C, D, dtype=torch.float64)
+    L = torch.zeros(hq, C, dtype=torch.float64)
+    qpos_all = t0 + torch.arange(C)
+    for g in range(hkv):
+        pages = attended_pages(t0, C, P, None if sel is None else sel[g])
+        pos, K, V = _keys(k_pool, v_pool, table, g, pages, P, t0 + C)
+        Qg = q[g * G:(g + 1) * G].to(torch.float64)
+        for i0, i1 in _rows(C, row_block):
+            Pm, lse = _probs(Qg[:, i0:i1], K, pos, qpos_all[i0:i1], scale)
+            O[g * G:(g + 1) * G, i0:i1] = torch.matmul(Pm, V)
+            L[g * G:(g + 1) * G, i0:i1] = lse
+    return O, L
+
+
+def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
+        dk_pool=None, dv_pool=None, gtable=None, row_block: int = 256):
+    """Analytic backward of fwd for the loss sum(dout * O), with O and LSE recomputed
+    here (explainer 2.A: activations are recomputed just before the gradient).
+
+    Returns dQ [Hq, C, D] float64. With dk_pool/dv_pool (float64 [Ng, P, D]) and
+    gtable, adds dK/dV of every attended key into its gradient page (explainer 2.B:
+    gradients accumulate in place in paged storage). Also returns the per-head
+    key-gradient arrays as a list of (positions, dK, dV).
+        Delta_i = dO_i . O_i
+        dP_it   = dO_i . v_t
+        dS_it   = P_it (dP_it - Delta_i)
+        dQ_i    = scale * sum_t dS_it k_t
+        dK_t    = scale * sum_{h in group, i} dS_it q_i
+        dV_t    = sum_{h in group, i} P_it dO_i
+    """
+    hq, C, D = q.shape
+    hkv = table.shape[0]
+    G = hq // hkv
+    P = k_pool.shape[1]
+    dQ = torch.zeros(hq, C, D, dtype=torch.float64)
+    per_head = []
+    qpos_all = t0 + torch.arange(C)
+    for g in range(hkv):
+        pages = attended_pages(t0, C, P, None if sel is None else sel[g])
+        pos, K, V = _keys(k_pool, v_pool, table, g, pages, P, t0 + C)
+        Qg = q[g * G:(g + 1) * G].to(torch.float64)
+        dOg = dout[g * G:(g + 1) * G].to(torch.float64)
+        dK = torch.zeros_like(K)
+        dV = torch.zeros_like(V)
+        for i0, i1 in _rows(C, row_block):
+            Qb, dOb = Qg[:, i0:i1], dOg[:, i0:i1]
+            Pm, _ = _probs(Qb, K, pos, qpos_all[i0:i1], scale)
+            Ob = torch.matmul(Pm, V)
+            delta = (dOb * Ob).sum(dim=-1, keepdim=True)
+            dP = torch.matmul(dOb, V.T)
+            dS = Pm * (dP - delta)
+            dQ[g * G:(g + 1) * G, i0:i1] = scale * torch.matmul(dS, K)
+            dK += scale * torch.einsum("hik,hid->kd", dS, Qb)
+            dV += torch.einsum("hik,hid->kd", Pm, dOb)
+        per_head.append((pos, dK, dV))
+        if dk_pool is not None:
+            phys = gtable[g].long()[pos // P]
+            dk_pool.index_put_((phys, pos % P), dK, accumulate=True)
+            dv_pool.index_put_((phys, pos % P), dV, accumulate=True)
+    return dQ, per_head
+
+
+def sweep(q_all, k_all, v_all, do_all, table, gtable, n_pool: int, page: int, chunk: int,
+          scale: float, top_k: Optional[int] = None):
+    """Chunk-recurrent pass over a whole sequence (explainer 2.A).
+
+    Forward, chunk c = 0..S-1: append chunk c's K/V into the pool, summarize its
+    pages, select pages (when top_k is set), attend. Reverse, c = S-1..0: recompute
+    chunk c's attention with the selection made in the forward pass, then its
+    backward; dQ is per chunk and dK/dV accumulate across chunks in the paged
+    float64 gradient pools. Returns O, LSE, dQ over the whole sequence, the gradient
+    pools and the selections."""
+    hq, T, D = q_all.shape
+    hkv = k_all.shape[0]
+    G = hq // hkv
+    S = T // chunk
+    k_pool = torch.zeros(n_pool, page, D, dtype=k_all.dtype)
+    v_pool = torch.zeros(n_pool, page, D, dtype=v_all.dtype)
+    summary = torch.zeros(n_pool, 2, D, dtype=k_all.dtype)
+    dk_pool = torch.zeros(n_pool, page, D, dtype=torch.float64)
+    dv_pool = torch.zeros(n_pool, page, D, dtype=torch.float64)
+    O = torch.zeros(hq, T, D, dtype=torch.float64)
+    L = torch.zeros(hq, T, dtype=torch.float64)
+    dQ = torch.zeros(hq, T, D, dtype=torch.float64)
+    sels = []
+    for c in range(S):
+        t0 = c * chunk
+        sl = slice(t0, t0 + chunk)
+        append(k_pool, table, k_all[:, sl], t0)
+        append(v_pool, table, v_all[:, sl], t0)
+        first = t0 // page
+        summarize(k_pool, table, summary, first, (t0 + chunk - 1) // page - first + 1, t0 + chunk)
+        sel = None
+        if top_k is not None:
+            sel = [s for (_, _, s) in select_pages(q_all[:, sl], summary, table, t0, page, G, top_k)]
+        sels.append(sel)
+        O[:, sl], L[:, sl] = fwd(q_all[:, sl], k_pool, v_pool, table, t0, sel, scale)
+    for c in reversed(range(S)):
+        t0 = c * chunk
+        sl = slice(t0, t0 + chunk)
+        dQ[:, sl], _ = bwd(q_all[:, sl], k_pool, v_pool, table, t0, sels[c], scale,
+                           do_all[:, sl], dk_pool, dv_pool, gtable)
+    return {"O": O, "LSE": L, "dQ": dQ, "dk_pool": dk_pool, "dv_pool": dv_pool,
+            "sels": sels, "k_pool": k_pool, "v_pool": v_pool, "summary": summary}

@@ -1,0 +1,488 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test states the fact it checks: a library routine computing the same quantity
+by another route (torch SDPA with autograd, torch.amin/amax), finite differences,
+closed forms, hand-derived fp32 values (tests/golden/), brute-force order
+statistics, and invariances the definition implies.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as orc
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F64 = torch.float64
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def _rand(shape, seed, dtype=F64):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def _build(k, v, P, table, n_pool):
+    """Pool holding tokens [0, T) of k/v [hkv, T, D] at the given table."""
+    hkv, T, D = k.shape
+    kp = torch.full((n_pool, P, D), float("nan"), dtype=k.dtype)
+    vp = torch.full((n_pool, P, D), float("nan"), dtype=v.dtype)
+    orc.append(kp, table, k, 0)
+    orc.append(vp, table, v, 0)
+    return kp, vp
+
+
+def _table(hkv, n_pages, seed):
+    return torch.randperm(hkv * n_pages, generator=torch.Generator().manual_seed(seed)) \
+        .to(torch.int32).reshape(hkv, n_pages)
+
+
+def _sdpa(q, k, v, t0, pages_per_head, P, scale):
+    """torch SDPA in fp64 with GQA and an explicit boolean mask: query i (position
+    t0+i) of q head h sees key t iff page(t) is attended by head h // G and t <= t0+i.
+    Returns O, and grads wrt q, k, v of sum(dO * O) via autograd (dO passed later)."""
+    hq, C, D = q.shape
+    hkv, T, _ = k.shape
+    G = hq // hkv
+    mask = torch.zeros(hq, C, T, dtype=torch.bool)
+    qpos = t0 + torch.arange(C)
+    kpos = torch.arange(T)
+    for h in range(hq):
+        allowed = torch.zeros(T, dtype=torch.bool)
+        for j in pages_per_head[h // G]:
+            allowed[j * P:(j + 1) * P] = True
+        mask[h] = allowed[None, :] & (kpos[None, :] <= qpos[:, None])
+    return F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=mask[None],
+                                          scale=scale, enable_gqa=True)[0]
+
+
+# ----------------------------------------------------------------------------- paging
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_append_gather_roundtrip_bitwise(dtype):
+    """Appending in unaligned pieces then gathering returns the input bit for bit,
+    and every slot outside the written tokens keeps its sentinel."""
+    hkv, T, D, P = 2, 100, 8, 16
+    n_pages = -(-T // P)
+    table = _table(hkv, n_pages, 3)
+    n_pool = hkv * n_pages + 5
+    k = _rand((hkv, T, D), 1, dtype)
+    pool = torch.full((n_pool, P, D), 7.25, dtype=dtype)
+    for a, b in [(0, 13), (13, 16), (16, 70), (70, 100)]:
+        orc.append(pool, table, k[:, a:b], a)
+    for g in range(hkv):
+        back = orc.gather(pool, table, g, range(n_pages))[:T]
+        assert torch.equal(back.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                           k[g].view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+    written = torch.zeros(n_pool, P, dtype=torch.bool)
+    for g in range(hkv):
+        t = torch.arange(T)
+        written[table[g].long()[t // P], t % P] = True
+    assert bool((pool[~written] == 7.25).all())
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_summarize_equals_amin_amax(dtype):
+    """Summary values equal torch.amin/amax over each page's valid tokens (a partial
+    last page included); pages past seq_len are untouched."""
+    hkv, T, D, P = 2, 75, 16, 16
+    n_pages = 6
+    table = _table(hkv, n_pages, 4)
+    k = _rand((hkv, T, D), 2, dtype)
+    pool = torch.zeros(hkv * n_pages, P, D, dtype=dtype)
+    orc.append(pool, table, k, 0)
+    summ = torch.full((hkv * n_pages, 2, D), 99.0, dtype=dtype)
+    orc.summarize(pool, table, summ, 0, n_pages, T)
+    for g in range(hkv):
+        for j in range(n_pages):
+            phys = int(table[g, j])
+            tok = k[g, j * P:min(T, (j + 1) * P)]
+            if len(tok) == 0:
+                assert bool((summ[phys] == 99.0).all())
+                continue
+            assert torch.equal(summ[phys, 0], tok.amin(0))
+            assert torch.equal(summ[phys, 1], tok.amax(0))
+
+
+def test_summarize_signed_zero_rule():
+    """min/max follow the total order with -0 < +0, independent of token order."""
+    P, D = 4, 2
+    for order in ([0.0, -0.0, 1.0, -1.0], [-0.0, 0.0, -1.0, 1.0]):
+        page = torch.tensor(order, dtype=torch.float32)[:, None].repeat(1, D)
+        page[:, 1] = torch.tensor([0.0, -0.0, 0.0, -0.0]) if order[0] == 0.0 else \
+            torch.tensor([-0.0, 0.0, -0.0, 0.0])
+        pool = page[None].clone()
+        table = torch.zeros(1, 1, dtype=torch.int32)
+        summ = torch.zeros(1, 2, D)
+        orc.summarize(pool, table, summ, 0, 1, P)
+        assert summ[0, 0, 0].item() == -1.0 and summ[0, 1, 0].item() == 1.0
+        assert math.copysign(1.0, summ[0, 0, 1].item()) == -1.0   # min of {+0,-0} is -0
+        assert math.copysign(1.0, summ[0, 1, 1].item()) == 1.0    # max is +0
+
+
+# ----------------------------------------------------------------------------- selection
+
+def _parse_golden(name):
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        key, *vals = line.split()
+        if key == "case":
+            cur = {}
+            cases.append(cur)
+        else:
+            cur[key] = vals
+    return cases
+
+
+def _sparse_col(spec, n):
+    x = np.zeros(n, np.float32)
+    for item in spec:
+        idx, val = item.split(":")
+        if "-" in idx:
+            a, b = map(int, idx.split("-"))
+            x[a:b + 1] = float(val)
+        else:
+            x[int(idx)] = float(val)
+    return x
+
+
+def test_query_summary_golden_order():
+    """Hand-derived fp32 results that pin the blocked sequential order, the
+    stride-halving tree over block sums, and head-major row order."""
+    cases = _parse_golden("qbar_order.txt")
+    a = cases[0]
+    G, C, D = int(a["G"][0]), int(a["C"][0]), int(a["D"][0])
+    q = torch.zeros(G, C, D)
+    q[0, :, 0] = torch.from_numpy(_sparse_col(a["col0"], C))
+    q[0, :, 1] = torch.from_numpy(_sparse_col(a["col1"], C))
+    got = orc.query_summary(q, 0, G)
+    assert got.tolist() == [float(x) for x in a["expect"]]
+    b = cases[1]
+    G, C, D = int(b["G"][0]), int(b["C"][0]), int(b["D"][0])
+    q = torch.zeros(G, C, D)
+    q[0, :, 0] = torch.from_numpy(_sparse_col(b["head0"], C))
+    q[1, :, 0] = torch.from_numpy(_sparse_col(b["head1"], C))
+    assert orc.query_summary(q, 0, G).tolist() == [float(x) for x in b["expect"]]
+
+
+def test_query_summary_close_to_exact_mean():
+    """qbar is the group mean: within the fp32 error bound of a blocked sum
+    (<= (64 + log2 nb + 1) * eps * sum|x|) of the fp64 mean."""
+    G, C, D = 7, 300, 16
+    q = _rand((14, C, D), 5, torch.bfloat16)
+    for g in range(2):
+        x = q[g * G:(g + 1) * G].to(F64).reshape(-1, D)
+        exact = x.mean(0).numpy()
+        bound = (64 + 4 + 2) * 2.0 ** -24 * x.abs().sum(0).numpy() / (G * C) + 1e-30
+        assert np.all(np.abs(orc.query_summary(q, g, G) - exact) <= bound)
+
+
+def test_page_score_golden():
+    """Hand-derived fp32 scores pin the stride-halving tree over d and the max rule."""
+    for case in _parse_golden("score_order.txt"):
+        qbar = np.array([float(x) for x in case["qbar"]], np.float32)
+        kmin = torch.tensor([float(x) for x in case["kmin"]])
+        kmax = torch.tensor([float(x) for x in case["kmax"]])
+        summ = torch.stack([kmin, kmax])[None]
+        table = torch.zeros(1, 1, dtype=torch.int32)
+        assert orc.page_scores(qbar, summ, table, 0, 1).tolist() == [float(case["expect"][0])]
+
+
+def test_page_score_constant_keys_closed_form():
+    """Pages whose keys are c_j * e_0 score exactly qbar_0 * c_j."""
+    D = 8
+    qbar = np.zeros(D, np.float32)
+    qbar[0] = np.float32(0.75)
+    cs = [0.5, -2.0, 3.0, 1.25, -0.125]
+    summ = torch.zeros(len(cs), 2, D)
+    for j, c in enumerate(cs):
+        summ[j, :, 0] = c
+    table = torch.arange(len(cs), dtype=torch.int32)[None]
+    got = orc.page_scores(qbar, summ, table, 0, len(cs))
+    assert got.tolist() == [np.float32(0.75) * np.float32(c) for c in cs]
+
+
+def test_page_score_upper_bounds_every_key():
+    """Quest's property: sum_d max(q kmax, q kmin) >= q.k for every key of the page."""
+    P, D = 16, 32
+    k = _rand((1, 10 * P, D), 6, torch.bfloat16)
+    table = torch.arange(10, dtype=torch.int32)[None]
+    pool = k.reshape(10, P, D).clone()
+    summ = torch.zeros(10, 2, D, dtype=torch.bfloat16)
+    orc.summarize(pool, table, summ, 0, 10, 10 * P)
+    qbar = _rand((D,), 7, torch.float32).numpy()
+    sc = orc.page_scores(qbar, summ, table, 0, 10).astype(np.float64)
+    dots = (pool.to(F64) @ torch.from_numpy(qbar).to(F64)).numpy()   # [10, P]
+    assert np.all(sc + 1e-4 >= dots.max(axis=1))
+
+
+def _brute_topk(scores, k):
+    """Page j is chosen iff fewer than k pages beat it (higher score, or equal score
+    and lower id). Independent of any sort."""
+    n = len(scores)
+    out = []
+    for j in range(n):
+        better = sum(1 for i in range(n)
+                     if scores[i] > scores[j] or (scores[i] == scores[j] and i < j))
+        if better < k:
+            out.append(j)
+    return out
+
+
+def test_top_k_matches_brute_force_with_ties():
+    rng = np.random.default_rng(0)
+    for trial in range(30):
+        n = int(rng.integers(0, 60))
+        scores = rng.integers(-3, 4, size=n).astype(np.float32) * np.float32(0.5)
+        if n and trial % 3 == 0:
+            scores[rng.integers(0, n)] = -0.0
+        for k in (0, 1, 5, n, n + 3):
+            assert orc.top_k_pages(scores, k) == _brute_topk(list(scores), k)
+
+
+def test_top_k_special_cases():
+    s = np.zeros(10, np.float32)
+    assert orc.top_k_pages(s, 4) == [0, 1, 2, 3]            # all equal -> lowest ids
+    assert orc.top_k_pages(s, 99) == list(range(10))        # k >= n -> all
+    assert orc.top_k_pages(s, 0) == []
+    s2 = np.array([0.0, -0.0, 0.0], np.float32)             # -0 == +0
+    assert orc.top_k_pages(s2, 2) == [0, 1]
+
+
+def test_selection_invariant_under_page_permutation():
+    """The logical selection does not depend on where pages sit physically."""
+    w = wl.custom("sparse1m", hq=4, hkv=2, d=64, page=16, chunk=64, total=64 + 40 * 16,
+                  top_k=7, needles=3)
+    x = wl.make_inputs(w, with_grad=False)
+    res = []
+    for seed in (11, 12):
+        table = _table(w.hkv, w.pages_per_head, seed)
+        pool = torch.zeros(w.pool_pages, w.page, w.d, dtype=w.dtype)
+        orc.append(pool, table, x["k"], 0)
+        summ = torch.zeros(w.pool_pages, 2, w.d, dtype=w.dtype)
+        orc.summarize(pool, table, summ, 0, w.pages_per_head, w.total)
+        res.append(orc.select_pages(x["q"], summ, table, w.t0, w.page, w.group, w.top_k))
+    for (qa, sa, la), (qb, sb, lb) in zip(*res):
+        assert np.array_equal(qa, qb) and np.array_equal(sa, sb) and la == lb
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _case(hq=4, hkv=2, C=24, D=8, P=8, t0=37, seed=0, dtype=F64):
+    T = t0 + C
+    n_pages = -(-T // P)
+    q = _rand((hq, C, D), seed + 1, dtype)
+    k = _rand((hkv, T, D), seed + 2, dtype)
+    v = _rand((hkv, T, D), seed + 3, dtype)
+    do = _rand((hq, C, D), seed + 4, dtype)
+    table = _table(hkv, n_pages, seed + 5)
+    kp, vp = _build(k, v, P, table, hkv * n_pages)
+    return dict(q=q, k=k, v=v, do=do, table=table, kp=kp, vp=vp, P=P, t0=t0, T=T,
+                n_pages=n_pages)
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_fwd_bwd_match_sdpa_autograd(sparse):
+    """One chunk call equals torch SDPA (fp64, GQA, explicit mask) and its autograd
+    gradients, for dense and sparse page sets and an unaligned chunk start."""
+    c = _case()
+    P, t0 = c["P"], c["t0"]
+    hkv = c["table"].shape[0]
+    n_prior = t0 // P
+    sel = None if not sparse else [[0, 2], [1, 3]]
+    scale = 0.3
+    O, L = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], t0, sel, scale)
+    pages = [orc.attended_pages(t0, c["q"].shape[1], P, None if sel is None else sel[g])
+             for g in range(hkv)]
+    q = c["q"].clone().requires_grad_()
+    k = c["k"].clone().requires_grad_()
+    v = c["v"].clone().requires_grad_()
+    ref = _sdpa(q, k, v, t0, pages, P, scale)
+    (ref * c["do"]).sum().backward()
+    assert torch.allclose(O, ref.detach(), atol=1e-13, rtol=0)
+    gpool_k = torch.zeros(c["kp"].shape, dtype=F64)
+    gpool_v = torch.zeros(c["vp"].shape, dtype=F64)
+    gtable = _table(hkv, c["n_pages"], 99)
+    dQ, _ = orc.bwd(c["q"], c["kp"], c["vp"], c["table"], t0, sel, scale, c["do"],
+                    gpool_k, gpool_v, gtable)
+    assert torch.allclose(dQ, q.grad, atol=1e-12, rtol=0)
+    for g in range(hkv):
+        dk = orc.gather(gpool_k, gtable, g, range(c["n_pages"]))[:c["T"]]
+        dv = orc.gather(gpool_v, gtable, g, range(c["n_pages"]))[:c["T"]]
+        assert torch.allclose(dk, k.grad[g], atol=1e-12, rtol=0)
+        assert torch.allclose(dv, v.grad[g], atol=1e-12, rtol=0)
+    assert n_prior > 2
+
+
+def test_lse_matches_logsumexp():
+    c = _case(seed=3)
+    scale = 0.4
+    O, L = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], c["t0"], None, scale)
+    hq, C, _ = c["q"].shape
+    G = hq // c["k"].shape[0]
+    for h in range(hq):
+        for i in (0, 5, C - 1):
+            s = scale * (c["k"][h // G, :c["t0"] + i + 1] @ c["q"][h, i])
+            assert abs(L[h, i].item() - torch.logsumexp(s, 0).item()) < 1e-12
+
+
+def test_finite_differences():
+    """Central differences of L = sum(dO * O) agree with the analytic dQ, dK, dV."""
+    c = _case(hq=2, hkv=1, C=6, D=4, P=4, t0=9, seed=7)
+    P, t0, scale = c["P"], c["t0"], 0.7
+    sel = [[0, 1]]
+    table = c["table"]
+
+    def loss(q, kp, vp):
+        O, _ = orc.fwd(q, kp, vp, table, t0, sel, scale)
+        return float((O * c["do"]).sum())
+
+    gk = torch.zeros(c["kp"].shape, dtype=F64)
+    gv = torch.zeros(c["vp"].shape, dtype=F64)
+    dQ, _ = orc.bwd(c["q"], c["kp"], c["vp"], table, t0, sel, scale, c["do"], gk, gv, table)
+    h = 1e-6
+    rng = np.random.default_rng(1)
+    for _ in range(12):
+        idx = tuple(int(rng.integers(0, s)) for s in c["q"].shape)
+        qp, qm = c["q"].clone(), c["q"].clone()
+        qp[idx] += h
+        qm[idx] -= h
+        fd = (loss(qp, c["kp"], c["vp"]) - loss(qm, c["kp"], c["vp"])) / (2 * h)
+        assert abs(fd - dQ[idx].item()) < 1e-7
+    attended = orc.key_positions(orc.attended_pages(t0, 6, P, sel[0]), P, t0 + 6)
+    for t in attended.tolist()[::2]:
+        phys, slot = int(table[0, t // P]), t % P
+        for d in range(4):
+            for pool, grad in ((c["kp"], gk), (c["vp"], gv)):
+                p_, m_ = pool.clone(), pool.clone()
+                p_[phys, slot, d] += h
+                m_[phys, slot, d] -= h
+                if pool is c["kp"]:
+                    fd = (loss(c["q"], p_, c["vp"]) - loss(c["q"], m_, c["vp"])) / (2 * h)
+                else:
+                    fd = (loss(c["q"], c["kp"], p_) - loss(c["q"], c["kp"], m_)) / (2 * h)
+                assert abs(fd - grad[phys, slot, d].item()) < 1e-7
+
+
+def test_closed_forms():
+    """Single visible key: O = v0, LSE = s0, dQ = 0, dV += dO. All-zero keys: O is
+    the prefix mean of V. Per KV head: sum_t dK_t = 0 and sum_t dV_t = sum dO."""
+    hq, hkv, D, P = 2, 1, 4, 4
+    q = _rand((hq, 3, D), 1)
+    k = _rand((hkv, 3, D), 2)
+    v = _rand((hkv, 3, D), 3)
+    do = _rand((hq, 3, D), 4)
+    table = torch.zeros(1, 1, dtype=torch.int32)
+    kp, vp = _build(k, v, P, table, 1)
+    O, L = orc.fwd(q, kp, vp, table, 0, None, 0.5)
+    for h in range(hq):
+        assert torch.allclose(O[h, 0], v[0, 0], atol=1e-15)
+        assert abs(L[h, 0].item() - 0.5 * float(q[h, 0] @ k[0, 0])) < 1e-15
+    gk = torch.zeros(1, P, D, dtype=F64)
+    gv = torch.zeros(1, P, D, dtype=F64)
+    dQ, _ = orc.bwd(q[:, :1], kp, vp, table, 0, None, 0.5, do[:, :1], gk, gv, table)
+    assert torch.allclose(dQ, torch.zeros_like(dQ), atol=1e-15)
+    assert torch.allclose(gv[0, 0], do[:, 0].sum(0), atol=1e-15)
+
+    c = _case(seed=11)
+    kz = torch.zeros_like(c["kp"])
+    O, _ = orc.fwd(c["q"], kz, c["vp"], c["table"], c["t0"], None, 1.0)
+    G = c["q"].shape[0] // c["k"].shape[0]
+    for h in range(c["q"].shape[0]):
+        for i in range(c["q"].shape[1]):
+            m = c["v"][h // G, :c["t0"] + i + 1].mean(0)
+            assert torch.allclose(O[h, i], m, atol=1e-13)
+
+    c = _case(seed=12)
+    _, per_head = orc.bwd(c["q"], c["kp"], c["vp"], c["table"], c["t0"], [[1, 3], [0]], 0.35,
+                          c["do"])
+    for g, (pos, dK, dV) in enumerate(per_head):
+        assert torch.allclose(dK.sum(0), torch.zeros(dK.shape[1], dtype=F64), atol=1e-12)
+        G = c["q"].shape[0] // c["k"].shape[0]
+        assert torch.allclose(dV.sum(0), c["do"][g * G:(g + 1) * G].sum((0, 1)), atol=1e-12)
+
+
+def test_page_permutation_invariance_bitwise():
+    """O, LSE and dQ are bit-identical under two physical placements; gradient pools
+    agree after mapping pages back."""
+    c = _case(seed=21)
+    res = []
+    for seed in (1, 2):
+        table = _table(2, c["n_pages"], seed)
+        kp, vp = _build(c["k"], c["v"], c["P"], table, 2 * c["n_pages"])
+        gk = torch.zeros(kp.shape, dtype=F64)
+        gv = torch.zeros(kp.shape, dtype=F64)
+        O, L = orc.fwd(c["q"], kp, vp, table, c["t0"], [[0, 3], [2]], 0.4)
+        dQ, _ = orc.bwd(c["q"], kp, vp, table, c["t0"], [[0, 3], [2]], 0.4, c["do"], gk, gv,
+                        table)
+        dk = torch.stack([orc.gather(gk, table, g, range(c["n_pages"])) for g in range(2)])
+        res.append((O, L, dQ, dk))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
+def test_sparse_with_all_pages_equals_dense_bitwise():
+    c = _case(seed=31)
+    n_prior = c["t0"] // c["P"]
+    everything = [list(range(n_prior))] * 2
+    a = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], c["t0"], None, 0.3)
+    b = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], c["t0"], everything, 0.3)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_sweep_equals_full_sequence_causal_attention():
+    """Chunk-recurrent forward + reverse recompute/backward over the tiny workload
+    (1024 fp32 tokens, 16 chunks of 64, shuffled pages) equals full-sequence causal
+    SDPA and its autograd gradients (explainer 2.A: chunking with recomputation
+    computes the same result as ordinary training)."""
+    w = wl.WORKLOADS["tiny"]
+    x = wl.make_inputs(w)
+    r = orc.sweep(x["q"], x["k"], x["v"], x["do"], x["table"], x["gtable"], w.pool_pages,
+                  w.page, w.chunk, w.scale)
+    q = x["q"].to(F64).requires_grad_()
+    k = x["k"].to(F64).requires_grad_()
+    v = x["v"].to(F64).requires_grad_()
+    ref = F.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True,
+                                         scale=w.scale, enable_gqa=True)[0]
+    (ref * x["do"].to(F64)).sum().backward()
+    assert torch.allclose(r["O"], ref.detach(), atol=1e-12, rtol=0)
+    assert torch.allclose(r["dQ"], q.grad, atol=1e-12, rtol=0)
+    for g in range(w.hkv):
+        dk = orc.gather(r["dk_pool"], x["gtable"], g, range(w.pages_per_head))
+        dv = orc.gather(r["dv_pool"], x["gtable"], g, range(w.pages_per_head))
+        assert torch.allclose(dk, k.grad[g], atol=1e-12, rtol=0)
+        assert torch.allclose(dv, v.grad[g], atol=1e-12, rtol=0)
+
+
+def test_sparse_sweep_selects_and_matches_masked_sdpa():
+    """A top-k sweep: every chunk's O and the accumulated dK/dV equal SDPA with the
+    page mask implied by the sweep's own selections."""
+    w = wl.custom("sweep256k_top64", hq=4, hkv=2, d=16, page=8, chunk=32, total=160, top_k=3)
+    x = wl.make_inputs(w)
+    r = orc.sweep(x["q"], x["k"], x["v"], x["do"], x["table"], x["gtable"], w.pool_pages,
+                  w.page, w.chunk, w.scale, top_k=w.top_k)
+    q = x["q"].to(F64).requires_grad_()
+    k = x["k"].to(F64).requires_grad_()
+    v = x["v"].to(F64).requires_grad_()
+    outs = []
+    for c in range(w.n_chunks):
+        t0 = c * w.chunk
+        pages = [orc.attended_pages(t0, w.chunk, w.page, r["sels"][c][g]) for g in range(w.hkv)]
+        for g in range(w.hkv):
+            assert len(r["sels"][c][g]) == min(w.top_k, t0 // w.page)
+        outs.append(_sdpa(q[:, t0:t0 + w.chunk], k, v, t0, pages, w.page, w.scale))
+    ref = torch.cat(outs, dim=1)
+    (ref * x["do"].to(F64)).sum().backward()
+    assert torch.allclose(r["O"], ref.detach(), atol=1e-12, rtol=0)
+    assert torch.allclose(r["dQ"], q.grad, atol=1e-12, rtol=0)
+    for g in range(w.hkv):
+        dk = orc.gather(r["dk_pool"], x["gtable"], g, range(w.pages_per_head))
+        assert torch.allclose(dk, k.grad[g], atol=1e-12, rtol=0)
