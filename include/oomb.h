@@ -1,0 +1,190 @@
+/*
+ * oomb.h - C ABI of the paged chunk-attention library (MI355X / gfx950).
+ *
+ * The library computes the per-chunk attention step of OOMB's chunk-recurrent
+ * long-context training (arXiv 2602.02108): one chunk of queries attends, causally,
+ * to a key/value cache kept in fixed-size pages; the backward pass recomputes the
+ * attention probabilities and adds the key/value gradients, in place, into a paged
+ * gradient pool; optionally only the top-k most relevant prior pages are attended.
+ *   - chunking and recomputation: gist.science explainer of the paper, 2.A
+ *     "Chunk-Recurrent Training with Activation Recomputation";
+ *   - paged K/V and paged K/V gradients, in-place accumulation, no autograd:
+ *     explainer 2.B "Paged KV Cache and Gradient Management"; the mlsanity page's
+ *     abstract ("a paged memory manager for both the KV cache and its gradients");
+ *   - top-k page retrieval: explainer 2.D "Page-Level Sparse Attention".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every buffer argument is a DEVICE pointer owned by the caller. The library never
+ *    allocates, frees or synchronises; every call only enqueues kernels on `stream`
+ *    (a hipStream_t passed as void*, NULL = the default stream) and returns.
+ *  - Return value: OOMB_OK, or an error code. On an error no kernel was launched,
+ *    except OOMB_ERR_HIP, which reports a failed launch (hipGetLastError). A short
+ *    description of the last error of the calling thread: oomb_last_error().
+ *  - Calls are stateless and reentrant. Two calls that write the same memory race
+ *    unless they are ordered (same stream, or events).
+ *  - Element strides are counted in elements of the tensor's dtype. The last
+ *    dimension (head_dim) is always contiguous. Q/O/dO/dQ are viewed as
+ *    [head][token][head_dim] with (head_stride, tok_stride), which accepts both
+ *    [H, C, D] and [C, H, D] storage. For bf16 tensors, pointers must be 16-byte
+ *    aligned and strides multiples of 8; for fp32, 16-byte aligned and multiples of 4.
+ *  - Token positions are absolute positions in the sequence. Token t of KV head g
+ *    lives in logical page t / P, slot t % P, i.e. physical page table[g][t / P].
+ *  - Page-table CONTENTS are not read on the host. Kernels skip (never touch) a row
+ *    whose physical id is outside [0, num_pages) or whose selected logical id is
+ *    outside the candidate range, so a bad table gives wrong results, not a fault.
+ *    A well-formed table is injective within a call: no physical page appears twice.
+ */
+#ifndef OOMB_H
+#define OOMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  OOMB_OK = 0,
+  OOMB_ERR_INVALID = 1,      /* bad argument: null pointer, bad size, stride or alignment */
+  OOMB_ERR_UNSUPPORTED = 2,  /* dtype / head_dim / page_size combination not built */
+  OOMB_ERR_HIP = 3,          /* a kernel launch failed */
+  OOMB_ERR_WORKSPACE = 4     /* workspace missing or smaller than the query function says */
+};
+
+enum { OOMB_DTYPE_BF16 = 0, OOMB_DTYPE_FP32 = 1 };
+
+/* One layer's paged storage (host-side descriptor; the arrays are device memory).
+ *   k_pool, v_pool : [num_pages, page_size, head_dim]       in `dtype`
+ *   k_summary      : [num_pages, 2, head_dim]                in `dtype`
+ *                    row 0 = per-dimension minimum of the page's keys, row 1 = maximum
+ *                    (needed by oomb_page_summarize and oomb_select_pages only)
+ *   dk_pool,dv_pool: [num_grad_pages, page_size, head_dim]  fp32
+ *                    (needed by oomb_paged_chunk_attn_bwd only)
+ * Supported: dtype BF16 or FP32; head_dim 64 or 128; page_size a power of two in
+ * [16, 256]. The matrix-core kernels serve bf16 with head_dim 128; every other
+ * supported combination runs on the scalar kernels. */
+typedef struct oomb_pool {
+  int32_t dtype;
+  int32_t page_size;
+  int32_t head_dim;
+  int32_t num_q_heads;     /* Hq, a multiple of num_kv_heads (grouped-query attention) */
+  int32_t num_kv_heads;    /* Hkv; query head h reads KV head h / (Hq / Hkv) */
+  int32_t reserved;        /* must be 0 */
+  int64_t num_pages;
+  int64_t num_grad_pages;
+  void* k_pool;
+  void* v_pool;
+  void* k_summary;
+  float* dk_pool;
+  float* dv_pool;
+} oomb_pool;
+
+const char* oomb_status_string(int status);
+/* Description of the last error returned on the calling thread ("" if none). */
+const char* oomb_last_error(void);
+/* ABI version: bumped whenever a signature or a layout changes. */
+int oomb_abi_version(void);
+
+/* KV append - write a chunk's keys and values into their pages (explainer 2.B:
+ * the paged cache grows by filling the next page slots, never by reallocation).
+ * For every KV head g and token t in [start_pos, start_pos + n_tok):
+ *   k_pool[table[g*table_stride + t/P]][t%P][:] = k_new[g*head_stride + (t-start_pos)*tok_stride + :]
+ * and the same for V. A bitwise copy; no other slot is touched.
+ * table: int32 [Hkv][table_stride]; (start_pos + n_tok - 1) / P must be < table_stride.
+ * n_tok == 0 is a no-op. */
+int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                   const void* k_new, const void* v_new, int64_t head_stride,
+                   int64_t tok_stride, int32_t n_tok, int64_t start_pos, void* stream);
+
+/* Page summarize - per-page key summary used to rank pages (explainer 2.D retrieves
+ * pages "based on a representative vector"; the min/max form follows Quest, cited
+ * by the paper). For KV head g and logical page j in [first_page, first_page+n_pages):
+ *   k_summary[phys][0][d] = min, k_summary[phys][1][d] = max of K[t][d] over the
+ *   page's tokens t with t < seq_len,
+ * under the total order of values in which -0 < +0 (result independent of the
+ * reduction order). Pages with no token below seq_len are left unchanged.
+ * first_page + n_pages must be <= table_stride. */
+int oomb_page_summarize(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                        int64_t first_page, int64_t n_pages, int64_t seq_len, void* stream);
+
+/* Bytes of device workspace oomb_select_pages needs for n_q queries after t0 prior
+ * tokens (256-byte aligned pointer). */
+size_t oomb_select_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0);
+
+/* Page select - top-k page retrieval (explainer 2.D), one selection per KV head
+ * shared by all its query heads and all n_q queries. In IEEE fp32, no fused
+ * multiply-add, in this fixed order (bit-reproducible):
+ *   1. qbar[d]: the mean of x_m = q[g*G + m/n_q][m%n_q][d], m in [0, G*n_q)
+ *      (G = Hq/Hkv): sequential sums from +0 over blocks of 64 consecutive m, then a
+ *      stride-halving tree over the block sums zero-padded to a power of two, then
+ *      one multiply by fp32(1/(G*n_q)) (reciprocal taken in fp64).
+ *   2. For candidate logical pages j in [0, t0/P) (complete pages before the chunk):
+ *      e[d] = qbar[d]*kmax[d] if that product is greater than qbar[d]*kmin[d],
+ *      else qbar[d]*kmin[d]; score_j = stride-halving tree sum of e over d.
+ *   3. Keep the min(top_k, t0/P) pages with the largest score, ties to the lower
+ *      logical id (-0 and +0 compare equal), written in ascending id order to
+ *      sel[g*sel_stride + 0..count[g]).
+ * The chunk's own pages (including one straddling t0) are never candidates: the
+ * attention calls always add them. q: [Hq][n_q][D] view. sel_stride >=
+ * min(top_k, t0/P). qbar_out ([Hkv][D] fp32) and score_out ([Hkv][score_stride]
+ * fp32, score_stride >= t0/P) are optional diagnostics (NULL to skip).
+ * top_k >= 0; top_k >= t0/P selects every candidate. */
+int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                      const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                      int32_t n_q, int64_t t0, int32_t top_k, int32_t* sel,
+                      int64_t sel_stride, int32_t* count, float* qbar_out,
+                      float* score_out, int64_t score_stride, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Chunk attention forward (explainer 2.A/2.B/2.D). Query i of the chunk sits at
+ * position t0 + i; q head h uses KV head g = h / (Hq/Hkv). It attends to key t iff
+ *   t <= t0 + i  and  page(t) is in  Sel_g U Local,
+ * where Local = [t0/P, (t0+n_q-1)/P] (the chunk's own pages, appended beforehand)
+ * and Sel_g = sel[g*sel_stride + 0..count[g]) (count clamped to [0, sel_stride] and
+ * to t0/P), or every page before t0/P when sel == NULL (dense).
+ *   s_t = scale * q.k_t ;  LSE = ln sum_t exp(s_t) ;  O = sum_t exp(s_t - LSE) v_t
+ * Writes o ([Hq][n_q][D] view, dtype of the pool) and lse (fp32 [Hq][n_q],
+ * contiguous). Keys beyond t0 + n_q are never read into the result. */
+int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table,
+                              int64_t table_stride, const void* q, int64_t q_head_stride,
+                              int64_t q_tok_stride, int32_t n_q, int64_t t0,
+                              const int32_t* sel, int64_t sel_stride, const int32_t* count,
+                              float scale, void* o, int64_t o_head_stride,
+                              int64_t o_tok_stride, float* lse, void* stream);
+
+/* Bytes of device workspace oomb_paged_chunk_attn_bwd needs (256-byte aligned). */
+size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q);
+
+/* Chunk attention backward, with the attention probabilities recomputed from the
+ * saved LSE (explainer 2.A: activations are recomputed just before use) and the
+ * key/value gradients added in place into the paged gradient pool (explainer 2.B:
+ * in-place accumulation without intermediate buffers). Same q / table / sel / count /
+ * scale as the forward call it differentiates; o and lse are that call's outputs.
+ * For the loss sum(dout * O):
+ *   Delta_i = dO_i . O_i ; P_it = exp(s_it - LSE_i) ; dS_it = P_it (dO_i . v_t - Delta_i)
+ *   dq[h][i]  = scale * sum_t dS_it k_t                        (fp32, OVERWRITTEN)
+ *   dk_pool[gtable[g][t/P]][t%P] += scale * sum_{h in g, i} dS_it q_hi   (fp32, ADDED)
+ *   dv_pool[gtable[g][t/P]][t%P] += sum_{h in g, i} P_it dO_hi           (fp32, ADDED)
+ * Every attended key row is owned by exactly one workgroup, so the pool update is a
+ * plain read-modify-write with no races and no atomics; the caller zeroes the
+ * gradient pool when a step starts. gtable: int32 [Hkv][gtable_stride], may alias
+ * table. dq: fp32 [Hq][n_q][D] view. */
+int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table,
+                              int64_t table_stride, const int32_t* gtable,
+                              int64_t gtable_stride, const void* q, int64_t q_head_stride,
+                              int64_t q_tok_stride, int32_t n_q, int64_t t0,
+                              const int32_t* sel, int64_t sel_stride, const int32_t* count,
+                              float scale, const void* o, int64_t o_head_stride,
+                              int64_t o_tok_stride, const void* dout,
+                              int64_t do_head_stride, int64_t do_tok_stride,
+                              const float* lse, float* dq, int64_t dq_head_stride,
+                              int64_t dq_tok_stride, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OOMB_H */

@@ -1,0 +1,19 @@
+"""Paged chunk attention for AMD MI355X (gfx950).
+
+The hot path of OOMB-style chunk-recurrent long-context training as a small HIP
+library (liboomb.so, C ABI in include/oomb.h) plus this thin torch binding:
+KV append into fixed-size pages, per-page key summaries, top-k page selection,
+chunk attention forward, and the recomputing backward that writes dQ and adds
+dK/dV into a paged fp32 gradient pool.
+"""
+from .binding import (  # noqa: F401
+    PagedPool,
+    bwd_workspace_bytes,
+    oomb_kv_append,
+    oomb_page_summarize,
+    oomb_paged_chunk_attn_bwd,
+    oomb_paged_chunk_attn_fwd,
+    oomb_select_pages,
+    select_workspace_bytes,
+)
+from ._lib import LIB_PATH, OombError, lib  # noqa: F401

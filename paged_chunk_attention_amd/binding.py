@@ -1,0 +1,214 @@
+"""Thin Python binding of the C ABI (include/oomb.h), over torch device tensors.
+
+Each function has the C name, checks tensor devices/dtypes/shapes, allocates
+outputs and workspace with torch when the caller passes none, and calls the
+library on torch's current stream. No step of the computation happens here.
+
+`PagedPool` owns one layer's page pool (K, V, key summaries, fp32 dK/dV) as torch
+tensors and describes it to the library. The page tables are plain int32 tensors
+[num_kv_heads, pages_per_head] mapping logical pages to physical ones; the
+gradient table may be the same tensor or a separate one. The cache and its
+gradients are not tracked by autograd: callers invoke forward and backward
+explicitly (gist.science explainer of OOMB, 2.B: the KV cache is decoupled from
+the autograd graph).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import OOMB_DTYPE_BF16, OOMB_DTYPE_FP32, OombPool, call, lib
+
+_DTYPES = {torch.bfloat16: OOMB_DTYPE_BF16, torch.float32: OOMB_DTYPE_FP32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class PagedPool:
+    """K/V page pool of one layer, plus its key summaries and fp32 gradient pool."""
+
+    def __init__(self, num_pages: int, page_size: int, head_dim: int, num_q_heads: int,
+                 num_kv_heads: int, dtype: torch.dtype = torch.bfloat16, device="cuda",
+                 num_grad_pages: Optional[int] = None, with_summary: bool = True,
+                 with_grad: bool = True):
+        if dtype not in _DTYPES:
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.page_size, self.head_dim = page_size, head_dim
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.dtype, self.device = dtype, torch.device(device)
+        self.k = torch.zeros(num_pages, page_size, head_dim, dtype=dtype, device=device)
+        self.device = self.k.device  # concrete index, e.g. cuda:0
+        self.v = torch.zeros_like(self.k)
+        self.summary = (torch.zeros(num_pages, 2, head_dim, dtype=dtype, device=device)
+                        if with_summary else None)
+        ng = num_pages if num_grad_pages is None else num_grad_pages
+        self.dk = torch.zeros(ng, page_size, head_dim, dtype=torch.float32, device=device) \
+            if with_grad else None
+        self.dv = torch.zeros_like(self.dk) if with_grad else None
+        self.desc = OombPool(
+            dtype=_DTYPES[dtype], page_size=page_size, head_dim=head_dim,
+            num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, reserved=0,
+            num_pages=num_pages, num_grad_pages=ng if with_grad else 0,
+            k_pool=self.k.data_ptr(), v_pool=self.v.data_ptr(),
+            k_summary=self.summary.data_ptr() if with_summary else None,
+            dk_pool=self.dk.data_ptr() if with_grad else None,
+            dv_pool=self.dv.data_ptr() if with_grad else None)
+
+    @property
+    def num_pages(self) -> int:
+        return self.k.shape[0]
+
+    def zero_grad(self):
+        if self.dk is not None:
+            self.dk.zero_()
+            self.dv.zero_()
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def _check_table(t: torch.Tensor, pool: PagedPool, name: str):
+    if t.dtype != torch.int32 or t.device != pool.device or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be an int32 [num_kv_heads, pages] tensor on {pool.device}")
+    if t.shape[0] != pool.num_kv_heads:
+        raise ValueError(f"{name} has {t.shape[0]} rows, expected {pool.num_kv_heads}")
+
+
+def _view(x: torch.Tensor, pool: PagedPool, heads: int, name: str, dtype=None):
+    dtype = pool.dtype if dtype is None else dtype
+    if x.dtype != dtype or x.device != pool.device or x.dim() != 3:
+        raise ValueError(f"{name} must be a [heads, tokens, {pool.head_dim}] {dtype} tensor "
+                         f"on {pool.device}")
+    if x.shape[0] != heads or x.shape[2] != pool.head_dim or x.stride(2) != 1:
+        raise ValueError(f"{name} has shape {tuple(x.shape)} / strides {x.stride()}")
+    return x.stride(0), x.stride(1)
+
+
+def oomb_kv_append(pool: PagedPool, table: torch.Tensor, k_new: torch.Tensor,
+                   v_new: torch.Tensor, start_pos: int, stream=None) -> None:
+    """Write tokens [start_pos, start_pos + n) of every KV head into their pages."""
+    _check_table(table, pool, "table")
+    hs, ts = _view(k_new, pool, pool.num_kv_heads, "k_new")
+    if _view(v_new, pool, pool.num_kv_heads, "v_new") != (hs, ts) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must have the same shape and strides")
+    call("oomb_kv_append", pool.ref(), _ptr(table), table.stride(0), _ptr(k_new), _ptr(v_new),
+         hs, ts, k_new.shape[1], start_pos, _stream(stream))
+
+
+def oomb_page_summarize(pool: PagedPool, table: torch.Tensor, first_page: int, n_pages: int,
+                        seq_len: int, stream=None) -> None:
+    """Per-page key min/max for logical pages [first_page, first_page + n_pages)."""
+    _check_table(table, pool, "table")
+    call("oomb_page_summarize", pool.ref(), _ptr(table), table.stride(0), first_page, n_pages,
+         seq_len, _stream(stream))
+
+
+def select_workspace_bytes(pool: PagedPool, n_q: int, t0: int) -> int:
+    return int(lib().oomb_select_workspace_bytes(pool.ref(), n_q, t0))
+
+
+def bwd_workspace_bytes(pool: PagedPool, n_q: int) -> int:
+    return int(lib().oomb_bwd_workspace_bytes(pool.ref(), n_q))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is None:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws.numel() < nbytes or ws.data_ptr() % 256:
+        raise ValueError(f"workspace must hold {nbytes} bytes at a 256-byte aligned address")
+    return ws
+
+
+def oomb_select_pages(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0: int, top_k: int,
+                      sel: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                      qbar_out: Optional[torch.Tensor] = None,
+                      score_out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k prior pages per KV head. Returns (sel int32 [Hkv, k], count int32 [Hkv])."""
+    _check_table(table, pool, "table")
+    hs, ts = _view(q, pool, pool.num_q_heads, "q")
+    n_q = q.shape[1]
+    n_cand = t0 // pool.page_size
+    k = max(0, min(top_k, n_cand))
+    if sel is None:
+        sel = torch.full((pool.num_kv_heads, max(k, 1)), -1, dtype=torch.int32, device=q.device)
+    if count is None:
+        count = torch.zeros(pool.num_kv_heads, dtype=torch.int32, device=q.device)
+    ws = _workspace(select_workspace_bytes(pool, n_q, t0), q.device, workspace)
+    score_stride = 0 if score_out is None else score_out.stride(0)
+    call("oomb_select_pages", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts, n_q, t0,
+         top_k, _ptr(sel), sel.stride(0), _ptr(count), _ptr(qbar_out), _ptr(score_out),
+         score_stride, _ptr(ws), ws.numel(), _stream(stream))
+    return sel, count
+
+
+def oomb_paged_chunk_attn_fwd(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0: int,
+                              sel: Optional[torch.Tensor] = None,
+                              count: Optional[torch.Tensor] = None,
+                              scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None,
+                              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention of the chunk q [Hq, n_q, D] (first query at position t0) over the
+    selected (or all, when sel is None) prior pages and its own pages.
+    Returns (O [Hq, n_q, D] in the pool dtype, LSE fp32 [Hq, n_q])."""
+    _check_table(table, pool, "table")
+    hs, ts = _view(q, pool, pool.num_q_heads, "q")
+    n_q = q.shape[1]
+    if scale is None:
+        scale = pool.head_dim ** -0.5
+    if o is None:
+        o = torch.empty_like(q, memory_format=torch.contiguous_format)
+    ohs, ots = _view(o, pool, pool.num_q_heads, "o")
+    if lse is None:
+        lse = torch.empty(pool.num_q_heads, n_q, dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
+        raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
+    sel_stride = 0 if sel is None else sel.stride(0)
+    call("oomb_paged_chunk_attn_fwd", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts,
+         n_q, t0, _ptr(sel), sel_stride, _ptr(count), float(scale), _ptr(o), ohs, ots, _ptr(lse),
+         _stream(stream))
+    return o, lse
+
+
+def oomb_paged_chunk_attn_bwd(pool: PagedPool, table: torch.Tensor, gtable: torch.Tensor,
+                              q: torch.Tensor, t0: int, sel: Optional[torch.Tensor],
+                              count: Optional[torch.Tensor], o: torch.Tensor, dout: torch.Tensor,
+                              lse: torch.Tensor, scale: Optional[float] = None,
+                              dq: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None,
+                              stream=None) -> torch.Tensor:
+    """Backward of oomb_paged_chunk_attn_fwd: returns dQ (fp32 [Hq, n_q, D]) and adds
+    dK/dV into pool.dk / pool.dv at the pages gtable maps to."""
+    _check_table(table, pool, "table")
+    _check_table(gtable, pool, "gtable")
+    if pool.dk is None:
+        raise ValueError("pool has no gradient storage")
+    hs, ts = _view(q, pool, pool.num_q_heads, "q")
+    n_q = q.shape[1]
+    if scale is None:
+        scale = pool.head_dim ** -0.5
+    ohs, ots = _view(o, pool, pool.num_q_heads, "o")
+    dhs, dts = _view(dout, pool, pool.num_q_heads, "dout")
+    if dq is None:
+        dq = torch.empty(pool.num_q_heads, n_q, pool.head_dim, dtype=torch.float32, device=q.device)
+    qhs, qts = _view(dq, pool, pool.num_q_heads, "dq", torch.float32)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
+        raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
+    ws = _workspace(bwd_workspace_bytes(pool, n_q), q.device, workspace)
+    sel_stride = 0 if sel is None else sel.stride(0)
+    call("oomb_paged_chunk_attn_bwd", pool.ref(), _ptr(table), table.stride(0), _ptr(gtable),
+         gtable.stride(0), _ptr(q), hs, ts, n_q, t0, _ptr(sel), sel_stride, _ptr(count),
+         float(scale), _ptr(o), ohs, ots, _ptr(dout), dhs, dts, _ptr(lse), _ptr(dq), qhs, qts,
+         _ptr(ws), ws.numel(), _stream(stream))
+    return dq

@@ -1,0 +1,370 @@
+// C ABI of the paged chunk-attention library: argument validation, workspace
+// layout and kernel dispatch. Every check runs on the host before any HIP call,
+// so an invalid call returns its status without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+#include "oomb.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return OOMB_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(OOMB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+constexpr int64_t kMaxPos = (int64_t(1) << 31) - 4096;  // positions are 32-bit in kernels
+
+int check_pool(const oomb_pool* p, oomb::PoolView* v, bool need_summary, bool need_grad) {
+  if (p == nullptr) return fail(OOMB_ERR_INVALID, "pool descriptor is NULL");
+  if (p->reserved != 0) return fail(OOMB_ERR_INVALID, "pool.reserved must be 0");
+  if (p->dtype != OOMB_DTYPE_BF16 && p->dtype != OOMB_DTYPE_FP32)
+    return fail(OOMB_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(OOMB_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+  const int P = p->page_size;
+  if (P < 16 || P > 256 || (P & (P - 1)) != 0)
+    return fail(OOMB_ERR_UNSUPPORTED, "page_size %d not supported (power of two in [16, 256])", P);
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads != 0)
+    return fail(OOMB_ERR_INVALID, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads > 4096 || p->num_kv_heads > 4096)
+    return fail(OOMB_ERR_INVALID, "too many heads");
+  if (p->num_pages <= 0 || p->num_pages > (int64_t(1) << 40))
+    return fail(OOMB_ERR_INVALID, "num_pages %lld out of range", (long long)p->num_pages);
+  if (p->k_pool == nullptr || p->v_pool == nullptr)
+    return fail(OOMB_ERR_INVALID, "k_pool / v_pool is NULL");
+  if (!aligned16(p->k_pool) || !aligned16(p->v_pool))
+    return fail(OOMB_ERR_INVALID, "k_pool / v_pool must be 16-byte aligned");
+  if (need_summary && (p->k_summary == nullptr || !aligned16(p->k_summary)))
+    return fail(OOMB_ERR_INVALID, "k_summary must be a 16-byte aligned device pointer");
+  if (need_grad) {
+    if (p->dk_pool == nullptr || p->dv_pool == nullptr)
+      return fail(OOMB_ERR_INVALID, "dk_pool / dv_pool is NULL");
+    if (!aligned16(p->dk_pool) || !aligned16(p->dv_pool))
+      return fail(OOMB_ERR_INVALID, "dk_pool / dv_pool must be 16-byte aligned");
+    if (p->num_grad_pages <= 0)
+      return fail(OOMB_ERR_INVALID, "num_grad_pages must be positive");
+  }
+  v->dtype = p->dtype;
+  v->P = P;
+  v->log2p = ilog2(P);
+  v->D = p->head_dim;
+  v->Hq = p->num_q_heads;
+  v->Hkv = p->num_kv_heads;
+  v->N = p->num_pages;
+  v->Ng = p->num_grad_pages;
+  v->k_pool = p->k_pool;
+  v->v_pool = p->v_pool;
+  v->k_pool_w = p->k_pool;
+  v->v_pool_w = p->v_pool;
+  v->k_summary = p->k_summary;
+  v->dk_pool = p->dk_pool;
+  v->dv_pool = p->dv_pool;
+  return OOMB_OK;
+}
+
+int elem_size(const oomb::PoolView& v) { return v.dtype == OOMB_DTYPE_BF16 ? 2 : 4; }
+
+// A [head][token][D] view: pointer 16-byte aligned, strides non-negative and a
+// whole number of 16-byte units.
+int check_view(const void* ptr, int64_t hs, int64_t ts, int esize, const char* name) {
+  if (ptr == nullptr) return fail(OOMB_ERR_INVALID, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(OOMB_ERR_INVALID, "%s must be 16-byte aligned", name);
+  const int unit = 16 / esize;
+  if (hs < 0 || ts < 0 || hs % unit != 0 || ts % unit != 0)
+    return fail(OOMB_ERR_INVALID, "%s strides (%lld, %lld) must be non-negative multiples of %d",
+                name, (long long)hs, (long long)ts, unit);
+  return OOMB_OK;
+}
+
+int check_table(const int32_t* t, int64_t stride, int64_t pages_needed, const char* name) {
+  if (t == nullptr) return fail(OOMB_ERR_INVALID, "%s is NULL", name);
+  if ((reinterpret_cast<uintptr_t>(t) & 3u) != 0) return fail(OOMB_ERR_INVALID, "%s misaligned", name);
+  if (stride < pages_needed)
+    return fail(OOMB_ERR_INVALID, "%s stride %lld < %lld logical pages needed", name,
+                (long long)stride, (long long)pages_needed);
+  return OOMB_OK;
+}
+
+struct ChunkGeom {
+  int n_cand, first_local, n_local;
+};
+
+int check_chunk(const oomb::PoolView& v, int32_t n_q, int64_t t0, ChunkGeom* cg) {
+  if (n_q <= 0) return fail(OOMB_ERR_INVALID, "n_q must be positive (got %d)", n_q);
+  if (t0 < 0 || t0 + n_q > kMaxPos) return fail(OOMB_ERR_INVALID, "t0 %lld out of range", (long long)t0);
+  if (n_q > (1 << 24)) return fail(OOMB_ERR_INVALID, "n_q %d too large", n_q);
+  cg->n_cand = static_cast<int>(t0 / v.P);
+  cg->first_local = cg->n_cand;
+  cg->n_local = static_cast<int>((t0 + n_q - 1) / v.P) - cg->first_local + 1;
+  return OOMB_OK;
+}
+
+// Shared argument checks of the forward and backward calls.
+int check_attn(const oomb_pool* pool, const int32_t* table, int64_t tstride, const void* q,
+               int64_t q_hs, int64_t q_ts, int32_t n_q, int64_t t0, const int32_t* sel,
+               int64_t sel_stride, const int32_t* count, bool need_grad, oomb::AttnArgs* a) {
+  *a = oomb::AttnArgs{};
+  int st = check_pool(pool, &a->pool, false, need_grad);
+  if (st) return st;
+  ChunkGeom cg;
+  if ((st = check_chunk(a->pool, n_q, t0, &cg))) return st;
+  if ((st = check_table(table, tstride, cg.first_local + cg.n_local, "table"))) return st;
+  if ((st = check_view(q, q_hs, q_ts, elem_size(a->pool), "q"))) return st;
+  if (sel != nullptr) {
+    if (count == nullptr) return fail(OOMB_ERR_INVALID, "count is NULL while sel is given");
+    if (sel_stride < 0) return fail(OOMB_ERR_INVALID, "sel_stride must be >= 0");
+  }
+  a->table = table;
+  a->tstride = tstride;
+  a->q = q;
+  a->q_hs = q_hs;
+  a->q_ts = q_ts;
+  a->n_q = n_q;
+  a->t0 = static_cast<int>(t0);
+  a->n_cand = cg.n_cand;
+  a->first_local = cg.first_local;
+  a->n_local = cg.n_local;
+  a->sel = sel;
+  a->sel_stride = sel_stride;
+  a->count = count;
+  const int64_t prior = sel ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
+  a->max_att_pages = static_cast<int>(prior + cg.n_local);
+  return OOMB_OK;
+}
+
+bool use_mfma(const oomb::PoolView& v) { return v.dtype == OOMB_DTYPE_BF16 && v.D == 128; }
+
+}  // namespace
+
+extern "C" {
+
+const char* oomb_status_string(int status) {
+  switch (status) {
+    case OOMB_OK: return "ok";
+    case OOMB_ERR_INVALID: return "invalid argument";
+    case OOMB_ERR_UNSUPPORTED: return "unsupported configuration";
+    case OOMB_ERR_HIP: return "HIP launch failure";
+    case OOMB_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* oomb_last_error(void) { return g_last_error.c_str(); }
+
+int oomb_abi_version(void) { return 1; }
+
+int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                   const void* k_new, const void* v_new, int64_t head_stride,
+                   int64_t tok_stride, int32_t n_tok, int64_t start_pos, void* stream) {
+  oomb::AppendArgs a{};
+  int st = check_pool(pool, &a.pool, false, false);
+  if (st) return st;
+  if (n_tok < 0) return fail(OOMB_ERR_INVALID, "n_tok must be >= 0");
+  if (start_pos < 0 || start_pos + n_tok > kMaxPos) return fail(OOMB_ERR_INVALID, "start_pos out of range");
+  if (n_tok == 0) return ok();
+  if ((st = check_table(table, table_stride, (start_pos + n_tok - 1) / a.pool.P + 1, "table"))) return st;
+  if ((st = check_view(k_new, head_stride, tok_stride, elem_size(a.pool), "k_new"))) return st;
+  if ((st = check_view(v_new, head_stride, tok_stride, elem_size(a.pool), "v_new"))) return st;
+  a.table = table;
+  a.tstride = table_stride;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.hs = head_stride;
+  a.ts = tok_stride;
+  a.n_tok = n_tok;
+  a.start = start_pos;
+  return hip_status(oomb::launch_kv_append(a, static_cast<hipStream_t>(stream)), "kv_append");
+}
+
+int oomb_page_summarize(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                        int64_t first_page, int64_t n_pages, int64_t seq_len, void* stream) {
+  oomb::SummarizeArgs a{};
+  int st = check_pool(pool, &a.pool, true, false);
+  if (st) return st;
+  if (first_page < 0 || n_pages < 0 || seq_len < 0 || seq_len > kMaxPos)
+    return fail(OOMB_ERR_INVALID, "first_page / n_pages / seq_len out of range");
+  if (n_pages > 0x7FFFFFFF) return fail(OOMB_ERR_INVALID, "n_pages too large");
+  if (n_pages == 0) return ok();
+  if ((st = check_table(table, table_stride, first_page + n_pages, "table"))) return st;
+  a.table = table;
+  a.tstride = table_stride;
+  a.first_page = first_page;
+  a.n_pages = n_pages;
+  a.seq_len = seq_len;
+  return hip_status(oomb::launch_page_summarize(a, static_cast<hipStream_t>(stream)), "page_summarize");
+}
+
+static void select_layout(int Hkv, int D, int nb, int n_cand, size_t* off_qbar, size_t* off_score,
+                          size_t* total) {
+  const size_t partial = align256(static_cast<size_t>(Hkv) * nb * D * sizeof(float));
+  const size_t qbar = align256(static_cast<size_t>(Hkv) * D * sizeof(float));
+  const size_t score = align256(static_cast<size_t>(Hkv) * (n_cand > 0 ? n_cand : 1) * sizeof(float));
+  *off_qbar = partial;
+  *off_score = partial + qbar;
+  *total = partial + qbar + score;
+}
+
+size_t oomb_select_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0) {
+  oomb::PoolView v{};
+  if (check_pool(pool, &v, false, false) != OOMB_OK || n_q <= 0 || t0 < 0) return 0;
+  const int G = v.Hq / v.Hkv;
+  const int64_t nb = (static_cast<int64_t>(G) * n_q + 63) / 64;
+  size_t oq, os, total;
+  select_layout(v.Hkv, v.D, static_cast<int>(nb), static_cast<int>(t0 / v.P), &oq, &os, &total);
+  return total;
+}
+
+int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                      const void* q, int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q,
+                      int64_t t0, int32_t top_k, int32_t* sel, int64_t sel_stride,
+                      int32_t* count, float* qbar_out, float* score_out, int64_t score_stride,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  oomb::SelectArgs a{};
+  int st = check_pool(pool, &a.pool, true, false);
+  if (st) return st;
+  ChunkGeom cg;
+  if ((st = check_chunk(a.pool, n_q, t0, &cg))) return st;
+  if (top_k < 0) return fail(OOMB_ERR_INVALID, "top_k must be >= 0");
+  if ((st = check_table(table, table_stride, cg.n_cand, "table"))) return st;
+  if ((st = check_view(q, q_head_stride, q_tok_stride, elem_size(a.pool), "q"))) return st;
+  if (count == nullptr) return fail(OOMB_ERR_INVALID, "count is NULL");
+  const int k = top_k < cg.n_cand ? top_k : cg.n_cand;
+  if (k > 0 && (sel == nullptr || sel_stride < k))
+    return fail(OOMB_ERR_INVALID, "sel must hold min(top_k, t0/P) = %d ids per head", k);
+  if (score_out != nullptr && score_stride < cg.n_cand)
+    return fail(OOMB_ERR_INVALID, "score_stride %lld < %d candidates", (long long)score_stride, cg.n_cand);
+  const int G = a.pool.Hq / a.pool.Hkv;
+  const int64_t nb = (static_cast<int64_t>(G) * n_q + 63) / 64;
+  if (nb > 16384) return fail(OOMB_ERR_INVALID, "G * n_q = %lld exceeds 1048576", (long long)G * n_q);
+  size_t off_qbar, off_score, total;
+  select_layout(a.pool.Hkv, a.pool.D, static_cast<int>(nb), cg.n_cand, &off_qbar, &off_score, &total);
+  if (workspace == nullptr || workspace_bytes < total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(OOMB_ERR_WORKSPACE, "select needs %zu bytes of 256-byte aligned workspace", total);
+  char* ws = static_cast<char*>(workspace);
+  a.table = table;
+  a.tstride = table_stride;
+  a.q = q;
+  a.q_hs = q_head_stride;
+  a.q_ts = q_tok_stride;
+  a.n_q = n_q;
+  a.t0 = t0;
+  a.top_k = top_k;
+  a.sel = sel;
+  a.sel_stride = sel_stride;
+  a.count = count;
+  a.partial = reinterpret_cast<float*>(ws);
+  a.qbar = qbar_out ? qbar_out : reinterpret_cast<float*>(ws + off_qbar);
+  a.score = score_out ? score_out : reinterpret_cast<float*>(ws + off_score);
+  a.score_stride = score_out ? score_stride : (cg.n_cand > 0 ? cg.n_cand : 1);
+  a.n_cand = cg.n_cand;
+  a.nb = static_cast<int>(nb);
+  a.inv = static_cast<float>(1.0 / (static_cast<double>(G) * n_q));
+  return hip_status(oomb::launch_select(a, static_cast<hipStream_t>(stream)), "select_pages");
+}
+
+int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                              const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                              int32_t n_q, int64_t t0, const int32_t* sel, int64_t sel_stride,
+                              const int32_t* count, float scale, void* o, int64_t o_head_stride,
+                              int64_t o_tok_stride, float* lse, void* stream) {
+  oomb::AttnArgs a;
+  int st = check_attn(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, sel,
+                      sel_stride, count, false, &a);
+  if (st) return st;
+  if ((st = check_view(o, o_head_stride, o_tok_stride, elem_size(a.pool), "o"))) return st;
+  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(OOMB_ERR_INVALID, "lse must be a 4-byte aligned device pointer");
+  if (!(scale > 0.0f) || scale > 1e30f) return fail(OOMB_ERR_INVALID, "scale must be positive and finite");
+  a.scale = scale;
+  a.o = o;
+  a.o_hs = o_head_stride;
+  a.o_ts = o_tok_stride;
+  a.lse = lse;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(use_mfma(a.pool) ? oomb::launch_fwd_mfma(a, s) : oomb::launch_fwd_scalar(a, s),
+                    "paged_chunk_attn_fwd");
+}
+
+size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q) {
+  oomb::PoolView v{};
+  if (check_pool(pool, &v, false, false) != OOMB_OK || n_q <= 0) return 0;
+  return align256(static_cast<size_t>(v.Hq) * n_q * sizeof(float));
+}
+
+int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                              const int32_t* gtable, int64_t gtable_stride, const void* q,
+                              int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q, int64_t t0,
+                              const int32_t* sel, int64_t sel_stride, const int32_t* count,
+                              float scale, const void* o, int64_t o_head_stride,
+                              int64_t o_tok_stride, const void* dout, int64_t do_head_stride,
+                              int64_t do_tok_stride, const float* lse, float* dq,
+                              int64_t dq_head_stride, int64_t dq_tok_stride, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  oomb::AttnArgs a;
+  int st = check_attn(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, sel,
+                      sel_stride, count, true, &a);
+  if (st) return st;
+  if ((st = check_table(gtable, gtable_stride, a.first_local + a.n_local, "gtable"))) return st;
+  if ((st = check_view(o, o_head_stride, o_tok_stride, elem_size(a.pool), "o"))) return st;
+  if ((st = check_view(dout, do_head_stride, do_tok_stride, elem_size(a.pool), "dout"))) return st;
+  if ((st = check_view(dq, dq_head_stride, dq_tok_stride, 4, "dq"))) return st;
+  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(OOMB_ERR_INVALID, "lse must be a 4-byte aligned device pointer");
+  if (!(scale > 0.0f) || scale > 1e30f) return fail(OOMB_ERR_INVALID, "scale must be positive and finite");
+  const size_t need = align256(static_cast<size_t>(a.pool.Hq) * n_q * sizeof(float));
+  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(OOMB_ERR_WORKSPACE, "bwd needs %zu bytes of 256-byte aligned workspace", need);
+  a.gtable = gtable;
+  a.gtstride = gtable_stride;
+  a.scale = scale;
+  a.o = const_cast<void*>(o);
+  a.o_hs = o_head_stride;
+  a.o_ts = o_tok_stride;
+  a.dout = dout;
+  a.do_hs = do_head_stride;
+  a.do_ts = do_tok_stride;
+  a.lse_in = lse;
+  a.dq = dq;
+  a.dq_hs = dq_head_stride;
+  a.dq_ts = dq_tok_stride;
+  a.delta = static_cast<float*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(use_mfma(a.pool) ? oomb::launch_bwd_mfma(a, s) : oomb::launch_bwd_scalar(a, s),
+                    "paged_chunk_attn_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel files.
+// Every launcher only enqueues work on `stream`; argument checking is done by the
+// caller (api.cpp) before any of these is reached.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oomb {
+
+struct PoolView {
+  int dtype;        // 0 = bf16, 1 = fp32
+  int P, log2p, D, Hq, Hkv;
+  int64_t N, Ng;
+  const void* k_pool;
+  const void* v_pool;
+  void* k_pool_w;   // writable aliases (append / summarize)
+  void* v_pool_w;
+  void* k_summary;
+  float* dk_pool;
+  float* dv_pool;
+};
+
+struct AppendArgs {
+  PoolView pool;
+  const int32_t* table;
+  int64_t tstride;
+  const void* k_new;
+  const void* v_new;
+  int64_t hs, ts;
+  int n_tok;
+  int64_t start;
+};
+
+struct SummarizeArgs {
+  PoolView pool;
+  const int32_t* table;
+  int64_t tstride;
+  int64_t first_page, n_pages, seq_len;
+};
+
+struct SelectArgs {
+  PoolView pool;
+  const int32_t* table;
+  int64_t tstride;
+  const void* q;
+  int64_t q_hs, q_ts;
+  int n_q;
+  int64_t t0;
+  int top_k;
+  int32_t* sel;
+  int64_t sel_stride;
+  int32_t* count;
+  float* partial;   // [Hkv][nb][D]
+  float* qbar;      // [Hkv][D]
+  float* score;     // [Hkv][score_stride]
+  int64_t score_stride;
+  int n_cand;
+  int nb;           // query blocks of 64 rows
+  float inv;        // fp32(1 / (G * n_q)), rounded once from fp64
+};
+
+struct AttnArgs {
+  PoolView pool;
+  const int32_t* table;
+  int64_t tstride;
+  const int32_t* gtable;
+  int64_t gtstride;
+  const void* q;
+  int64_t q_hs, q_ts;
+  int n_q;
+  int t0;
+  int n_cand;        // t0 / P: prior pages
+  int first_local;   // t0 / P
+  int n_local;       // local pages
+  const int32_t* sel;  // nullptr = dense
+  int64_t sel_stride;
+  const int32_t* count;
+  float scale;
+  void* o;
+  int64_t o_hs, o_ts;
+  const void* dout;
+  int64_t do_hs, do_ts;
+  float* lse;        // forward output
+  const float* lse_in;
+  float* dq;
+  int64_t dq_hs, dq_ts;
+  float* delta;      // [Hq][n_q] workspace
+  int max_att_pages; // upper bound of attended pages per head (grid sizing)
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_page_summarize(const SummarizeArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+// Scalar kernels: any supported dtype / head_dim / page size.
+hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_scalar(const AttnArgs& a, hipStream_t s);
+// Matrix-core kernels: bf16, head_dim 128, page size >= 16.
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t s);
+// Delta_i = dO_i . O_i, shared by both backward paths.
+hipError_t launch_delta(const AttnArgs& a, hipStream_t s);
+
+}  // namespace oomb

@@ -1,0 +1,131 @@
+// Paged K/V storage kernels for gfx950: appending a chunk's keys/values into
+// their pages, and the per-page key min/max summaries used for page retrieval.
+//
+// Paging follows the gist.science explainer of OOMB, 2.B "Paged KV Cache and
+// Gradient Management": the cache is a pool of fixed-size pages and grows by
+// filling page slots, never by reallocating or copying what is already stored.
+// The min/max summary is the per-page representative for top-k retrieval
+// (explainer 2.D), in the form used by Quest (cited by the paper).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace oomb {
+
+// One work item = one 16-byte chunk of one token row of one KV head; K and V are
+// copied together. Rows whose page is unmapped are skipped.
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+  const int esize = a.pool.dtype == 0 ? 2 : 4;
+  const int cpr = a.pool.D * esize / 16;  // 16-byte chunks per row
+  const int64_t total = static_cast<int64_t>(a.pool.Hkv) * a.n_tok * cpr;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t w = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; w < total;
+       w += stride) {
+    const int c = static_cast<int>(w % cpr);
+    const int64_t r = w / cpr;
+    const int i = static_cast<int>(r % a.n_tok);
+    const int g = static_cast<int>(r / a.n_tok);
+    const int64_t t = a.start + i;
+    const int64_t ph = a.table[g * a.tstride + (t >> a.pool.log2p)];
+    if (ph < 0 || ph >= a.pool.N) continue;
+    const int64_t src = (g * a.hs + i * a.ts) * esize + c * 16;
+    const int64_t dst = ((ph << a.pool.log2p) + (t & (a.pool.P - 1))) * a.pool.D * esize + c * 16;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k_new) + src);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v_new) + src);
+    *reinterpret_cast<u32x4*>(static_cast<char*>(a.pool.k_pool_w) + dst) = kv;
+    *reinterpret_cast<u32x4*>(static_cast<char*>(a.pool.v_pool_w) + dst) = vv;
+  }
+}
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s) {
+  const int esize = a.pool.dtype == 0 ? 2 : 4;
+  const int64_t total = static_cast<int64_t>(a.pool.Hkv) * a.n_tok * (a.pool.D * esize / 16);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Order-preserving integer key of a float: increasing in value, -0 below +0. It is
+// an involution on the bit pattern, so the same function maps a key back to bits.
+__device__ __forceinline__ int32_t order_key_bf16(uint32_t bits16) {
+  const int32_t b = static_cast<int32_t>(static_cast<int16_t>(bits16));
+  return b ^ ((b >> 31) & 0x7FFF);
+}
+__device__ __forceinline__ int32_t order_key_f32(uint32_t bits) {
+  const int32_t b = static_cast<int32_t>(bits);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+
+// One workgroup per (logical page, KV head). Each thread owns one 16-byte column
+// chunk and a strided subset of the page's valid rows; the row groups are merged
+// in LDS. Min/max are taken on order keys, so the result does not depend on the
+// reduction order.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void page_summarize_kernel(SummarizeArgs a) {
+  constexpr int kEsize = kBf16 ? 2 : 4;
+  constexpr int kPer = 16 / kEsize;  // elements per 16-byte chunk
+  __shared__ int32_t s_min[256 * kPer];
+  __shared__ int32_t s_max[256 * kPer];
+  const int g = blockIdx.y;
+  const int64_t lp = a.first_page + blockIdx.x;
+  const int P = a.pool.P, D = a.pool.D;
+  const int64_t n_valid64 = a.seq_len - (lp << a.pool.log2p);
+  if (n_valid64 <= 0) return;
+  const int n_valid = n_valid64 < P ? static_cast<int>(n_valid64) : P;
+  const int64_t ph = a.table[g * a.tstride + lp];
+  if (ph < 0 || ph >= a.pool.N) return;
+  const int cpr = D / kPer;             // chunks per row
+  const int groups = 256 / cpr;         // row groups
+  const int c = threadIdx.x % cpr, rg = threadIdx.x / cpr;
+  int32_t mn[kPer], mx[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) { mn[e] = 0x7FFFFFFF; mx[e] = static_cast<int32_t>(0x80000000); }
+  const char* base = static_cast<const char*>(a.pool.k_pool) + (ph << a.pool.log2p) * D * kEsize;
+  for (int r = rg; r < n_valid; r += groups) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (static_cast<int64_t>(r) * D + c * kPer) * kEsize);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const uint32_t word = v[e * kEsize / 4];
+      const int32_t key = kBf16 ? order_key_bf16((e & 1) ? (word >> 16) : (word & 0xFFFF))
+                                : order_key_f32(word);
+      mn[e] = key < mn[e] ? key : mn[e];
+      mx[e] = key > mx[e] ? key : mx[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    s_min[rg * D + c * kPer + e] = mn[e];
+    s_max[rg * D + c * kPer + e] = mx[e];
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += 256) {
+    int32_t lo = 0x7FFFFFFF, hi = static_cast<int32_t>(0x80000000);
+    const int used = groups < n_valid ? groups : n_valid;
+    for (int j = 0; j < used; ++j) {
+      const int32_t x = s_min[j * D + d], y = s_max[j * D + d];
+      lo = x < lo ? x : lo;
+      hi = y > hi ? y : hi;
+    }
+    char* out = static_cast<char*>(a.pool.k_summary) + ph * 2 * D * kEsize;
+    if (kBf16) {
+      reinterpret_cast<uint16_t*>(out)[d] = static_cast<uint16_t>(order_key_bf16(static_cast<uint32_t>(lo) & 0xFFFF));
+      reinterpret_cast<uint16_t*>(out)[D + d] = static_cast<uint16_t>(order_key_bf16(static_cast<uint32_t>(hi) & 0xFFFF));
+    } else {
+      reinterpret_cast<uint32_t*>(out)[d] = static_cast<uint32_t>(order_key_f32(static_cast<uint32_t>(lo)));
+      reinterpret_cast<uint32_t*>(out)[D + d] = static_cast<uint32_t>(order_key_f32(static_cast<uint32_t>(hi)));
+    }
+  }
+}
+
+hipError_t launch_page_summarize(const SummarizeArgs& a, hipStream_t s) {
+  if (a.n_pages <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(a.n_pages), a.pool.Hkv);
+  if (a.pool.dtype == 0)
+    hipLaunchKernelGGL(page_summarize_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(page_summarize_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace oomb

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports every function include/oomb.h declares, and
+rejects invalid arguments on the host with the documented status (no GPU needed:
+every call here fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_chunk_attention_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "oomb.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(oomb_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from paged_chunk_attention_amd.build import build
+        build()
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert lib.oomb_abi_version() == 1
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
+                       (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
+        assert lib.oomb_status_string(code) == text
+
+
+def _pool(**kw):
+    base = dict(dtype=0, page_size=128, head_dim=128, num_q_heads=28, num_kv_heads=4, reserved=0,
+                num_pages=64, num_grad_pages=64, k_pool=0x100000, v_pool=0x200000,
+                k_summary=0x300000, dk_pool=0x400000, dv_pool=0x500000)
+    base.update(kw)
+    return L.OombPool(**base)
+
+
+# Fake but well-aligned device addresses: never dereferenced, every call below is
+# rejected by the host-side checks first.
+T, Q, O, B = 0x600000, 0x700000, 0x800000, 0x900000
+
+
+def _fwd(lib, pool, **kw):
+    a = dict(table=T, tstride=64, q=Q, qhs=4096 * 128, qts=128, n_q=4096, t0=4096, sel=None,
+             sstride=0, count=None, scale=0.088, o=O, ohs=4096 * 128, ots=128, lse=B)
+    a.update(kw)
+    return lib.oomb_paged_chunk_attn_fwd(ctypes.byref(pool), a["table"], a["tstride"], a["q"],
+                                         a["qhs"], a["qts"], a["n_q"], a["t0"], a["sel"],
+                                         a["sstride"], a["count"], a["scale"], a["o"], a["ohs"],
+                                         a["ots"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), L.OOMB_ERR_UNSUPPORTED),
+    (dict(head_dim=96), L.OOMB_ERR_UNSUPPORTED),
+    (dict(page_size=100), L.OOMB_ERR_UNSUPPORTED),
+    (dict(page_size=8), L.OOMB_ERR_UNSUPPORTED),
+    (dict(num_q_heads=27), L.OOMB_ERR_INVALID),
+    (dict(num_kv_heads=0), L.OOMB_ERR_INVALID),
+    (dict(k_pool=None), L.OOMB_ERR_INVALID),
+    (dict(v_pool=0x200008), L.OOMB_ERR_INVALID),
+    (dict(reserved=1), L.OOMB_ERR_INVALID),
+    (dict(num_pages=0), L.OOMB_ERR_INVALID),
+])
+def test_pool_descriptor_errors(lib, kw, code):
+    assert _fwd(lib, _pool(**kw)) == code
+    assert lib.oomb_last_error() != b""
+
+
+@pytest.mark.parametrize("kw", [
+    dict(table=None), dict(q=None), dict(q=Q + 2), dict(qts=100), dict(n_q=0), dict(n_q=-5),
+    dict(t0=-1), dict(tstride=10), dict(o=None), dict(lse=None), dict(lse=B + 2),
+    dict(scale=0.0), dict(scale=-1.0), dict(scale=float("nan")), dict(sel=T, count=None),
+])
+def test_fwd_argument_errors(lib, kw):
+    assert _fwd(lib, _pool(), **kw) == L.OOMB_ERR_INVALID
+
+
+def test_null_pool_and_append_errors(lib):
+    assert lib.oomb_kv_append(None, T, 64, Q, O, 128, 128, 1, 0, None) == L.OOMB_ERR_INVALID
+    p = _pool()
+    # table too short for the last token's page
+    assert lib.oomb_kv_append(ctypes.byref(p), T, 2, Q, O, 128, 128, 300, 0, None) == L.OOMB_ERR_INVALID
+    assert lib.oomb_kv_append(ctypes.byref(p), T, 64, Q, O, 128, 128, -1, 0, None) == L.OOMB_ERR_INVALID
+    assert lib.oomb_kv_append(ctypes.byref(p), T, 64, Q, O, 128, 127, 4, 0, None) == L.OOMB_ERR_INVALID
+    assert lib.oomb_kv_append(ctypes.byref(p), T, 64, Q, O, 128, 128, 0, 0, None) == L.OOMB_OK
+
+
+def test_summarize_and_select_errors(lib):
+    p = _pool()
+    nosum = _pool(k_summary=None)
+    assert lib.oomb_page_summarize(ctypes.byref(nosum), T, 64, 0, 4, 512, None) == L.OOMB_ERR_INVALID
+    assert lib.oomb_page_summarize(ctypes.byref(p), T, 3, 0, 4, 512, None) == L.OOMB_ERR_INVALID
+    assert lib.oomb_page_summarize(ctypes.byref(p), T, 64, 0, 0, 512, None) == L.OOMB_OK
+    ws = lib.oomb_select_workspace_bytes(ctypes.byref(p), 4096, 4096)
+    assert ws > 0 and ws % 256 == 0
+
+    def sel(**kw):
+        a = dict(top_k=4, sel=B, sstride=4, count=B + 256, score=None, sstr=0, ws=0xA00000,
+                 wsb=ws)
+        a.update(kw)
+        return lib.oomb_select_pages(ctypes.byref(p), T, 64, Q, 4096 * 128, 128, 4096, 4096,
+                                     a["top_k"], a["sel"], a["sstride"], a["count"], None,
+                                     a["score"], a["sstr"], a["ws"], a["wsb"], None)
+    assert sel(top_k=-1) == L.OOMB_ERR_INVALID and b"top_k" in lib.oomb_last_error()
+    assert sel(sstride=3) == L.OOMB_ERR_INVALID and b"sel must hold" in lib.oomb_last_error()
+    assert sel(count=None) == L.OOMB_ERR_INVALID
+    assert sel(score=B, sstr=10) == L.OOMB_ERR_INVALID and b"score_stride" in lib.oomb_last_error()
+    assert sel(wsb=ws - 1) == L.OOMB_ERR_WORKSPACE
+    assert sel(ws=0xA00010) == L.OOMB_ERR_WORKSPACE
+
+
+def test_bwd_errors(lib):
+    p = _pool()
+    nograd = _pool(dk_pool=None)
+    need = lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096)
+    assert need == 28 * 4096 * 4
+
+    def bwd(pool, **kw):
+        a = dict(gtable=T, gts=64, dq=B, dqhs=4096 * 128, dqts=128, ws=0xA00000, wsb=need)
+        a.update(kw)
+        return lib.oomb_paged_chunk_attn_bwd(
+            ctypes.byref(pool), T, 64, a["gtable"], a["gts"], Q, 4096 * 128, 128, 4096, 4096,
+            None, 0, None, 0.088, O, 4096 * 128, 128, O, 4096 * 128, 128, B, a["dq"], a["dqhs"],
+            a["dqts"], a["ws"], a["wsb"], None)
+    assert bwd(nograd) == L.OOMB_ERR_INVALID
+    assert bwd(p, gtable=None) == L.OOMB_ERR_INVALID
+    assert bwd(p, gts=5) == L.OOMB_ERR_INVALID
+    assert bwd(p, dqts=130) == L.OOMB_ERR_INVALID
+    assert bwd(p, wsb=need - 4) == L.OOMB_ERR_WORKSPACE

@@ -1,0 +1,139 @@
+"""GPU parity: the HIP library (through its C-ABI binding) against the CPU oracle,
+element by element on identical seeded inputs, at sizes the oracle finishes in
+seconds that still span several tiles and ragged tails.
+
+Bars: bit-exact for pages, summaries, query summaries, scores and selections;
+max-abs 2e-2 and relative-L2 1e-2 for bf16 outputs (O, dQ, dK, dV), 1e-5 for fp32.
+"""
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_harness import DEV, bits, compare, log, run_chunk_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(**kw):
+    base = dict(name="case", hq=8, hkv=2, d=128, page=128, chunk=300, total=1300,
+                dtype=torch.bfloat16, top_k=None, needles=0)
+    base.update(kw)
+    return wl.Workload(**base)
+
+
+# matrix-core path: bf16, head_dim 128
+@pytest.mark.parametrize("kw", [
+    dict(name="mfma_dense_ragged"),                                   # t0=1000 straddles a page
+    dict(name="mfma_sparse_k5", chunk=333, total=2597 + 333, top_k=5, needles=3),
+    dict(name="mfma_gqa7_sparse", hq=28, hkv=4, chunk=256, total=1024 + 256, top_k=3),
+    dict(name="mfma_page16_sparse", hq=4, hkv=2, page=16, chunk=200, total=500, top_k=6),
+    dict(name="mfma_page32_dense", hq=6, hkv=3, page=32, chunk=130, total=130 + 517),
+    dict(name="mfma_first_chunk", hq=4, hkv=1, chunk=200, total=200),  # t0 = 0
+    dict(name="mfma_single_query", hq=4, hkv=2, chunk=1, total=777),
+    dict(name="mfma_k0_local_only", hq=4, hkv=2, chunk=128, total=1024, top_k=0),
+    dict(name="mfma_k_exceeds", hq=4, hkv=2, chunk=64, total=640, top_k=50),
+])
+def test_chunk_parity_mfma(kw):
+    run_chunk_parity(_w(**kw))
+
+
+# scalar path: fp32 (any head_dim) and bf16 head_dim 64
+@pytest.mark.parametrize("kw", [
+    dict(name="f32_d64_p16", hq=2, hkv=1, d=64, page=16, chunk=64, total=1024, dtype=torch.float32),
+    dict(name="f32_d128_sparse", hq=4, hkv=2, d=128, page=32, chunk=70, total=70 + 300,
+         dtype=torch.float32, top_k=4),
+    dict(name="bf16_d64_dense", hq=4, hkv=1, d=64, page=64, chunk=100, total=300),
+    dict(name="bf16_d64_sparse", hq=6, hkv=2, d=64, page=16, chunk=50, total=50 + 400, top_k=7),
+])
+def test_chunk_parity_scalar(kw):
+    run_chunk_parity(_w(**kw))
+
+
+def test_selection_ties_break_to_lower_id():
+    """Pages with identical keys score identically; the lower logical ids win."""
+    w = _w(name="ties", hq=4, hkv=1, chunk=128, total=128 * 12 + 128, top_k=4)
+    x = wl.make_inputs(w)
+    k = x["k"].clone()
+    for j in (2, 5, 6, 9, 10):
+        k[:, j * 128:(j + 1) * 128] = k[:, 3 * 128:4 * 128]
+    x["k"] = k
+    run_chunk_parity(w, x)
+
+
+def test_results_independent_of_page_placement():
+    """Two different physical placements give bit-identical O, LSE, dQ and
+    selections, and the same gradient rows after mapping pages back."""
+    import paged_chunk_attention_amd as pca
+    w = _w(name="placement", hq=8, hkv=2, chunk=256, total=256 + 1100, top_k=4)
+    x = wl.make_inputs(w)
+    outs = []
+    for seed in (5, 50):
+        perm = torch.randperm(w.pool_pages, generator=torch.Generator().manual_seed(seed))
+        table = perm.to(torch.int32).reshape(w.hkv, -1).to(DEV)
+        pool = pca.PagedPool(w.pool_pages, w.page, w.d, w.hq, w.hkv, w.dtype, DEV)
+        log(f"[case placement seed={seed}]")
+        pca.oomb_kv_append(pool, table, x["k"].to(DEV), x["v"].to(DEV), 0)
+        pca.oomb_page_summarize(pool, table, 0, w.pages_per_head, w.total)
+        q, do = x["q"].to(DEV), x["do"].to(DEV)
+        sel, cnt = pca.oomb_select_pages(pool, table, q, w.t0, w.top_k)
+        o, lse = pca.oomb_paged_chunk_attn_fwd(pool, table, q, w.t0, sel, cnt)
+        dq = pca.oomb_paged_chunk_attn_bwd(pool, table, table, q, w.t0, sel, cnt, o, do, lse)
+        torch.cuda.synchronize()
+        idx = table.long()
+        dk = pool.dk[idx].reshape(w.hkv, -1, w.d).cpu()
+        outs.append((sel.cpu(), bits(o), lse.cpu(), dq.cpu(), dk))
+    a, b = outs
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3]) and torch.equal(a[4], b[4])
+
+
+def test_backward_deterministic_run_twice():
+    """dK/dV are written by exclusive owners (no atomics): two runs agree bitwise."""
+    import paged_chunk_attention_amd as pca
+    w = _w(name="determinism", hq=8, hkv=2, chunk=300, total=2000, top_k=6)
+    x = wl.make_inputs(w)
+    table = x["table"].to(DEV)
+    pool = pca.PagedPool(w.pool_pages, w.page, w.d, w.hq, w.hkv, w.dtype, DEV)
+    log("[case determinism]")
+    pca.oomb_kv_append(pool, table, x["k"].to(DEV), x["v"].to(DEV), 0)
+    pca.oomb_page_summarize(pool, table, 0, w.pages_per_head, w.total)
+    q, do = x["q"].to(DEV), x["do"].to(DEV)
+    sel, cnt = pca.oomb_select_pages(pool, table, q, w.t0, w.top_k)
+    o, lse = pca.oomb_paged_chunk_attn_fwd(pool, table, q, w.t0, sel, cnt)
+    res = []
+    for _ in range(2):
+        pool.zero_grad()
+        dq = pca.oomb_paged_chunk_attn_bwd(pool, table, table, q, w.t0, sel, cnt, o, do, lse)
+        torch.cuda.synchronize()
+        res.append((dq.cpu(), pool.dk.cpu(), pool.dv.cpu()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
+def test_strided_views_match_contiguous():
+    """[C, H, D] storage (token-major) gives the same results as [H, C, D]."""
+    import paged_chunk_attention_amd as pca
+    w = _w(name="strided", hq=8, hkv=2, chunk=192, total=192 + 640, top_k=2)
+    x = wl.make_inputs(w)
+    table = x["table"].to(DEV)
+    pool = pca.PagedPool(w.pool_pages, w.page, w.d, w.hq, w.hkv, w.dtype, DEV)
+    log("[case strided]")
+    kt = x["k"].transpose(0, 1).contiguous().to(DEV).transpose(0, 1)
+    vt = x["v"].transpose(0, 1).contiguous().to(DEV).transpose(0, 1)
+    pca.oomb_kv_append(pool, table, kt, vt, 0)
+    pca.oomb_page_summarize(pool, table, 0, w.pages_per_head, w.total)
+    q = x["q"].to(DEV)
+    do = x["do"].to(DEV)
+    qt = x["q"].transpose(0, 1).contiguous().to(DEV).transpose(0, 1)
+    dot = x["do"].transpose(0, 1).contiguous().to(DEV).transpose(0, 1)
+    s1, c1 = pca.oomb_select_pages(pool, table, q, w.t0, w.top_k)
+    s2, c2 = pca.oomb_select_pages(pool, table, qt, w.t0, w.top_k)
+    o1, l1 = pca.oomb_paged_chunk_attn_fwd(pool, table, q, w.t0, s1, c1)
+    o2 = torch.empty(w.chunk, w.hq, w.d, dtype=w.dtype, device=DEV).transpose(0, 1)
+    o2, l2 = pca.oomb_paged_chunk_attn_fwd(pool, table, qt, w.t0, s2, c2, o=o2)
+    d1 = pca.oomb_paged_chunk_attn_bwd(pool, table, table, q, w.t0, s1, c1, o1, do, l1)
+    d2 = pca.oomb_paged_chunk_attn_bwd(pool, table, table, qt, w.t0, s2, c2, o2, dot, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(c1, c2)
+    assert torch.equal(bits(o1), bits(o2.contiguous())) and torch.equal(l1, l2)
+    assert torch.equal(d1, d2)
