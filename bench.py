@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged chunk-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one chunk of synthetic Qwen2.5-7B-shaped
+input (28 query heads, 4 KV heads, head_dim 128, bf16, 128-token pages):
+append the chunk's K/V into the page pool, summarize its pages, select the top-k
+prior pages (sparse workloads), forward, backward (dQ written, dK/dV added into the
+fp32 gradient pool). The prior context is written into the pool before timing.
+
+    python bench.py [--steps K] [--warmup W] [--workload sparse1m|dense128k|sparse4m]
+
+Prints one JSON line (stdout). Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd paged chunk-attn TFLOP/s @1M ctx; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Algorithmic FLOP per attended (query, key) pair and head_dim unit, per kernel:
+# forward = S and PV; the dK/dV pass = S, dP (recomputed), dV, dK; the dQ pass is
+# credited with dQ only (its S and dP are recomputation).
+FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attended_pairs(w, counts):
+    """(query, key) pairs the chunk attends, summed over query heads."""
+    C, P, t0 = w.chunk, w.page, w.t0
+    first_local = t0 // P
+    # local keys visible to query i: positions first_local*P .. t0+i
+    local = sum((t0 + i) - first_local * P + 1 for i in range(C))
+    total = 0
+    for g in range(w.hkv):
+        prior = counts[g] if counts is not None else t0 // P
+        total += w.group * (prior * P * C + local)
+    return total
+
+
+def cpu_baseline(w, x, table_cpu, sel_cpu, rows: int):
+    """The oracle (fp64 CPU) on a bounded sample of the same step: KV head 0, its
+    query heads, the last `rows` queries of the chunk, over exactly the keys those
+    queries attend in the full chunk."""
+    import torch
+    import oracle as orc
+
+    P, C, t0, G = w.page, w.chunk, w.t0, w.group
+    rows = min(rows, C)
+    t0s = t0 + C - rows
+    sel0 = list(sel_cpu[0]) if sel_cpu is not None else list(range(t0 // P))
+    # the chunk's own pages before the sample are selected pages for the sample
+    sel_s = sorted(set(sel0) | set(range(t0 // P, t0s // P)))
+    pages = orc.attended_pages(t0s, rows, P, sel_s)
+    # compact oracle pool holding only the attended pages of head 0
+    tab = torch.zeros(1, (t0 + C) // P + 1, dtype=torch.int32)
+    for i, lp in enumerate(pages):
+        tab[0, lp] = i
+    kp = torch.zeros(len(pages), P, w.d, dtype=w.dtype)
+    vp = torch.zeros_like(kp)
+    kh, vh = x["k"][0:1], x["v"][0:1]
+    for lp in pages:
+        a, b = lp * P, min((lp + 1) * P, t0 + C)
+        orc.append(kp, tab, kh[:, a:b].cpu(), a)
+        orc.append(vp, tab, vh[:, a:b].cpu(), a)
+    q = x["q"][0:G, C - rows:].cpu()
+    do = x["do"][0:G, C - rows:].cpu()
+    pairs = 0
+    for i in range(rows):
+        p = t0s + i
+        pairs += sum(min(P, p - lp * P + 1) for lp in pages if lp * P <= p)
+    pairs *= G
+    threads = torch.get_num_threads()
+    t = time.perf_counter()
+    orc.fwd(q, kp, vp, tab, t0s, [sel_s], w.scale)
+    orc.bwd(q, kp, vp, tab, t0s, [sel_s], w.scale, do)
+    dt = time.perf_counter() - t
+    flop = 14 * w.d * pairs
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"KV head 0 of {w.hkv} ({G} query heads), last {rows} of {C} chunk queries "
+                      f"over the same {len(pages)} attended pages; oracle fwd+bwd in fp64; "
+                      f"{pairs} pairs, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sparse1m",
+                    choices=["sparse1m", "dense128k", "sparse4m"])
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="chunk queries in the oracle's CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the hot path here is "
+              "the single-GPU share; no multi-GPU configuration is built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_chunk_attention_amd as pca
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+    w = wl.WORKLOADS[args.workload]
+    P, C, t0 = w.page, w.chunk, w.t0
+    log(f"[bench] workload={w.name} hq={w.hq} hkv={w.hkv} d={w.d} page={P} chunk={C} t0={t0} "
+        f"top_k={w.top_k}")
+    x = wl.make_inputs(w, device=dev)
+    table = x["table"].to(dev)
+    gtable = x["gtable"].to(dev)
+    pool = pca.PagedPool(w.pool_pages, P, w.d, w.hq, w.hkv, w.dtype, dev)
+    # prior context, untimed
+    pca.oomb_kv_append(pool, table, x["k"][:, :t0], x["v"][:, :t0], 0)
+    pca.oomb_page_summarize(pool, table, 0, t0 // P, t0)
+    k_new = x["k"][:, t0:t0 + C].contiguous()
+    v_new = x["v"][:, t0:t0 + C].contiguous()
+    q, do = x["q"], x["do"]
+    first_local = t0 // P
+    n_local = (t0 + C - 1) // P - first_local + 1
+    k = max(0, min(w.top_k, t0 // P)) if w.top_k is not None else 0
+    sel = torch.zeros(w.hkv, max(k, 1), dtype=torch.int32, device=dev)
+    count = torch.zeros(w.hkv, dtype=torch.int32, device=dev)
+    ws_sel = torch.empty(pca.select_workspace_bytes(pool, C, t0), dtype=torch.uint8, device=dev)
+    ws_bwd = torch.empty(pca.bwd_workspace_bytes(pool, C, t0, sel.stride(0) if w.top_k is not None else -1),
+                         dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.hq, C, dtype=torch.float32, device=dev)
+    dq = torch.empty(w.hq, C, w.d, dtype=torch.float32, device=dev)
+    sparse = w.top_k is not None
+
+    def step():
+        pca.oomb_kv_append(pool, table, k_new, v_new, t0)
+        pca.oomb_page_summarize(pool, table, first_local, n_local, t0 + C)
+        s_, c_ = (None, None)
+        if sparse:
+            s_, c_ = pca.oomb_select_pages(pool, table, q, t0, w.top_k, sel=sel, count=count,
+                                           workspace=ws_sel)
+        pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, s_, c_, w.scale, o=o, lse=lse)
+        pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, s_, c_, o, do, lse, w.scale,
+                                      dq=dq, workspace=ws_bwd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    # timed region: every kernel is bracketed by HIP events on its own stream
+    with pca.kernel_timer() as timer:
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    per_kernel = {}
+    for name, ms in timer.records:
+        tot, n = per_kernel.get(name, (0.0, 0))
+        per_kernel[name] = (tot + ms, n + 1)
+    counts = count.cpu().tolist() if sparse else None
+    pairs = attended_pairs(w, counts)
+    flop = 14 * w.d * pairs
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s, "
+        f"pairs={pairs}")
+    breakdown = {}
+    for name, (tot, n) in sorted(per_kernel.items(), key=lambda kv: -kv[1][0]):
+        breakdown[name] = {"ms_per_launch": tot / n, "launches_per_step": n / args.steps}
+        log(f"    {name:16s} {tot / n:9.4f} ms x {n / args.steps:.0f}/step")
+
+    # roofline of the dominant kernel (largest time per step)
+    dom = max(per_kernel, key=lambda k_: per_kernel[k_][0])
+    dom_ms = per_kernel[dom][0] / per_kernel[dom][1]
+    if dom in FLOP_PER_PAIR_D:
+        ach = FLOP_PER_PAIR_D[dom] * w.d * pairs / (dom_ms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "algorithmic_flop_per_launch": FLOP_PER_PAIR_D[dom] * w.d * pairs,
+                "ms_per_launch": dom_ms}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": None, "traffic": None, "ms_per_launch": dom_ms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        x_cpu = {"k": x["k"], "v": x["v"], "q": x["q"], "do": x["do"]}
+        sel_cpu = [sel[g, :counts[g]].tolist() for g in range(w.hkv)] if sparse else None
+        log("[bench] timing the oracle on the CPU sample ...")
+        cpu = cpu_baseline(w, x_cpu, x["table"], sel_cpu, args.cpu_rows)
+        log(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
+                   "page": P, "chunk": C, "prior_tokens": t0, "top_k": w.top_k,
+                   "attended_pairs": pairs, "model_flop_per_step": flop,
+                   "step": "kv_append+page_summarize+select_pages+fwd+bwd"},
+        "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": roof,
+        "kernels": breakdown,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -154,8 +154,13 @@ int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table,
                               float scale, void* o, int64_t o_head_stride,
                               int64_t o_tok_stride, float* lse, void* stream);
 
-/* Bytes of device workspace oomb_paged_chunk_attn_bwd needs (256-byte aligned). */
-size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q);
+/* Bytes of device workspace oomb_paged_chunk_attn_bwd needs (256-byte aligned) for
+ * n_q queries after t0 prior tokens, with at most sel_stride selected prior pages
+ * per KV head (sel_stride < 0: dense, every prior page). It holds Delta and, when
+ * the dK/dV pass is split over the query stream to fill the GPU, fp32 partials.
+ * Returns 0 for invalid arguments. */
+size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
+                                int64_t sel_stride);
 
 /* Chunk attention backward, with the attention probabilities recomputed from the
  * saved LSE (explainer 2.A: activations are recomputed just before use) and the
@@ -167,9 +172,12 @@ size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q);
  *   dq[h][i]  = scale * sum_t dS_it k_t                        (fp32, OVERWRITTEN)
  *   dk_pool[gtable[g][t/P]][t%P] += scale * sum_{h in g, i} dS_it q_hi   (fp32, ADDED)
  *   dv_pool[gtable[g][t/P]][t%P] += sum_{h in g, i} P_it dO_hi           (fp32, ADDED)
- * Every attended key row is owned by exactly one workgroup, so the pool update is a
- * plain read-modify-write with no races and no atomics; the caller zeroes the
- * gradient pool when a step starts. gtable: int32 [Hkv][gtable_stride], may alias
+ * Every gradient row is written by exactly one workgroup (a plain read-modify-write,
+ * no atomics, no races; when the key pass is split over the query stream, the split
+ * partials go through the workspace and one merge kernel adds them in split order),
+ * so results are bit-reproducible. The caller zeroes the gradient pool when a step
+ * starts. The workspace must hold oomb_bwd_workspace_bytes(pool, n_q, t0,
+ * sel ? sel_stride : -1) bytes. gtable: int32 [Hkv][gtable_stride], may alias
  * table. dq: fp32 [Hq][n_q][D] view. */
 int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table,
                               int64_t table_stride, const int32_t* gtable,
@@ -182,6 +190,15 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table,
                               const float* lse, float* dq, int64_t dq_head_stride,
                               int64_t dq_tok_stride, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Kernel timing for profiling tools; not needed for normal use. While enabled on
+ * the calling thread, each kernel that a call above launches is bracketed by two
+ * HIP events on that call's stream (a small cost per launch). oomb_profile_collect
+ * waits for the recorded events, writes up to `max` (kernel name, milliseconds)
+ * pairs in launch order, releases the events and returns how many it wrote. Names
+ * are static strings owned by the library. */
+int oomb_profile_enable(int on);
+int oomb_profile_collect(const char** names, float* ms, int max);
 
 #ifdef __cplusplus
 }

@@ -117,8 +117,9 @@ def select_workspace_bytes(pool: PagedPool, n_q: int, t0: int) -> int:
     return int(lib().oomb_select_workspace_bytes(pool.ref(), n_q, t0))
 
 
-def bwd_workspace_bytes(pool: PagedPool, n_q: int) -> int:
-    return int(lib().oomb_bwd_workspace_bytes(pool.ref(), n_q))
+def bwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1) -> int:
+    """Workspace of oomb_paged_chunk_attn_bwd (sel_stride = -1 for dense calls)."""
+    return int(lib().oomb_bwd_workspace_bytes(pool.ref(), n_q, t0, sel_stride))
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
@@ -205,10 +206,32 @@ def oomb_paged_chunk_attn_bwd(pool: PagedPool, table: torch.Tensor, gtable: torc
     qhs, qts = _view(dq, pool, pool.num_q_heads, "dq", torch.float32)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
         raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
-    ws = _workspace(bwd_workspace_bytes(pool, n_q), q.device, workspace)
     sel_stride = 0 if sel is None else sel.stride(0)
+    ws = _workspace(bwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride),
+                    q.device, workspace)
     call("oomb_paged_chunk_attn_bwd", pool.ref(), _ptr(table), table.stride(0), _ptr(gtable),
          gtable.stride(0), _ptr(q), hs, ts, n_q, t0, _ptr(sel), sel_stride, _ptr(count),
          float(scale), _ptr(o), ohs, ots, _ptr(dout), dhs, dts, _ptr(lse), _ptr(dq), qhs, qts,
          _ptr(ws), ws.numel(), _stream(stream))
     return dq
+
+
+class kernel_timer:
+    """Context manager: time every kernel the library launches on this thread with
+    HIP events. After exit, `records` holds (kernel name, milliseconds) pairs."""
+
+    def __init__(self, max_records: int = 1 << 16):
+        self.max_records = max_records
+        self.records = []
+
+    def __enter__(self):
+        lib().oomb_profile_enable(1)
+        return self
+
+    def __exit__(self, *exc):
+        lib().oomb_profile_enable(0)
+        names = (ctypes.c_char_p * self.max_records)()
+        ms = (ctypes.c_float * self.max_records)()
+        n = lib().oomb_profile_collect(names, ms, self.max_records)
+        self.records = [(names[i].decode(), float(ms[i])) for i in range(n)]
+        return False

@@ -28,6 +28,7 @@ SOURCES = {
     "attn_scalar.hip": [],
     "attn_mfma.hip": [],
     "api.cpp": [],
+    "profiling.cpp": [],
 }
 
 COMMON = [

@@ -185,7 +185,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 1; }
+int oomb_abi_version(void) { return 2; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -319,10 +319,26 @@ int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64
                     "paged_chunk_attn_fwd");
 }
 
-size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q) {
-  oomb::PoolView v{};
-  if (check_pool(pool, &v, false, false) != OOMB_OK || n_q <= 0) return 0;
-  return align256(static_cast<size_t>(v.Hq) * n_q * sizeof(float));
+// Backward workspace: Delta [Hq][n_q] fp32, then (for the matrix-core path, when the
+// dK/dV pass is split over the query stream) the fp32 split partials.
+static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part) {
+  const size_t delta = align256(static_cast<size_t>(a.pool.Hq) * a.n_q * sizeof(float));
+  *off_part = delta;
+  if (!use_mfma(a.pool)) return delta;
+  return delta + align256(oomb::dkdv_partial_bytes(a, oomb::dkdv_splits(a)));
+}
+
+size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
+                                int64_t sel_stride) {
+  oomb::AttnArgs a{};
+  if (check_pool(pool, &a.pool, false, false) != OOMB_OK) return 0;
+  ChunkGeom cg;
+  if (check_chunk(a.pool, n_q, t0, &cg) != OOMB_OK) return 0;
+  a.n_q = n_q;
+  const int64_t prior = sel_stride >= 0 ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
+  a.max_att_pages = static_cast<int>(prior + cg.n_local);
+  size_t off;
+  return bwd_workspace(a, &off);
 }
 
 int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
@@ -345,7 +361,8 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(OOMB_ERR_INVALID, "lse must be a 4-byte aligned device pointer");
   if (!(scale > 0.0f) || scale > 1e30f) return fail(OOMB_ERR_INVALID, "scale must be positive and finite");
-  const size_t need = align256(static_cast<size_t>(a.pool.Hq) * n_q * sizeof(float));
+  size_t off_part = 0;
+  const size_t need = bwd_workspace(a, &off_part);
   if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(OOMB_ERR_WORKSPACE, "bwd needs %zu bytes of 256-byte aligned workspace", need);
   a.gtable = gtable;
@@ -363,8 +380,9 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   a.dq_ts = dq_tok_stride;
   a.delta = static_cast<float*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(use_mfma(a.pool) ? oomb::launch_bwd_mfma(a, s) : oomb::launch_bwd_scalar(a, s),
-                    "paged_chunk_attn_bwd");
+  if (!use_mfma(a.pool)) return hip_status(oomb::launch_bwd_scalar(a, s), "paged_chunk_attn_bwd");
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
+  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, s), "paged_chunk_attn_bwd");
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@
 // P = exp(s - LSE) and writes dQ and adds dK/dV into the gradient pool.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "profiling.hpp"
 
 namespace oomb {
 
@@ -210,19 +211,16 @@ __global__ __launch_bounds__(256) void dkdv_scalar_kernel(AttnArgs a) {
   }
 }
 
-template <template <typename, int> class K>
-static void dispatch(const AttnArgs& a, dim3 grid, hipStream_t s);
-
 #define OOMB_DISPATCH(KERNEL, GRID)                                                       \
   do {                                                                                    \
     if (a.pool.dtype == 0 && a.pool.D == 128)                                             \
-      hipLaunchKernelGGL((KERNEL<bf16_t, 128>), GRID, dim3(256), 0, s, a);                \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<bf16_t, 128>), GRID, dim3(256), 0, s, a);                \
     else if (a.pool.dtype == 0)                                                           \
-      hipLaunchKernelGGL((KERNEL<bf16_t, 64>), GRID, dim3(256), 0, s, a);                 \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<bf16_t, 64>), GRID, dim3(256), 0, s, a);                 \
     else if (a.pool.D == 128)                                                             \
-      hipLaunchKernelGGL((KERNEL<float, 128>), GRID, dim3(256), 0, s, a);                 \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<float, 128>), GRID, dim3(256), 0, s, a);                 \
     else                                                                                  \
-      hipLaunchKernelGGL((KERNEL<float, 64>), GRID, dim3(256), 0, s, a);                  \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<float, 64>), GRID, dim3(256), 0, s, a);                  \
   } while (0)
 
 hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s) {

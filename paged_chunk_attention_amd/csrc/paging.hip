@@ -8,6 +8,7 @@
 // (explainer 2.D), in the form used by Quest (cited by the paper).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "profiling.hpp"
 
 namespace oomb {
 
@@ -42,7 +43,7 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s) {
   int64_t blocks = (total + 255) / 256;
   if (blocks > 256 * 32) blocks = 256 * 32;
   if (blocks < 1) return hipSuccess;
-  hipLaunchKernelGGL(kv_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  OOMB_LAUNCH("kv_append", kv_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -122,9 +123,9 @@ hipError_t launch_page_summarize(const SummarizeArgs& a, hipStream_t s) {
   if (a.n_pages <= 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(a.n_pages), a.pool.Hkv);
   if (a.pool.dtype == 0)
-    hipLaunchKernelGGL(page_summarize_kernel<true>, grid, dim3(256), 0, s, a);
+    OOMB_LAUNCH("page_summarize", page_summarize_kernel<true>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(page_summarize_kernel<false>, grid, dim3(256), 0, s, a);
+    OOMB_LAUNCH("page_summarize", page_summarize_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

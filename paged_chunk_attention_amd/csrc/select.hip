@@ -15,6 +15,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "profiling.hpp"
 
 namespace oomb {
 
@@ -200,23 +201,23 @@ static void launch_scores(const SelectArgs& a, hipStream_t s) {
   const bool bf = a.pool.dtype == 0;
   const int D = a.pool.D;
   dim3 g1(a.nb, a.pool.Hkv);
-  if (bf) hipLaunchKernelGGL(qbar_partial_kernel<true>, g1, dim3(128), 0, s, a);
-  else hipLaunchKernelGGL(qbar_partial_kernel<false>, g1, dim3(128), 0, s, a);
+  if (bf) OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<true>, g1, dim3(128), 0, s, a);
+  else OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<false>, g1, dim3(128), 0, s, a);
   int n2 = 1;
   while (n2 < a.nb) n2 <<= 1;
-  hipLaunchKernelGGL(qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
+  OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
   dim3 g3((a.n_cand + 3) / 4, a.pool.Hkv);
-  if (bf && D == 128) hipLaunchKernelGGL((page_score_kernel<true, 128>), g3, dim3(256), 0, s, a);
-  else if (bf) hipLaunchKernelGGL((page_score_kernel<true, 64>), g3, dim3(256), 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((page_score_kernel<false, 128>), g3, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((page_score_kernel<false, 64>), g3, dim3(256), 0, s, a);
+  if (bf && D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<true, 128>), g3, dim3(256), 0, s, a);
+  else if (bf) OOMB_LAUNCH("page_score", (page_score_kernel<true, 64>), g3, dim3(256), 0, s, a);
+  else if (D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<false, 128>), g3, dim3(256), 0, s, a);
+  else OOMB_LAUNCH("page_score", (page_score_kernel<false, 64>), g3, dim3(256), 0, s, a);
 }
 
 // Scores are always computed when there are candidates (the top-k needs them unless
 // k = 0 or k >= n_cand; the query summary and scores are also diagnostics).
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (a.n_cand > 0) launch_scores(a, s);
-  hipLaunchKernelGGL(topk_kernel, dim3(a.pool.Hkv), dim3(kTopkThreads), 0, s, a);
+  OOMB_LAUNCH("topk", topk_kernel, dim3(a.pool.Hkv), dim3(kTopkThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,14 +28,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 1
+    assert lib.oomb_abi_version() == 2
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text
@@ -127,8 +127,9 @@ def test_summarize_and_select_errors(lib):
 def test_bwd_errors(lib):
     p = _pool()
     nograd = _pool(dk_pool=None)
-    need = lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096)
-    assert need == 28 * 4096 * 4
+    need = lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1)
+    assert need >= 28 * 4096 * 4 and need % 256 == 0
+    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 0, 4096, -1) == 0
 
     def bwd(pool, **kw):
         a = dict(gtable=T, gts=64, dq=B, dqhs=4096 * 128, dqts=128, ws=0xA00000, wsb=need)
