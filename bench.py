@@ -36,6 +36,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (profiles/<workload>_step_traffic.txt, FETCH_SIZE/WRITE_SIZE scaled by a copy of
+    known size), or None when there is none or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_step_traffic.txt")
+    src = os.path.join(ROOT, "paged_chunk_attention_amd", "csrc", "attn_mfma.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    fields = {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 2 and parts[0] == "source_sha256_16":
+            fields["sha"] = parts[1]
+        elif len(parts) == 4 and parts[0] == "kernel":
+            fields[parts[1]] = (int(parts[2]), int(parts[3]))
+    if fields.get("sha") != sha:
+        return None
+    rec = fields.get(kernel + "_kernel") or fields.get(kernel)
+    return None if rec is None else {"read_bytes": rec[0], "write_bytes": rec[1],
+                                     "bytes": rec[0] + rec[1]}
+
+
 def attended_pairs(w, counts):
     """(query, key) pairs the chunk attends, summed over query heads."""
     C, P, t0 = w.chunk, w.page, w.t0
@@ -155,6 +179,14 @@ def main():
         pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, s_, c_, o, do, lse, w.scale,
                                       dq=dq, workspace=ws_bwd)
 
+    # One plain copy of known size, untimed: under rocprofv3 --pmc its FETCH_SIZE and
+    # WRITE_SIZE calibrate the counters against 256 MiB read + 256 MiB written.
+    calib_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -189,8 +221,11 @@ def main():
     dom_ms = per_kernel[dom][0] / per_kernel[dom][1]
     if dom in FLOP_PER_PAIR_D:
         ach = FLOP_PER_PAIR_D[dom] * w.d * pairs / (dom_ms * 1e-3) / 1e12
+        tr = measured_traffic(w.name, dom)
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "traffic": None if tr is None else tr["bytes"],
+                "traffic_detail": tr,
                 "algorithmic_flop_per_launch": FLOP_PER_PAIR_D[dom] * w.d * pairs,
                 "ms_per_launch": dom_ms}
     else:

@@ -276,9 +276,13 @@ void fwd_mfma_kernel(AttnArgs a) {
     f32x16 st[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      bf16x8 ka[8];  // all fragments first, so the MFMA chain does not wait per step
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) ka[kk] = row_frag(kt, 32 * sub, kk, lane);
+      __builtin_amdgcn_sched_barrier(0);
       st[sub] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) st[sub] = mfma(row_frag(kt, 32 * sub, kk, lane), qf[kk], st[sub]);
+      for (int kk = 0; kk < 8; ++kk) st[sub] = mfma(ka[kk], qf[kk], st[sub]);
     }
     // Causal / tail mask, only in blocks that reach past the tile's first query.
     if (b * KB + KB - 1 > klim_tile) {
@@ -317,14 +321,18 @@ void fwd_mfma_kernel(AttnArgs a) {
         }
         pb[sub][s] = pack8(p);
       }
-    // O^T += V^T P^T.
+    // O^T += V^T P^T, four transposed fragments in flight per step.
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 va[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          ot[db] = mfma(tr_frag(vt, 32 * sub, 32 * db, s, lane), pb[sub][s], ot[db]);
+        for (int db = 0; db < 4; ++db) va[db] = tr_frag(vt, 32 * sub, 32 * db, s, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) ot[db] = mfma(va[db], pb[sub][s], ot[db]);
+      }
 
     if (b + 1 < nblk) ks.store(sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
     __syncthreads();
@@ -425,10 +433,14 @@ void dq_mfma_kernel(AttnArgs a) {
       }
       // dQ^T += K^T dS^T.
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 ta[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          dqt[db] = mfma(tr_frag(kt, 32 * sub, 32 * db, s, lane), dsb[s], dqt[db]);
+        for (int db = 0; db < 4; ++db) ta[db] = tr_frag(kt, 32 * sub, 32 * db, s, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqt[db] = mfma(ta[db], dsb[s], dqt[db]);
+      }
     }
     if (b + 1 < nblk) ks.store(sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
     __syncthreads();
@@ -546,9 +558,10 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
       rd[i] = y;
     }
     if (tid < QTB) {
+      // raw loads only: any arithmetic on them here would wait for the whole prefetch
       const int qi = q0 + tid;
       const int64_t rid = static_cast<int64_t>(hq) * a.n_q + qi;
-      r_lse2 = qi < a.n_q ? a.lse_in[rid] * kLog2e : __builtin_inff();
+      r_lse2 = qi < a.n_q ? a.lse_in[rid] : __builtin_inff();
       r_delta = qi < a.n_q ? a.delta[rid] : 0.0f;
     }
   };
@@ -561,7 +574,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
       sts16(sm.d[buf], toff(r, 8 * c), rd[i]);
     }
     if (tid < QTB) {
-      sm.lse2[buf][tid] = r_lse2;
+      sm.lse2[buf][tid] = r_lse2 * kLog2e;
       sm.delta[buf][tid] = r_delta;
     }
   };
@@ -581,13 +594,32 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
     const bool wmask = __any(kpos > a.t0 + q0);
 #pragma unroll
     for (int us = 0; us < QTB / 32; ++us) {
-      // S = Q K^T and dP = dO V^T over d: 32 queries x this wave's 32 keys.
+      // Phase 1: all row fragments of Q and dO in registers, then S = Q K^T and
+      // dP = dO V^T (two independent chains) for 32 queries x this wave's 32 keys.
+      bf16x8 qa[8], da[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        qa[kk] = row_frag(qt, 32 * us, kk, lane);
+        da[kk] = row_frag(dt, 32 * us, kk, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s_acc = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        s_acc = mfma(row_frag(qt, 32 * us, kk, lane), kf[kk], s_acc);
-        dp = mfma(row_frag(dt, 32 * us, kk, lane), vf[kk], dp);
+        s_acc = mfma(qa[kk], kf[kk], s_acc);
+        dp = mfma(da[kk], vf[kk], dp);
       }
+      // Phase 2: transposed fragments of dO and Q for dV / dK, issued before the
+      // softmax arithmetic so that their latency hides behind it.
+      bf16x8 tdo[2][4], tq[2][4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          tdo[s][nb] = tr_frag(dt, 32 * us, 32 * nb, s, lane);
+          tq[s][nb] = tr_frag(qt, 32 * us, 32 * nb, s, lane);
+        }
+      __builtin_amdgcn_sched_barrier(0);
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -611,13 +643,14 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         pb[s] = pack8(p);
         dsb[s] = pack8(ds);
       }
-      // dV += P^T dO, dK += dS^T Q (the scale is applied once, at the end).
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase 3: dV += P^T dO, dK += dS^T Q (the scale is applied once, at the end).
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          dv[nb] = mfma(pb[s], tr_frag(dt, 32 * us, 32 * nb, s, lane), dv[nb]);
-          dk[nb] = mfma(dsb[s], tr_frag(qt, 32 * us, 32 * nb, s, lane), dk[nb]);
+          dv[nb] = mfma(pb[s], tdo[s][nb], dv[nb]);
+          dk[nb] = mfma(dsb[s], tq[s][nb], dk[nb]);
         }
     }
     if (u + 1 < u_end) store_tile(buf ^ 1);
