@@ -89,17 +89,25 @@ def summarize(k_pool, table, summary, first_page: int, n_pages: int, seq_len: in
     depends on evaluation order). Pages without a valid token are left unchanged."""
     P = k_pool.shape[1]
     for g in range(table.shape[0]):
-        for j in range(first_page, first_page + n_pages):
-            n_valid = min(P, seq_len - j * P)
-            if n_valid <= 0:
+        pages = torch.arange(first_page, first_page + n_pages)
+        n_valid = torch.clamp(seq_len - pages * P, max=P)
+        # pages whose every token is valid, a batch at a time
+        full = pages[n_valid == P]
+        for b0 in range(0, len(full), 2048):
+            phys = table[g].long()[full[b0:b0 + 2048]]
+            x = k_pool[phys]                                   # [n, P, D]
+            key = total_order_key(x)
+            summary[phys, 0] = torch.gather(x, 1, key.argmin(dim=1, keepdim=True))[:, 0]
+            summary[phys, 1] = torch.gather(x, 1, key.argmax(dim=1, keepdim=True))[:, 0]
+        # partially filled pages, one at a time
+        for j, nv in zip(pages.tolist(), n_valid.tolist()):
+            if nv <= 0 or nv == P:
                 continue
             phys = int(table[g, j])
-            x = k_pool[phys, :n_valid]
+            x = k_pool[phys, :nv]
             key = total_order_key(x)
-            lo = torch.gather(x, 0, key.argmin(dim=0, keepdim=True))[0]
-            hi = torch.gather(x, 0, key.argmax(dim=0, keepdim=True))[0]
-            summary[phys, 0] = lo
-            summary[phys, 1] = hi
+            summary[phys, 0] = torch.gather(x, 0, key.argmin(dim=0, keepdim=True))[0]
+            summary[phys, 1] = torch.gather(x, 0, key.argmax(dim=0, keepdim=True))[0]
 
 
 # ---------------------------------------------------------------------------

@@ -83,11 +83,11 @@ WORKLOADS = {
 }
 
 
-def custom(name: str, **kw) -> Workload:
+def custom(base_name: str, **kw) -> Workload:
     """A reduced workload with the same structure (for parity tests at small sizes)."""
-    base = dataclasses.asdict(WORKLOADS[name])
+    base = dataclasses.asdict(WORKLOADS[base_name])
     base.update(kw)
-    base["name"] = kw.get("name", name + "_custom")
+    base["name"] = kw.get("name", base_name + "_custom")
     return Workload(**base)
 
 
