@@ -40,12 +40,11 @@ def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (profiles/<workload>_step_traffic.txt, FETCH_SIZE/WRITE_SIZE scaled by a copy of
     known size), or None when there is none or the kernel source changed since."""
-    import hashlib
+    from paged_chunk_attention_amd.build import mfma_source_hash
     path = os.path.join(ROOT, "profiles", f"{workload}_step_traffic.txt")
-    src = os.path.join(ROOT, "paged_chunk_attention_amd", "csrc", "attn_mfma.hip")
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = mfma_source_hash()
     fields = {}
     for line in open(path):
         parts = line.split()

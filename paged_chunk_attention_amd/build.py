@@ -26,7 +26,12 @@ SOURCES = {
     # the selector's float arithmetic must not be contracted into fused multiply-adds
     "select.hip": ["-ffp-contract=off"],
     "attn_scalar.hip": [],
-    "attn_mfma.hip": [],
+    "attn_fwd_mfma.hip": [],
+    "attn_dq_mfma.hip": [],
+    # one wave per SIMD with ~400 live registers: MFMA results in VGPRs (the softmax
+    # reads them) and the ILP-first scheduler measure faster for this kernel
+    "attn_dkdv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                           "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "api.cpp": [],
     "profiling.cpp": [],
 }
@@ -38,6 +43,23 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
+
+
+# Sources of the matrix-core attention kernels, whose hash tags measured profiles.
+MFMA_SOURCES = ["device_common.hpp", "mfma_tiles.hpp", "attn_fwd_mfma.hip",
+                "attn_dq_mfma.hip", "attn_dkdv_mfma.hip"]
+
+
+def mfma_source_hash() -> str:
+    """First 16 hex digits of the sha256 over the matrix-core kernel sources and their
+    compile flags (a profile taken from other sources no longer describes the kernels)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in MFMA_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+        h.update(" ".join(SOURCES.get(name, [])).encode())
+    return h.hexdigest()[:16]
 
 
 def hipcc() -> str:

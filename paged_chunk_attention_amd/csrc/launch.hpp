@@ -102,6 +102,8 @@ hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
 // n_split > 1 splits the dK/dV pass over the query stream; `part` then holds
 // dkdv_partial_bytes(a, n_split) bytes of fp32 partials.
 hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, hipStream_t s);
+// dQ pass of the matrix-core backward (launched by launch_bwd_mfma after Delta).
+hipError_t launch_dq_mfma(const AttnArgs& a, hipStream_t s);
 int dkdv_splits(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, int n_split);
 // Delta_i = dO_i . O_i, shared by both backward paths.
