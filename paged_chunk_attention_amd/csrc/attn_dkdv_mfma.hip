@@ -114,10 +114,10 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
     }
   };
 
-  zero_tile(s_q0, tid);
-  zero_tile(s_d0, tid);
-  zero_tile(s_q1, tid);
-  zero_tile(s_d1, tid);
+  zero_tile<QTB, 256>(s_q0, tid);
+  zero_tile<QTB, 256>(s_d0, tid);
+  zero_tile<QTB, 256>(s_q1, tid);
+  zero_tile<QTB, 256>(s_d1, tid);
   __syncthreads();
   if (u_begin < u_end) issue_tile(u_begin, s_q0, s_d0);
   wait_dma();

@@ -61,7 +61,7 @@ __device__ __forceinline__ void reg_prefetch_next(RegKeyStream& ks, DqSmem& sm, 
   const int last_e = ((b + 1) * KB + KB - 1) >> km.log2p;
   if (last_e >= ks.win + PCAP) {  // uniform over the workgroup
     ks.win = ((b + 1) * KB) >> km.log2p;
-    fill_pages(km, sm.page, ks.win, tid);
+    fill_pages<256>(km, sm.page, ks.win, tid);
     __syncthreads();
   }
   ks.load(b + 1, tid);
@@ -108,7 +108,7 @@ void dq_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) dqt[db] = f32x16{};
 
-  fill_pages(km, sm.page, 0, tid);
+  fill_pages<256>(km, sm.page, 0, tid);
   __syncthreads();
   RegKeyStream ks{km, sm.page, 0, a.pool.k_pool, a.pool.v_pool};
   if (nblk > 0) {

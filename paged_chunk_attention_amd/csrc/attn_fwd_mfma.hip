@@ -1,32 +1,66 @@
 // Matrix-core forward of paged chunk attention (online softmax over the attended
 // key blocks; writes O and the log-sum-exp the backward recomputes P from).
+//
+// A workgroup is 8 wavefronts and owns 256 queries of one head, 32 per wavefront;
+// wavefronts w and w + 4 share a SIMD. Each wavefront alternates two kinds of phase:
+//   M(b): O^T += V_b^T P_b^T and S_{b+1}^T = K_{b+1} Q^T   (matrix cores, LDS reads)
+//   V(b): mask, row max, lazy rescale, P_b = exp2(S_b - m)  (vector ALU)
+// and the second group (waves 4..7) runs one phase behind the first, so on every SIMD
+// one wavefront is in an M phase while the other is in a V phase ("ping-pong"). A
+// barrier ends every phase. K and V blocks of 64 keys arrive by global -> LDS DMA four
+// phases ahead of their first use, in triple buffers whose roles are static in each of
+// the six phases of the loop body: no read ever waits for a DMA into a buffer it does
+// not read, and each wave waits only for its batch of two phases ago.
+#include <type_traits>
+
 #include "mfma_tiles.hpp"
 
 namespace oomb {
 namespace mf {
 
-// ============================================================================ forward
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+constexpr int FWD_WAVES = 8;
+constexpr int FWD_Q = 32 * FWD_WAVES;  // queries per workgroup
+
+// Page ids held in LDS: all of them when a head attends at most FWD_CAP pages (no window
+// slides, and no slide code in the loop), else a window of PCAP that slides.
+constexpr int FWD_CAP = 8192;
+
+template <int CAP, bool SLIDE>
+__global__ __launch_bounds__(64 * FWD_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_mfma_kernel(AttnArgs a) {
-  OOMB_KV_BUFFERS
-  constexpr int QT = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k2[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v2[KB * D];
+  __shared__ int s_page[CAP];
+  constexpr int NT = 64 * FWD_WAVES;
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: leading group, 1: one phase behind
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
-  const int n_qt = (a.n_q + QT - 1) / QT;
+  const int n_qt = (a.n_q + FWD_Q - 1) / FWD_Q;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hh = L % G, rest = L / G;
-  const int qt = rest % n_qt, g = rest / n_qt;
+  // Latest query tiles (most local keys, the longest) are dispatched first.
+  const int qt = n_qt - 1 - rest % n_qt, g = rest / n_qt;
   const int h = g * G + hh;
   const Keys km = make_keys(a, g);
-  const int q0 = qt * QT;
-  const int klim_tile = km.klim(a.t0 + q0);
-  const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + QT) - 1);
+  const int q0 = qt * FWD_Q;
+  const int nb = n_blocks(km, a.t0 + min(a.n_q, q0 + FWD_Q) - 1);  // key blocks of the tile
   const float c2 = a.scale * kLog2e;
 
+  // This wave's queries: blocks past its last query are skipped; blocks reaching past
+  // its first query need the mask.
+  const int wq0 = q0 + 32 * wave;
+  const int wq_last = min(a.n_q, wq0 + 32) - 1;
+  const int nblk_w = wq_last < wq0 ? 0 : n_blocks(km, a.t0 + wq_last);
+  const int klim_w0 = km.klim(a.t0 + wq0);
+
   // This lane's query (column of S^T) and its Q fragments (B operand over d).
-  const int i = q0 + wave * 32 + col;
+  const int i = wq0 + col;
   const int klim = km.klim(a.t0 + i);
   bf16x8 qf[8];
   {
@@ -41,29 +75,85 @@ void fwd_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) ot[db] = f32x16{};
   float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x16 st[2];     // S^T of the block last multiplied: from its M phase to its V phase
+  bf16x8 pb[2][2];  // P^T of the block last normalised: from its V phase to the next M phase
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    st[sub] = f32x16{};
+    pb[sub][0] = pb[sub][1] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
 
-  KeyStream ks{km, s_page, 0, static_cast<const uint16_t*>(a.pool.k_pool),
-               static_cast<const uint16_t*>(a.pool.v_pool)};
-  start_stream(ks, s_page, km, nblk, tid, wave, lane, s_k0, s_v0, s_k1, s_v1);
-  // One key block: prefetch block b + 1 into (kn, vn), compute block b from (kt, vt).
-  auto step = [&](int b, const uint16_t* kt, const uint16_t* vt, uint16_t* kn,
-                  uint16_t* vn) __attribute__((always_inline)) {
-    prefetch_next(ks, s_page, km, b, nblk, tid, wave, lane, kn, vn);
+  FragOffsets fo;
+  fo.init(lane);
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.pool.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.pool.v_pool);
+  // All 8 waves stage the first blocks; afterwards each group of 4 stages one tensor.
+  KeyStage<KB, FWD_WAVES, CAP> ks{km, s_page, 0, kpool, vpool,
+                                  KeyStage<KB, FWD_WAVES, CAP>::lane_offset(wave, lane)};
+  KeyStage<KB, 4, CAP> kg{km, s_page, 0, kpool, vpool,
+                          KeyStage<KB, 4, CAP>::lane_offset(wave & 3, lane)};
+  fill_pages<NT, CAP>(km, s_page, 0, tid);
+  zero_tile<KB, NT>(s_v1, tid);  // read (times a zero P^T) before their first DMA
+  zero_tile<KB, NT>(s_v2, tid);
+  wait_dma();  // the page-table loads are retired here, not at a later register reuse
+  __syncthreads();
+  // K_0, K_1 and V_0 before the first phase; every later block arrives four phases
+  // ahead of its first use.
+  ks.issue_fixed(0, kpool, s_k0, wave, lane);
+  ks.issue_fixed(1, kpool, s_k1, wave, lane);
+  ks.issue_fixed(0, vpool, s_v0, wave, lane);
+  wait_dma();
+  __syncthreads();
 
-    // S^T = K Q^T for the block's two 32-key halves (raw dot products).
-    f32x16 st[2];
+  // Both products of an M phase as one software pipeline of eight steps of four MFMAs:
+  // four PV steps (one k-step of one 32-key half each) then four S steps (k-steps 2i and
+  // 2i + 1 of both halves, alternating halves so that consecutive MFMAs are
+  // independent). The fragments of step i + 1 are read from LDS while step i multiplies.
+  auto mul_pv_s = [&](const uint16_t* vt, const uint16_t* kt) __attribute__((always_inline)) {
+    FragOffsets o = fo;
+    o.opaque();
+    auto load = [&](int i, bf16x8 (&f)[4]) __attribute__((always_inline)) {
+      if (i < 4) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      bf16x8 ka[8];  // all fragments first, so the MFMA chain does not wait per step
+        for (int db = 0; db < 4; ++db) f[db] = tr_frag_at(vt, 32 * (i >> 1), i & 1, o, db);
+      } else {
+        const int kk = 2 * (i - 4);
+        f[0] = row_frag_at(kt, 0, o, kk);
+        f[1] = row_frag_at(kt, 32, o, kk);
+        f[2] = row_frag_at(kt, 0, o, kk + 1);
+        f[3] = row_frag_at(kt, 32, o, kk + 1);
+      }
+    };
+    auto mul = [&](int i, const bf16x8 (&f)[4]) __attribute__((always_inline)) {
+      if (i < 4) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) ka[kk] = row_frag(kt, 32 * sub, kk, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      st[sub] = f32x16{};
+        for (int db = 0; db < 4; ++db) ot[db] = mfma(f[db], pb[i >> 1][i & 1], ot[db]);
+      } else {
+        const int kk = 2 * (i - 4);
+        if (i == 4) {
+          st[0] = f32x16{};
+          st[1] = f32x16{};
+        }
+        st[0] = mfma(f[0], qf[kk], st[0]);
+        st[1] = mfma(f[1], qf[kk], st[1]);
+        st[0] = mfma(f[2], qf[kk + 1], st[0]);
+        st[1] = mfma(f[3], qf[kk + 1], st[1]);
+      }
+    };
+    bf16x8 fa[4], fb[4];
+    load(0, fa);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) st[sub] = mfma(ka[kk], qf[kk], st[sub]);
+    for (int i = 0; i < 8; i += 2) {
+      load(i + 1, fb);
+      mul(i, fa);
+      if (i + 2 < 8) load(i + 2, fa);
+      mul(i + 1, fb);
     }
-    // Causal / tail mask, only in blocks that reach past the tile's first query.
-    if (b * KB + KB - 1 > klim_tile) {
+  };
+  // Softmax numerator of block b from st into pb.
+  auto softmax = [&](int b) __attribute__((always_inline)) {
+    // Causal / tail mask, only in blocks that reach past this wave's first query.
+    if (b * KB + KB - 1 > klim_w0) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -78,7 +168,7 @@ void fwd_mfma_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r)
         if (sub || r >= 4) mx4[r & 3] = fmaxf(mx4[r & 3], st[sub][r]);
     float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    mx = max_halves(mx) * c2;
     // Lazy rescale: move the reference only when the maximum grew by more than 2^kTau.
     const bool grow = mx > m_run + kTau;
     if (__any(grow)) {
@@ -89,7 +179,6 @@ void fwd_mfma_kernel(AttnArgs a) {
       for (int db = 0; db < 4; ++db) ot[db] *= alpha;
     }
     const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
-    bf16x8 pb[2][2];
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // partial row sums (short dependency chains)
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -104,30 +193,85 @@ void fwd_mfma_kernel(AttnArgs a) {
         pb[sub][s] = pack8(p);
       }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // O^T += V^T P^T, four transposed fragments in flight per step.
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 va[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) va[db] = tr_frag(vt, 32 * sub, 32 * db, s, lane);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) ot[db] = mfma(va[db], pb[sub][s], ot[db]);
-      }
-
-    wait_dma();  // block b + 1 has landed (this wave's part) ...
-    __syncthreads();  // ... everyone's, and nobody reads block b any more
   };
-  // Unrolled by two so that each half names its read and write buffers statically.
-  for (int b = 0; b < nblk; b += 2) {
-    step(b, s_k0, s_v0, s_k1, s_v1);
-    if (b + 1 < nblk) step(b + 1, s_k1, s_v1, s_k0, s_v0);
+
+  // Phase t, j = t / 2. DMA duties, always in the wave's V phase: at even t the second
+  // group stages K_{j+2} into kd, at odd t the first group stages V_{j+1} into vd, a
+  // fixed number of instructions each, and each wave waits (at the end of each phase in
+  // which it issued) for all but the batch it just issued. A wave's own phase index is
+  // u = t - grp: u = 0 computes S_0; odd u runs V(u / 2); even u >= 2 runs M(u / 2 - 1).
+  // kr / vr hold K_{b+1} / V_b of whichever M phase runs. Block j's K and V live in
+  // buffer j % 3. IS_M and G1 (compile time) make every phase straight-line code.
+  auto phase = [&](auto is_m, auto g1, int t, uint16_t* kd, uint16_t* vd, const uint16_t* kr,
+                   const uint16_t* vr) __attribute__((always_inline)) {
+    constexpr bool kG1 = decltype(g1)::value;
+    const int j = t >> 1;
+    if constexpr (SLIDE) {
+      if ((t & 1) == 0) {
+        const int last_e = (min(nb, j + 3) * KB - 1) >> km.log2p;
+        if (j + 1 < nb && last_e >= ks.win + CAP) {  // uniform: slide the page window
+          ks.win = kg.win = ((j + 1) * KB) >> km.log2p;
+          fill_pages<NT, CAP>(km, s_page, ks.win, tid);
+          wait_dma();
+          __syncthreads();
+        }
+      }
+    }
+    // DMA duty: its page ids are read first (LDS reads queue behind the M phases' tile
+    // reads), the DMA itself is issued after this wave's softmax.
+    const bool dma = kG1 ? (t & 1) == 0 : (t & 1) == 1;
+    const int dst = kG1 ? j + 2 : j + 1;
+    int pid[KeyStage<KB, 4, CAP>::NI];
+    if (dma) kg.read_pages(dst, wave & 3, pid);
+    const int u = t - grp;
+    if constexpr (decltype(is_m)::value) {
+      const int b = (u >> 1) - 1;  // M(b): PV of block b, S of block b + 1
+      if (u >= 0) {
+        __builtin_amdgcn_s_setprio(1);
+        // M(-1) multiplies the zero P^T by the zero-filled V buffer (adds exact zeros);
+        // M(nblk_w - 1) computes an S^T no softmax will read.
+        if (b < nblk_w) mul_pv_s(vr, kr);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    } else {
+      const int b = u >> 1;
+      if (u >= 0 && b < nblk_w) softmax(b);
+    }
+    if (dma) {
+      __builtin_amdgcn_sched_barrier(0);
+      kg.dma_fixed(dst, kG1 ? kpool : vpool, kG1 ? kd : vd, wave & 3, lane, pid);
+      wait_vm<KeyStage<KB, 4, CAP>::NI>();  // the batch of two phases ago has landed
+    }
+    phase_barrier();
+  };
+  using M = std::integral_constant<bool, true>;
+  using V = std::integral_constant<bool, false>;
+  const int T = 2 * nb + 2;
+  if (grp == 0) {
+    using G = std::integral_constant<bool, false>;
+    for (int t = 0; t < T; t += 6) {
+      phase(M{}, G{}, t + 0, s_k2, nullptr, s_k0, s_v2);
+      phase(V{}, G{}, t + 1, nullptr, s_v1, s_k0, s_v2);
+      phase(M{}, G{}, t + 2, s_k0, nullptr, s_k1, s_v0);
+      phase(V{}, G{}, t + 3, nullptr, s_v2, s_k1, s_v0);
+      phase(M{}, G{}, t + 4, s_k1, nullptr, s_k2, s_v1);
+      phase(V{}, G{}, t + 5, nullptr, s_v0, s_k2, s_v1);
+    }
+  } else {
+    using G = std::integral_constant<bool, true>;
+    for (int t = 0; t < T; t += 6) {
+      phase(V{}, G{}, t + 0, s_k2, nullptr, s_k0, s_v2);
+      phase(M{}, G{}, t + 1, nullptr, s_v1, s_k0, s_v2);
+      phase(V{}, G{}, t + 2, s_k0, nullptr, s_k1, s_v0);
+      phase(M{}, G{}, t + 3, nullptr, s_v2, s_k1, s_v0);
+      phase(V{}, G{}, t + 4, s_k1, nullptr, s_k2, s_v1);
+      phase(M{}, G{}, t + 5, nullptr, s_v0, s_k2, s_v1);
+    }
   }
+  wait_dma();  // no DMA may outlive the workgroup's LDS
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
+  const float lt = add_halves(l_run);
   const float inv = 1.0f / lt;
   if (i < a.n_q) {
     uint16_t* orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + static_cast<int64_t>(i) * a.o_ts;
@@ -147,8 +291,13 @@ void fwd_mfma_kernel(AttnArgs a) {
 }  // namespace mf
 
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s) {
-  const int n_qt = (a.n_q + 127) / 128;
-  OOMB_LAUNCH("fwd_mfma", mf::fwd_mfma_kernel, dim3(a.pool.Hq * n_qt), dim3(256), 0, s, a);
+  const int n_qt = (a.n_q + mf::FWD_Q - 1) / mf::FWD_Q;
+  const dim3 grid(a.pool.Hq * n_qt), block(64 * mf::FWD_WAVES);
+  if (a.max_att_pages <= mf::FWD_CAP) {
+    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::FWD_CAP, false>), grid, block, 0, s, a);
+  } else {
+    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::PCAP, true>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

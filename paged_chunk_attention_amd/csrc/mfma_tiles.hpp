@@ -56,6 +56,16 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// max(x[l], x[l ^ 32]) in every lane l, by one v_permlane32_swap (no LDS traffic).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- swizzled row-major tiles -----------------------------------------------------------
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 // Element offset of (row r, column c) with c a multiple of 4.
@@ -88,6 +98,48 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* t, int r0, int c0, int
   const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + toff(row + 8, col)));
   // a shuffle (not an element-wise rebuild) lets both loads land in one register quad
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Per-lane element offsets of every fragment of a [rows][128] tile: row fragments of k-step
+// kk (rows r0 + 32j share them, the swizzle repeating every 16 rows) and the two halves of
+// the transposed fragment of column block db (rows r0 + 16j share them). Keeping these
+// 16 values, rather than one address per fragment per buffer, keeps register use flat
+// however many LDS buffers a kernel reads; opaque() makes the compiler re-add the buffer
+// base at each use instead of keeping one address register per buffer and fragment.
+struct FragOffsets {
+  int rf[8];  // row fragment, k-step kk
+  int tr[8];  // transposed fragment, column block db: [2 db] rows +0, [2 db + 1] rows +8
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) rf[kk] = toff(lane & 31, 16 * kk + 8 * (lane >> 5));
+    const int s16 = lane & 15;
+    const int row = 4 * (lane >> 5) + (s16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+      tr[2 * db] = toff(row, col);
+      tr[2 * db + 1] = toff(row + 8, col);
+    }
+  }
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      asm volatile("" : "+v"(rf[i]));
+      asm volatile("" : "+v"(tr[i]));
+    }
+  }
+};
+// row_frag(t, r0, kk, lane) for r0 a multiple of 16 (of 32 for the swizzle to repeat:
+// swz depends on r % 16 only, so any multiple of 16 works).
+__device__ __forceinline__ bf16x8 row_frag_at(const uint16_t* t, int r0, const FragOffsets& o, int kk) {
+  return as_bf16x8(lds16(t + r0 * D, o.rf[kk]));
+}
+// tr_frag(t, r0, 32 db, s, lane) for r0 a multiple of 16.
+__device__ __forceinline__ bf16x8 tr_frag_at(const uint16_t* t, int r0, int s, const FragOffsets& o, int db) {
+  const uint16_t* b = t + (r0 + 16 * s) * D;
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.tr[2 * db]));
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + o.tr[2 * db + 1]));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Pack 8 fp32 (registers 8s..8s+7 of a C-layout accumulator) into a bf16 operand.
@@ -174,7 +226,27 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* ldst) 
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
-// Global column (in elements) that lane L of wave w fetches for its row: 8 * logical chunk.
+// Workgroup barrier without the release/acquire fences of __syncthreads(). Those fences
+// make the compiler wait for every outstanding global->LDS DMA of the wave, which would
+// defeat prefetching several phases ahead. Callers order the LDS data themselves: DMA
+// data by explicit vmcnt waits before the barrier, and a wave's own LDS reads are all
+// consumed (so complete) before it reaches the barrier. The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (they
+// complete in issue order), leaving the LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Global column (in elements) that lane L of wave w fetches when a DMA instruction of the
+// wave fills four rows r with swz(r) = 4 (L/16) + w: 8 * the logical chunk of its slot.
 // The empty asm makes the value opaque at each use, so that the compiler recomputes the
 // per-lane 64-bit addresses near the loads instead of hoisting (and spilling) them.
 __device__ __forceinline__ int dma_col(int wave, int lane) {
@@ -183,112 +255,127 @@ __device__ __forceinline__ int dma_col(int wave, int lane) {
   return c;
 }
 
-// Zero a [64][128] bf16 tile (once, before the first DMA into it).
+// Zero a [ROWS][128] bf16 tile with NT threads (once, before the first DMA into it).
+template <int ROWS, int NT>
 __device__ __forceinline__ void zero_tile(uint16_t* t, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sts16(t, (tid + 256 * i) * 8, u32x4{0u, 0u, 0u, 0u});
+  for (int c = tid; c < ROWS * 16; c += NT) sts16(t, c * 8, u32x4{0u, 0u, 0u, 0u});
 }
 
-// Key blocks for the forward and dQ kernels, through the LDS page-id window.
-struct KeyStream {
+// Fill spage with the page ids of entries [win, win + CAP), NT threads.
+template <int NT, int CAP = PCAP>
+__device__ __forceinline__ void fill_pages(const Keys& k, int* spage, int win, int tid) {
+  const int end = min(k.n_entries, win + CAP);
+  for (int e = win + tid; e < end; e += NT) spage[e - win] = k.phys(e);
+}
+
+// Direct staging of a stage of ROWS attended keys (K and V rows) by NW wavefronts.
+// Instruction i of wave w fills LDS rows r0 = 4 (NW i + w) .. r0 + 3. Those four rows are
+// 4-aligned, so they lie in one page (pages hold >= 16 tokens): one broadcast page-id read
+// gives a uniform page base, and lane L adds a fixed offset, row L/16 of the four plus
+// the logical column whose 16 bytes land in its physical slot. With NW a multiple of 4,
+// swz(r) = 4 (L/16) + (w % 4) for every instruction, so that offset is one register.
+template <int ROWS, int NW, int CAP = PCAP>
+struct KeyStage {
+  static_assert(NW % 4 == 0 && ROWS % (4 * NW) == 0, "rows per wave must tile the stage");
+  static constexpr int NI = ROWS / (4 * NW);
   const Keys& k;
-  const int* spage;  // LDS page ids of entries [win, win + PCAP)
+  const int* spage;  // LDS page ids of entries [win, win + CAP)
   int win;
   const uint16_t* kp;
   const uint16_t* vp;
+  int lane_off;      // (L/16) D + 8 ((L%16) ^ swz)
 
-  __device__ __forceinline__ void issue(int b, uint16_t* kt, uint16_t* vt, int wave, int lane) const {
-    const int c8 = dma_col(wave, lane);
-    const int a0 = b * KB;
-    if (k.log2p >= 6) {
-      // Pages of 64+ keys: the whole block lies in one page, so one (broadcast) page-id
-      // read and a uniform page base serve all rows; only the sequence tail is per row.
-      const int e = a0 >> k.log2p;
-      const int ph = e < k.n_entries ? __builtin_amdgcn_readfirstlane(spage[e - win]) : -1;
-      if (ph < 0) return;
-      const int64_t base = (static_cast<int64_t>(ph) << k.log2p) * D;
-      const int slot0 = a0 & ((1 << k.log2p) - 1);
+  __device__ static int lane_offset(int wave, int lane) {
+    return (lane >> 4) * D + 8 * ((lane & 15) ^ (((lane >> 4) << 2) | (wave & 3)));
+  }
+
+  // DMA the rows of stage st (attended keys st*ROWS ..) of one pool (K or V) into t.
+  __device__ __forceinline__ void issue_one(int st, const uint16_t* pool, uint16_t* t, int wave,
+                                            int lane) const {
+    // opaque per call: keeps the compiler from hoisting (and spilling) 64-bit lane pointers
+    int lo = lane_off;
+    asm volatile("" : "+v"(lo));
+    const int a0 = st * ROWS;
+    int ph[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 16 * i + 4 * wave;
-        const int r = r0 + (lane >> 4);
-        if (k.in_seq(a0 + r)) {
-          const int off = (slot0 + r) * D + c8;
-          lds_dma16(kp + base + off, kt + r0 * D);
-          lds_dma16(vp + base + off, vt + r0 * D);
-        }
-      }
-      return;
-    }
-    // Smaller pages: each row looks up its own page id (all four reads issued together).
-    int ph[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int a = a0 + 16 * i + 4 * wave + (lane >> 4);
-      const int e = a >> k.log2p;
-      ph[i] = k.in_seq(a) ? spage[e - win] : -1;
+    for (int i = 0; i < NI; ++i) {
+      const int a = a0 + 4 * (NW * i + wave);
+      ph[i] = a < k.n_keys ? spage[(a >> k.log2p) - win] : -1;  // all reads, then one wait
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = 16 * i + 4 * wave;
-      const int a = a0 + r0 + (lane >> 4);
-      if (ph[i] >= 0) {
-        const int64_t off = ((static_cast<int64_t>(ph[i]) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D + c8;
-        lds_dma16(kp + off, kt + r0 * D);
-        lds_dma16(vp + off, vt + r0 * D);
+    for (int i = 0; i < NI; ++i) {
+      const int r0 = 4 * (NW * i + wave);
+      const int a = a0 + r0;
+      const int p = __builtin_amdgcn_readfirstlane(ph[i]);
+      if (p < 0) continue;
+      const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
+      if (k.in_seq(a + (lane >> 4))) lds_dma16(pool + base + lo, t + r0 * D);
+    }
+  }
+
+  // As issue_one, but every wave issues exactly NI DMA instructions with all lanes active,
+  // whatever the rows: a lane whose row does not exist, lies past the end of the
+  // sequence or has an invalid page copies the first rows of the pool instead (such rows
+  // are masked or, for invalid pages, documented as undefined). A fixed count per call
+  // lets the caller wait for all but its most recent batches with vmcnt(n). Split in
+  // two so that the page-id reads (LDS) can be issued well before the DMA needs them.
+  __device__ __forceinline__ void read_pages(int st, int wave, int (&ph)[NI]) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      // branch-free: the read index is clamped into the window, the result discarded
+      // for rows past the attended keys
+      const int a = st * ROWS + 4 * (NW * i + wave);
+      const int e = min(a >> k.log2p, k.n_entries - 1) - win;
+      const int v = spage[max(0, min(e, CAP - 1))];
+      ph[i] = a < k.n_keys ? v : -1;
+    }
+  }
+  __device__ __forceinline__ void dma_fixed(int st, const uint16_t* pool, uint16_t* t, int wave,
+                                            int lane, const int (&ph)[NI]) const {
+    int lo = lane_off;
+    asm volatile("" : "+v"(lo));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r0 = 4 * (NW * i + wave);
+      const int a = st * ROWS + r0;
+      const int p = __builtin_amdgcn_readfirstlane(ph[i]);
+      const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
+      const bool ok = p >= 0 && k.in_seq(a + (lane >> 4));
+      lds_dma16(pool + (ok ? base : 0) + lo, t + r0 * D);
+    }
+  }
+  __device__ __forceinline__ void issue_fixed(int st, const uint16_t* pool, uint16_t* t, int wave,
+                                              int lane) const {
+    int ph[NI];
+    read_pages(st, wave, ph);
+    dma_fixed(st, pool, t, wave, lane, ph);
+  }
+
+  // DMA stage st (attended keys st*ROWS ..) into (kt, vt). Rows past the attended keys or
+  // past the end of the sequence, and rows of invalid pages, are not written.
+  __device__ __forceinline__ void issue(int st, uint16_t* kt, uint16_t* vt, int wave, int lane) const {
+    const int a0 = st * ROWS;
+    int ph[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int a = a0 + 4 * (NW * i + wave);
+      ph[i] = a < k.n_keys ? spage[(a >> k.log2p) - win] : -1;  // all reads, then one wait
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r0 = 4 * (NW * i + wave);
+      const int a = a0 + r0;
+      const int p = __builtin_amdgcn_readfirstlane(ph[i]);
+      if (p < 0) continue;
+      const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
+      if (k.in_seq(a + (lane >> 4))) {
+        lds_dma16(kp + base + lane_off, kt + r0 * D);
+        lds_dma16(vp + base + lane_off, vt + r0 * D);
       }
     }
   }
 };
-
-// Fill spage with the page ids of entries [win, win + PCAP).
-__device__ __forceinline__ void fill_pages(const Keys& k, int* spage, int win, int tid) {
-  const int end = min(k.n_entries, win + PCAP);
-  for (int e = win + tid; e < end; e += 256) spage[e - win] = k.phys(e);
-}
-
-// Issue the loads of block b + 1 into (kn, vn), sliding the page-id window first when
-// needed. The two K/V buffers are distinct __shared__ objects and every call site
-// names them at compile time, so the compiler can see that a DMA into one buffer does
-// not alias reads of the other and does not wait for it.
-__device__ __forceinline__ void prefetch_next(KeyStream& ks, int* spage, const Keys& km, int b,
-                                              int nblk, int tid, int wave, int lane,
-                                              uint16_t* kn, uint16_t* vn) {
-  if (b + 1 >= nblk) return;
-  const int last_e = ((b + 1) * KB + KB - 1) >> km.log2p;
-  if (last_e >= ks.win + PCAP) {  // uniform over the workgroup
-    ks.win = ((b + 1) * KB) >> km.log2p;
-    fill_pages(km, spage, ks.win, tid);
-    // Retire every table load here: a load the compiler cannot prove consumed would
-    // otherwise make it wait for all loads (the DMA included) at later register reuse.
-    wait_dma();
-    __syncthreads();
-  }
-  ks.issue(b + 1, kn, vn, wave, lane);
-}
-
-// Start a key stream: page window, zeroed tiles, block 0 loaded and visible.
-__device__ __forceinline__ void start_stream(KeyStream& ks, int* spage, const Keys& km, int nblk,
-                                             int tid, int wave, int lane, uint16_t* k0,
-                                             uint16_t* v0, uint16_t* k1, uint16_t* v1) {
-  fill_pages(km, spage, 0, tid);
-  zero_tile(k0, tid);
-  zero_tile(v0, tid);
-  zero_tile(k1, tid);
-  zero_tile(v1, tid);
-  wait_dma();
-  __syncthreads();
-  if (nblk > 0) ks.issue(0, k0, v0, wave, lane);
-  wait_dma();
-  __syncthreads();
-}
-
-#define OOMB_KV_BUFFERS                                  \
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D]; \
-  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * D]; \
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D]; \
-  __shared__ __attribute__((aligned(16))) uint16_t s_v1[KB * D]; \
-  __shared__ int s_page[PCAP];
 
 }  // namespace mf
 }  // namespace oomb
