@@ -202,6 +202,7 @@ void fwd_mfma_kernel(AttnArgs a) {
   // u = t - grp: u = 0 computes S_0; odd u runs V(u / 2); even u >= 2 runs M(u / 2 - 1).
   // kr / vr hold K_{b+1} / V_b of whichever M phase runs. Block j's K and V live in
   // buffer j % 3. IS_M and G1 (compile time) make every phase straight-line code.
+  int pid[KeyStage<KB, 4, CAP>::NI];  // page ids of this wave's next DMA duty
   auto phase = [&](auto is_m, auto g1, int t, uint16_t* kd, uint16_t* vd, const uint16_t* kr,
                    const uint16_t* vr) __attribute__((always_inline)) {
     constexpr bool kG1 = decltype(g1)::value;
@@ -217,12 +218,14 @@ void fwd_mfma_kernel(AttnArgs a) {
         }
       }
     }
-    // DMA duty: its page ids are read first (LDS reads queue behind the M phases' tile
-    // reads), the DMA itself is issued after this wave's softmax.
+    // DMA duty. Its page ids are LDS reads, which queue behind the M phases' tile reads:
+    // with every page id resident they are read one duty ahead; with a sliding window,
+    // at the start of the phase. The DMA itself is issued after this wave's softmax.
     const bool dma = kG1 ? (t & 1) == 0 : (t & 1) == 1;
     const int dst = kG1 ? j + 2 : j + 1;
-    int pid[KeyStage<KB, 4, CAP>::NI];
-    if (dma) kg.read_pages(dst, wave & 3, pid);
+    if constexpr (SLIDE) {
+      if (dma) kg.read_pages(dst, wave & 3, pid);
+    }
     const int u = t - grp;
     if constexpr (decltype(is_m)::value) {
       const int b = (u >> 1) - 1;  // M(b): PV of block b, S of block b + 1
@@ -240,6 +243,7 @@ void fwd_mfma_kernel(AttnArgs a) {
     if (dma) {
       __builtin_amdgcn_sched_barrier(0);
       kg.dma_fixed(dst, kG1 ? kpool : vpool, kG1 ? kd : vd, wave & 3, lane, pid);
+      if constexpr (!SLIDE) kg.read_pages(dst + 1, wave & 3, pid);  // the next duty's
       wait_vm<KeyStage<KB, 4, CAP>::NI>();  // the batch of two phases ago has landed
     }
     phase_barrier();
@@ -247,6 +251,7 @@ void fwd_mfma_kernel(AttnArgs a) {
   using M = std::integral_constant<bool, true>;
   using V = std::integral_constant<bool, false>;
   const int T = 2 * nb + 2;
+  if constexpr (!SLIDE) kg.read_pages(grp ? 2 : 1, wave & 3, pid);  // first duty: K_2 / V_1
   if (grp == 0) {
     using G = std::integral_constant<bool, false>;
     for (int t = 0; t < T; t += 6) {
