@@ -1,93 +1,54 @@
 // Matrix-core backward of paged chunk attention, dQ pass: recompute P from the saved
 // log-sum-exp and dP = dO V^T per key block, then dQ^T += K^T dS^T.
 //
-// Key blocks are staged through registers (a global load at the top of a block, an
-// LDS store at its end) rather than by global->LDS DMA: this kernel keeps Q and dO
-// fragments, the dQ accumulator and two score tiles live at once, and the register
-// path leaves the compiler more room than the DMA address arithmetic does.
+// A workgroup is 4 wavefronts and owns 128 queries of one head (32 per wavefront, Q and
+// dO fragments held in registers); two workgroups share a CU, so each SIMD interleaves
+// two independent wavefronts. Key blocks of 64 rows (K and V) are copied global -> LDS
+// by DMA one block ahead, a fixed number of instructions per wave, into double buffers
+// whose roles are static in each half of the unrolled loop. The page ids a DMA needs
+// are read from LDS one block before it is issued, so the read has left the LDS queue
+// by then. Fragment reads are software-pipelined one step ahead of the products.
 #include "mfma_tiles.hpp"
 
 namespace oomb {
 namespace mf {
 
-// 256 threads stage one 64-key block: thread = (rows tid/16 + 16i, 16-byte chunk tid%16).
-struct RegKeyStream {
-  const Keys& k;
-  const int* spage;  // LDS page ids of entries [win, win + PCAP)
-  int win;
-  const void* kp;
-  const void* vp;
-  u32x4 kr[4], vr[4];
+constexpr int DQ_WAVES = 4;
+constexpr int DQ_Q = 32 * DQ_WAVES;  // queries per workgroup
 
-  __device__ __forceinline__ void load(int b, int tid) {
-    const int c = tid & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int a = b * KB + (tid >> 4) + 16 * i;
-      u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = x;
-      if (k.in_seq(a)) {
-        const int ph = spage[(a >> k.log2p) - win];
-        if (ph >= 0) {
-          const int64_t row = (static_cast<int64_t>(ph) << k.log2p) + (a & ((1 << k.log2p) - 1));
-          x = gld16(kp, row * D + 8 * c);
-          y = gld16(vp, row * D + 8 * c);
-        }
-      }
-      kr[i] = x;
-      vr[i] = y;
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* kt, uint16_t* vt, int tid) const {
-    const int c = tid & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 4) + 16 * i;
-      sts16(kt, toff(r, 8 * c), kr[i]);
-      sts16(vt, toff(r, 8 * c), vr[i]);
-    }
-  }
-};
-
-struct DqSmem {
-  uint16_t k[2][KB * D];
-  uint16_t v[2][KB * D];
-  int page[PCAP];
-};
-
-// Load block b + 1 into registers (sliding the page-id window first when needed).
-__device__ __forceinline__ void reg_prefetch_next(RegKeyStream& ks, DqSmem& sm, const Keys& km,
-                                                  int b, int nblk, int tid) {
-  if (b + 1 >= nblk) return;
-  const int last_e = ((b + 1) * KB + KB - 1) >> km.log2p;
-  if (last_e >= ks.win + PCAP) {  // uniform over the workgroup
-    ks.win = ((b + 1) * KB) >> km.log2p;
-    fill_pages<256>(km, sm.page, ks.win, tid);
-    __syncthreads();
-  }
-  ks.load(b + 1, tid);
-}
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_mfma_kernel(AttnArgs a) {
-  __shared__ DqSmem sm;
-  constexpr int QT = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[KB * D];
+  __shared__ int s_page[PCAP];
+  constexpr int NT = 64 * DQ_WAVES;
+  using Stage = KeyStage<KB, DQ_WAVES>;
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
-  const int n_qt = (a.n_q + QT - 1) / QT;
+  const int n_qt = (a.n_q + DQ_Q - 1) / DQ_Q;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int hh = L % G, rest = L / G;
-  const int qt = rest % n_qt, g = rest / n_qt;
+  // Latest query tiles (most local keys, the longest) are dispatched first.
+  const int qt = n_qt - 1 - rest % n_qt, g = rest / n_qt;
   const int h = g * G + hh;
   const Keys km = make_keys(a, g);
-  const int q0 = qt * QT;
-  const int klim_tile = km.klim(a.t0 + q0);
-  const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + QT) - 1);
+  const int q0 = qt * DQ_Q;
+  const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);
   const float c2 = a.scale * kLog2e;
 
+  // This wave's queries: blocks past its last query are skipped; blocks reaching past
+  // its first query need the mask.
+  const int wq0 = q0 + 32 * wave;
+  const int wq_last = min(a.n_q, wq0 + 32) - 1;
+  const int nblk_w = wq_last < wq0 ? 0 : n_blocks(km, a.t0 + wq_last);
+  const int klim_w0 = km.klim(a.t0 + wq0);
+
   // This lane's query (column of S^T and dP^T) with its Q and dO fragments.
-  const int i = q0 + wave * 32 + col;
+  const int i = wq0 + col;
   const int klim = km.klim(a.t0 + i);
   bf16x8 qf[8], df[8];
   {
@@ -108,54 +69,97 @@ void dq_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) dqt[db] = f32x16{};
 
-  fill_pages<256>(km, sm.page, 0, tid);
+  FragOffsets fo;
+  fo.init(lane);
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.pool.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.pool.v_pool);
+  Stage ks{km, s_page, 0, kpool, vpool, Stage::lane_offset(wave, lane)};
+  fill_pages<NT>(km, s_page, 0, tid);
+  wait_dma();  // the page-table loads are retired here, not at a later register reuse
   __syncthreads();
-  RegKeyStream ks{km, sm.page, 0, a.pool.k_pool, a.pool.v_pool};
-  if (nblk > 0) {
-    ks.load(0, tid);
-    ks.store(sm.k[0], sm.v[0], tid);
-  }
+  int pid[Stage::NI];  // page ids of the next block's DMA (K and V rows share them)
+  ks.read_pages(0, wave, pid);
+  ks.dma_fixed(0, kpool, s_k0, wave, lane, pid);
+  ks.dma_fixed(0, vpool, s_v0, wave, lane, pid);
+  ks.read_pages(1, wave, pid);
+  wait_dma();
   __syncthreads();
-  for (int b = 0; b < nblk; ++b) {
-    const int buf = b & 1;
-    reg_prefetch_next(ks, sm, km, b, nblk, tid);
-    const uint16_t* kt = sm.k[buf];
-    const uint16_t* vt = sm.v[buf];
-    const bool mask = b * KB + KB - 1 > klim_tile;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      f32x16 st = f32x16{}, dpt = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        st = mfma(row_frag(kt, 32 * sub, kk, lane), qf[kk], st);
-        dpt = mfma(row_frag(vt, 32 * sub, kk, lane), df[kk], dpt);
+
+  // One key block b from (kt, vt); DMA of block b + 1 into (kn, vn) first.
+  auto block = [&](int b, const uint16_t* kt, const uint16_t* vt, uint16_t* kn,
+                   uint16_t* vn) __attribute__((always_inline)) {
+    if (b + 1 < nblk) {
+      const int last_e = ((b + 1) * KB + KB - 1) >> km.log2p;
+      if (last_e >= ks.win + PCAP) {  // uniform over the workgroup: slide the page window
+        ks.win = ((b + 1) * KB) >> km.log2p;
+        fill_pages<NT>(km, s_page, ks.win, tid);
+        wait_dma();
+        __syncthreads();
+        ks.read_pages(b + 1, wave, pid);
       }
-      bf16x8 dsb[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        float ds[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * s + j;
-          float p = fast_exp2(__builtin_fmaf(st[r], c2, -lse2));
-          if (mask && b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3) > klim) p = 0.0f;
-          ds[j] = p * (dpt[r] - delta);
-        }
-        dsb[s] = pack8(ds);
-      }
-      // dQ^T += K^T dS^T.
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 ta[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) ta[db] = tr_frag(kt, 32 * sub, 32 * db, s, lane);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dqt[db] = mfma(ta[db], dsb[s], dqt[db]);
+      ks.dma_fixed(b + 1, kpool, kn, wave, lane, pid);
+      ks.dma_fixed(b + 1, vpool, vn, wave, lane, pid);
+      if (b + 2 < nblk) {
+        const int last2 = ((b + 2) * KB + KB - 1) >> km.log2p;
+        if (last2 < ks.win + PCAP) ks.read_pages(b + 2, wave, pid);  // else after the slide
       }
     }
-    if (b + 1 < nblk) ks.store(sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
-    __syncthreads();
+    if (b < nblk_w) {
+      FragOffsets o = fo;
+      o.opaque();
+      const bool mask = b * KB + KB - 1 > klim_w0;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        // S^T = K Q^T and dP^T = V dO^T for 32 keys: two independent chains, fragment
+        // reads one k-step ahead.
+        f32x16 st = f32x16{}, dpt = f32x16{};
+        bf16x8 fk = row_frag_at(kt, 32 * sub, o, 0), fv = row_frag_at(vt, 32 * sub, o, 0);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          bf16x8 nk = fk, nv = fv;
+          if (kk + 1 < 8) {
+            nk = row_frag_at(kt, 32 * sub, o, kk + 1);
+            nv = row_frag_at(vt, 32 * sub, o, kk + 1);
+          }
+          st = mfma(fk, qf[kk], st);
+          dpt = mfma(fv, df[kk], dpt);
+          fk = nk;
+          fv = nv;
+        }
+        // dS^T = P^T (dP^T - Delta), P = exp2(S c - lse log2 e); masked keys give 0.
+        bf16x8 ta[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) ta[db] = tr_frag_at(kt, 32 * sub, 0, o, db);
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          float ds[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * s + j;
+            float p = fast_exp2(__builtin_fmaf(st[r], c2, -lse2));
+            if (mask && b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3) > klim) p = 0.0f;
+            ds[j] = p * (dpt[r] - delta);
+          }
+          dsb[s] = pack8(ds);
+        }
+        // dQ^T += K^T dS^T, the second k-step's fragments read during the first's products.
+        bf16x8 tb[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) tb[db] = tr_frag_at(kt, 32 * sub, 1, o, db);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqt[db] = mfma(ta[db], dsb[0], dqt[db]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqt[db] = mfma(tb[db], dsb[1], dqt[db]);
+      }
+    }
+    wait_vm<0>();     // block b + 1 has landed (this wave's part) ...
+    phase_barrier();  // ... everyone's, and nobody reads block b any more
+  };
+  // Unrolled by two so that each half names its read and write buffers statically.
+  for (int b = 0; b < nblk; b += 2) {
+    block(b, s_k0, s_v0, s_k1, s_v1);
+    if (b + 1 < nblk) block(b + 1, s_k1, s_v1, s_k0, s_v0);
   }
 
   if (i < a.n_q) {
@@ -175,8 +179,8 @@ void dq_mfma_kernel(AttnArgs a) {
 }  // namespace mf
 
 hipError_t launch_dq_mfma(const AttnArgs& a, hipStream_t s) {
-  const int n_qt = (a.n_q + 127) / 128;
-  OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, dim3(a.pool.Hq * n_qt), dim3(256), 0, s, a);
+  const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
+  OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, dim3(a.pool.Hq * n_qt), dim3(64 * mf::DQ_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
