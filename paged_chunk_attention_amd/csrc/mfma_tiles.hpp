@@ -226,6 +226,7 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* ldst) 
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Workgroup barrier without the release/acquire fences of __syncthreads(). Those fences
 // make the compiler wait for every outstanding global->LDS DMA of the wave, which would
 // defeat prefetching several phases ahead. Callers order the LDS data themselves: DMA
