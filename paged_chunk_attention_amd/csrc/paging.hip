@@ -13,37 +13,63 @@
 namespace oomb {
 
 // One work item = one 16-byte chunk of one token row of one KV head; K and V are
-// copied together. Rows whose page is unmapped are skipped.
-__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+// copied together. Rows whose page is unmapped are skipped. Grid: x strides over the
+// chunks of one head's tokens, y = KV head. The chunks per row (D * esize / 16) are a
+// power of two, so indices come from shifts. The copy is streaming: non-temporal loads
+// and stores keep it from evicting the caches.
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a, int log2_cpr) {
   const int esize = a.pool.dtype == 0 ? 2 : 4;
-  const int cpr = a.pool.D * esize / 16;  // 16-byte chunks per row
-  const int64_t total = static_cast<int64_t>(a.pool.Hkv) * a.n_tok * cpr;
+  const int g = blockIdx.y;
+  const int64_t total = static_cast<int64_t>(a.n_tok) << log2_cpr;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t w = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; w < total;
-       w += stride) {
-    const int c = static_cast<int>(w % cpr);
-    const int64_t r = w / cpr;
-    const int i = static_cast<int>(r % a.n_tok);
-    const int g = static_cast<int>(r / a.n_tok);
-    const int64_t t = a.start + i;
-    const int64_t ph = a.table[g * a.tstride + (t >> a.pool.log2p)];
-    if (ph < 0 || ph >= a.pool.N) continue;
-    const int64_t src = (g * a.hs + i * a.ts) * esize + c * 16;
-    const int64_t dst = ((ph << a.pool.log2p) + (t & (a.pool.P - 1))) * a.pool.D * esize + c * 16;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k_new) + src);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v_new) + src);
-    *reinterpret_cast<u32x4*>(static_cast<char*>(a.pool.k_pool_w) + dst) = kv;
-    *reinterpret_cast<u32x4*>(static_cast<char*>(a.pool.v_pool_w) + dst) = vv;
+  const char* ks = static_cast<const char*>(a.k_new) + g * a.hs * esize;
+  const char* vs = static_cast<const char*>(a.v_new) + g * a.hs * esize;
+  const int32_t* trow = a.table + g * a.tstride;
+  const int64_t row_bytes = static_cast<int64_t>(a.pool.D) * esize;
+  // Four chunks per thread per pass: all eight loads are issued before the stores.
+  constexpr int kU = 4;
+  for (int64_t w0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; w0 < total;
+       w0 += kU * stride) {
+    u32x4 kv[kU], vv[kU];
+    int64_t dst[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t w = w0 + u * stride;
+      dst[u] = -1;
+      if (w < total) {
+        const int c = static_cast<int>(w & ((1 << log2_cpr) - 1));
+        const int i = static_cast<int>(w >> log2_cpr);
+        const int64_t t = a.start + i;
+        const int64_t ph = trow[t >> a.pool.log2p];
+        if (ph >= 0 && ph < a.pool.N) {
+          const int64_t src = i * a.ts * esize + c * 16;
+          dst[u] = ((ph << a.pool.log2p) + (t & (a.pool.P - 1))) * row_bytes + c * 16;
+          kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + src));
+          vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + src));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (dst[u] < 0) continue;
+      __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(static_cast<char*>(a.pool.k_pool_w) + dst[u]));
+      __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(static_cast<char*>(a.pool.v_pool_w) + dst[u]));
+    }
   }
 }
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s) {
   const int esize = a.pool.dtype == 0 ? 2 : 4;
-  const int64_t total = static_cast<int64_t>(a.pool.Hkv) * a.n_tok * (a.pool.D * esize / 16);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 256 * 32) blocks = 256 * 32;
+  const int cpr = a.pool.D * esize / 16;
+  int log2_cpr = 0;
+  while ((1 << log2_cpr) < cpr) ++log2_cpr;
+  const int64_t per_head = static_cast<int64_t>(a.n_tok) << log2_cpr;
+  int64_t blocks = (per_head + 255) / 256;
+  const int64_t cap = (256 * 16 + a.pool.Hkv - 1) / a.pool.Hkv;  // ~16 waves of 256 per CU
+  if (blocks > cap) blocks = cap;
   if (blocks < 1) return hipSuccess;
-  OOMB_LAUNCH("kv_append", kv_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  OOMB_LAUNCH("kv_append", kv_append_kernel, dim3(static_cast<unsigned>(blocks), a.pool.Hkv), dim3(256), 0,
+              s, a, log2_cpr);
   return hipGetLastError();
 }
 
@@ -83,8 +109,7 @@ __global__ __launch_bounds__(256) void page_summarize_kernel(SummarizeArgs a) {
 #pragma unroll
   for (int e = 0; e < kPer; ++e) { mn[e] = 0x7FFFFFFF; mx[e] = static_cast<int32_t>(0x80000000); }
   const char* base = static_cast<const char*>(a.pool.k_pool) + (ph << a.pool.log2p) * D * kEsize;
-  for (int r = rg; r < n_valid; r += groups) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (static_cast<int64_t>(r) * D + c * kPer) * kEsize);
+  auto fold = [&](const u32x4& v) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const uint32_t word = v[e * kEsize / 4];
@@ -93,7 +118,21 @@ __global__ __launch_bounds__(256) void page_summarize_kernel(SummarizeArgs a) {
       mn[e] = key < mn[e] ? key : mn[e];
       mx[e] = key > mx[e] ? key : mx[e];
     }
+  };
+  auto row = [&](int r) {
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(base + (static_cast<int64_t>(r) * D + c * kPer) * kEsize));
+  };
+  int r = rg;
+  // eight rows per thread in flight at a time (a full page of 128 rows at 16 groups)
+  for (; r + 7 * groups < n_valid; r += 8 * groups) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = row(r + j * groups);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fold(v[j]);
   }
+  for (; r < n_valid; r += groups) fold(row(r));
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     s_min[rg * D + c * kPer + e] = mn[e];
