@@ -37,6 +37,14 @@ def test_chunk_parity_mfma(kw):
     run_chunk_parity(_w(**kw))
 
 
+def test_chunk_parity_mfma_page_window_slides():
+    """More attended pages than the kernels keep resident: 8,208 pages of 16 tokens per
+    head, so the forward's page-id window (2,048 when a head attends over 8,192 pages)
+    and the dQ pass's window slide several times within one workgroup."""
+    run_chunk_parity(_w(name="mfma_window_slide", hq=4, hkv=1, page=16, chunk=256,
+                        total=16 * 8192 + 256))
+
+
 # scalar path: fp32 (any head_dim) and bf16 head_dim 64
 @pytest.mark.parametrize("kw", [
     dict(name="f32_d64_p16", hq=2, hkv=1, d=64, page=16, chunk=64, total=1024, dtype=torch.float32),
