@@ -337,6 +337,7 @@ size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
   a.n_q = n_q;
   const int64_t prior = sel_stride >= 0 ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
   a.max_att_pages = static_cast<int>(prior + cg.n_local);
+  a.n_local = cg.n_local;
   size_t off;
   return bwd_workspace(a, &off);
 }

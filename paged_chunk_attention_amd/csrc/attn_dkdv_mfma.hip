@@ -8,30 +8,55 @@ namespace mf {
 // ============================================================================ dK / dV
 // Grid: Hkv * (key blocks of 128) * n_split. With n_split > 1, split s writes its
 // partial dK/dV rows to part[((s * Hkv + g) * part_keys + key) * 2D + {0: dK, D: dV}].
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+//
+// A workgroup is 8 wavefronts that own 128 keys, 32 per key group kg = wave % 4. The
+// two wavefronts of a key group share a SIMD and split its work by role:
+//  * the P wave holds K (B operand over d) and dV: per 64-query tile it computes
+//    S = Q K^T, P = exp(S - LSE) (masked), hands P (bf16) to its partner through LDS,
+//    and adds P^T dO into dV;
+//  * the D wave holds V and dK: it computes dP = dO V^T of a tile, and one tile later,
+//    once that tile's P has arrived, dS = P (dP - Delta) and dK += dS^T Q.
+// Each wave carries half of the state of one owner of 32 keys, so two fit on a SIMD,
+// and the hardware overlaps one wave's softmax arithmetic with the other's products.
+// The D wave's order (dS and dK of the previous tile, then dP of this one) puts its
+// 32 products under the P wave's softmax. Query tiles arrive by DMA one tile ahead in
+// three buffers (the D wave still reads the previous tile); roles of the buffers are
+// static in each third of the unrolled loop.
+constexpr int DKV_WAVES = 8;
+
+__global__ __launch_bounds__(64 * DKV_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
-  // Double-buffered Q / dO tiles and their rows' LSE (x log2 e) and Delta, each buffer
-  // its own object (see prefetch_next), and the output row of each key.
   __shared__ __attribute__((aligned(16))) uint16_t s_q0[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_d0[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_q1[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_d1[QTB * D];
-  __shared__ __attribute__((aligned(16))) float s_lse0[QTB], s_lse1[QTB], s_del0[QTB], s_del1[QTB];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q2[QTB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_d2[QTB * D];
+  __shared__ __attribute__((aligned(16))) float s_lse0[QTB], s_lse1[QTB], s_lse2[QTB];
+  __shared__ __attribute__((aligned(16))) float s_del0[QTB], s_del1[QTB], s_del2[QTB];
+  // P of one tile for each key group: [tile parity][kg][register group 2us + s][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 s_p[2 * 4 * 4 * 64];
   __shared__ int64_t s_grow[KPW];  // gradient pool row (or partial row) of each key, -1 = skip
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;
+  const bool pwave = wave < 4;
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int nkb = (a.max_att_pages * a.pool.P + KPW - 1) / KPW;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = L % n_split, kb = (L / n_split) % nkb, g = L / (n_split * nkb);
+  // Key-block-major order: the blocks of one key block index (equal work) are
+  // consecutive, and the work per block only falls with the index (local blocks see
+  // fewer query tiles), so the round-robin dispatch over XCDs and CUs is longest
+  // first and every XCD gets the same mix.
+  const int L = blockIdx.x;
+  const int split = L % n_split, g = (L / n_split) % a.pool.Hkv, kb = L / (n_split * a.pool.Hkv);
   const Keys km = make_keys(a, g);
   const int k0 = kb * KPW;
-  if (k0 >= km.n_keys) return;  // uniform: block past this head's attended keys
+  if (kb >= nkb || k0 >= km.n_keys) return;  // uniform: block past this head's attended keys
   const float c2 = a.scale * kLog2e;
 
-  // This lane's key (column of S = Q K^T) and its K / V fragments (B operands over d).
-  const int kidx = k0 + 32 * wave + col;
+  // This lane's key (column of S = Q K^T) and its K (P wave) or V (D wave) fragments.
+  const int kidx = k0 + 32 * kg + col;
   int64_t krow = -1;
   int kpos = 0x7FFFFFFF;
   if (km.in_seq(kidx)) {
@@ -43,7 +68,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
       kpos = (km.logical(e) << km.log2p) + slot;
     }
   }
-  if (h2 == 0) {
+  if (pwave && h2 == 0) {
     int64_t out = -1;
     if (krow >= 0) {
       if (n_split > 1) {
@@ -53,14 +78,14 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         if (gp >= 0 && gp < a.pool.Ng) out = (gp << km.log2p) + (kpos & ((1 << km.log2p) - 1));
       }
     }
-    s_grow[32 * wave + col] = out;
+    s_grow[32 * kg + col] = out;
   }
-  bf16x8 kf[8], vf[8];
+  bf16x8 kvf[8];
+  {
+    const void* src = pwave ? a.pool.k_pool : a.pool.v_pool;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-    kf[kk] = as_bf16x8(krow >= 0 ? gld16(a.pool.k_pool, krow * D + 16 * kk + 8 * h2) : z);
-    vf[kk] = as_bf16x8(krow >= 0 ? gld16(a.pool.v_pool, krow * D + 16 * kk + 8 * h2) : z);
+    for (int kk = 0; kk < 8; ++kk)
+      kvf[kk] = as_bf16x8(krow >= 0 ? gld16(src, krow * D + 16 * kk + 8 * h2) : u32x4{0u, 0u, 0u, 0u});
   }
 
   // Query tiles that can see some key of this block: every head of the group, from
@@ -77,152 +102,212 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   const int n_tiles = G * tph;
   const int u_begin = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / n_split);
   const int u_end = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / n_split);
+  const int n_it = u_end - u_begin;
 
-  f32x16 dv[4], dk[4];
+  f32x16 acc[4];  // dV (P wave) or dK (D wave): register r = key row, lane column = d
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    dv[nb] = f32x16{};
-    dk[nb] = f32x16{};
-  }
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x16{};
+  f32x16 dpa[2] = {f32x16{}, f32x16{}};  // D wave: dP of the tile in flight
 
-  // Query tiles go straight from global memory into LDS (DMA); the LSE and Delta of
-  // the tile's rows take a small register path.
-  float r_lse = 0.0f, r_delta = 0.0f;
+  // Query tiles go straight from global memory into LDS (DMA): Q by the P waves, dO by
+  // the D waves. The LSE (wave 0) and Delta (wave 4) of the tile's rows take a small
+  // register path, stored once the tile has landed.
+  float r_row = 0.0f;
   auto issue_tile = [&](int u, uint16_t* qd, uint16_t* dd) {
     const int hq = g * G + u / tph, q0 = (qt0 + u % tph) * QTB;
-    const int c8 = dma_col(wave, lane);
+    const int c8 = dma_col(kg, lane);
+    const uint16_t* src = pwave ? static_cast<const uint16_t*>(a.q) + hq * a.q_hs
+                                : static_cast<const uint16_t*>(a.dout) + hq * a.do_hs;
+    const int64_t ts = pwave ? a.q_ts : a.do_ts;
+    uint16_t* dst = pwave ? qd : dd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r0 = 16 * i + 4 * wave;
+      const int r0 = 16 * i + 4 * kg;
       const int qi = q0 + r0 + (lane >> 4);
-      if (qi < a.n_q) {
-        lds_dma16(static_cast<const uint16_t*>(a.q) + hq * a.q_hs + static_cast<int64_t>(qi) * a.q_ts + c8, qd + r0 * D);
-        lds_dma16(static_cast<const uint16_t*>(a.dout) + hq * a.do_hs + static_cast<int64_t>(qi) * a.do_ts + c8, dd + r0 * D);
-      }
+      if (qi < a.n_q) lds_dma16(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
     }
-    if (tid < QTB) {  // raw loads: arithmetic here would wait for the whole prefetch
-      const int qi = q0 + tid;
+    if (kg == 0) {  // raw loads: arithmetic here would wait for the whole prefetch
+      const int qi = q0 + lane;
       const int64_t rid = static_cast<int64_t>(hq) * a.n_q + qi;
-      r_lse = qi < a.n_q ? a.lse_in[rid] : __builtin_inff();
-      r_delta = qi < a.n_q ? a.delta[rid] : 0.0f;
+      if (pwave) r_row = qi < a.n_q ? a.lse_in[rid] : __builtin_inff();
+      else r_row = qi < a.n_q ? a.delta[rid] : 0.0f;
     }
   };
   auto store_rows = [&](float* lse, float* del) {
-    if (tid < QTB) {
-      lse[tid] = r_lse * kLog2e;
-      del[tid] = r_delta;
+    if (kg == 0) {
+      if (pwave) lse[lane] = r_row * kLog2e;
+      else del[lane] = r_row;
     }
   };
 
-  zero_tile<QTB, 256>(s_q0, tid);
-  zero_tile<QTB, 256>(s_d0, tid);
-  zero_tile<QTB, 256>(s_q1, tid);
-  zero_tile<QTB, 256>(s_d1, tid);
+  FragOffsets fo;
+  fo.init(lane);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_q0, tid);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_d0, tid);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_q1, tid);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_d1, tid);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_q2, tid);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_d2, tid);
   __syncthreads();
-  if (u_begin < u_end) issue_tile(u_begin, s_q0, s_d0);
+  if (n_it > 0) issue_tile(u_begin, s_q0, s_d0);
   wait_dma();
   store_rows(s_lse0, s_del0);
   __syncthreads();
-  // One query tile: prefetch tile u + 1 into (qn, dn, lsen, deln), compute tile u.
-  auto step = [&](int u, const uint16_t* qt, const uint16_t* dt, const float* lse,
-                  const float* del, uint16_t* qn, uint16_t* dn, float* lsen,
-                  float* deln) __attribute__((always_inline)) {
-    if (u + 1 < u_end) issue_tile(u + 1, qn, dn);
+
+  // P wave, tile u from (qt, dt, lse); writes P into s_p parity xp.
+  auto p_tile = [&](int u, const uint16_t* qt, const uint16_t* dt, const float* lse, int xp)
+      __attribute__((always_inline)) {
     const int q0 = (qt0 + u % tph) * QTB;
-    // Some (key, query) pair of this tile is hidden for this lane's key?
-    const bool wmask = __any(kpos > a.t0 + q0);
-    // S = Q K^T and dP = dO V^T over d for both 32-query halves (four MFMA chains),
-    // so that the softmax arithmetic of one half can overlap the other's products.
-    f32x16 sa[2], dpa[2];
+    const bool wmask = __any(kpos > a.t0 + q0);  // some pair of this tile hidden for this lane's key?
+    FragOffsets o = fo;
+    o.opaque();
+    // S = Q K^T for both 32-query halves, the two chains interleaved, fragments read one
+    // step ahead.
+    f32x16 sa[2] = {f32x16{}, f32x16{}};
+    bf16x8 fq = row_frag_at(qt, 0, o, 0);
 #pragma unroll
-    for (int us = 0; us < 2; ++us) {
-      bf16x8 qa[8], da[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        qa[kk] = row_frag(qt, 32 * us, kk, lane);
-        da[kk] = row_frag(dt, 32 * us, kk, lane);
-      }
-      sa[us] = f32x16{};
-      dpa[us] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        sa[us] = mfma(qa[kk], kf[kk], sa[us]);
-        dpa[us] = mfma(da[kk], vf[kk], dpa[us]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int us = i & 1, kk = i >> 1;
+      bf16x8 nq = fq;
+      if (i + 1 < 16) nq = row_frag_at(qt, 32 * ((i + 1) & 1), o, (i + 1) >> 1);
+      sa[us] = mfma(fq, kvf[kk], sa[us]);
+      fq = nq;
     }
+    bf16x8 pb[2][2];
 #pragma unroll
-    for (int us = 0; us < 2; ++us) {
-      bf16x8 tdo[2][4], tq[2][4];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          tdo[s][nb] = tr_frag(dt, 32 * us, 32 * nb, s, lane);
-          tq[s][nb] = tr_frag(qt, 32 * us, 32 * nb, s, lane);
-        }
-      bf16x8 pb[2], dsb[2];
+    for (int us = 0; us < 2; ++us)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         // query rows rA + 8(j/4) + (j%4), j = 0..7, rA = 32us + 16s + 4h2
         const int rA = 32 * us + 16 * s + 4 * h2;
         const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse + rA);
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse + rA + 8);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(del + rA);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(del + rA + 8);
-        float p[8], ds[8];
+        float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int r = 8 * s + j;
           const float lse_r = j < 4 ? l0[j] : l1[j - 4];
-          const float del_r = j < 4 ? d0[j] : d1[j - 4];
-          float pv = fast_exp2(__builtin_fmaf(sa[us][r], c2, -lse_r));
+          float pv = fast_exp2(__builtin_fmaf(sa[us][8 * s + j], c2, -lse_r));
           if (wmask && kpos > a.t0 + q0 + rA + 8 * (j >> 2) + (j & 3)) pv = 0.0f;
           p[j] = pv;
-          ds[j] = pv * (dpa[us][r] - del_r);
         }
-        pb[s] = pack8(p);
-        dsb[s] = pack8(ds);
+        pb[us][s] = pack8(p);
+        s_p[((xp * 4 + kg) * 4 + 2 * us + s) * 64 + lane] = __builtin_bit_cast(u32x4, pb[us][s]);
       }
-      // dV += P^T dO, dK += dS^T Q (the scale is applied once, at the end).
+    // dV += P^T dO, transposed dO fragments read one step ahead.
+    bf16x8 ft = tr_frag_at(dt, 0, 0, o, 0);
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          dv[nb] = mfma(pb[s], tdo[s][nb], dv[nb]);
-          dk[nb] = mfma(dsb[s], tq[s][nb], dk[nb]);
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int nb = i & 3, s = (i >> 2) & 1, us = i >> 3;
+      bf16x8 nt = ft;
+      if (i + 1 < 16) {
+        const int j = i + 1;
+        nt = tr_frag_at(dt, 32 * (j >> 3), (j >> 2) & 1, o, j & 3);
+      }
+      acc[nb] = mfma(pb[us][s], ft, acc[nb]);
+      ft = nt;
     }
-    wait_dma();  // the next tile has landed (this wave's part)
-    if (u + 1 < u_end) store_rows(lsen, deln);
+  };
+
+  // D wave: dS and dK of the previous tile (qp, delp, P parity xp), if any, then dP of
+  // tile dt, if any.
+  auto d_tile = [&](bool prev, const uint16_t* qp, const float* delp, int xp, bool cur,
+                    const uint16_t* dt) __attribute__((always_inline)) {
+    FragOffsets o = fo;
+    o.opaque();
+    if (prev) {
+      bf16x8 dsb[2][2];
+#pragma unroll
+      for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int rA = 32 * us + 16 * s + 4 * h2;
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(delp + rA);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(delp + rA + 8);
+          const u32x4 pw = s_p[((xp * 4 + kg) * 4 + 2 * us + s) * 64 + lane];
+          float ds[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t w = pw[j >> 1];
+            const float pv = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            const float del_r = j < 4 ? d0[j] : d1[j - 4];
+            ds[j] = pv * (dpa[us][8 * s + j] - del_r);
+          }
+          dsb[us][s] = pack8(ds);
+        }
+      // dK += dS^T Q (the scale is applied once, at the end).
+      bf16x8 ft = tr_frag_at(qp, 0, 0, o, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int nb = i & 3, s = (i >> 2) & 1, us = i >> 3;
+        bf16x8 nt = ft;
+        if (i + 1 < 16) {
+          const int j = i + 1;
+          nt = tr_frag_at(qp, 32 * (j >> 3), (j >> 2) & 1, o, j & 3);
+        }
+        acc[nb] = mfma(dsb[us][s], ft, acc[nb]);
+        ft = nt;
+      }
+    }
+    if (cur) {
+      // dP = dO V^T for both halves, interleaved, fragments one step ahead.
+      dpa[0] = f32x16{};
+      dpa[1] = f32x16{};
+      bf16x8 fd = row_frag_at(dt, 0, o, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int us = i & 1, kk = i >> 1;
+        bf16x8 nd = fd;
+        if (i + 1 < 16) nd = row_frag_at(dt, 32 * ((i + 1) & 1), o, (i + 1) >> 1);
+        dpa[us] = mfma(fd, kvf[kk], dpa[us]);
+        fd = nd;
+      }
+    }
+  };
+
+  // Iteration it (0 .. n_it): DMA of tile it + 1 into set (qn, dn, lsen, deln); the P
+  // wave does tile it from set (qc, dc, lsec); the D wave finishes tile it - 1 from set
+  // (qp, delp) and starts tile it from dc. Each role has its own loop (so neither keeps
+  // the other's registers live); both pass the same barriers.
+  auto iter = [&](int it, const uint16_t* qc, const uint16_t* dc, const float* lsec,
+                  uint16_t* qn, uint16_t* dn, float* lsen, float* deln, const uint16_t* qp,
+                  const float* delp, auto is_p) __attribute__((always_inline)) {
+    if (it + 1 < n_it) issue_tile(u_begin + it + 1, qn, dn);
+    if constexpr (decltype(is_p)::value) {
+      if (it < n_it) p_tile(u_begin + it, qc, dc, lsec, it & 1);
+    } else {
+      d_tile(it > 0, qp, delp, (it + 1) & 1, it < n_it, dc);
+    }
+    wait_dma();  // the next tile has landed (this wave's part); P is written
+    if (it + 1 < n_it) store_rows(lsen, deln);
     __syncthreads();
   };
-  for (int u = u_begin; u < u_end; u += 2) {
-    step(u, s_q0, s_d0, s_lse0, s_del0, s_q1, s_d1, s_lse1, s_del1);
-    if (u + 1 < u_end) step(u + 1, s_q1, s_d1, s_lse1, s_del1, s_q0, s_d0, s_lse0, s_del0);
-  }
+  auto loop = [&](auto is_p) __attribute__((always_inline)) {
+    for (int it = 0; it <= n_it; it += 3) {
+      iter(it, s_q0, s_d0, s_lse0, s_q1, s_d1, s_lse1, s_del1, s_q2, s_del2, is_p);
+      if (it + 1 <= n_it) iter(it + 1, s_q1, s_d1, s_lse1, s_q2, s_d2, s_lse2, s_del2, s_q0, s_del0, is_p);
+      if (it + 2 <= n_it) iter(it + 2, s_q2, s_d2, s_lse2, s_q0, s_d0, s_lse0, s_del0, s_q1, s_del1, is_p);
+    }
+  };
+  if (pwave) loop(std::true_type{});
+  else loop(std::false_type{});
 
-  // Write out: register r holds key row m = 8(r/4) + 4h2 + r%4 of this wave, column
-  // 32nb + col of d.
+  // Write out: register r holds key row m = 8(r/4) + 4h2 + r%4 of this key group,
+  // column 32nb + col of d. The P wave owns dV, the D wave dK.
+  const float mul = pwave ? 1.0f : a.scale;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = 8 * (r >> 2) + 4 * h2 + (r & 3);
-    const int64_t out = s_grow[32 * wave + m];
+    const int64_t out = s_grow[32 * kg + m];
     if (out < 0) continue;
     if (n_split == 1) {
-      float* dkr = a.pool.dk_pool + out * D;
-      float* dvr = a.pool.dv_pool + out * D;
+      float* row = (pwave ? a.pool.dv_pool : a.pool.dk_pool) + out * D;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        dkr[32 * nb + col] += dk[nb][r] * a.scale;
-        dvr[32 * nb + col] += dv[nb][r];
-      }
+      for (int nb = 0; nb < 4; ++nb) row[32 * nb + col] += acc[nb][r] * mul;
     } else {
-      float* pk = part + ((static_cast<int64_t>(split) * a.pool.Hkv + g) * part_keys + out) * (2 * D);
+      float* pk = part + ((static_cast<int64_t>(split) * a.pool.Hkv + g) * part_keys + out) * (2 * D) +
+                  (pwave ? D : 0);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        pk[32 * nb + col] = dk[nb][r] * a.scale;
-        pk[D + 32 * nb + col] = dv[nb][r];
-      }
+      for (int nb = 0; nb < 4; ++nb) pk[32 * nb + col] = acc[nb][r] * mul;
     }
   }
 }
@@ -260,14 +345,27 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(AttnArgs a, int n_split
 
 }  // namespace mf
 
-// Query-stream splits of the dK/dV pass: double until the grid has two workgroups
-// per CU of a 256-CU MI355X (at most 4 splits). A fixed CU count keeps the choice,
-// and so the result bits and the workspace size, independent of the device queried.
+// Query-stream splits of the dK/dV pass, chosen for load balance: a workgroup's work
+// is G times the query tiles its key block can see (all of them for prior pages, fewer
+// for the chunk's own pages), and the largest unit (a prior block's share) is kept at
+// most a quarter of the average work per CU, so that longest-first list scheduling
+// over the CUs ends evenly. The CU count is fixed at the MI355X's 256, which keeps the
+// choice, and so the result bits and the workspace size, independent of the device.
 int dkdv_splits(const AttnArgs& a) {
-  const int nkb = (a.max_att_pages * a.pool.P + mf::KPW - 1) / mf::KPW;
-  const int blocks = a.pool.Hkv * nkb;
+  const int G = a.pool.Hq / a.pool.Hkv;
+  const int n_qt = (a.n_q + mf::QTB - 1) / mf::QTB;
+  const int64_t n_keys = static_cast<int64_t>(a.max_att_pages) * a.pool.P;
+  const int64_t local0 = static_cast<int64_t>(a.max_att_pages - a.n_local) * a.pool.P;
+  const int64_t nkb = (n_keys + mf::KPW - 1) / mf::KPW;
+  double total = 0.0;
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const int64_t k0 = kb * mf::KPW;
+    const int64_t qt0 = k0 < local0 ? 0 : (k0 - local0) / mf::QTB;
+    total += static_cast<double>(G) * (qt0 < n_qt ? n_qt - qt0 : 0);
+  }
+  const double per_cu = total * a.pool.Hkv / 256.0;
   int ns = 1;
-  while (ns < 4 && blocks * ns < 2 * 256) ns *= 2;
+  while (ns < 8 && static_cast<double>(G) * n_qt / ns > per_cu / 4.0) ns *= 2;
   return ns;
 }
 
@@ -284,7 +382,8 @@ hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, hipStrea
   if (err != hipSuccess) return err;
   const int nkb = (a.max_att_pages * a.pool.P + mf::KPW - 1) / mf::KPW;
   const int part_keys = a.max_att_pages * a.pool.P;
-  OOMB_LAUNCH("dkdv_mfma", mf::dkdv_mfma_kernel, dim3(a.pool.Hkv * nkb * n_split), dim3(256), 0, s,
+  OOMB_LAUNCH("dkdv_mfma", mf::dkdv_mfma_kernel, dim3(a.pool.Hkv * nkb * n_split),
+              dim3(64 * mf::DKV_WAVES), 0, s,
               a, n_split, part, part_keys);
   if (n_split > 1) {
     dim3 grid((part_keys + 3) / 4, a.pool.Hkv);

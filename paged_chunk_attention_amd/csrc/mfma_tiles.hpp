@@ -21,13 +21,13 @@
 //    directly the B operand of the next product (P^T or dS^T). The forward rescales
 //    its output only when a row maximum grows by more than 2^8 (exact: P and the
 //    running sum always share one reference), which removes almost every rescale.
-//  * The dK/dV pass owns 128 keys per workgroup (32 per wavefront, K and V held in
-//    registers), streams the query tiles of all heads of its KV group through
-//    double-buffered LDS, and does one read-modify-write of its gradient rows. When
-//    that grid would under-fill the GPU the query stream is split across workgroups;
-//    each split writes fp32 partials and a merge kernel adds them in split order.
-//    No two workgroups ever write the same gradient row: no atomics, no races, and
-//    bit-reproducible results.
+//  * The dK/dV pass owns 128 keys per workgroup (32 per pair of wavefronts: one holds
+//    K and dV, the other V and dK, and P passes between them through LDS), streams the
+//    query tiles of all heads of its KV group through triple-buffered LDS, and does one
+//    read-modify-write of its gradient rows. When the work would not spread evenly
+//    over the CUs, the query stream is split across workgroups; each split writes fp32
+//    partials and a merge kernel adds them in split order. No two workgroups ever
+//    write the same gradient row: no atomics, no races, and bit-reproducible results.
 //  * Workgroup ids are remapped so that each XCD works on one contiguous range (one
 //    KV head's queries and pages share that XCD's L2).
 #pragma once
