@@ -319,13 +319,16 @@ int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64
                     "paged_chunk_attn_fwd");
 }
 
-// Backward workspace: Delta [Hq][n_q] fp32, then (for the matrix-core path, when the
-// dK/dV pass is split over the query stream) the fp32 split partials.
-static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part) {
+// Backward workspace: Delta [Hq][n_q] fp32, then (matrix-core path) the fp32 partials
+// of the dK/dV pass when it is split over the query stream, then those of the dQ pass
+// when it is split over key ranges.
+static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part, size_t* off_dq) {
   const size_t delta = align256(static_cast<size_t>(a.pool.Hq) * a.n_q * sizeof(float));
   *off_part = delta;
+  *off_dq = delta;
   if (!use_mfma(a.pool)) return delta;
-  return delta + align256(oomb::dkdv_partial_bytes(a, oomb::dkdv_splits(a)));
+  *off_dq = delta + align256(oomb::dkdv_partial_bytes(a, oomb::dkdv_splits(a)));
+  return *off_dq + align256(oomb::dq_partial_bytes(a, oomb::dq_splits(a)));
 }
 
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
@@ -338,8 +341,10 @@ size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
   const int64_t prior = sel_stride >= 0 ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
   a.max_att_pages = static_cast<int>(prior + cg.n_local);
   a.n_local = cg.n_local;
-  size_t off;
-  return bwd_workspace(a, &off);
+  a.first_local = cg.first_local;
+  a.t0 = static_cast<int>(t0);
+  size_t off, off_dq;
+  return bwd_workspace(a, &off, &off_dq);
 }
 
 int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
@@ -362,8 +367,8 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(OOMB_ERR_INVALID, "lse must be a 4-byte aligned device pointer");
   if (!(scale > 0.0f) || scale > 1e30f) return fail(OOMB_ERR_INVALID, "scale must be positive and finite");
-  size_t off_part = 0;
-  const size_t need = bwd_workspace(a, &off_part);
+  size_t off_part = 0, off_dq = 0;
+  const size_t need = bwd_workspace(a, &off_part, &off_dq);
   if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(OOMB_ERR_WORKSPACE, "bwd needs %zu bytes of 256-byte aligned workspace", need);
   a.gtable = gtable;
@@ -383,7 +388,9 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!use_mfma(a.pool)) return hip_status(oomb::launch_bwd_scalar(a, s), "paged_chunk_attn_bwd");
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
-  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, s), "paged_chunk_attn_bwd");
+  float* dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dq);
+  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, oomb::dq_splits(a), dq_part, s),
+                    "paged_chunk_attn_bwd");
 }
 
 }  // extern "C"

@@ -12,30 +12,30 @@ namespace mf {
 // A workgroup is 8 wavefronts that own 128 keys, 32 per key group kg = wave % 4. The
 // two wavefronts of a key group share a SIMD and split its work by role:
 //  * the P wave holds K (B operand over d) and dV: per 64-query tile it computes
-//    S = Q K^T, P = exp(S - LSE) (masked), hands P (bf16) to its partner through LDS,
+//    S = Q K^T, P = exp(S - LSE) (masked), hands P (fp32) to its partner through LDS,
 //    and adds P^T dO into dV;
 //  * the D wave holds V and dK: it computes dP = dO V^T of a tile, and one tile later,
 //    once that tile's P has arrived, dS = P (dP - Delta) and dK += dS^T Q.
 // Each wave carries half of the state of one owner of 32 keys, so two fit on a SIMD,
 // and the hardware overlaps one wave's softmax arithmetic with the other's products.
 // The D wave's order (dS and dK of the previous tile, then dP of this one) puts its
-// 32 products under the P wave's softmax. Query tiles arrive by DMA one tile ahead in
-// three buffers (the D wave still reads the previous tile); roles of the buffers are
-// static in each third of the unrolled loop.
+// 32 products under the P wave's softmax. Query tiles arrive by DMA one tile ahead:
+// Q in three buffers (the D wave still reads the previous tile's), dO in two; the
+// buffers' roles are static in each sixth of the unrolled loop.
 constexpr int DKV_WAVES = 8;
 
 __global__ __launch_bounds__(64 * DKV_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q0[QTB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_d0[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_q1[QTB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_d1[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_q2[QTB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_d2[QTB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_d0[QTB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_d1[QTB * D];
+  // LSE (x log2 e) and Delta of the rows of the tile in the Q buffer of the same index
   __shared__ __attribute__((aligned(16))) float s_lse0[QTB], s_lse1[QTB], s_lse2[QTB];
   __shared__ __attribute__((aligned(16))) float s_del0[QTB], s_del1[QTB], s_del2[QTB];
-  // P of one tile for each key group: [tile parity][kg][register group 2us + s][lane]
-  __shared__ __attribute__((aligned(16))) u32x4 s_p[2 * 4 * 4 * 64];
+  // P (fp32) of one tile for each key group: [tile parity][kg][8 (2us + s) + 4 (j/4)..][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 s_p[2 * 4 * 8 * 64];
   __shared__ int64_t s_grow[KPW];  // gradient pool row (or partial row) of each key, -1 = skip
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,11 +143,10 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   FragOffsets fo;
   fo.init(lane);
   zero_tile<QTB, 64 * DKV_WAVES>(s_q0, tid);
-  zero_tile<QTB, 64 * DKV_WAVES>(s_d0, tid);
   zero_tile<QTB, 64 * DKV_WAVES>(s_q1, tid);
-  zero_tile<QTB, 64 * DKV_WAVES>(s_d1, tid);
   zero_tile<QTB, 64 * DKV_WAVES>(s_q2, tid);
-  zero_tile<QTB, 64 * DKV_WAVES>(s_d2, tid);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_d0, tid);
+  zero_tile<QTB, 64 * DKV_WAVES>(s_d1, tid);
   __syncthreads();
   if (n_it > 0) issue_tile(u_begin, s_q0, s_d0);
   wait_dma();
@@ -191,7 +190,9 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
           p[j] = pv;
         }
         pb[us][s] = pack8(p);
-        s_p[((xp * 4 + kg) * 4 + 2 * us + s) * 64 + lane] = __builtin_bit_cast(u32x4, pb[us][s]);
+        f32x4* px = s_p + ((xp * 4 + kg) * 8 + 2 * (2 * us + s)) * 64 + lane;
+        px[0] = f32x4{p[0], p[1], p[2], p[3]};
+        px[64] = f32x4{p[4], p[5], p[6], p[7]};
       }
     // dV += P^T dO, transposed dO fragments read one step ahead.
     bf16x8 ft = tr_frag_at(dt, 0, 0, o, 0);
@@ -223,12 +224,12 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
           const int rA = 32 * us + 16 * s + 4 * h2;
           const f32x4 d0 = *reinterpret_cast<const f32x4*>(delp + rA);
           const f32x4 d1 = *reinterpret_cast<const f32x4*>(delp + rA + 8);
-          const u32x4 pw = s_p[((xp * 4 + kg) * 4 + 2 * us + s) * 64 + lane];
+          const f32x4* px = s_p + ((xp * 4 + kg) * 8 + 2 * (2 * us + s)) * 64 + lane;
+          const f32x4 p0 = px[0], p1 = px[64];
           float ds[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const uint32_t w = pw[j >> 1];
-            const float pv = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            const float pv = j < 4 ? p0[j] : p1[j - 4];
             const float del_r = j < 4 ? d0[j] : d1[j - 4];
             ds[j] = pv * (dpa[us][8 * s + j] - del_r);
           }
@@ -282,10 +283,18 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
     __syncthreads();
   };
   auto loop = [&](auto is_p) __attribute__((always_inline)) {
-    for (int it = 0; it <= n_it; it += 3) {
+    for (int it = 0; it <= n_it; it += 6) {
       iter(it, s_q0, s_d0, s_lse0, s_q1, s_d1, s_lse1, s_del1, s_q2, s_del2, is_p);
-      if (it + 1 <= n_it) iter(it + 1, s_q1, s_d1, s_lse1, s_q2, s_d2, s_lse2, s_del2, s_q0, s_del0, is_p);
-      if (it + 2 <= n_it) iter(it + 2, s_q2, s_d2, s_lse2, s_q0, s_d0, s_lse0, s_del0, s_q1, s_del1, is_p);
+      if (it + 1 > n_it) break;
+      iter(it + 1, s_q1, s_d1, s_lse1, s_q2, s_d0, s_lse2, s_del2, s_q0, s_del0, is_p);
+      if (it + 2 > n_it) break;
+      iter(it + 2, s_q2, s_d0, s_lse2, s_q0, s_d1, s_lse0, s_del0, s_q1, s_del1, is_p);
+      if (it + 3 > n_it) break;
+      iter(it + 3, s_q0, s_d1, s_lse0, s_q1, s_d0, s_lse1, s_del1, s_q2, s_del2, is_p);
+      if (it + 4 > n_it) break;
+      iter(it + 4, s_q1, s_d0, s_lse1, s_q2, s_d1, s_lse2, s_del2, s_q0, s_del0, is_p);
+      if (it + 5 > n_it) break;
+      iter(it + 5, s_q2, s_d1, s_lse2, s_q0, s_d0, s_lse0, s_del0, s_q1, s_del1, is_p);
     }
   };
   if (pwave) loop(std::true_type{});
@@ -375,10 +384,11 @@ size_t dkdv_partial_bytes(const AttnArgs& a, int n_split) {
   return static_cast<size_t>(n_split) * a.pool.Hkv * keys * 2 * mf::D * sizeof(float);
 }
 
-hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, hipStream_t s) {
+hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, int n_ks, float* dq_part,
+                           hipStream_t s) {
   hipError_t err = launch_delta(a, s);
   if (err != hipSuccess) return err;
-  err = launch_dq_mfma(a, s);
+  err = launch_dq_mfma(a, n_ks, dq_part, s);
   if (err != hipSuccess) return err;
   const int nkb = (a.max_att_pages * a.pool.P + mf::KPW - 1) / mf::KPW;
   const int part_keys = a.max_att_pages * a.pool.P;

@@ -8,6 +8,10 @@
 // whose roles are static in each half of the unrolled loop. The page ids a DMA needs
 // are read from LDS one block before it is issued, so the read has left the LDS queue
 // by then. Fragment reads are software-pipelined one step ahead of the products.
+//
+// A query tile's key blocks may be cut into n_ks equal ranges, one workgroup each, for
+// load balance (the tiles' work differs, and there are few of them per CU); each range
+// then writes an fp32 partial dQ and a merge kernel adds them in range order.
 #include "mfma_tiles.hpp"
 
 namespace oomb {
@@ -17,7 +21,7 @@ constexpr int DQ_WAVES = 4;
 constexpr int DQ_Q = 32 * DQ_WAVES;  // queries per workgroup
 
 __global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void dq_mfma_kernel(AttnArgs a) {
+void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D];
@@ -30,14 +34,15 @@ void dq_mfma_kernel(AttnArgs a) {
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + DQ_Q - 1) / DQ_Q;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int hh = L % G, rest = L / G;
-  // Latest query tiles (most local keys, the longest) are dispatched first.
-  const int qt = n_qt - 1 - rest % n_qt, g = rest / n_qt;
-  const int h = g * G + hh;
+  // Latest query tiles (most local keys, the longest) are dispatched first, all heads
+  // of a tile and all key ranges of a head consecutive: longest-first over the CUs.
+  const int kr = blockIdx.x % n_ks, rest = blockIdx.x / n_ks;
+  const int h = rest % a.pool.Hq, qt = n_qt - 1 - rest / a.pool.Hq;
+  const int g = h / G;
   const Keys km = make_keys(a, g);
   const int q0 = qt * DQ_Q;
   const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);
+  const int b0 = nblk * kr / n_ks, b1 = nblk * (kr + 1) / n_ks;  // this workgroup's blocks
   const float c2 = a.scale * kLog2e;
 
   // This wave's queries: blocks past its last query are skipped; blocks reaching past
@@ -73,22 +78,25 @@ void dq_mfma_kernel(AttnArgs a) {
   fo.init(lane);
   const uint16_t* kpool = static_cast<const uint16_t*>(a.pool.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.pool.v_pool);
-  Stage ks{km, s_page, 0, kpool, vpool, Stage::lane_offset(wave, lane)};
-  fill_pages<NT>(km, s_page, 0, tid);
+  const int win0 = (b0 * KB) >> km.log2p;
+  Stage ks{km, s_page, win0, kpool, vpool, Stage::lane_offset(wave, lane)};
+  fill_pages<NT>(km, s_page, win0, tid);
   wait_dma();  // the page-table loads are retired here, not at a later register reuse
   __syncthreads();
   int pid[Stage::NI];  // page ids of the next block's DMA (K and V rows share them)
-  ks.read_pages(0, wave, pid);
-  ks.dma_fixed(0, kpool, s_k0, wave, lane, pid);
-  ks.dma_fixed(0, vpool, s_v0, wave, lane, pid);
-  ks.read_pages(1, wave, pid);
+  if (b0 < b1) {
+    ks.read_pages(b0, wave, pid);
+    ks.dma_fixed(b0, kpool, s_k0, wave, lane, pid);
+    ks.dma_fixed(b0, vpool, s_v0, wave, lane, pid);
+  }
+  ks.read_pages(b0 + 1, wave, pid);
   wait_dma();
   __syncthreads();
 
   // One key block b from (kt, vt); DMA of block b + 1 into (kn, vn) first.
   auto block = [&](int b, const uint16_t* kt, const uint16_t* vt, uint16_t* kn,
                    uint16_t* vn) __attribute__((always_inline)) {
-    if (b + 1 < nblk) {
+    if (b + 1 < b1) {
       const int last_e = ((b + 1) * KB + KB - 1) >> km.log2p;
       if (last_e >= ks.win + PCAP) {  // uniform over the workgroup: slide the page window
         ks.win = ((b + 1) * KB) >> km.log2p;
@@ -99,7 +107,7 @@ void dq_mfma_kernel(AttnArgs a) {
       }
       ks.dma_fixed(b + 1, kpool, kn, wave, lane, pid);
       ks.dma_fixed(b + 1, vpool, vn, wave, lane, pid);
-      if (b + 2 < nblk) {
+      if (b + 2 < b1) {
         const int last2 = ((b + 2) * KB + KB - 1) >> km.log2p;
         if (last2 < ks.win + PCAP) ks.read_pages(b + 2, wave, pid);  // else after the slide
       }
@@ -157,13 +165,15 @@ void dq_mfma_kernel(AttnArgs a) {
     phase_barrier();  // ... everyone's, and nobody reads block b any more
   };
   // Unrolled by two so that each half names its read and write buffers statically.
-  for (int b = 0; b < nblk; b += 2) {
+  for (int b = b0; b < b1; b += 2) {
     block(b, s_k0, s_v0, s_k1, s_v1);
-    if (b + 1 < nblk) block(b + 1, s_k1, s_v1, s_k0, s_v0);
+    if (b + 1 < b1) block(b + 1, s_k1, s_v1, s_k0, s_v0);
   }
 
   if (i < a.n_q) {
-    float* drow = a.dq + h * a.dq_hs + static_cast<int64_t>(i) * a.dq_ts;
+    // the whole dQ row, or this key range's partial of it
+    float* drow = n_ks == 1 ? a.dq + h * a.dq_hs + static_cast<int64_t>(i) * a.dq_ts
+                            : part + ((static_cast<int64_t>(kr) * a.pool.Hq + h) * a.n_q + i) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -176,11 +186,62 @@ void dq_mfma_kernel(AttnArgs a) {
   }
 }
 
+// dQ = the sum of the key ranges' partials, in range order. One thread per 4 columns
+// of a row.
+__global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, const float* part) {
+  const int64_t rows = static_cast<int64_t>(a.pool.Hq) * a.n_q;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= rows * (D / 4)) return;
+  const int64_t row = idx / (D / 4);
+  const int c = static_cast<int>(idx % (D / 4)) * 4;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + row * D + c);
+  for (int k = 1; k < n_ks; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + (k * rows + row) * D + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] += v[j];
+  }
+  const int h = static_cast<int>(row / a.n_q), i = static_cast<int>(row % a.n_q);
+  *reinterpret_cast<f32x4*>(a.dq + h * a.dq_hs + static_cast<int64_t>(i) * a.dq_ts + c) = s;
+}
+
 }  // namespace mf
 
-hipError_t launch_dq_mfma(const AttnArgs& a, hipStream_t s) {
+// Key ranges per query tile of the dQ pass, chosen for load balance as in the dK/dV
+// pass: a tile's work is its key blocks (prior keys plus the chunk keys its last query
+// sees); the largest range is kept at most a quarter of the average work per workgroup
+// slot (two per CU, 256 CUs, fixed so the choice and the result bits do not depend on
+// the device).
+int dq_splits(const AttnArgs& a) {
   const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
-  OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, dim3(a.pool.Hq * n_qt), dim3(64 * mf::DQ_WAVES), 0, s, a);
+  const int64_t prior_keys = static_cast<int64_t>(a.max_att_pages - a.n_local) * a.pool.P;
+  const int64_t off = a.t0 - static_cast<int64_t>(a.first_local) * a.pool.P;  // chunk keys before query 0
+  double total = 0.0, largest = 0.0;
+  for (int qt = 0; qt < n_qt; ++qt) {
+    const int64_t last = (qt + 1) * static_cast<int64_t>(mf::DQ_Q) < a.n_q ? (qt + 1) * static_cast<int64_t>(mf::DQ_Q) : a.n_q;
+    const double blocks = static_cast<double>((prior_keys + off + last + mf::KB - 1) / mf::KB);
+    total += blocks;
+    largest = blocks > largest ? blocks : largest;
+  }
+  const double per_slot = total * a.pool.Hq / 512.0;
+  int nk = 1;
+  while (nk < 4 && largest / nk > per_slot / 4.0) nk *= 2;
+  return nk;
+}
+
+size_t dq_partial_bytes(const AttnArgs& a, int n_ks) {
+  if (n_ks <= 1) return 0;
+  return static_cast<size_t>(n_ks) * a.pool.Hq * a.n_q * mf::D * sizeof(float);
+}
+
+hipError_t launch_dq_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s) {
+  const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
+  OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, dim3(a.pool.Hq * n_qt * n_ks), dim3(64 * mf::DQ_WAVES), 0,
+              s, a, n_ks, part);
+  if (n_ks > 1) {
+    const int64_t threads = static_cast<int64_t>(a.pool.Hq) * a.n_q * (mf::D / 4);
+    OOMB_LAUNCH("dq_merge", mf::dq_merge_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                dim3(256), 0, s, a, n_ks, part);
+  }
   return hipGetLastError();
 }
 

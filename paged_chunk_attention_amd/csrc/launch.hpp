@@ -100,12 +100,16 @@ hipError_t launch_bwd_scalar(const AttnArgs& a, hipStream_t s);
 // Matrix-core kernels: bf16, head_dim 128, page size >= 16.
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
 // n_split > 1 splits the dK/dV pass over the query stream; `part` then holds
-// dkdv_partial_bytes(a, n_split) bytes of fp32 partials.
-hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, hipStream_t s);
+// dkdv_partial_bytes(a, n_split) bytes of fp32 partials. n_ks > 1 splits the dQ pass
+// over key ranges; `dq_part` then holds dq_partial_bytes(a, n_ks) bytes.
+hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, int n_ks, float* dq_part,
+                           hipStream_t s);
 // dQ pass of the matrix-core backward (launched by launch_bwd_mfma after Delta).
-hipError_t launch_dq_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_dq_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s);
 int dkdv_splits(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, int n_split);
+int dq_splits(const AttnArgs& a);
+size_t dq_partial_bytes(const AttnArgs& a, int n_ks);
 // Delta_i = dO_i . O_i, shared by both backward paths.
 hipError_t launch_delta(const AttnArgs& a, hipStream_t s);
 
