@@ -233,6 +233,8 @@ def main():
     ws_sel = torch.empty(pca.select_workspace_bytes(pool, C, t0), dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(pca.bwd_workspace_bytes(pool, C, t0, sel.stride(0) if w.top_k is not None else -1),
                          dtype=torch.uint8, device=dev)
+    ws_fwd = torch.empty(max(256, pca.fwd_workspace_bytes(pool, C, t0, sel.stride(0) if w.top_k is not None else -1)),
+                         dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty(w.hq, C, dtype=torch.float32, device=dev)
     dq = torch.empty(w.hq, C, w.d, dtype=torch.float32, device=dev)
@@ -245,7 +247,8 @@ def main():
         if sparse:
             s_, c_ = pca.oomb_select_pages(pool, table, q, t0, w.top_k, sel=sel, count=count,
                                            workspace=ws_sel)
-        pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, s_, c_, w.scale, o=o, lse=lse)
+        pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, s_, c_, w.scale, o=o, lse=lse,
+                                      workspace=ws_fwd)
         pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, s_, c_, o, do, lse, w.scale,
                                       dq=dq, workspace=ws_bwd)
 

@@ -146,18 +146,32 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
  * to t0/P), or every page before t0/P when sel == NULL (dense).
  *   s_t = scale * q.k_t ;  LSE = ln sum_t exp(s_t) ;  O = sum_t exp(s_t - LSE) v_t
  * Writes o ([Hq][n_q][D] view, dtype of the pool) and lse (fp32 [Hq][n_q],
- * contiguous). Keys beyond t0 + n_q are never read into the result. */
+ * contiguous). Keys beyond t0 + n_q are never read into the result. The workspace
+ * must hold oomb_fwd_workspace_bytes(pool, n_q, t0, sel ? sel_stride : -1) bytes at a
+ * 256-byte aligned address (it may be NULL when that is 0); its contents on entry do
+ * not matter. */
 int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table,
                               int64_t table_stride, const void* q, int64_t q_head_stride,
                               int64_t q_tok_stride, int32_t n_q, int64_t t0,
                               const int32_t* sel, int64_t sel_stride, const int32_t* count,
                               float scale, void* o, int64_t o_head_stride,
-                              int64_t o_tok_stride, float* lse, void* stream);
+                              int64_t o_tok_stride, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace oomb_paged_chunk_attn_fwd needs (256-byte aligned) for
+ * n_q queries after t0 prior tokens, with at most sel_stride selected prior pages per
+ * KV head (sel_stride < 0: dense). It holds fp32 partial outputs when the query tiles'
+ * key blocks are cut into ranges so that the work spreads evenly over the GPU (an
+ * in-order merge then combines them: results stay bit-reproducible). May be 0.
+ * Returns 0 for invalid arguments. */
+size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
+                                int64_t sel_stride);
 
 /* Bytes of device workspace oomb_paged_chunk_attn_bwd needs (256-byte aligned) for
  * n_q queries after t0 prior tokens, with at most sel_stride selected prior pages
  * per KV head (sel_stride < 0: dense, every prior page). It holds Delta and, when
- * the dK/dV pass is split over the query stream to fill the GPU, fp32 partials.
+ * the dK/dV pass is split over the query stream or the dQ pass over key ranges (so
+ * that the work spreads evenly over the GPU), their fp32 partials.
  * Returns 0 for invalid arguments. */
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
                                 int64_t sel_stride);

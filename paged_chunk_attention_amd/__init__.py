@@ -9,6 +9,7 @@ dK/dV into a paged fp32 gradient pool.
 from .binding import (  # noqa: F401
     PagedPool,
     bwd_workspace_bytes,
+    fwd_workspace_bytes,
     kernel_timer,
     oomb_kv_append,
     oomb_page_summarize,

@@ -122,6 +122,11 @@ def bwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1
     return int(lib().oomb_bwd_workspace_bytes(pool.ref(), n_q, t0, sel_stride))
 
 
+def fwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1) -> int:
+    """Workspace of oomb_paged_chunk_attn_fwd (sel_stride = -1 for dense calls)."""
+    return int(lib().oomb_fwd_workspace_bytes(pool.ref(), n_q, t0, sel_stride))
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
     if ws is None:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -159,6 +164,7 @@ def oomb_paged_chunk_attn_fwd(pool: PagedPool, table: torch.Tensor, q: torch.Ten
                               count: Optional[torch.Tensor] = None,
                               scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None,
                               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention of the chunk q [Hq, n_q, D] (first query at position t0) over the
     selected (or all, when sel is None) prior pages and its own pages.
@@ -176,9 +182,11 @@ def oomb_paged_chunk_attn_fwd(pool: PagedPool, table: torch.Tensor, q: torch.Ten
     if not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
         raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
     sel_stride = 0 if sel is None else sel.stride(0)
+    need = fwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride)
+    ws = _workspace(need, q.device, workspace) if need > 0 or workspace is not None else None
     call("oomb_paged_chunk_attn_fwd", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts,
          n_q, t0, _ptr(sel), sel_stride, _ptr(count), float(scale), _ptr(o), ohs, ots, _ptr(lse),
-         _stream(stream))
+         _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     return o, lse
 
 

@@ -185,7 +185,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 2; }
+int oomb_abi_version(void) { return 3; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -296,11 +296,34 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
   return hip_status(oomb::launch_select(a, static_cast<hipStream_t>(stream)), "select_pages");
 }
 
+// Forward workspace: (matrix-core path, when query tiles are split into key ranges)
+// the ranges' fp32 partials.
+static size_t fwd_workspace(const oomb::AttnArgs& a) {
+  if (!use_mfma(a.pool)) return 0;
+  return align256(oomb::fwd_partial_bytes(a, oomb::fwd_splits(a)));
+}
+
+size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
+                                int64_t sel_stride) {
+  oomb::AttnArgs a{};
+  if (check_pool(pool, &a.pool, false, false) != OOMB_OK) return 0;
+  ChunkGeom cg;
+  if (check_chunk(a.pool, n_q, t0, &cg) != OOMB_OK) return 0;
+  a.n_q = n_q;
+  const int64_t prior = sel_stride >= 0 ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
+  a.max_att_pages = static_cast<int>(prior + cg.n_local);
+  a.n_local = cg.n_local;
+  a.first_local = cg.first_local;
+  a.t0 = static_cast<int>(t0);
+  return fwd_workspace(a);
+}
+
 int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                               const void* q, int64_t q_head_stride, int64_t q_tok_stride,
                               int32_t n_q, int64_t t0, const int32_t* sel, int64_t sel_stride,
                               const int32_t* count, float scale, void* o, int64_t o_head_stride,
-                              int64_t o_tok_stride, float* lse, void* stream) {
+                              int64_t o_tok_stride, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   oomb::AttnArgs a;
   int st = check_attn(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, sel,
                       sel_stride, count, false, &a);
@@ -314,8 +337,13 @@ int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64
   a.o_hs = o_head_stride;
   a.o_ts = o_tok_stride;
   a.lse = lse;
+  const size_t need = fwd_workspace(a);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return fail(OOMB_ERR_WORKSPACE, "fwd needs %zu bytes of 256-byte aligned workspace", need);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(use_mfma(a.pool) ? oomb::launch_fwd_mfma(a, s) : oomb::launch_fwd_scalar(a, s),
+  if (!use_mfma(a.pool)) return hip_status(oomb::launch_fwd_scalar(a, s), "paged_chunk_attn_fwd");
+  return hip_status(oomb::launch_fwd_mfma(a, oomb::fwd_splits(a), static_cast<float*>(workspace), s),
                     "paged_chunk_attn_fwd");
 }
 

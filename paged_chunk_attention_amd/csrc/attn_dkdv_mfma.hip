@@ -44,12 +44,11 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int nkb = (a.max_att_pages * a.pool.P + KPW - 1) / KPW;
-  // Key-block-major order: the blocks of one key block index (equal work) are
-  // consecutive, and the work per block only falls with the index (local blocks see
-  // fewer query tiles), so the round-robin dispatch over XCDs and CUs is longest
-  // first and every XCD gets the same mix.
-  const int L = blockIdx.x;
-  const int split = L % n_split, g = (L / n_split) % a.pool.Hkv, kb = L / (n_split * a.pool.Hkv);
+  // A head's units in key-block order (the splits of a block consecutive): the work per
+  // block only falls with the index (local blocks see fewer query tiles), so this is
+  // longest first.
+  const HeadUnit hu = head_unit(blockIdx.x, gridDim.x, a.pool.Hkv);
+  const int g = hu.head, split = hu.unit % n_split, kb = hu.unit / n_split;
   const Keys km = make_keys(a, g);
   const int k0 = kb * KPW;
   if (kb >= nkb || k0 >= km.n_keys) return;  // uniform: block past this head's attended keys
@@ -356,11 +355,13 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(AttnArgs a, int n_split
 
 // Query-stream splits of the dK/dV pass, chosen for load balance: a workgroup's work
 // is G times the query tiles its key block can see (all of them for prior pages, fewer
-// for the chunk's own pages), and the largest unit (a prior block's share) is kept at
-// most a quarter of the average work per CU, so that longest-first list scheduling
-// over the CUs ends evenly. The CU count is fixed at the MI355X's 256, which keeps the
-// choice, and so the result bits and the workspace size, independent of the device.
+// for the chunk's own pages). The splits are doubled while the largest unit (a prior
+// block's share) is more than a quarter of the average work per CU and would stay at
+// least 64 tiles, so that longest-first list scheduling over the CUs ends evenly. The
+// CU count is fixed at the MI355X's 256, which keeps the choice, and so the result
+// bits and the workspace size, independent of the device.
 int dkdv_splits(const AttnArgs& a) {
+  if (const int n = split_override("OOMB_DKDV_SPLITS")) return n;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + mf::QTB - 1) / mf::QTB;
   const int64_t n_keys = static_cast<int64_t>(a.max_att_pages) * a.pool.P;
@@ -374,7 +375,8 @@ int dkdv_splits(const AttnArgs& a) {
   }
   const double per_cu = total * a.pool.Hkv / 256.0;
   int ns = 1;
-  while (ns < 8 && static_cast<double>(G) * n_qt / ns > per_cu / 4.0) ns *= 2;
+  const double largest = static_cast<double>(G) * n_qt;
+  while (ns < 8 && largest / ns > per_cu / 4.0 && largest / (2 * ns) >= 64.0) ns *= 2;
   return ns;
 }
 

@@ -34,11 +34,12 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + DQ_Q - 1) / DQ_Q;
-  // Latest query tiles (most local keys, the longest) are dispatched first, all heads
-  // of a tile and all key ranges of a head consecutive: longest-first over the CUs.
-  const int kr = blockIdx.x % n_ks, rest = blockIdx.x / n_ks;
-  const int h = rest % a.pool.Hq, qt = n_qt - 1 - rest / a.pool.Hq;
-  const int g = h / G;
+  // A KV head's units: latest query tiles (most local keys, the longest) first, then
+  // the group's heads, then the key ranges of one tile.
+  const HeadUnit hu = head_unit(blockIdx.x, gridDim.x, a.pool.Hkv);
+  const int g = hu.head, kr = hu.unit % n_ks;
+  const int hh = (hu.unit / n_ks) % G, qt = n_qt - 1 - hu.unit / (n_ks * G);
+  const int h = g * G + hh;
   const Keys km = make_keys(a, g);
   const int q0 = qt * DQ_Q;
   const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);
@@ -206,12 +207,14 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, con
 
 }  // namespace mf
 
-// Key ranges per query tile of the dQ pass, chosen for load balance as in the dK/dV
-// pass: a tile's work is its key blocks (prior keys plus the chunk keys its last query
-// sees); the largest range is kept at most a quarter of the average work per workgroup
+// Key ranges per query tile of the dQ pass, chosen for load balance: a tile's work is
+// its key blocks (prior keys plus the chunk keys its last query sees). The ranges are
+// halved while the largest is more than a quarter of the average work per workgroup
 // slot (two per CU, 256 CUs, fixed so the choice and the result bits do not depend on
-// the device).
+// the device) and would stay at least 64 blocks, below which the partials' traffic and
+// each workgroup's start-up outweigh the balance gained.
 int dq_splits(const AttnArgs& a) {
+  if (const int n = split_override("OOMB_DQ_SPLITS")) return n;
   const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
   const int64_t prior_keys = static_cast<int64_t>(a.max_att_pages - a.n_local) * a.pool.P;
   const int64_t off = a.t0 - static_cast<int64_t>(a.first_local) * a.pool.P;  // chunk keys before query 0
@@ -224,7 +227,7 @@ int dq_splits(const AttnArgs& a) {
   }
   const double per_slot = total * a.pool.Hq / 512.0;
   int nk = 1;
-  while (nk < 4 && largest / nk > per_slot / 4.0) nk *= 2;
+  while (nk < 4 && largest / nk > per_slot / 4.0 && largest / (2 * nk) >= 64.0) nk *= 2;
   return nk;
 }
 

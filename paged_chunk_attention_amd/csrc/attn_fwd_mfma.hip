@@ -11,6 +11,10 @@
 // phases ahead of their first use, in triple buffers whose roles are static in each of
 // the six phases of the loop body: no read ever waits for a DMA into a buffer it does
 // not read, and each wave waits only for its batch of two phases ago.
+//
+// A query tile's key blocks may be cut into n_ks equal ranges, one workgroup each, for
+// load balance; each range then writes its unnormalised fp32 O with its running
+// maximum and sum, and a merge kernel combines them in range order.
 #include <type_traits>
 
 #include "mfma_tiles.hpp"
@@ -27,7 +31,7 @@ constexpr int FWD_CAP = 8192;
 
 template <int CAP, bool SLIDE>
 __global__ __launch_bounds__(64 * FWD_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_mfma_kernel(AttnArgs a) {
+void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k2[KB * D];
@@ -42,21 +46,25 @@ void fwd_mfma_kernel(AttnArgs a) {
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + FWD_Q - 1) / FWD_Q;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int hh = L % G, rest = L / G;
-  // Latest query tiles (most local keys, the longest) are dispatched first.
-  const int qt = n_qt - 1 - rest % n_qt, g = rest / n_qt;
+  // A KV head's units: latest query tiles (most local keys, the longest) first, then
+  // the group's heads, then the key ranges of one tile.
+  const HeadUnit hu = head_unit(blockIdx.x, gridDim.x, a.pool.Hkv);
+  const int g = hu.head, krange = hu.unit % n_ks;
+  const int hh = (hu.unit / n_ks) % G, qt = n_qt - 1 - hu.unit / (n_ks * G);
   const int h = g * G + hh;
   const Keys km = make_keys(a, g);
   const int q0 = qt * FWD_Q;
-  const int nb = n_blocks(km, a.t0 + min(a.n_q, q0 + FWD_Q) - 1);  // key blocks of the tile
+  const int nb_tile = n_blocks(km, a.t0 + min(a.n_q, q0 + FWD_Q) - 1);  // key blocks of the tile
+  // This workgroup's blocks are b0 .. b0 + nb - 1; below, block indices are relative
+  // to b0 and made absolute (b0 + .) wherever keys are addressed or masked.
+  const int b0 = nb_tile * krange / n_ks, nb = nb_tile * (krange + 1) / n_ks - b0;
   const float c2 = a.scale * kLog2e;
 
   // This wave's queries: blocks past its last query are skipped; blocks reaching past
   // its first query need the mask.
   const int wq0 = q0 + 32 * wave;
   const int wq_last = min(a.n_q, wq0 + 32) - 1;
-  const int nblk_w = wq_last < wq0 ? 0 : n_blocks(km, a.t0 + wq_last);
+  const int nblk_w = min(nb, max(0, (wq_last < wq0 ? 0 : n_blocks(km, a.t0 + wq_last)) - b0));
   const int klim_w0 = km.klim(a.t0 + wq0);
 
   // This lane's query (column of S^T) and its Q fragments (B operand over d).
@@ -88,20 +96,22 @@ void fwd_mfma_kernel(AttnArgs a) {
   const uint16_t* kpool = static_cast<const uint16_t*>(a.pool.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.pool.v_pool);
   // All 8 waves stage the first blocks; afterwards each group of 4 stages one tensor.
-  KeyStage<KB, FWD_WAVES, CAP> ks{km, s_page, 0, kpool, vpool,
+  // With every page id resident the window starts at entry 0, else at block b0's.
+  const int win0 = SLIDE ? (b0 * KB) >> km.log2p : 0;
+  KeyStage<KB, FWD_WAVES, CAP> ks{km, s_page, win0, kpool, vpool,
                                   KeyStage<KB, FWD_WAVES, CAP>::lane_offset(wave, lane)};
-  KeyStage<KB, 4, CAP> kg{km, s_page, 0, kpool, vpool,
+  KeyStage<KB, 4, CAP> kg{km, s_page, win0, kpool, vpool,
                           KeyStage<KB, 4, CAP>::lane_offset(wave & 3, lane)};
-  fill_pages<NT, CAP>(km, s_page, 0, tid);
+  fill_pages<NT, CAP>(km, s_page, win0, tid);
   zero_tile<KB, NT>(s_v1, tid);  // read (times a zero P^T) before their first DMA
   zero_tile<KB, NT>(s_v2, tid);
   wait_dma();  // the page-table loads are retired here, not at a later register reuse
   __syncthreads();
   // K_0, K_1 and V_0 before the first phase; every later block arrives four phases
   // ahead of its first use.
-  ks.issue_fixed(0, kpool, s_k0, wave, lane);
-  ks.issue_fixed(1, kpool, s_k1, wave, lane);
-  ks.issue_fixed(0, vpool, s_v0, wave, lane);
+  ks.issue_fixed(b0, kpool, s_k0, wave, lane);
+  ks.issue_fixed(b0 + 1, kpool, s_k1, wave, lane);
+  ks.issue_fixed(b0, vpool, s_v0, wave, lane);
   wait_dma();
   __syncthreads();
 
@@ -152,13 +162,14 @@ void fwd_mfma_kernel(AttnArgs a) {
   };
   // Softmax numerator of block b from st into pb.
   auto softmax = [&](int b) __attribute__((always_inline)) {
+    const int k0 = (b0 + b) * KB;  // first key of the block
     // Causal / tail mask, only in blocks that reach past this wave's first query.
-    if (b * KB + KB - 1 > klim_w0) {
+    if (k0 + KB - 1 > klim_w0) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3) > klim) st[sub][r] = -__builtin_inff();
+          if (k0 + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3) > klim) st[sub][r] = -__builtin_inff();
     }
     // Row maximum: four independent chains, then the other half-wave's rows.
     float mx4[4] = {st[0][0], st[0][1], st[0][2], st[0][3]};
@@ -209,9 +220,9 @@ void fwd_mfma_kernel(AttnArgs a) {
     const int j = t >> 1;
     if constexpr (SLIDE) {
       if ((t & 1) == 0) {
-        const int last_e = (min(nb, j + 3) * KB - 1) >> km.log2p;
+        const int last_e = ((b0 + min(nb, j + 3)) * KB - 1) >> km.log2p;
         if (j + 1 < nb && last_e >= ks.win + CAP) {  // uniform: slide the page window
-          ks.win = kg.win = ((j + 1) * KB) >> km.log2p;
+          ks.win = kg.win = ((b0 + j + 1) * KB) >> km.log2p;
           fill_pages<NT, CAP>(km, s_page, ks.win, tid);
           wait_dma();
           __syncthreads();
@@ -222,7 +233,7 @@ void fwd_mfma_kernel(AttnArgs a) {
     // with every page id resident they are read one duty ahead; with a sliding window,
     // at the start of the phase. The DMA itself is issued after this wave's softmax.
     const bool dma = kG1 ? (t & 1) == 0 : (t & 1) == 1;
-    const int dst = kG1 ? j + 2 : j + 1;
+    const int dst = b0 + (kG1 ? j + 2 : j + 1);  // absolute block
     if constexpr (SLIDE) {
       if (dma) kg.read_pages(dst, wave & 3, pid);
     }
@@ -251,7 +262,7 @@ void fwd_mfma_kernel(AttnArgs a) {
   using M = std::integral_constant<bool, true>;
   using V = std::integral_constant<bool, false>;
   const int T = 2 * nb + 2;
-  if constexpr (!SLIDE) kg.read_pages(grp ? 2 : 1, wave & 3, pid);  // first duty: K_2 / V_1
+  if constexpr (!SLIDE) kg.read_pages(b0 + (grp ? 2 : 1), wave & 3, pid);  // first duty: K_2 / V_1
   if (grp == 0) {
     using G = std::integral_constant<bool, false>;
     for (int t = 0; t < T; t += 6) {
@@ -275,8 +286,25 @@ void fwd_mfma_kernel(AttnArgs a) {
   }
   wait_dma();  // no DMA may outlive the workgroup's LDS
 
-  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
+  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; or this key range's partial.
   const float lt = add_halves(l_run);
+  if (n_ks > 1) {
+    if (i < a.n_q) {
+      const int64_t row = (static_cast<int64_t>(krange) * a.pool.Hq + h) * a.n_q + i;
+      float* prow = part + row * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int ga = 0; ga < 4; ++ga) {
+          f32x4 w;
+#pragma unroll
+          for (int b2 = 0; b2 < 4; ++b2) w[b2] = ot[db][4 * ga + b2];
+          *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * ga + 4 * h2) = w;
+        }
+      if (h2 == 0) *reinterpret_cast<f32x2*>(part_ml + 2 * row) = f32x2{m_run, lt};
+    }
+    return;
+  }
   const float inv = 1.0f / lt;
   if (i < a.n_q) {
     uint16_t* orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + static_cast<int64_t>(i) * a.o_ts;
@@ -293,15 +321,87 @@ void fwd_mfma_kernel(AttnArgs a) {
   }
 }
 
+// O and LSE from the key ranges' partials: with M the largest running maximum (log2
+// units), w_r = 2^(m_r - M), O = sum_r w_r O_r / sum_r w_r l_r and
+// LSE = (M + log2 sum_r w_r l_r) ln 2, the ranges taken in order. One thread per 4
+// columns of a row.
+__global__ __launch_bounds__(256) void fwd_merge_kernel(AttnArgs a, int n_ks, const float* part,
+                                                        const float* part_ml) {
+  const int64_t rows = static_cast<int64_t>(a.pool.Hq) * a.n_q;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= rows * (D / 4)) return;
+  const int64_t row = idx / (D / 4);
+  const int c = static_cast<int>(idx % (D / 4)) * 4;
+  float mx = -__builtin_inff();
+  for (int k = 0; k < n_ks; ++k) mx = fmaxf(mx, part_ml[2 * (k * rows + row)]);
+  float l = 0.0f;
+  f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < n_ks; ++k) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(part_ml + 2 * (k * rows + row));
+    const float w = ml[0] == -__builtin_inff() ? 0.0f : exp2f(ml[0] - mx);  // empty range: 0
+    l += w * ml[1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + (k * rows + row) * D + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] += w * v[j];
+  }
+  const float inv = 1.0f / l;
+  const int h = static_cast<int>(row / a.n_q), i = static_cast<int>(row % a.n_q);
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + h * a.o_hs + static_cast<int64_t>(i) * a.o_ts;
+  u32x2 w2;
+  w2[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+  w2[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+  *reinterpret_cast<u32x2*>(orow + c) = w2;
+  if (c == 0) a.lse[row] = (mx + __log2f(l)) * kLn2;
+}
+
 }  // namespace mf
 
-hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s) {
+// Key ranges per query tile of the forward, chosen for load balance: a tile's work is
+// its key blocks. The ranges are halved while the largest is more than a quarter of
+// the average work per CU (256 CUs, one workgroup each, fixed so the choice and the
+// result bits do not depend on the device) and would stay at least 128 blocks: a CU
+// runs one forward workgroup at a time, so each one's start-up (query fragments, page
+// list, first key blocks) is exposed, and shorter ranges cost more than they balance.
+int fwd_splits(const AttnArgs& a) {
+  if (const int n = split_override("OOMB_FWD_SPLITS")) return n;
   const int n_qt = (a.n_q + mf::FWD_Q - 1) / mf::FWD_Q;
-  const dim3 grid(a.pool.Hq * n_qt), block(64 * mf::FWD_WAVES);
+  const int64_t prior_keys = static_cast<int64_t>(a.max_att_pages - a.n_local) * a.pool.P;
+  const int64_t off = a.t0 - static_cast<int64_t>(a.first_local) * a.pool.P;  // chunk keys before query 0
+  double total = 0.0, largest = 0.0;
+  for (int qt = 0; qt < n_qt; ++qt) {
+    const int64_t end = (qt + 1) * static_cast<int64_t>(mf::FWD_Q);
+    const int64_t last = end < a.n_q ? end : a.n_q;
+    const double blocks = static_cast<double>((prior_keys + off + last + mf::KB - 1) / mf::KB);
+    total += blocks;
+    largest = blocks > largest ? blocks : largest;
+  }
+  const double per_cu = total * a.pool.Hq / 256.0;
+  int nk = 1;
+  while (nk < 4 && largest / nk > per_cu / 4.0 && largest / (2 * nk) >= 128.0) nk *= 2;
+  return nk;
+}
+
+size_t fwd_partial_bytes(const AttnArgs& a, int n_ks) {
+  if (n_ks <= 1) return 0;
+  return static_cast<size_t>(n_ks) * a.pool.Hq * a.n_q * (mf::D + 2) * sizeof(float);
+}
+
+hipError_t launch_fwd_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s) {
+  const int n_qt = (a.n_q + mf::FWD_Q - 1) / mf::FWD_Q;
+  const dim3 grid(a.pool.Hq * n_qt * n_ks), block(64 * mf::FWD_WAVES);
+  // partial O [n_ks][Hq][n_q][D], then (m, l) [n_ks][Hq][n_q][2]
+  float* part_ml = part ? part + static_cast<size_t>(n_ks) * a.pool.Hq * a.n_q * mf::D : nullptr;
   if (a.max_att_pages <= mf::FWD_CAP) {
-    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::FWD_CAP, false>), grid, block, 0, s, a);
+    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::FWD_CAP, false>), grid, block, 0, s, a, n_ks,
+                part, part_ml);
   } else {
-    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::PCAP, true>), grid, block, 0, s, a);
+    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::PCAP, true>), grid, block, 0, s, a, n_ks, part,
+                part_ml);
+  }
+  if (n_ks > 1) {
+    const int64_t threads = static_cast<int64_t>(a.pool.Hq) * a.n_q * (mf::D / 4);
+    OOMB_LAUNCH("fwd_merge", mf::fwd_merge_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                dim3(256), 0, s, a, n_ks, part, part_ml);
   }
   return hipGetLastError();
 }

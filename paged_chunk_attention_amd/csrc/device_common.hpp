@@ -91,13 +91,23 @@ __device__ __forceinline__ int clamp_count(const int32_t* count, int g, int64_t 
 
 // ---- XCD-aware workgroup order ---------------------------------------------------------
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD
-// i % 8). Renumber them so that each XCD receives one contiguous range of logical
-// workgroup ids: neighbours in logical order then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int i, int n) {
+// i % 8), and within an XCD to whichever CU frees up first. A grid of n workgroups
+// holds n / Hkv work units per KV head, each head's units numbered longest first.
+// head_unit gives workgroup i its (head, unit): each head's units run on their own
+// 8 / Hkv XCDs (the head's keys and queries share those XCDs' L2) and are dealt
+// round-robin among them, so every XCD receives the same mix of long and short units
+// in longest-first order and the greedy fill of its CUs ends evenly. When Hkv does not
+// divide 8 (or n is not a multiple of 8) the units are taken head by head instead.
+struct HeadUnit {
+  int head, unit;
+};
+__device__ __forceinline__ HeadUnit head_unit(int i, int n, int n_heads) {
   constexpr int kXcd = 8;
-  int q = n / kXcd, r = n % kXcd;
-  int x = i % kXcd, local = i / kXcd;
-  return (x < r) ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+  const int per = n / n_heads;
+  if (kXcd % n_heads != 0 || n % kXcd != 0) return {i / per, i % per};
+  const int x_per_head = kXcd / n_heads;
+  const int x = i % kXcd, local = i / kXcd;
+  return {x / x_per_head, local * x_per_head + x % x_per_head};
 }
 
 }  // namespace oomb

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace oomb {
 
@@ -98,7 +99,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_scalar(const AttnArgs& a, hipStream_t s);
 // Matrix-core kernels: bf16, head_dim 128, page size >= 16.
-hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t s);
+// n_ks > 1 splits each query tile's key blocks into ranges; `part` then holds
+// fwd_partial_bytes(a, n_ks) bytes of fp32 partials.
+hipError_t launch_fwd_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s);
+int fwd_splits(const AttnArgs& a);
+size_t fwd_partial_bytes(const AttnArgs& a, int n_ks);
 // n_split > 1 splits the dK/dV pass over the query stream; `part` then holds
 // dkdv_partial_bytes(a, n_split) bytes of fp32 partials. n_ks > 1 splits the dQ pass
 // over key ranges; `dq_part` then holds dq_partial_bytes(a, n_ks) bytes.
@@ -106,6 +111,17 @@ hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, int n_ks
                            hipStream_t s);
 // dQ pass of the matrix-core backward (launched by launch_bwd_mfma after Delta).
 hipError_t launch_dq_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s);
+// The split counts below are chosen for load balance; OOMB_FWD_SPLITS, OOMB_DQ_SPLITS
+// and OOMB_DKDV_SPLITS (1..16) fix them instead, read at every call, so the workspace
+// query and the call agree while the variable does not change. Every count gives the
+// same results up to rounding order; the variables exist so that each code path can
+// be tested at small sizes. Returns 0 when the variable is unset or out of range.
+inline int split_override(const char* var) {
+  const char* v = getenv(var);
+  if (v == nullptr) return 0;
+  const int n = atoi(v);
+  return n >= 1 && n <= 16 ? n : 0;
+}
 int dkdv_splits(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, int n_split);
 int dq_splits(const AttnArgs& a);

@@ -28,14 +28,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 2
+    assert lib.oomb_abi_version() == 3
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text
@@ -56,12 +56,13 @@ T, Q, O, B = 0x600000, 0x700000, 0x800000, 0x900000
 
 def _fwd(lib, pool, **kw):
     a = dict(table=T, tstride=64, q=Q, qhs=4096 * 128, qts=128, n_q=4096, t0=4096, sel=None,
-             sstride=0, count=None, scale=0.088, o=O, ohs=4096 * 128, ots=128, lse=B)
+             sstride=0, count=None, scale=0.088, o=O, ohs=4096 * 128, ots=128, lse=B, ws=0xA00000,
+             wsb=1 << 30)
     a.update(kw)
     return lib.oomb_paged_chunk_attn_fwd(ctypes.byref(pool), a["table"], a["tstride"], a["q"],
                                          a["qhs"], a["qts"], a["n_q"], a["t0"], a["sel"],
                                          a["sstride"], a["count"], a["scale"], a["o"], a["ohs"],
-                                         a["ots"], a["lse"], None)
+                                         a["ots"], a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -122,6 +123,23 @@ def test_summarize_and_select_errors(lib):
     assert sel(score=B, sstr=10) == L.OOMB_ERR_INVALID and b"score_stride" in lib.oomb_last_error()
     assert sel(wsb=ws - 1) == L.OOMB_ERR_WORKSPACE
     assert sel(ws=0xA00010) == L.OOMB_ERR_WORKSPACE
+
+
+def test_fwd_workspace(lib):
+    """The forward's workspace: sized by oomb_fwd_workspace_bytes (empty for a short
+    prior context; for a dense 4096-query chunk after 126,976 tokens the query tiles are
+    split into key ranges, so it is not), and a missing, short or misaligned one is
+    rejected before any launch."""
+    p = _pool()
+    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1) == 0
+    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 0, 4096, -1) == 0
+    t0 = 126976
+    need = lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, t0, -1)
+    assert need >= 2 * 28 * 4096 * 130 * 4 and need % 256 == 0
+    kw = dict(t0=t0, tstride=1024)
+    assert _fwd(lib, p, ws=None, wsb=0, **kw) == L.OOMB_ERR_WORKSPACE
+    assert _fwd(lib, p, wsb=need - 1, **kw) == L.OOMB_ERR_WORKSPACE
+    assert _fwd(lib, p, ws=0xA00010, wsb=need, **kw) == L.OOMB_ERR_WORKSPACE
 
 
 def test_bwd_errors(lib):

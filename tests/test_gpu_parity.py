@@ -45,6 +45,20 @@ def test_chunk_parity_mfma_page_window_slides():
                         total=16 * 8192 + 256))
 
 
+@pytest.mark.parametrize("n", [1, 2, 3])
+@pytest.mark.parametrize("kw", [
+    dict(name="mfma_sparse_k5", chunk=333, total=2597 + 333, top_k=5, needles=3),
+    dict(name="mfma_window_slide", hq=4, hkv=1, page=16, chunk=256, total=16 * 8192 + 256),
+])
+def test_chunk_parity_mfma_fixed_splits(kw, n, monkeypatch):
+    """The split counts fixed through the environment: 1 (forward and dQ tiles whole,
+    dK/dV query stream unsplit), 2 and 3 (ranges of unequal length): every path of the
+    forward, dQ and dK/dV passes and their merges, at sizes whose own choice differs."""
+    for var in ("OOMB_FWD_SPLITS", "OOMB_DQ_SPLITS", "OOMB_DKDV_SPLITS"):
+        monkeypatch.setenv(var, str(n))
+    run_chunk_parity(_w(**dict(kw, name=f"{kw['name']}_splits{n}")))
+
+
 # scalar path: fp32 (any head_dim) and bf16 head_dim 64
 @pytest.mark.parametrize("kw", [
     dict(name="f32_d64_p16", hq=2, hkv=1, d=64, page=16, chunk=64, total=1024, dtype=torch.float32),
