@@ -14,6 +14,7 @@ Prints one JSON line (stdout). Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -62,6 +63,8 @@ def measured_traffic(workload: str, kernel: str):
 def attended_pairs(w, counts):
     """(query, key) pairs the chunk attends, summed over query heads."""
     C, P, t0 = w.chunk, w.page, w.t0
+    if w.window > 0:  # local attention: min(window, p + 1) keys for the query at p
+        return w.hq * sum(min(w.window, t0 + i + 1) for i in range(C))
     first_local = t0 // P
     # local keys visible to query i: positions first_local*P .. t0+i
     local = sum((t0 + i) - first_local * P + 1 for i in range(C))
@@ -82,7 +85,12 @@ def cpu_baseline(w, x, table_cpu, sel_cpu, rows: int):
     P, C, t0, G = w.page, w.chunk, w.t0, w.group
     rows = min(rows, C)
     t0s = t0 + C - rows
-    sel0 = list(sel_cpu[0]) if sel_cpu is not None else list(range(t0 // P))
+    shift = 0
+    if w.window > 0:
+        # local attention depends on positions only through p - t: renumber the pages
+        # from the first one the sample's windows reach, so the oracle scans no others
+        shift = max(0, t0s - w.window + 1) // P * P
+    sel0 = list(sel_cpu[0]) if sel_cpu is not None else list(range(shift // P, t0 // P))
     # the chunk's own pages before the sample are selected pages for the sample
     sel_s = sorted(set(sel0) | set(range(t0 // P, t0s // P)))
     pages = orc.attended_pages(t0s, rows, P, sel_s)
@@ -102,12 +110,22 @@ def cpu_baseline(w, x, table_cpu, sel_cpu, rows: int):
     pairs = 0
     for i in range(rows):
         p = t0s + i
-        pairs += sum(min(P, p - lp * P + 1) for lp in pages if lp * P <= p)
+        lo = p - w.window + 1 if w.window > 0 else 0
+        pairs += sum(max(0, min(P, p - lp * P + 1) - max(0, lo - lp * P)) for lp in pages
+                     if lp * P <= p)
     pairs *= G
     threads = torch.get_num_threads()
     t = time.perf_counter()
-    orc.fwd(q, kp, vp, tab, t0s, [sel_s], w.scale)
-    orc.bwd(q, kp, vp, tab, t0s, [sel_s], w.scale, do)
+    if w.window > 0:
+        # the same computation with every position moved down by `shift` (dense call)
+        tab_w = torch.zeros_like(tab)
+        for lp in pages:
+            tab_w[0, lp - shift // P] = tab[0, lp]
+        orc.fwd(q, kp, vp, tab_w, t0s - shift, None, w.scale, window=w.window)
+        orc.bwd(q, kp, vp, tab_w, t0s - shift, None, w.scale, do, window=w.window)
+    else:
+        orc.fwd(q, kp, vp, tab, t0s, [sel_s], w.scale)
+        orc.bwd(q, kp, vp, tab, t0s, [sel_s], w.scale, do)
     dt = time.perf_counter() - t
     flop = 14 * w.d * pairs
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -191,7 +209,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sparse1m",
-                    choices=["sparse1m", "dense128k", "sparse4m"])
+                    choices=["sparse1m", "dense128k", "sparse4m", "local1m"])
+    ap.add_argument("--window", type=int, default=None,
+                    help="local-attention window overriding the workload's (dense workloads)")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="chunk queries in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -212,6 +232,11 @@ def main():
         sys.exit(1)
     dev = "cuda"
     w = wl.WORKLOADS[args.workload]
+    if args.window is not None:
+        if w.top_k is not None:
+            print("--window applies to dense workloads only", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, window=args.window, name=f"{w.name}_w{args.window}")
     P, C, t0 = w.page, w.chunk, w.t0
     log(f"[bench] workload={w.name} hq={w.hq} hkv={w.hkv} d={w.d} page={P} chunk={C} t0={t0} "
         f"top_k={w.top_k}")
@@ -231,9 +256,10 @@ def main():
     sel = torch.zeros(w.hkv, max(k, 1), dtype=torch.int32, device=dev)
     count = torch.zeros(w.hkv, dtype=torch.int32, device=dev)
     ws_sel = torch.empty(pca.select_workspace_bytes(pool, C, t0), dtype=torch.uint8, device=dev)
-    ws_bwd = torch.empty(pca.bwd_workspace_bytes(pool, C, t0, sel.stride(0) if w.top_k is not None else -1),
+    sstride = sel.stride(0) if w.top_k is not None else -1
+    ws_bwd = torch.empty(pca.bwd_workspace_bytes(pool, C, t0, sstride, w.window),
                          dtype=torch.uint8, device=dev)
-    ws_fwd = torch.empty(max(256, pca.fwd_workspace_bytes(pool, C, t0, sel.stride(0) if w.top_k is not None else -1)),
+    ws_fwd = torch.empty(max(256, pca.fwd_workspace_bytes(pool, C, t0, sstride, w.window)),
                          dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty(w.hq, C, dtype=torch.float32, device=dev)
@@ -248,9 +274,9 @@ def main():
             s_, c_ = pca.oomb_select_pages(pool, table, q, t0, w.top_k, sel=sel, count=count,
                                            workspace=ws_sel)
         pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, s_, c_, w.scale, o=o, lse=lse,
-                                      workspace=ws_fwd)
+                                      workspace=ws_fwd, window=w.window)
         pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, s_, c_, o, do, lse, w.scale,
-                                      dq=dq, workspace=ws_bwd)
+                                      dq=dq, workspace=ws_bwd, window=w.window)
 
     # One plain copy of known size, untimed: under rocprofv3 --pmc its FETCH_SIZE and
     # WRITE_SIZE calibrate the counters against 256 MiB read + 256 MiB written.
@@ -333,6 +359,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
                    "page": P, "chunk": C, "prior_tokens": t0, "top_k": w.top_k,
+                   "window": w.window,
                    "attended_pairs": pairs, "model_flop_per_step": flop,
                    "step": "kv_append+page_summarize+select_pages+fwd+bwd"},
         "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS,

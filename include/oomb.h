@@ -140,32 +140,36 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
 
 /* Chunk attention forward (explainer 2.A/2.B/2.D). Query i of the chunk sits at
  * position t0 + i; q head h uses KV head g = h / (Hq/Hkv). It attends to key t iff
- *   t <= t0 + i  and  page(t) is in  Sel_g U Local,
+ *   t <= t0 + i  and  page(t) is in  Sel_g U Local  (and t > t0 + i - window),
  * where Local = [t0/P, (t0+n_q-1)/P] (the chunk's own pages, appended beforehand)
  * and Sel_g = sel[g*sel_stride + 0..count[g]) (count clamped to [0, sel_stride] and
  * to t0/P), or every page before t0/P when sel == NULL (dense).
+ * window > 0 is local attention, the attention of the sparse layers of sparse-native
+ * models (explainer 2.D): each query sees only the `window` most recent positions up
+ * to its own. It requires sel == NULL; only the pages the windows reach are read.
+ * window == 0: no window; window < 0 is invalid.
  *   s_t = scale * q.k_t ;  LSE = ln sum_t exp(s_t) ;  O = sum_t exp(s_t - LSE) v_t
  * Writes o ([Hq][n_q][D] view, dtype of the pool) and lse (fp32 [Hq][n_q],
  * contiguous). Keys beyond t0 + n_q are never read into the result. The workspace
- * must hold oomb_fwd_workspace_bytes(pool, n_q, t0, sel ? sel_stride : -1) bytes at a
+ * must hold oomb_fwd_workspace_bytes(pool, n_q, t0, sel ? sel_stride : -1, window) bytes at a
  * 256-byte aligned address (it may be NULL when that is 0); its contents on entry do
  * not matter. */
 int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table,
                               int64_t table_stride, const void* q, int64_t q_head_stride,
                               int64_t q_tok_stride, int32_t n_q, int64_t t0,
                               const int32_t* sel, int64_t sel_stride, const int32_t* count,
-                              float scale, void* o, int64_t o_head_stride,
+                              int32_t window, float scale, void* o, int64_t o_head_stride,
                               int64_t o_tok_stride, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace oomb_paged_chunk_attn_fwd needs (256-byte aligned) for
  * n_q queries after t0 prior tokens, with at most sel_stride selected prior pages per
- * KV head (sel_stride < 0: dense). It holds fp32 partial outputs when the query tiles'
- * key blocks are cut into ranges so that the work spreads evenly over the GPU (an
- * in-order merge then combines them: results stay bit-reproducible). May be 0.
- * Returns 0 for invalid arguments. */
+ * KV head (sel_stride < 0: dense) and the call's window. It holds fp32 partial
+ * outputs when the query tiles' key blocks are cut into ranges so that the work
+ * spreads evenly over the GPU (an in-order merge then combines them: results stay
+ * bit-reproducible). May be 0. Returns 0 for invalid arguments. */
 size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
-                                int64_t sel_stride);
+                                int64_t sel_stride, int32_t window);
 
 /* Bytes of device workspace oomb_paged_chunk_attn_bwd needs (256-byte aligned) for
  * n_q queries after t0 prior tokens, with at most sel_stride selected prior pages
@@ -174,13 +178,14 @@ size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
  * that the work spreads evenly over the GPU), their fp32 partials.
  * Returns 0 for invalid arguments. */
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
-                                int64_t sel_stride);
+                                int64_t sel_stride, int32_t window);
 
 /* Chunk attention backward, with the attention probabilities recomputed from the
  * saved LSE (explainer 2.A: activations are recomputed just before use) and the
  * key/value gradients added in place into the paged gradient pool (explainer 2.B:
  * in-place accumulation without intermediate buffers). Same q / table / sel / count /
- * scale as the forward call it differentiates; o and lse are that call's outputs.
+ * window / scale as the forward call it differentiates; o and lse are that call's
+ * outputs.
  * For the loss sum(dout * O):
  *   Delta_i = dO_i . O_i ; P_it = exp(s_it - LSE_i) ; dS_it = P_it (dO_i . v_t - Delta_i)
  *   dq[h][i]  = scale * sum_t dS_it k_t                        (fp32, OVERWRITTEN)
@@ -191,15 +196,15 @@ size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
  * partials go through the workspace and one merge kernel adds them in split order),
  * so results are bit-reproducible. The caller zeroes the gradient pool when a step
  * starts. The workspace must hold oomb_bwd_workspace_bytes(pool, n_q, t0,
- * sel ? sel_stride : -1) bytes. gtable: int32 [Hkv][gtable_stride], may alias
+ * sel ? sel_stride : -1, window) bytes. gtable: int32 [Hkv][gtable_stride], may alias
  * table. dq: fp32 [Hq][n_q][D] view. */
 int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table,
                               int64_t table_stride, const int32_t* gtable,
                               int64_t gtable_stride, const void* q, int64_t q_head_stride,
                               int64_t q_tok_stride, int32_t n_q, int64_t t0,
                               const int32_t* sel, int64_t sel_stride, const int32_t* count,
-                              float scale, const void* o, int64_t o_head_stride,
-                              int64_t o_tok_stride, const void* dout,
+                              int32_t window, float scale, const void* o,
+                              int64_t o_head_stride, int64_t o_tok_stride, const void* dout,
                               int64_t do_head_stride, int64_t do_tok_stride,
                               const float* lse, float* dq, int64_t dq_head_stride,
                               int64_t dq_tok_stride, void* workspace, size_t workspace_bytes,

@@ -12,6 +12,9 @@ Sources (the OOMB pages; "explainer" = the gist.science explainer of arXiv 2602.
     "Paged KV Cache and Gradient Management"; mlsanity abstract.
   * top-K page retrieval from a representative vector: explainer, 2.D "Page-Level
     Sparse Attention".
+  * local attention for the sparse layers of sparse-native models: explainer, 2.D
+    ("Native Support"). The pages do not define it further; it is read here as the
+    usual sliding window: a query at position p sees the keys at p - W < t <= p.
 The pages give no formula. Attention itself is the textbook definition (softmax of
 scaled dot products, causal), so the forward/backward below is that definition
 written out in fp64. Page selection is a heuristic the pages leave open; it is
@@ -24,7 +27,9 @@ multiply-add, in the order documented on each function.
 
 Pins (tests marked "not gpu"): finite differences; equality of the chunk sweep with
 full-sequence causal attention from torch's SDPA; an explicitly masked SDPA call for
-sparse selections; closed forms (single visible key, all-zero keys, row sums of P,
+sparse selections and for windows; window 1 (each query sees only itself) and a
+window covering the whole context (equal to none); closed forms (single visible key,
+all-zero keys, row sums of P,
 column sums of dK and dV); page-permutation invariance; hand-derived values for the
 summation orders (tests/golden/); brute-force order statistics for the top-k.
 No function here is parity-unpinned.
@@ -201,7 +206,8 @@ def select_pages(q, summary, table, t0: int, page: int, group: int, top_k: int):
 # ---------------------------------------------------------------------------
 # Attention of one chunk over the paged cache (explainer 2.A-2.B, 2.D).
 # Query i of the chunk sits at absolute position t0 + i and sees key t iff
-# page(t) is selected or local and t <= t0 + i.
+# page(t) is selected or local and t <= t0 + i; with a window W (local attention,
+# dense calls only) also t > t0 + i - W.
 # ---------------------------------------------------------------------------
 
 def attended_pages(t0: int, n_q: int, page: int, sel: Optional[Sequence[int]]) -> List[int]:
@@ -233,23 +239,34 @@ def _rows(n, rb):
         yield i0, min(n, i0 + rb)
 
 
-def _probs(Qb, K, pos, qpos, scale):
+def _probs(Qb, K, pos, qpos, scale, window=0):
     """P = softmax over visible keys of scale * Q K^T, and the natural-log LSE."""
     S = scale * torch.matmul(Qb, K.T)
-    S = S.masked_fill(pos[None, None, :] > qpos[None, :, None], -math.inf)
+    hidden = pos[None, :] > qpos[:, None]
+    if window > 0:
+        hidden = hidden | (pos[None, :] <= qpos[:, None] - window)
+    S = S.masked_fill(hidden[None], -math.inf)
     m = S.amax(dim=-1, keepdim=True)
     E = torch.exp(S - m)
     Z = E.sum(dim=-1, keepdim=True)
     return E / Z, (m + torch.log(Z))[..., 0]
 
 
-def fwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, row_block: int = 256):
+def _check_window(sel, window):
+    if window < 0 or (window > 0 and sel is not None):
+        raise ValueError("window must be >= 0, and a window (local attention) takes no selection")
+
+
+def fwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, row_block: int = 256,
+        window: int = 0):
     """O [Hq, C, D] and LSE [Hq, C] in float64.
 
     sel: None for dense, else one list of selected logical pages per KV head.
+    window > 0: local attention (sel None), only keys t > p - window are visible.
     For q head h (KV head g = h // G) and query i at p = t0 + i, over the visible
     keys t: s_t = scale * q.k_t, LSE = log sum_t exp(s_t), P_t = exp(s_t - LSE),
     O = sum_t P_t v_t."""
+    _check_window(sel, window)
     hq, C, D = q.shape
     hkv = table.shape[0]
     G = hq // hkv
@@ -262,14 +279,14 @@ def fwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, row_block: int = 2
         pos, K, V = _keys(k_pool, v_pool, table, g, pages, P, t0 + C)
         Qg = q[g * G:(g + 1) * G].to(torch.float64)
         for i0, i1 in _rows(C, row_block):
-            Pm, lse = _probs(Qg[:, i0:i1], K, pos, qpos_all[i0:i1], scale)
+            Pm, lse = _probs(Qg[:, i0:i1], K, pos, qpos_all[i0:i1], scale, window)
             O[g * G:(g + 1) * G, i0:i1] = torch.matmul(Pm, V)
             L[g * G:(g + 1) * G, i0:i1] = lse
     return O, L
 
 
 def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
-        dk_pool=None, dv_pool=None, gtable=None, row_block: int = 256):
+        dk_pool=None, dv_pool=None, gtable=None, row_block: int = 256, window: int = 0):
     """Analytic backward of fwd for the loss sum(dout * O), with O and LSE recomputed
     here (explainer 2.A: activations are recomputed just before the gradient).
 
@@ -284,6 +301,7 @@ def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
         dK_t    = scale * sum_{h in group, i} dS_it q_i
         dV_t    = sum_{h in group, i} P_it dO_i
     """
+    _check_window(sel, window)
     hq, C, D = q.shape
     hkv = table.shape[0]
     G = hq // hkv
@@ -300,7 +318,7 @@ def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
         dV = torch.zeros_like(V)
         for i0, i1 in _rows(C, row_block):
             Qb, dOb = Qg[:, i0:i1], dOg[:, i0:i1]
-            Pm, _ = _probs(Qb, K, pos, qpos_all[i0:i1], scale)
+            Pm, _ = _probs(Qb, K, pos, qpos_all[i0:i1], scale, window)
             Ob = torch.matmul(Pm, V)
             delta = (dOb * Ob).sum(dim=-1, keepdim=True)
             dP = torch.matmul(dOb, V.T)
@@ -317,7 +335,7 @@ def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
 
 
 def sweep(q_all, k_all, v_all, do_all, table, gtable, n_pool: int, page: int, chunk: int,
-          scale: float, top_k: Optional[int] = None):
+          scale: float, top_k: Optional[int] = None, window: int = 0):
     """Chunk-recurrent pass over a whole sequence (explainer 2.A).
 
     Forward, chunk c = 0..S-1: append chunk c's K/V into the pool, summarize its
@@ -350,11 +368,12 @@ def sweep(q_all, k_all, v_all, do_all, table, gtable, n_pool: int, page: int, ch
         if top_k is not None:
             sel = [s for (_, _, s) in select_pages(q_all[:, sl], summary, table, t0, page, G, top_k)]
         sels.append(sel)
-        O[:, sl], L[:, sl] = fwd(q_all[:, sl], k_pool, v_pool, table, t0, sel, scale)
+        O[:, sl], L[:, sl] = fwd(q_all[:, sl], k_pool, v_pool, table, t0, sel, scale,
+                                 window=window)
     for c in reversed(range(S)):
         t0 = c * chunk
         sl = slice(t0, t0 + chunk)
         dQ[:, sl], _ = bwd(q_all[:, sl], k_pool, v_pool, table, t0, sels[c], scale,
-                           do_all[:, sl], dk_pool, dv_pool, gtable)
+                           do_all[:, sl], dk_pool, dv_pool, gtable, window=window)
     return {"O": O, "LSE": L, "dQ": dQ, "dk_pool": dk_pool, "dv_pool": dv_pool,
             "sels": sels, "k_pool": k_pool, "v_pool": v_pool, "summary": summary}

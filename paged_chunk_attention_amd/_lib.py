@@ -43,16 +43,18 @@ SIGNATURES = {
                                   c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p,
                                   c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
     "oomb_paged_chunk_attn_fwd": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64,
-                                          c_int32, c_int64, c_void_p, c_int64, c_void_p, c_float,
+                                          c_int32, c_int64, c_void_p, c_int64, c_void_p, c_int32,
+                                          c_float,
                                           c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                           c_size_t, c_void_p]),
-    "oomb_fwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64]),
-    "oomb_bwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64]),
+    "oomb_fwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64, c_int32]),
+    "oomb_bwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64, c_int32]),
     "oomb_profile_enable": (c_int, [c_int]),
     "oomb_profile_collect": (c_int, [ctypes.POINTER(c_char_p), ctypes.POINTER(c_float), c_int]),
     "oomb_paged_chunk_attn_bwd": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
                                           c_int64, c_int64, c_int32, c_int64, c_void_p, c_int64,
-                                          c_void_p, c_float, c_void_p, c_int64, c_int64, c_void_p,
+                                          c_void_p, c_int32, c_float, c_void_p, c_int64, c_int64,
+                                          c_void_p,
                                           c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int64,
                                           c_void_p, c_size_t, c_void_p]),
 }

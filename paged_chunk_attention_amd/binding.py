@@ -117,14 +117,16 @@ def select_workspace_bytes(pool: PagedPool, n_q: int, t0: int) -> int:
     return int(lib().oomb_select_workspace_bytes(pool.ref(), n_q, t0))
 
 
-def bwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1) -> int:
+def bwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1,
+                        window: int = 0) -> int:
     """Workspace of oomb_paged_chunk_attn_bwd (sel_stride = -1 for dense calls)."""
-    return int(lib().oomb_bwd_workspace_bytes(pool.ref(), n_q, t0, sel_stride))
+    return int(lib().oomb_bwd_workspace_bytes(pool.ref(), n_q, t0, sel_stride, window))
 
 
-def fwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1) -> int:
+def fwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1,
+                        window: int = 0) -> int:
     """Workspace of oomb_paged_chunk_attn_fwd (sel_stride = -1 for dense calls)."""
-    return int(lib().oomb_fwd_workspace_bytes(pool.ref(), n_q, t0, sel_stride))
+    return int(lib().oomb_fwd_workspace_bytes(pool.ref(), n_q, t0, sel_stride, window))
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
@@ -165,9 +167,11 @@ def oomb_paged_chunk_attn_fwd(pool: PagedPool, table: torch.Tensor, q: torch.Ten
                               scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None,
                               workspace: Optional[torch.Tensor] = None,
+                              window: int = 0,
                               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention of the chunk q [Hq, n_q, D] (first query at position t0) over the
-    selected (or all, when sel is None) prior pages and its own pages.
+    selected (or all, when sel is None) prior pages and its own pages; with
+    window > 0 (sel None), local attention over the `window` most recent positions.
     Returns (O [Hq, n_q, D] in the pool dtype, LSE fp32 [Hq, n_q])."""
     _check_table(table, pool, "table")
     hs, ts = _view(q, pool, pool.num_q_heads, "q")
@@ -182,11 +186,11 @@ def oomb_paged_chunk_attn_fwd(pool: PagedPool, table: torch.Tensor, q: torch.Ten
     if not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
         raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
     sel_stride = 0 if sel is None else sel.stride(0)
-    need = fwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride)
+    need = fwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride, window)
     ws = _workspace(need, q.device, workspace) if need > 0 or workspace is not None else None
     call("oomb_paged_chunk_attn_fwd", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts,
-         n_q, t0, _ptr(sel), sel_stride, _ptr(count), float(scale), _ptr(o), ohs, ots, _ptr(lse),
-         _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+         n_q, t0, _ptr(sel), sel_stride, _ptr(count), int(window), float(scale), _ptr(o), ohs,
+         ots, _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     return o, lse
 
 
@@ -196,6 +200,7 @@ def oomb_paged_chunk_attn_bwd(pool: PagedPool, table: torch.Tensor, gtable: torc
                               lse: torch.Tensor, scale: Optional[float] = None,
                               dq: Optional[torch.Tensor] = None,
                               workspace: Optional[torch.Tensor] = None,
+                              window: int = 0,
                               stream=None) -> torch.Tensor:
     """Backward of oomb_paged_chunk_attn_fwd: returns dQ (fp32 [Hq, n_q, D]) and adds
     dK/dV into pool.dk / pool.dv at the pages gtable maps to."""
@@ -215,11 +220,11 @@ def oomb_paged_chunk_attn_bwd(pool: PagedPool, table: torch.Tensor, gtable: torc
     if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
         raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
     sel_stride = 0 if sel is None else sel.stride(0)
-    ws = _workspace(bwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride),
+    ws = _workspace(bwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride, window),
                     q.device, workspace)
     call("oomb_paged_chunk_attn_bwd", pool.ref(), _ptr(table), table.stride(0), _ptr(gtable),
          gtable.stride(0), _ptr(q), hs, ts, n_q, t0, _ptr(sel), sel_stride, _ptr(count),
-         float(scale), _ptr(o), ohs, ots, _ptr(dout), dhs, dts, _ptr(lse), _ptr(dq), qhs, qts,
+         int(window), float(scale), _ptr(o), ohs, ots, _ptr(dout), dhs, dts, _ptr(lse), _ptr(dq), qhs, qts,
          _ptr(ws), ws.numel(), _stream(stream))
     return dq
 

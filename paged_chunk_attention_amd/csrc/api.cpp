@@ -133,16 +133,42 @@ int check_chunk(const oomb::PoolView& v, int32_t n_q, int64_t t0, ChunkGeom* cg)
   return OOMB_OK;
 }
 
+// The attended-page geometry of a chunk, shared by the attention calls and their
+// workspace queries so that both derive the same split counts. With a window (local
+// attention, dense calls only) the prior pages attended are the suffix from the page
+// holding position t0 - window + 1.
+int attn_geometry(const oomb::PoolView& v, int32_t n_q, int64_t t0, bool has_sel,
+                  int64_t sel_stride, int32_t window, oomb::AttnArgs* a) {
+  ChunkGeom cg;
+  int st = check_chunk(v, n_q, t0, &cg);
+  if (st) return st;
+  if (window < 0) return fail(OOMB_ERR_INVALID, "window must be >= 0 (got %d)", window);
+  if (window > 0 && has_sel)
+    return fail(OOMB_ERR_INVALID, "a window (local attention) excludes a page selection");
+  int64_t prior0 = 0;
+  if (window > 0 && t0 - window + 1 > 0) prior0 = (t0 - window + 1) / v.P;
+  a->n_q = n_q;
+  a->t0 = static_cast<int>(t0);
+  a->window = window;
+  a->prior0 = static_cast<int>(prior0);
+  a->n_cand = static_cast<int>(cg.n_cand - prior0);
+  a->first_local = cg.first_local;
+  a->n_local = cg.n_local;
+  const int64_t prior = has_sel ? (sel_stride < a->n_cand ? sel_stride : a->n_cand) : a->n_cand;
+  a->max_att_pages = static_cast<int>(prior + cg.n_local);
+  return OOMB_OK;
+}
+
 // Shared argument checks of the forward and backward calls.
 int check_attn(const oomb_pool* pool, const int32_t* table, int64_t tstride, const void* q,
                int64_t q_hs, int64_t q_ts, int32_t n_q, int64_t t0, const int32_t* sel,
-               int64_t sel_stride, const int32_t* count, bool need_grad, oomb::AttnArgs* a) {
+               int64_t sel_stride, const int32_t* count, int32_t window, bool need_grad,
+               oomb::AttnArgs* a) {
   *a = oomb::AttnArgs{};
   int st = check_pool(pool, &a->pool, false, need_grad);
   if (st) return st;
-  ChunkGeom cg;
-  if ((st = check_chunk(a->pool, n_q, t0, &cg))) return st;
-  if ((st = check_table(table, tstride, cg.first_local + cg.n_local, "table"))) return st;
+  if ((st = attn_geometry(a->pool, n_q, t0, sel != nullptr, sel_stride, window, a))) return st;
+  if ((st = check_table(table, tstride, a->first_local + a->n_local, "table"))) return st;
   if ((st = check_view(q, q_hs, q_ts, elem_size(a->pool), "q"))) return st;
   if (sel != nullptr) {
     if (count == nullptr) return fail(OOMB_ERR_INVALID, "count is NULL while sel is given");
@@ -153,16 +179,9 @@ int check_attn(const oomb_pool* pool, const int32_t* table, int64_t tstride, con
   a->q = q;
   a->q_hs = q_hs;
   a->q_ts = q_ts;
-  a->n_q = n_q;
-  a->t0 = static_cast<int>(t0);
-  a->n_cand = cg.n_cand;
-  a->first_local = cg.first_local;
-  a->n_local = cg.n_local;
   a->sel = sel;
   a->sel_stride = sel_stride;
   a->count = count;
-  const int64_t prior = sel ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
-  a->max_att_pages = static_cast<int>(prior + cg.n_local);
   return OOMB_OK;
 }
 
@@ -185,7 +204,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 3; }
+int oomb_abi_version(void) { return 4; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -304,29 +323,22 @@ static size_t fwd_workspace(const oomb::AttnArgs& a) {
 }
 
 size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
-                                int64_t sel_stride) {
+                                int64_t sel_stride, int32_t window) {
   oomb::AttnArgs a{};
   if (check_pool(pool, &a.pool, false, false) != OOMB_OK) return 0;
-  ChunkGeom cg;
-  if (check_chunk(a.pool, n_q, t0, &cg) != OOMB_OK) return 0;
-  a.n_q = n_q;
-  const int64_t prior = sel_stride >= 0 ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
-  a.max_att_pages = static_cast<int>(prior + cg.n_local);
-  a.n_local = cg.n_local;
-  a.first_local = cg.first_local;
-  a.t0 = static_cast<int>(t0);
+  if (attn_geometry(a.pool, n_q, t0, sel_stride >= 0, sel_stride, window, &a) != OOMB_OK) return 0;
   return fwd_workspace(a);
 }
 
 int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                               const void* q, int64_t q_head_stride, int64_t q_tok_stride,
                               int32_t n_q, int64_t t0, const int32_t* sel, int64_t sel_stride,
-                              const int32_t* count, float scale, void* o, int64_t o_head_stride,
-                              int64_t o_tok_stride, float* lse, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              const int32_t* count, int32_t window, float scale, void* o,
+                              int64_t o_head_stride, int64_t o_tok_stride, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   oomb::AttnArgs a;
   int st = check_attn(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, sel,
-                      sel_stride, count, false, &a);
+                      sel_stride, count, window, false, &a);
   if (st) return st;
   if ((st = check_view(o, o_head_stride, o_tok_stride, elem_size(a.pool), "o"))) return st;
   if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u))
@@ -360,17 +372,10 @@ static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part, size_t* o
 }
 
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
-                                int64_t sel_stride) {
+                                int64_t sel_stride, int32_t window) {
   oomb::AttnArgs a{};
   if (check_pool(pool, &a.pool, false, false) != OOMB_OK) return 0;
-  ChunkGeom cg;
-  if (check_chunk(a.pool, n_q, t0, &cg) != OOMB_OK) return 0;
-  a.n_q = n_q;
-  const int64_t prior = sel_stride >= 0 ? (sel_stride < cg.n_cand ? sel_stride : cg.n_cand) : cg.n_cand;
-  a.max_att_pages = static_cast<int>(prior + cg.n_local);
-  a.n_local = cg.n_local;
-  a.first_local = cg.first_local;
-  a.t0 = static_cast<int>(t0);
+  if (attn_geometry(a.pool, n_q, t0, sel_stride >= 0, sel_stride, window, &a) != OOMB_OK) return 0;
   size_t off, off_dq;
   return bwd_workspace(a, &off, &off_dq);
 }
@@ -379,14 +384,14 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
                               const int32_t* gtable, int64_t gtable_stride, const void* q,
                               int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q, int64_t t0,
                               const int32_t* sel, int64_t sel_stride, const int32_t* count,
-                              float scale, const void* o, int64_t o_head_stride,
+                              int32_t window, float scale, const void* o, int64_t o_head_stride,
                               int64_t o_tok_stride, const void* dout, int64_t do_head_stride,
                               int64_t do_tok_stride, const float* lse, float* dq,
                               int64_t dq_head_stride, int64_t dq_tok_stride, void* workspace,
                               size_t workspace_bytes, void* stream) {
   oomb::AttnArgs a;
   int st = check_attn(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, sel,
-                      sel_stride, count, true, &a);
+                      sel_stride, count, window, true, &a);
   if (st) return st;
   if ((st = check_table(gtable, gtable_stride, a.first_local + a.n_local, "gtable"))) return st;
   if ((st = check_view(o, o_head_stride, o_tok_stride, elem_size(a.pool), "o"))) return st;

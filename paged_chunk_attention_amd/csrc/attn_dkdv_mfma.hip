@@ -88,16 +88,21 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   }
 
   // Query tiles that can see some key of this block: every head of the group, from
-  // the first query at or after the block's first key; cut into n_split parts.
+  // the first query at or after the block's first key (with a window, up to the last
+  // query whose window still reaches the block's last key); cut into n_split parts.
   const int n_qt = (a.n_q + QTB - 1) / QTB;
-  int qt0 = 0;
+  int qt0 = 0, qt_end = n_qt;
   if (!km.in_seq(k0)) {
     qt0 = n_qt;
-  } else if (k0 >= km.local0) {
-    const int first_pos = (km.first_local << km.log2p) + (k0 - km.local0);
+  } else if (k0 >= km.local0 || km.window > 0) {  // positions linear (window calls are dense)
+    const int first_pos = km.pos_linear(k0);
     qt0 = first_pos > a.t0 ? (first_pos - a.t0) / QTB : 0;
   }
-  const int tph = n_qt - qt0;
+  if (km.window > 0) {
+    const int lim = km.pos_linear(min(k0 + KPW, km.n_keys) - 1) + km.window - 1 - a.t0;
+    qt_end = lim < 0 ? 0 : min(n_qt, lim / QTB + 1);
+  }
+  const int tph = max(0, qt_end - qt0);
   const int n_tiles = G * tph;
   const int u_begin = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / n_split);
   const int u_end = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / n_split);
@@ -156,7 +161,9 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   auto p_tile = [&](int u, const uint16_t* qt, const uint16_t* dt, const float* lse, int xp)
       __attribute__((always_inline)) {
     const int q0 = (qt0 + u % tph) * QTB;
-    const bool wmask = __any(kpos > a.t0 + q0);  // some pair of this tile hidden for this lane's key?
+    // Some pair of this tile hidden for this lane's key (in its future, or past the end
+    // of a window: q - kpos >= window, written so that kpos = INT_MAX cannot overflow)?
+    const bool wmask = __any(kpos > a.t0 + q0 || (km.window > 0 && a.t0 + q0 + QTB - 1 - kpos >= km.window));
     FragOffsets o = fo;
     o.opaque();
     // S = Q K^T for both 32-query halves, the two chains interleaved, fragments read one
@@ -185,7 +192,8 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         for (int j = 0; j < 8; ++j) {
           const float lse_r = j < 4 ? l0[j] : l1[j - 4];
           float pv = fast_exp2(__builtin_fmaf(sa[us][8 * s + j], c2, -lse_r));
-          if (wmask && kpos > a.t0 + q0 + rA + 8 * (j >> 2) + (j & 3)) pv = 0.0f;
+          const int qpos = a.t0 + q0 + rA + 8 * (j >> 2) + (j & 3);
+          if (wmask && (kpos > qpos || (km.window > 0 && qpos - kpos >= km.window))) pv = 0.0f;
           p[j] = pv;
         }
         pb[us][s] = pack8(p);
@@ -364,18 +372,28 @@ int dkdv_splits(const AttnArgs& a) {
   if (const int n = split_override("OOMB_DKDV_SPLITS")) return n;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + mf::QTB - 1) / mf::QTB;
-  const int64_t n_keys = static_cast<int64_t>(a.max_att_pages) * a.pool.P;
-  const int64_t local0 = static_cast<int64_t>(a.max_att_pages - a.n_local) * a.pool.P;
+  const int64_t P = a.pool.P;
+  const int64_t n_keys = static_cast<int64_t>(a.max_att_pages) * P;
+  const int64_t local0 = static_cast<int64_t>(a.max_att_pages - a.n_local) * P;
   const int64_t nkb = (n_keys + mf::KPW - 1) / mf::KPW;
-  double total = 0.0;
+  double total = 0.0, largest = 0.0;
   for (int64_t kb = 0; kb < nkb; ++kb) {
+    // the query tiles of key block kb, as the kernel bounds them
     const int64_t k0 = kb * mf::KPW;
-    const int64_t qt0 = k0 < local0 ? 0 : (k0 - local0) / mf::QTB;
-    total += static_cast<double>(G) * (qt0 < n_qt ? n_qt - qt0 : 0);
+    const int64_t pos0 = static_cast<int64_t>(a.first_local) * P - local0;  // position of index 0
+    int64_t qt0 = 0, qt_end = n_qt;
+    if (k0 >= local0 || a.window > 0) qt0 = pos0 + k0 > a.t0 ? (pos0 + k0 - a.t0) / mf::QTB : 0;
+    if (a.window > 0) {
+      const int64_t last = (k0 + mf::KPW < n_keys ? k0 + mf::KPW : n_keys) - 1;
+      const int64_t lim = pos0 + last + a.window - 1 - a.t0;
+      qt_end = lim < 0 ? 0 : (lim / mf::QTB + 1 < n_qt ? lim / mf::QTB + 1 : n_qt);
+    }
+    const double t = static_cast<double>(G) * (qt_end > qt0 ? qt_end - qt0 : 0);
+    total += t;
+    largest = t > largest ? t : largest;
   }
   const double per_cu = total * a.pool.Hkv / 256.0;
   int ns = 1;
-  const double largest = static_cast<double>(G) * n_qt;
   while (ns < 8 && largest / ns > per_cu / 4.0 && largest / (2 * ns) >= 64.0) ns *= 2;
   return ns;
 }

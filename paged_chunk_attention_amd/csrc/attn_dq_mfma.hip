@@ -43,7 +43,9 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
   const Keys km = make_keys(a, g);
   const int q0 = qt * DQ_Q;
   const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);
-  const int b0 = nblk * kr / n_ks, b1 = nblk * (kr + 1) / n_ks;  // this workgroup's blocks
+  const int blo_tile = first_block(km, a.t0 + q0);  // 0 without a window
+  const int span = max(0, nblk - blo_tile);
+  const int b0 = blo_tile + span * kr / n_ks, b1 = blo_tile + span * (kr + 1) / n_ks;  // this workgroup's blocks
   const float c2 = a.scale * kLog2e;
 
   // This wave's queries: blocks past its last query are skipped; blocks reaching past
@@ -51,11 +53,13 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
   const int wq0 = q0 + 32 * wave;
   const int wq_last = min(a.n_q, wq0 + 32) - 1;
   const int nblk_w = wq_last < wq0 ? 0 : n_blocks(km, a.t0 + wq_last);
+  const int blo_w = first_block(km, a.t0 + wq0);
   const int klim_w0 = km.klim(a.t0 + wq0);
+  const int klo_wl = km.klo(a.t0 + wq_last);
 
   // This lane's query (column of S^T and dP^T) with its Q and dO fragments.
   const int i = wq0 + col;
-  const int klim = km.klim(a.t0 + i);
+  const int klim = km.klim(a.t0 + i), klo = km.klo(a.t0 + i);
   bf16x8 qf[8], df[8];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + h * a.q_hs + static_cast<int64_t>(i) * a.q_ts;
@@ -113,10 +117,10 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
         if (last2 < ks.win + PCAP) ks.read_pages(b + 2, wave, pid);  // else after the slide
       }
     }
-    if (b < nblk_w) {
+    if (b < nblk_w && b >= blo_w) {
       FragOffsets o = fo;
       o.opaque();
-      const bool mask = b * KB + KB - 1 > klim_w0;
+      const bool mask = b * KB + KB - 1 > klim_w0 || b * KB < klo_wl;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         // S^T = K Q^T and dP^T = V dO^T for 32 keys: two independent chains, fragment
@@ -147,7 +151,8 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
           for (int j = 0; j < 8; ++j) {
             const int r = 8 * s + j;
             float p = fast_exp2(__builtin_fmaf(st[r], c2, -lse2));
-            if (mask && b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3) > klim) p = 0.0f;
+            const int key = b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (mask && (key > klim || key < klo)) p = 0.0f;
             ds[j] = p * (dpt[r] - delta);
           }
           dsb[s] = pack8(ds);
@@ -216,12 +221,9 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, con
 int dq_splits(const AttnArgs& a) {
   if (const int n = split_override("OOMB_DQ_SPLITS")) return n;
   const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
-  const int64_t prior_keys = static_cast<int64_t>(a.max_att_pages - a.n_local) * a.pool.P;
-  const int64_t off = a.t0 - static_cast<int64_t>(a.first_local) * a.pool.P;  // chunk keys before query 0
   double total = 0.0, largest = 0.0;
   for (int qt = 0; qt < n_qt; ++qt) {
-    const int64_t last = (qt + 1) * static_cast<int64_t>(mf::DQ_Q) < a.n_q ? (qt + 1) * static_cast<int64_t>(mf::DQ_Q) : a.n_q;
-    const double blocks = static_cast<double>((prior_keys + off + last + mf::KB - 1) / mf::KB);
+    const double blocks = static_cast<double>(tile_key_blocks(a, qt * mf::DQ_Q, mf::DQ_Q, mf::KB));
     total += blocks;
     largest = blocks > largest ? blocks : largest;
   }

@@ -54,22 +54,29 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
   const int h = g * G + hh;
   const Keys km = make_keys(a, g);
   const int q0 = qt * FWD_Q;
-  const int nb_tile = n_blocks(km, a.t0 + min(a.n_q, q0 + FWD_Q) - 1);  // key blocks of the tile
+  // Key blocks of the tile: from the first one its first query sees (0 without a
+  // window) to the last one its last query sees.
+  const int blo_tile = first_block(km, a.t0 + q0);
+  const int nb_tile = n_blocks(km, a.t0 + min(a.n_q, q0 + FWD_Q) - 1);
+  const int span = max(0, nb_tile - blo_tile);
   // This workgroup's blocks are b0 .. b0 + nb - 1; below, block indices are relative
   // to b0 and made absolute (b0 + .) wherever keys are addressed or masked.
-  const int b0 = nb_tile * krange / n_ks, nb = nb_tile * (krange + 1) / n_ks - b0;
+  const int b0 = blo_tile + span * krange / n_ks, nb = blo_tile + span * (krange + 1) / n_ks - b0;
   const float c2 = a.scale * kLog2e;
 
-  // This wave's queries: blocks past its last query are skipped; blocks reaching past
-  // its first query need the mask.
+  // This wave's queries: blocks past its last query, or (with a window) before its
+  // first query's window, are skipped; blocks reaching past its first query, or below
+  // its last query's window, need the mask.
   const int wq0 = q0 + 32 * wave;
   const int wq_last = min(a.n_q, wq0 + 32) - 1;
   const int nblk_w = min(nb, max(0, (wq_last < wq0 ? 0 : n_blocks(km, a.t0 + wq_last)) - b0));
+  const int blo_w = max(0, first_block(km, a.t0 + wq0) - b0);
   const int klim_w0 = km.klim(a.t0 + wq0);
+  const int klo_wl = km.klo(a.t0 + wq_last);
 
   // This lane's query (column of S^T) and its Q fragments (B operand over d).
   const int i = wq0 + col;
-  const int klim = km.klim(a.t0 + i);
+  const int klim = km.klim(a.t0 + i), klo = km.klo(a.t0 + i);
   bf16x8 qf[8];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + h * a.q_hs + static_cast<int64_t>(i) * a.q_ts;
@@ -163,13 +170,16 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
   // Softmax numerator of block b from st into pb.
   auto softmax = [&](int b) __attribute__((always_inline)) {
     const int k0 = (b0 + b) * KB;  // first key of the block
-    // Causal / tail mask, only in blocks that reach past this wave's first query.
-    if (k0 + KB - 1 > klim_w0) {
+    // Causal / tail mask (and window mask), only in blocks that reach past this wave's
+    // first query (or below its last query's window).
+    if (k0 + KB - 1 > klim_w0 || k0 < klo_wl) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (k0 + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3) > klim) st[sub][r] = -__builtin_inff();
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if (key > klim || key < klo) st[sub][r] = -__builtin_inff();
+        }
     }
     // Row maximum: four independent chains, then the other half-wave's rows.
     float mx4[4] = {st[0][0], st[0][1], st[0][2], st[0][3]};
@@ -243,13 +253,14 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
       if (u >= 0) {
         __builtin_amdgcn_s_setprio(1);
         // M(-1) multiplies the zero P^T by the zero-filled V buffer (adds exact zeros);
-        // M(nblk_w - 1) computes an S^T no softmax will read.
-        if (b < nblk_w) mul_pv_s(vr, kr);
+        // M(nblk_w - 1) computes an S^T no softmax will read. Before this wave's first
+        // block (a window) P^T is still zero: M(blo_w - 1) only computes S^T of blo_w.
+        if (b < nblk_w && b + 1 >= blo_w) mul_pv_s(vr, kr);
         __builtin_amdgcn_s_setprio(0);
       }
     } else {
       const int b = u >> 1;
-      if (u >= 0 && b < nblk_w) softmax(b);
+      if (u >= 0 && b < nblk_w && b >= blo_w) softmax(b);
     }
     if (dma) {
       __builtin_amdgcn_sched_barrier(0);
@@ -365,13 +376,9 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(AttnArgs a, int n_ks, co
 int fwd_splits(const AttnArgs& a) {
   if (const int n = split_override("OOMB_FWD_SPLITS")) return n;
   const int n_qt = (a.n_q + mf::FWD_Q - 1) / mf::FWD_Q;
-  const int64_t prior_keys = static_cast<int64_t>(a.max_att_pages - a.n_local) * a.pool.P;
-  const int64_t off = a.t0 - static_cast<int64_t>(a.first_local) * a.pool.P;  // chunk keys before query 0
   double total = 0.0, largest = 0.0;
   for (int qt = 0; qt < n_qt; ++qt) {
-    const int64_t end = (qt + 1) * static_cast<int64_t>(mf::FWD_Q);
-    const int64_t last = end < a.n_q ? end : a.n_q;
-    const double blocks = static_cast<double>((prior_keys + off + last + mf::KB - 1) / mf::KB);
+    const double blocks = static_cast<double>(tile_key_blocks(a, qt * mf::FWD_Q, mf::FWD_Q, mf::KB));
     total += blocks;
     largest = blocks > largest ? blocks : largest;
   }

@@ -7,7 +7,8 @@
 // What is computed (gist.science explainer of OOMB, 2.A recomputation, 2.B paged
 // K/V and paged gradients with in-place accumulation, 2.D page selection): query
 // i at position t0+i attends to key t iff t <= t0+i and page(t) is selected or
-// local; forward writes O and the natural-log LSE, backward recomputes
+// local (and, with a window W, t > t0+i-W); forward writes O and the natural-log LSE,
+// backward recomputes
 // P = exp(s - LSE) and writes dQ and adds dK/dV into the gradient pool.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -20,6 +21,7 @@ __device__ __forceinline__ AttendMap make_map(const AttnArgs& a, int g) {
   m.table = a.table + g * a.tstride;
   m.sel = a.sel ? a.sel + g * a.sel_stride : nullptr;
   m.n_sel = a.sel ? clamp_count(a.count, g, a.sel_stride, a.n_cand) : a.n_cand;
+  m.prior0 = a.prior0;
   m.first_local = a.first_local;
   m.n_pages_att = m.n_sel + a.n_local;
   m.num_pages = a.pool.N;
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(256) void fwd_scalar_kernel(AttnArgs a) {
     acc[r] = 0.0f;
   }
   const int qpos = a.t0 + i;
+  const int kmin = a.window > 0 ? qpos - a.window + 1 : 0;  // first visible position
   float mx = -__builtin_inff(), l = 0.0f;
   for (int e = 0; e < m.n_pages_att; ++e) {
     const int lp = checked_logical(m, e);
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void fwd_scalar_kernel(AttnArgs a) {
     const int base = lp << m.log2p;
     if (base > qpos) break;  // local pages ascend: every later page is in the future
     const int n = min(a.pool.P, qpos - base + 1);
-    for (int s = 0; s < n; ++s) {
+    for (int s = max(0, kmin - base); s < n; ++s) {
       const int64_t row = ((ph << m.log2p) + s) * D;
       float dot = 0.0f;
 #pragma unroll
@@ -124,6 +127,7 @@ __global__ __launch_bounds__(256) void dq_scalar_kernel(AttnArgs a) {
   const float lse2 = a.lse_in[row_id] * kLog2e;
   const float delta = a.delta[row_id];
   const int qpos = a.t0 + i;
+  const int kmin = a.window > 0 ? qpos - a.window + 1 : 0;  // first visible position
   for (int e = 0; e < m.n_pages_att; ++e) {
     const int lp = checked_logical(m, e);
     const int64_t ph = m.physical(e, lp);
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) void dq_scalar_kernel(AttnArgs a) {
     const int base = lp << m.log2p;
     if (base > qpos) break;
     const int n = min(a.pool.P, qpos - base + 1);
-    for (int s = 0; s < n; ++s) {
+    for (int s = max(0, kmin - base); s < n; ++s) {
       const int64_t row = ((ph << m.log2p) + s) * D;
       float dot = 0.0f, dpv = 0.0f;
       float k[R];
@@ -182,9 +186,11 @@ __global__ __launch_bounds__(256) void dkdv_scalar_kernel(AttnArgs a) {
     dv[r] = 0.0f;
   }
   const int i0 = kpos > a.t0 ? kpos - a.t0 : 0;
+  // with a window, queries at kpos + window and later no longer see this key
+  const int i1 = a.window > 0 ? min(a.n_q, kpos + a.window - a.t0) : a.n_q;
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
-    for (int i = i0; i < a.n_q; ++i) {
+    for (int i = i0; i < i1; ++i) {
       float q[R], dob[R], dot = 0.0f, dpv = 0.0f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {

@@ -63,6 +63,7 @@ struct AttendMap {
   const int32_t* table;   // this head's page-table row
   const int32_t* sel;     // this head's selected logical pages, or nullptr (dense)
   int n_sel;              // entries taken from sel (or number of prior pages if dense)
+  int prior0;             // dense: logical page of entry 0 (0, or a window's first page)
   int first_local;        // first local logical page
   int n_pages_att;        // n_sel + number of local pages
   int64_t num_pages;      // pool size, for the bounds check
@@ -70,7 +71,7 @@ struct AttendMap {
 
   // Logical page of list entry e.
   __device__ __forceinline__ int logical(int e) const {
-    if (e < n_sel) return sel ? sel[e] : e;
+    if (e < n_sel) return sel ? sel[e] : prior0 + e;
     return first_local + (e - n_sel);
   }
   // Physical page of list entry e, or -1 when the entry is out of range.

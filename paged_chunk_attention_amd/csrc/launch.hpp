@@ -72,7 +72,9 @@ struct AttnArgs {
   int64_t q_hs, q_ts;
   int n_q;
   int t0;
-  int n_cand;        // t0 / P: prior pages
+  int n_cand;        // prior pages a dense call attends: t0 / P - prior0
+  int prior0;        // first prior page a dense call attends: 0, or the window's first page
+  int window;        // local attention: query p sees keys t with p - window < t; 0 = unbounded
   int first_local;   // t0 / P
   int n_local;       // local pages
   const int32_t* sel;  // nullptr = dense
@@ -121,6 +123,23 @@ inline int split_override(const char* var) {
   if (v == nullptr) return 0;
   const int n = atoi(v);
   return n >= 1 && n <= 16 ? n : 0;
+}
+// Key blocks (of kb keys) that the query tile [q_first, q_first + len) visits: from
+// the block its first query's window starts in (block 0 without a window) to the one
+// holding its last query's own key. With a selection the prior keys count at their
+// upper bound (sel_stride pages).
+inline int64_t tile_key_blocks(const AttnArgs& a, int q_first, int len, int kb) {
+  const int64_t P = a.pool.P;
+  const int64_t prior_keys = static_cast<int64_t>(a.max_att_pages - a.n_local) * P;
+  const int64_t off = a.t0 - static_cast<int64_t>(a.first_local) * P;  // chunk keys before query 0
+  const int64_t q_last = (q_first + len < a.n_q ? q_first + len : a.n_q) - 1;
+  const int64_t hi = prior_keys + off + q_last;  // attended index of the last query's own key
+  int64_t lo = 0;
+  if (a.window > 0) {
+    lo = static_cast<int64_t>(a.t0) + q_first - a.window + 1 - static_cast<int64_t>(a.prior0) * P;
+    if (lo < 0) lo = 0;
+  }
+  return hi / kb - lo / kb + 1;
 }
 int dkdv_splits(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, int n_split);

@@ -158,19 +158,21 @@ __device__ __forceinline__ u32x4 gld16(const void* base, int64_t elem) {
 
 // ---- attended keys ------------------------------------------------------------------------
 // Attended key index a: list entry a / P, slot a % P; entries are the selected prior
-// pages (all prior pages when dense) followed by the local pages. Positions of the
-// local keys are linear in a: first_local * P + (a - local0).
+// pages (when dense, the prior pages from prior0 on) followed by the local pages.
+// Positions of the local keys are linear in a: first_local * P + (a - local0); when
+// dense, so are all of them (prior0 * P + a). With a window W (dense calls only) a
+// query at position p sees the keys with p - W < position <= p.
 struct Keys {
   const int32_t* table;
   const int32_t* sel;
-  int n_sel, first_local, n_keys, local0, kv_end, log2p, n_entries;
+  int n_sel, prior0, first_local, n_keys, local0, kv_end, log2p, n_entries, window;
   int64_t num_pages;
 
   // Physical page of entry e (bounds-checked), or -1.
   __device__ __forceinline__ int phys(int e) const {
     int lp;
     if (e < n_sel) {
-      lp = sel ? sel[e] : e;
+      lp = sel ? sel[e] : prior0 + e;
       if (sel && (lp < 0 || lp >= first_local)) return -1;
     } else {
       lp = first_local + (e - n_sel);
@@ -179,12 +181,21 @@ struct Keys {
     return (ph >= 0 && ph < num_pages) ? static_cast<int>(ph) : -1;
   }
   __device__ __forceinline__ int logical(int e) const {
-    return e < n_sel ? (sel ? sel[e] : e) : first_local + (e - n_sel);
+    return e < n_sel ? (sel ? sel[e] : prior0 + e) : first_local + (e - n_sel);
   }
   // Last attended index visible to a query at position qpos (mask: a > klim).
   __device__ __forceinline__ int klim(int qpos) const {
     const int l = qpos - (first_local << log2p) + local0;
     return l < n_keys - 1 ? l : n_keys - 1;
+  }
+  // First attended index visible to a query at position qpos (mask: a < klo); may be
+  // negative, and is far below every index without a window.
+  __device__ __forceinline__ int klo(int qpos) const {
+    return window > 0 ? qpos - window + 1 - (prior0 << log2p) : -(1 << 30);
+  }
+  // Position of attended index a (dense calls: every key; else local keys only).
+  __device__ __forceinline__ int pos_linear(int a) const {
+    return (first_local << log2p) + (a - local0);
   }
   // Does attended key a exist and lie before the end of the sequence?
   __device__ __forceinline__ bool in_seq(int a) const {
@@ -197,6 +208,8 @@ __device__ __forceinline__ Keys make_keys(const AttnArgs& a, int g) {
   k.table = a.table + g * a.tstride;
   k.sel = a.sel ? a.sel + g * a.sel_stride : nullptr;
   k.n_sel = a.sel ? clamp_count(a.count, g, a.sel_stride, a.n_cand) : a.n_cand;
+  k.prior0 = a.prior0;
+  k.window = a.window;
   k.first_local = a.first_local;
   k.n_entries = k.n_sel + a.n_local;
   k.n_keys = k.n_entries << a.pool.log2p;
@@ -211,6 +224,11 @@ __device__ __forceinline__ Keys make_keys(const AttnArgs& a, int g) {
 __device__ __forceinline__ int n_blocks(const Keys& k, int qmax_pos) {
   const int last = k.klim(qmax_pos);
   return last < 0 ? 0 : last / KB + 1;
+}
+// First block a query at position qpos (or any later one) sees.
+__device__ __forceinline__ int first_block(const Keys& k, int qpos) {
+  const int lo = k.klo(qpos);
+  return lo > 0 ? lo / KB : 0;
 }
 
 // ---- direct global -> LDS staging ---------------------------------------------------------

@@ -97,7 +97,7 @@ def run_chunk_parity(w: wl.Workload, x: Optional[dict] = None, label: str = "",
         x = wl.make_inputs(w)
     t0, C, P = w.t0, w.chunk, w.page
     log(f"[case {label or w.name}] hq={w.hq} hkv={w.hkv} d={w.d} page={P} chunk={C} t0={t0} "
-        f"dtype={w.dtype} top_k={w.top_k}")
+        f"dtype={w.dtype} top_k={w.top_k} window={w.window}")
     L = GpuLayer(w, x)
     cuts = sorted({0, *[int(f * t0) for f in pieces], t0})
     for a, b in zip(cuts[:-1], cuts[1:]):
@@ -116,9 +116,10 @@ def run_chunk_parity(w: wl.Workload, x: Optional[dict] = None, label: str = "",
         score = torch.empty(w.hkv, max(n_cand, 1), dtype=torch.float32, device=DEV)
         sel, count = pca.oomb_select_pages(L.pool, L.table, q, t0, w.top_k, qbar_out=qbar,
                                            score_out=score)
-    o, lse = pca.oomb_paged_chunk_attn_fwd(L.pool, L.table, q, t0, sel, count, w.scale)
+    o, lse = pca.oomb_paged_chunk_attn_fwd(L.pool, L.table, q, t0, sel, count, w.scale,
+                                           window=w.window)
     dq = pca.oomb_paged_chunk_attn_bwd(L.pool, L.table, L.gtable, q, t0, sel, count, o, do, lse,
-                                       w.scale)
+                                       w.scale, window=w.window)
     torch.cuda.synchronize()
     log("    gpu done")
 
@@ -157,14 +158,15 @@ def run_chunk_parity(w: wl.Workload, x: Optional[dict] = None, label: str = "",
             osel.append(chosen)
         log(f"    selection bit-exact ({[len(s) for s in osel]} pages per head)")
 
-    O, LSE = orc.fwd(x["q"], kp, vp, x["table"], t0, osel, w.scale)
+    O, LSE = orc.fwd(x["q"], kp, vp, x["table"], t0, osel, w.scale, window=w.window)
     res["O"] = compare("O", o, O, w.dtype)
     lse_err = (lse.cpu().double() - LSE).abs().max().item()
     log(f"    LSE    max_abs={lse_err:.3e}")
     assert lse_err <= (1e-2 if w.dtype == torch.bfloat16 else 1e-5)
     gpk = torch.zeros(kp.shape, dtype=torch.float64)
     gpv = torch.zeros(kp.shape, dtype=torch.float64)
-    dQ, _ = orc.bwd(x["q"], kp, vp, x["table"], t0, osel, w.scale, x["do"], gpk, gpv, x["gtable"])
+    dQ, _ = orc.bwd(x["q"], kp, vp, x["table"], t0, osel, w.scale, x["do"], gpk, gpv, x["gtable"],
+                    window=w.window)
     res["dQ"] = compare("dQ", dq, dQ, w.dtype)
     # gradient pool: touched rows hold init + dK, everything else is bit-unchanged
     touched = torch.zeros(kp.shape[0], P, dtype=torch.bool)

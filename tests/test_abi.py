@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 3
+    assert lib.oomb_abi_version() == 4
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text
@@ -56,13 +56,13 @@ T, Q, O, B = 0x600000, 0x700000, 0x800000, 0x900000
 
 def _fwd(lib, pool, **kw):
     a = dict(table=T, tstride=64, q=Q, qhs=4096 * 128, qts=128, n_q=4096, t0=4096, sel=None,
-             sstride=0, count=None, scale=0.088, o=O, ohs=4096 * 128, ots=128, lse=B, ws=0xA00000,
-             wsb=1 << 30)
+             sstride=0, count=None, window=0, scale=0.088, o=O, ohs=4096 * 128, ots=128, lse=B,
+             ws=0xA00000, wsb=1 << 30)
     a.update(kw)
     return lib.oomb_paged_chunk_attn_fwd(ctypes.byref(pool), a["table"], a["tstride"], a["q"],
                                          a["qhs"], a["qts"], a["n_q"], a["t0"], a["sel"],
-                                         a["sstride"], a["count"], a["scale"], a["o"], a["ohs"],
-                                         a["ots"], a["lse"], a["ws"], a["wsb"], None)
+                                         a["sstride"], a["count"], a["window"], a["scale"], a["o"],
+                                         a["ohs"], a["ots"], a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -131,10 +131,10 @@ def test_fwd_workspace(lib):
     split into key ranges, so it is not), and a missing, short or misaligned one is
     rejected before any launch."""
     p = _pool()
-    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1) == 0
-    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 0, 4096, -1) == 0
+    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1, 0) == 0
+    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 0, 4096, -1, 0) == 0
     t0 = 126976
-    need = lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, t0, -1)
+    need = lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, t0, -1, 0)
     assert need >= 2 * 28 * 4096 * 130 * 4 and need % 256 == 0
     kw = dict(t0=t0, tstride=1024)
     assert _fwd(lib, p, ws=None, wsb=0, **kw) == L.OOMB_ERR_WORKSPACE
@@ -142,20 +142,33 @@ def test_fwd_workspace(lib):
     assert _fwd(lib, p, ws=0xA00010, wsb=need, **kw) == L.OOMB_ERR_WORKSPACE
 
 
+def test_window_arguments(lib):
+    """A window is local attention: negative windows and windows combined with a page
+    selection are rejected before any launch; the workspace queries reject them too."""
+    p = _pool()
+    assert _fwd(lib, p, window=-1) == L.OOMB_ERR_INVALID
+    assert b"window" in lib.oomb_last_error()
+    assert _fwd(lib, p, window=128, sel=0xB00000, sstride=4, count=0xB10000) == L.OOMB_ERR_INVALID
+    assert b"selection" in lib.oomb_last_error()
+    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1, -5) == 0
+    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096, 4096, 8, 128) == 0
+    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1, 128) > 0
+
+
 def test_bwd_errors(lib):
     p = _pool()
     nograd = _pool(dk_pool=None)
-    need = lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1)
+    need = lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1, 0)
     assert need >= 28 * 4096 * 4 and need % 256 == 0
-    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 0, 4096, -1) == 0
+    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 0, 4096, -1, 0) == 0
 
     def bwd(pool, **kw):
         a = dict(gtable=T, gts=64, dq=B, dqhs=4096 * 128, dqts=128, ws=0xA00000, wsb=need)
         a.update(kw)
         return lib.oomb_paged_chunk_attn_bwd(
             ctypes.byref(pool), T, 64, a["gtable"], a["gts"], Q, 4096 * 128, 128, 4096, 4096,
-            None, 0, None, 0.088, O, 4096 * 128, 128, O, 4096 * 128, 128, B, a["dq"], a["dqhs"],
-            a["dqts"], a["ws"], a["wsb"], None)
+            None, 0, None, a.get("window", 0), 0.088, O, 4096 * 128, 128, O, 4096 * 128, 128, B,
+            a["dq"], a["dqhs"], a["dqts"], a["ws"], a["wsb"], None)
     assert bwd(nograd) == L.OOMB_ERR_INVALID
     assert bwd(p, gtable=None) == L.OOMB_ERR_INVALID
     assert bwd(p, gts=5) == L.OOMB_ERR_INVALID

@@ -59,6 +59,28 @@ def test_chunk_parity_mfma_fixed_splits(kw, n, monkeypatch):
     run_chunk_parity(_w(**dict(kw, name=f"{kw['name']}_splits{n}")))
 
 
+# local attention (the sparse layers of sparse-native models): a window of W positions
+@pytest.mark.parametrize("kw", [
+    dict(name="mfma_window5", window=5),                              # inside one key block
+    dict(name="mfma_window64", window=64),
+    dict(name="mfma_window200_prior", window=200),                    # reaches the prior pages
+    dict(name="mfma_window777_gqa7", hq=28, hkv=4, chunk=256, total=2000 + 256, window=777),
+    dict(name="mfma_window_over_all", window=1 << 20),                # equals no window
+    dict(name="mfma_window_first_chunk", hq=4, hkv=1, chunk=200, total=200, window=50),
+    dict(name="mfma_window_page16", hq=4, hkv=2, page=16, chunk=200, total=900, window=130),
+])
+def test_chunk_parity_mfma_window(kw):
+    run_chunk_parity(_w(**kw))
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_chunk_parity_mfma_window_fixed_splits(n, monkeypatch):
+    """Windows with the split counts fixed: key ranges that start past block 0."""
+    for var in ("OOMB_FWD_SPLITS", "OOMB_DQ_SPLITS", "OOMB_DKDV_SPLITS"):
+        monkeypatch.setenv(var, str(n))
+    run_chunk_parity(_w(name=f"mfma_window300_splits{n}", chunk=333, total=2597 + 333, window=300))
+
+
 # scalar path: fp32 (any head_dim) and bf16 head_dim 64
 @pytest.mark.parametrize("kw", [
     dict(name="f32_d64_p16", hq=2, hkv=1, d=64, page=16, chunk=64, total=1024, dtype=torch.float32),
@@ -66,6 +88,9 @@ def test_chunk_parity_mfma_fixed_splits(kw, n, monkeypatch):
          dtype=torch.float32, top_k=4),
     dict(name="bf16_d64_dense", hq=4, hkv=1, d=64, page=64, chunk=100, total=300),
     dict(name="bf16_d64_sparse", hq=6, hkv=2, d=64, page=16, chunk=50, total=50 + 400, top_k=7),
+    dict(name="f32_d64_window", hq=2, hkv=1, d=64, page=16, chunk=64, total=1024, window=40,
+         dtype=torch.float32),
+    dict(name="bf16_d64_window", hq=4, hkv=1, d=64, page=64, chunk=100, total=300, window=150),
 ])
 def test_chunk_parity_scalar(kw):
     run_chunk_parity(_w(**kw))

@@ -42,10 +42,11 @@ def _table(hkv, n_pages, seed):
         .to(torch.int32).reshape(hkv, n_pages)
 
 
-def _sdpa(q, k, v, t0, pages_per_head, P, scale):
+def _sdpa(q, k, v, t0, pages_per_head, P, scale, window=0):
     """torch SDPA in fp64 with GQA and an explicit boolean mask: query i (position
-    t0+i) of q head h sees key t iff page(t) is attended by head h // G and t <= t0+i.
-    Returns O, and grads wrt q, k, v of sum(dO * O) via autograd (dO passed later)."""
+    t0+i) of q head h sees key t iff page(t) is attended by head h // G and t <= t0+i
+    (and, with a window W, t > t0+i-W). Returns O, and grads wrt q, k, v of
+    sum(dO * O) via autograd (dO passed later)."""
     hq, C, D = q.shape
     hkv, T, _ = k.shape
     G = hq // hkv
@@ -57,6 +58,8 @@ def _sdpa(q, k, v, t0, pages_per_head, P, scale):
         for j in pages_per_head[h // G]:
             allowed[j * P:(j + 1) * P] = True
         mask[h] = allowed[None, :] & (kpos[None, :] <= qpos[:, None])
+        if window:
+            mask[h] &= kpos[None, :] > qpos[:, None] - window
     return F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=mask[None],
                                           scale=scale, enable_gqa=True)[0]
 
@@ -320,6 +323,70 @@ def test_fwd_bwd_match_sdpa_autograd(sparse):
         assert torch.allclose(dk, k.grad[g], atol=1e-12, rtol=0)
         assert torch.allclose(dv, v.grad[g], atol=1e-12, rtol=0)
     assert n_prior > 2
+
+
+@pytest.mark.parametrize("window", [3, 8, 17, 40])
+def test_window_matches_banded_sdpa_autograd(window):
+    """Local attention (explainer 2.D, sparse layers) equals torch SDPA under a banded
+    causal mask, forward and autograd gradients: windows inside one page, across
+    pages, reaching into the prior pages, and longer than the context at early
+    queries."""
+    c = _case()
+    P, t0 = c["P"], c["t0"]
+    hkv = c["table"].shape[0]
+    scale = 0.3
+    O, L = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], t0, None, scale, window=window)
+    pages = [orc.attended_pages(t0, c["q"].shape[1], P, None) for _ in range(hkv)]
+    q = c["q"].clone().requires_grad_()
+    k = c["k"].clone().requires_grad_()
+    v = c["v"].clone().requires_grad_()
+    ref = _sdpa(q, k, v, t0, pages, P, scale, window)
+    (ref * c["do"]).sum().backward()
+    assert torch.allclose(O, ref.detach(), atol=1e-13, rtol=0)
+    gk = torch.zeros(c["kp"].shape, dtype=F64)
+    gv = torch.zeros(c["vp"].shape, dtype=F64)
+    dQ, _ = orc.bwd(c["q"], c["kp"], c["vp"], c["table"], t0, None, scale, c["do"], gk, gv,
+                    c["table"], window=window)
+    assert torch.allclose(dQ, q.grad, atol=1e-12, rtol=0)
+    for g in range(hkv):
+        dk = orc.gather(gk, c["table"], g, range(c["n_pages"]))[:c["T"]]
+        dv = orc.gather(gv, c["table"], g, range(c["n_pages"]))[:c["T"]]
+        assert torch.allclose(dk, k.grad[g], atol=1e-12, rtol=0)
+        assert torch.allclose(dv, v.grad[g], atol=1e-12, rtol=0)
+
+
+def test_window_one_and_window_covering_all():
+    """Window 1: each query sees only its own key, so O = v_p, LSE = scale q.k_p, and
+    the backward has dS = 0 (dQ = dK = 0) with dV_p = the sum of dO over the group's
+    heads at p. A window reaching position 0 from every query equals no window,
+    bitwise."""
+    c = _case()
+    P, t0, scale = c["P"], c["t0"], 0.3
+    hq, C, D = c["q"].shape
+    hkv = c["k"].shape[0]
+    G = hq // hkv
+    O, L = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], t0, None, scale, window=1)
+    gk = torch.zeros(c["kp"].shape, dtype=F64)
+    gv = torch.zeros(c["vp"].shape, dtype=F64)
+    dQ, per_head = orc.bwd(c["q"], c["kp"], c["vp"], c["table"], t0, None, scale, c["do"], gk,
+                           gv, c["table"], window=1)
+    for h in range(hq):
+        g = h // G
+        assert torch.equal(O[h], c["v"][g, t0:t0 + C])
+        lse = scale * (c["q"][h] * c["k"][g, t0:t0 + C]).sum(-1)
+        assert torch.allclose(L[h], lse, atol=1e-14, rtol=0)
+    assert dQ.abs().max().item() < 1e-14
+    for g, (pos, dk, dv) in enumerate(per_head):
+        assert dk.abs().max().item() < 1e-14
+        want = torch.zeros_like(dv)
+        own = (pos >= t0).nonzero()[:, 0]
+        want[own] = c["do"][g * G:(g + 1) * G, (pos[own] - t0)].sum(0)
+        assert torch.allclose(dv, want, atol=1e-14, rtol=0)
+    O0, L0 = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], t0, None, scale)
+    Ow, Lw = orc.fwd(c["q"], c["kp"], c["vp"], c["table"], t0, None, scale, window=t0 + C)
+    assert torch.equal(O0, Ow) and torch.equal(L0, Lw)
+    with pytest.raises(ValueError):
+        orc.fwd(c["q"], c["kp"], c["vp"], c["table"], t0, [[0], [1]], scale, window=4)
 
 
 def test_lse_matches_logsumexp():

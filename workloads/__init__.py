@@ -37,6 +37,7 @@ class Workload:
     needles: int = 0        # prior pages whose keys are pushed toward the chunk's mean query
     needle_gain: float = 1.5
     sweep: bool = False     # True: every chunk of the sequence, forward then reverse
+    window: int = 0         # local attention: each query sees its `window` latest positions
 
     @property
     def group(self) -> int:
@@ -75,6 +76,10 @@ WORKLOADS = {
     # 8192-token chunk closing a 4M-token context, top-128 pages + 64 local.
     "sparse4m": Workload("sparse4m", 28, 4, 128, 128, 8192, 4194304, torch.bfloat16, 128,
                          needles=32),
+    # local attention (sparse layers of sparse-native models): the sparse-1M chunk with
+    # each query seeing its 128 latest positions instead of a page selection.
+    "local1m": Workload("local1m", 28, 4, 128, 128, 4096, 1048576 + 4096, torch.bfloat16, None,
+                        window=128),
     # 256K tokens in 32 chunks of 8192, every chunk forward then reverse.
     "sweep256k": Workload("sweep256k", 28, 4, 128, 128, 8192, 262144, torch.bfloat16, None,
                           sweep=True),
