@@ -210,6 +210,49 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table,
                               int64_t dq_tok_stride, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* ---- Page movement between the device and pinned host memory ----------------------
+ * The asynchronous CPU offload of the KV cache and its gradients (explainer 2.C): pages
+ * move between the device pools and host copies while other work runs on other
+ * streams (for dense and local layers, the next layer's pages are fetched while the
+ * current layer computes; for sparse layers only the selected pages move). Every
+ * buffer below is device memory or pinned host memory (hipHostMalloc, or a torch
+ * tensor made with pin_memory=True), which the kernels read and write directly
+ * through its device mapping; pageable memory is rejected with OOMB_ERR_INVALID before
+ * any launch. Page-id lists are int32 arrays in such memory, read on the device, so a
+ * list computed on the GPU (a selection) needs no host round trip. Ids outside their
+ * page array are skipped. The calls are asynchronous on `stream`; the caller keeps
+ * the buffers alive and orders other streams with events. */
+
+/* dst page dst_ids[i] = src page src_ids[i], for i < n (or i < min(n, *n_dev) when
+ * n_dev, a device int32, is given). src holds n_src_pages pages of page_bytes bytes
+ * (a positive multiple of 16) and dst n_dst_pages; src and dst must not overlap.
+ * Copies are bitwise. */
+int oomb_copy_pages(const void* src, void* dst, int64_t page_bytes, int64_t n_src_pages,
+                    int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
+                    int32_t n, const int32_t* n_dev, void* stream);
+
+/* fp32 pages of page_elems floats (a multiple of 4): dst page dst_ids[i] += src page
+ * src_ids[i] (one fp32 rounding per element), then, if zero_src, src page src_ids[i]
+ * = 0; for i < n (or min(n, *n_dev)). For moving key/value gradient pages into an fp32
+ * pool elsewhere (explainer 2.B/2.C: gradients accumulate in paged storage and are
+ * offloaded too). The dst ids of one call must be distinct. */
+int oomb_add_pages_f32(const float* src, float* dst, int64_t page_elems, int64_t n_src_pages,
+                       int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
+                       int32_t n, const int32_t* n_dev, int32_t zero_src, void* stream);
+
+/* Fetch of the selected pages (sparse layers, explainer 2.C/2.D): for every KV head g
+ * and j < count[g] (j < sel_stride), with lp = sel[g*sel_stride + j] (skipped unless
+ * 0 <= lp < n_logical) and s = stage[g*stage_stride + j]: device page s of the pool's
+ * K and V = host page host_table[g*host_table_stride + lp] of host_k / host_v (each
+ * [host_pages][P][D] in the pool dtype), and table[g*table_stride + lp] = s. After it,
+ * the attention calls read the selected pages from the staging pages through `table`.
+ * The selection and counts come straight from oomb_select_pages. */
+int oomb_fetch_selected(const oomb_pool* pool, int32_t* table, int64_t table_stride,
+                        const void* host_k, const void* host_v, int64_t host_pages,
+                        const int32_t* host_table, int64_t host_table_stride, const int32_t* sel,
+                        int64_t sel_stride, const int32_t* count, const int32_t* stage,
+                        int64_t stage_stride, int64_t n_logical, void* stream);
+
 /* Kernel timing for profiling tools; not needed for normal use. While enabled on
  * the calling thread, each kernel that a call above launches is bracketed by two
  * HIP events on that call's stream (a small cost per launch). oomb_profile_collect

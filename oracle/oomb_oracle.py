@@ -12,6 +12,8 @@ Sources (the OOMB pages; "explainer" = the gist.science explainer of arXiv 2602.
     "Paged KV Cache and Gradient Management"; mlsanity abstract.
   * top-K page retrieval from a representative vector: explainer, 2.D "Page-Level
     Sparse Attention".
+  * CPU offload of pages and gradient pages: explainer, 2.C "Asynchronous KV Cache CPU
+    Offloading" (moving pages is a copy; moving gradient pages adds them in).
   * local attention for the sparse layers of sparse-native models: explainer, 2.D
     ("Native Support"). The pages do not define it further; it is read here as the
     usual sliding window: a query at position p sees the keys at p - W < t <= p.
@@ -46,6 +48,7 @@ __all__ = [
     "append", "gather", "summarize", "total_order_key",
     "query_summary", "page_scores", "top_k_pages", "select_pages",
     "attended_pages", "key_positions", "fwd", "bwd", "sweep",
+    "copy_pages", "add_pages", "fetch_selected",
 ]
 
 
@@ -377,3 +380,54 @@ def sweep(q_all, k_all, v_all, do_all, table, gtable, n_pool: int, page: int, ch
                            do_all[:, sl], dk_pool, dv_pool, gtable, window=window)
     return {"O": O, "LSE": L, "dQ": dQ, "dk_pool": dk_pool, "dv_pool": dv_pool,
             "sels": sels, "k_pool": k_pool, "v_pool": v_pool, "summary": summary}
+
+
+# ---------------------------------------------------------------------------
+# Page movement (explainer 2.C: the KV cache and its gradients move between GPU
+# and CPU memory). A page array is [N, ...]; page ids outside it are skipped.
+# ---------------------------------------------------------------------------
+
+def _valid(i: int, n: int) -> bool:
+    return 0 <= i < n
+
+
+def copy_pages(src: torch.Tensor, dst: torch.Tensor, src_ids, dst_ids, n: Optional[int] = None) -> None:
+    """dst[dst_ids[i]] = src[src_ids[i]] for i < n, in list order."""
+    n = len(src_ids) if n is None else n
+    for i in range(n):
+        s, d = int(src_ids[i]), int(dst_ids[i])
+        if _valid(s, src.shape[0]) and _valid(d, dst.shape[0]):
+            dst[d] = src[s]
+
+
+def add_pages(src: torch.Tensor, dst: torch.Tensor, src_ids, dst_ids, n: Optional[int] = None,
+              zero_src: bool = False) -> None:
+    """fp32 pages: dst[dst_ids[i]] = fp32(dst + src) element by element (one rounding),
+    then src[src_ids[i]] = 0 when zero_src; for i < n."""
+    n = len(src_ids) if n is None else n
+    for i in range(n):
+        s, d = int(src_ids[i]), int(dst_ids[i])
+        if _valid(s, src.shape[0]) and _valid(d, dst.shape[0]):
+            total = src[s].to(torch.float64) + dst[d].to(torch.float64)
+            dst[d] = total.to(torch.float32)  # the exact sum, rounded once
+            if zero_src:
+                src[s] = 0.0
+
+
+def fetch_selected(k_pool, v_pool, table, host_k, host_v, host_table, sel, count, stage,
+                   n_logical: int) -> None:
+    """For KV head g and j < count[g]: lp = sel[g][j] (skipped unless 0 <= lp < n_logical),
+    s = stage[g][j]: device page s of K and V = host page host_table[g][lp], and
+    table[g][lp] = s (in head order, then j)."""
+    for g in range(table.shape[0]):
+        for j in range(min(int(count[g]), sel.shape[1])):
+            lp = int(sel[g, j])
+            if not _valid(lp, n_logical):
+                continue
+            hp, s = int(host_table[g, lp]), int(stage[g, j])
+            if not (_valid(hp, host_k.shape[0]) and _valid(s, k_pool.shape[0])):
+                continue
+            k_pool[s] = host_k[hp]
+            v_pool[s] = host_v[hp]
+            table[g, lp] = s
+

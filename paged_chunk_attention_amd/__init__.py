@@ -9,6 +9,9 @@ dK/dV into a paged fp32 gradient pool.
 from .binding import (  # noqa: F401
     PagedPool,
     bwd_workspace_bytes,
+    oomb_add_pages_f32,
+    oomb_copy_pages,
+    oomb_fetch_selected,
     fwd_workspace_bytes,
     kernel_timer,
     oomb_kv_append,

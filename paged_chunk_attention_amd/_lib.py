@@ -49,6 +49,13 @@ SIGNATURES = {
                                           c_size_t, c_void_p]),
     "oomb_fwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64, c_int32]),
     "oomb_bwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64, c_int32]),
+    "oomb_copy_pages": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p,
+                                c_int32, c_void_p, c_void_p]),
+    "oomb_add_pages_f32": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p,
+                                   c_void_p, c_int32, c_void_p, c_int32, c_void_p]),
+    "oomb_fetch_selected": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                                    c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p,
+                                    c_int64, c_int64, c_void_p]),
     "oomb_profile_enable": (c_int, [c_int]),
     "oomb_profile_collect": (c_int, [ctypes.POINTER(c_char_p), ctypes.POINTER(c_float), c_int]),
     "oomb_paged_chunk_attn_bwd": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_void_p,

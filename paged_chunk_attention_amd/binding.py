@@ -229,6 +229,87 @@ def oomb_paged_chunk_attn_bwd(pool: PagedPool, table: torch.Tensor, gtable: torc
     return dq
 
 
+def _pages(x: torch.Tensor, name: str) -> torch.Tensor:
+    """A page array [N, ...]: contiguous, on a GPU or in pinned host memory (the kernels
+    read and write host pages directly; pageable memory would be rejected by the call)."""
+    if not x.is_contiguous() or x.dim() < 2:
+        raise ValueError(f"{name} must be a contiguous [pages, ...] tensor")
+    if not x.is_cuda and not x.is_pinned():
+        raise ValueError(f"{name} is in pageable host memory: allocate it with pin_memory=True")
+    return x
+
+
+def _ids(x: torch.Tensor, name: str) -> torch.Tensor:
+    if x.dtype != torch.int32 or not x.is_contiguous() or not (x.is_cuda or x.is_pinned()):
+        raise ValueError(f"{name} must be a contiguous int32 tensor on the GPU or pinned")
+    return x
+
+
+def oomb_copy_pages(src: torch.Tensor, dst: torch.Tensor, src_ids: torch.Tensor,
+                    dst_ids: torch.Tensor, n: Optional[int] = None,
+                    n_dev: Optional[torch.Tensor] = None, stream=None) -> None:
+    """dst[dst_ids[i]] = src[src_ids[i]] for i < n (default len(src_ids); or < n_dev[0]),
+    pages in device or pinned host memory (the CPU offload of K/V pages)."""
+    _pages(src, "src")
+    _pages(dst, "dst")
+    if src.dtype != dst.dtype or src.shape[1:] != dst.shape[1:]:
+        raise ValueError("src and dst pages differ in dtype or shape")
+    _ids(src_ids, "src_ids")
+    _ids(dst_ids, "dst_ids")
+    n = min(src_ids.numel(), dst_ids.numel()) if n is None else n
+    if n > min(src_ids.numel(), dst_ids.numel()):
+        raise ValueError("n exceeds the id lists")
+    page_bytes = src[0].numel() * src.element_size()
+    call("oomb_copy_pages", _ptr(src), _ptr(dst), page_bytes, src.shape[0], dst.shape[0],
+         _ptr(src_ids), _ptr(dst_ids), n, _ptr(None if n_dev is None else _ids(n_dev, "n_dev")),
+         _stream(stream))
+
+
+def oomb_add_pages_f32(src: torch.Tensor, dst: torch.Tensor, src_ids: torch.Tensor,
+                       dst_ids: torch.Tensor, n: Optional[int] = None,
+                       n_dev: Optional[torch.Tensor] = None, zero_src: bool = False,
+                       stream=None) -> None:
+    """dst[dst_ids[i]] += src[src_ids[i]] (fp32 pages), then src[src_ids[i]] = 0 if
+    zero_src: gradient pages into an fp32 pool elsewhere (e.g. pinned host memory)."""
+    _pages(src, "src")
+    _pages(dst, "dst")
+    if src.dtype != torch.float32 or dst.dtype != torch.float32 or src.shape[1:] != dst.shape[1:]:
+        raise ValueError("src and dst must be fp32 page arrays of one page shape")
+    _ids(src_ids, "src_ids")
+    _ids(dst_ids, "dst_ids")
+    n = min(src_ids.numel(), dst_ids.numel()) if n is None else n
+    if n > min(src_ids.numel(), dst_ids.numel()):
+        raise ValueError("n exceeds the id lists")
+    call("oomb_add_pages_f32", _ptr(src), _ptr(dst), src[0].numel(), src.shape[0], dst.shape[0],
+         _ptr(src_ids), _ptr(dst_ids), n, _ptr(None if n_dev is None else _ids(n_dev, "n_dev")),
+         int(bool(zero_src)), _stream(stream))
+
+
+def oomb_fetch_selected(pool: PagedPool, table: torch.Tensor, host_k: torch.Tensor,
+                        host_v: torch.Tensor, host_table: torch.Tensor, sel: torch.Tensor,
+                        count: torch.Tensor, stage: torch.Tensor, n_logical: Optional[int] = None,
+                        stream=None) -> None:
+    """Copy the selected pages of every KV head from the host copies host_k / host_v
+    ([pages, P, D], pinned) into the device staging pages `stage` [Hkv, >= k] and point
+    `table` at them, so that the attention calls read them there."""
+    _check_table(table, pool, "table")
+    for name, x in (("host_k", host_k), ("host_v", host_v)):
+        _pages(x, name)
+        if x.dtype != pool.dtype or tuple(x.shape[1:]) != (pool.page_size, pool.head_dim):
+            raise ValueError(f"{name} must be [pages, {pool.page_size}, {pool.head_dim}] "
+                             f"{pool.dtype}")
+    if host_k.shape != host_v.shape:
+        raise ValueError("host_k and host_v differ in shape")
+    for name, x in (("host_table", host_table), ("sel", sel), ("count", count), ("stage", stage)):
+        _ids(x, name)
+    if host_table.dim() != 2 or sel.dim() != 2 or stage.dim() != 2:
+        raise ValueError("host_table, sel and stage must be [Hkv, stride] tensors")
+    n_logical = min(table.shape[1], host_table.shape[1]) if n_logical is None else n_logical
+    call("oomb_fetch_selected", pool.ref(), _ptr(table), table.stride(0), _ptr(host_k),
+         _ptr(host_v), host_k.shape[0], _ptr(host_table), host_table.stride(0), _ptr(sel),
+         sel.stride(0), _ptr(count), _ptr(stage), stage.stride(0), n_logical, _stream(stream))
+
+
 class kernel_timer:
     """Context manager: time every kernel the library launches on this thread with
     HIP events. After exit, `records` holds (kernel name, milliseconds) pairs."""

@@ -30,10 +30,11 @@ SOURCES = {
     # NaN-quieting v_max of each operand
     "attn_fwd_mfma.hip": ["-fno-honor-nans"],
     "attn_dq_mfma.hip": [],
-    # one wave per SIMD with ~400 live registers: MFMA results in VGPRs (the softmax
-    # reads them) and the ILP-first scheduler measure faster for this kernel
+    # MFMA results in VGPRs (the softmax and dS arithmetic read them without AGPR
+    # copies) and the ILP-first scheduler
     "attn_dkdv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
                            "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "offload.hip": [],
     "api.cpp": [],
     "profiling.cpp": [],
 }

@@ -187,6 +187,69 @@ int check_attn(const oomb_pool* pool, const int32_t* table, int64_t tstride, con
 
 bool use_mfma(const oomb::PoolView& v) { return v.dtype == OOMB_DTYPE_BF16 && v.D == 128; }
 
+// The address a kernel uses for a buffer: device memory as given, pinned host memory
+// through its device mapping. Anything else (pageable host memory, an unknown pointer)
+// is rejected here, before a launch could fault on it. `align` is the alignment the
+// kernel's accesses need.
+int device_address(const void* p, uintptr_t align, const char* name, const void** out) {
+  if (p == nullptr) return fail(OOMB_ERR_INVALID, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & (align - 1))
+    return fail(OOMB_ERR_INVALID, "%s must be %u-byte aligned", name, static_cast<unsigned>(align));
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(OOMB_ERR_INVALID, "%s is neither device memory nor pinned host memory", name);
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    *out = p;
+    return OOMB_OK;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || d == nullptr) {
+      (void)hipGetLastError();
+      return fail(OOMB_ERR_INVALID, "%s is host memory without a device mapping", name);
+    }
+    *out = d;
+    return OOMB_OK;
+  }
+  // unregistered (pageable) host memory, managed or array memory
+  return fail(OOMB_ERR_INVALID, "%s is neither device memory nor pinned host memory (type %d)", name,
+              static_cast<int>(at.type));
+}
+template <typename T>
+int device_address(T* p, uintptr_t align, const char* name, T** out) {
+  const void* d = nullptr;
+  const int st = device_address(static_cast<const void*>(p), align, name, &d);
+  *out = static_cast<T*>(const_cast<void*>(d));
+  return st;
+}
+
+// Shared checks of the page-list calls.
+int check_page_list(const void* src, void* dst, int64_t page_bytes, int64_t n_src, int64_t n_dst,
+                    const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                    const int32_t* n_dev, oomb::PageCopyArgs* a) {
+  if (page_bytes <= 0 || page_bytes % 16 != 0)
+    return fail(OOMB_ERR_INVALID, "page size %lld bytes must be a positive multiple of 16",
+                static_cast<long long>(page_bytes));
+  if (n < 0) return fail(OOMB_ERR_INVALID, "n must be >= 0 (got %d)", n);
+  if (n_src <= 0 || n_dst <= 0) return fail(OOMB_ERR_INVALID, "page counts must be positive");
+  int st;
+  if ((st = device_address(src, 16, "src", &a->src))) return st;
+  void* d = nullptr;
+  if ((st = device_address(dst, 16, "dst", &d))) return st;
+  a->dst = d;
+  if ((st = device_address(src_ids, 4, "src_ids", &a->src_ids))) return st;
+  if ((st = device_address(dst_ids, 4, "dst_ids", &a->dst_ids))) return st;
+  a->n_dev = nullptr;
+  if (n_dev != nullptr && (st = device_address(n_dev, 4, "n_dev", &a->n_dev))) return st;
+  a->page_bytes = page_bytes;
+  a->n = n;
+  a->n_src = n_src;
+  a->n_dst = n_dst;
+  return OOMB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,7 +267,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 4; }
+int oomb_abi_version(void) { return 5; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -424,6 +487,72 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   float* dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dq);
   return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, oomb::dq_splits(a), dq_part, s),
                     "paged_chunk_attn_bwd");
+}
+
+int oomb_copy_pages(const void* src, void* dst, int64_t page_bytes, int64_t n_src_pages,
+                    int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                    const int32_t* n_dev, void* stream) {
+  oomb::PageCopyArgs a{};
+  const int st = check_page_list(src, dst, page_bytes, n_src_pages, n_dst_pages, src_ids, dst_ids,
+                                 n, n_dev, &a);
+  if (st) return st;
+  if (n == 0) return OOMB_OK;
+  return hip_status(oomb::launch_copy_pages(a, static_cast<hipStream_t>(stream)), "copy_pages");
+}
+
+int oomb_add_pages_f32(const float* src, float* dst, int64_t page_elems, int64_t n_src_pages,
+                       int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
+                       int32_t n, const int32_t* n_dev, int32_t zero_src, void* stream) {
+  oomb::PageCopyArgs a{};
+  if (page_elems <= 0 || page_elems % 4 != 0)
+    return fail(OOMB_ERR_INVALID, "page size %lld floats must be a positive multiple of 4",
+                static_cast<long long>(page_elems));
+  const int st = check_page_list(src, dst, page_elems * 4, n_src_pages, n_dst_pages, src_ids,
+                                 dst_ids, n, n_dev, &a);
+  if (st) return st;
+  if (n == 0) return OOMB_OK;
+  return hip_status(oomb::launch_add_pages(a, zero_src != 0, static_cast<hipStream_t>(stream)),
+                    "add_pages");
+}
+
+int oomb_fetch_selected(const oomb_pool* pool, int32_t* table, int64_t table_stride,
+                        const void* host_k, const void* host_v, int64_t host_pages,
+                        const int32_t* host_table, int64_t host_table_stride, const int32_t* sel,
+                        int64_t sel_stride, const int32_t* count, const int32_t* stage,
+                        int64_t stage_stride, int64_t n_logical, void* stream) {
+  oomb::FetchArgs a{};
+  oomb::PoolView v;
+  int st = check_pool(pool, &v, false, false);
+  if (st) return st;
+  if (host_pages <= 0) return fail(OOMB_ERR_INVALID, "host_pages must be positive");
+  if (sel_stride < 0) return fail(OOMB_ERR_INVALID, "sel_stride must be >= 0");
+  if (stage_stride < sel_stride)
+    return fail(OOMB_ERR_INVALID, "stage_stride %lld < sel_stride %lld",
+                static_cast<long long>(stage_stride), static_cast<long long>(sel_stride));
+  if (n_logical < 0 || table_stride < n_logical || host_table_stride < n_logical)
+    return fail(OOMB_ERR_INVALID, "table strides must cover the %lld logical pages",
+                static_cast<long long>(n_logical));
+  if ((st = device_address(host_k, 16, "host_k", &a.host_k))) return st;
+  if ((st = device_address(host_v, 16, "host_v", &a.host_v))) return st;
+  if ((st = device_address(host_table, 4, "host_table", &a.host_table))) return st;
+  if ((st = device_address(table, 4, "table", &a.table))) return st;
+  if ((st = device_address(sel, 4, "sel", &a.sel))) return st;
+  if ((st = device_address(count, 4, "count", &a.count))) return st;
+  if ((st = device_address(stage, 4, "stage", &a.stage))) return st;
+  if (sel_stride == 0 || n_logical == 0) return OOMB_OK;
+  a.host_pages = host_pages;
+  a.host_tstride = host_table_stride;
+  a.k_pool = v.k_pool_w;
+  a.v_pool = v.v_pool_w;
+  a.dev_pages = v.N;
+  a.tstride = table_stride;
+  a.sel_stride = sel_stride;
+  a.stage_stride = stage_stride;
+  a.n_logical = n_logical;
+  a.page_bytes = static_cast<int64_t>(v.P) * v.D * elem_size(v);
+  a.n_heads = v.Hkv;
+  return hip_status(oomb::launch_fetch_selected(a, static_cast<hipStream_t>(stream)),
+                    "fetch_selected");
 }
 
 }  // extern "C"

@@ -84,7 +84,7 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
   const uint16_t* kpool = static_cast<const uint16_t*>(a.pool.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.pool.v_pool);
   const int win0 = (b0 * KB) >> km.log2p;
-  Stage ks{km, s_page, win0, kpool, vpool, Stage::lane_offset(wave, lane)};
+  Stage ks{km, s_page, win0, Stage::lane_offset(wave, lane)};
   fill_pages<NT>(km, s_page, win0, tid);
   wait_dma();  // the page-table loads are retired here, not at a later register reuse
   __syncthreads();

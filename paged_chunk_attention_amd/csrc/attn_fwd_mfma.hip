@@ -105,10 +105,9 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
   // All 8 waves stage the first blocks; afterwards each group of 4 stages one tensor.
   // With every page id resident the window starts at entry 0, else at block b0's.
   const int win0 = SLIDE ? (b0 * KB) >> km.log2p : 0;
-  KeyStage<KB, FWD_WAVES, CAP> ks{km, s_page, win0, kpool, vpool,
+  KeyStage<KB, FWD_WAVES, CAP> ks{km, s_page, win0,
                                   KeyStage<KB, FWD_WAVES, CAP>::lane_offset(wave, lane)};
-  KeyStage<KB, 4, CAP> kg{km, s_page, win0, kpool, vpool,
-                          KeyStage<KB, 4, CAP>::lane_offset(wave & 3, lane)};
+  KeyStage<KB, 4, CAP> kg{km, s_page, win0, KeyStage<KB, 4, CAP>::lane_offset(wave & 3, lane)};
   fill_pages<NT, CAP>(km, s_page, win0, tid);
   zero_tile<KB, NT>(s_v1, tid);  // read (times a zero P^T) before their first DMA
   zero_tile<KB, NT>(s_v2, tid);

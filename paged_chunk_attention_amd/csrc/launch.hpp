@@ -93,6 +93,47 @@ struct AttnArgs {
   int max_att_pages; // upper bound of attended pages per head (grid sizing)
 };
 
+// A page list between two page arrays (device memory or the device mapping of pinned
+// host memory): page i of the list goes from src page src_ids[i] to dst page
+// dst_ids[i]; ids outside [0, n_src) / [0, n_dst) are skipped. The list length is n,
+// or min(n, *n_dev) when n_dev (a device int32) is given.
+struct PageCopyArgs {
+  const void* src;
+  void* dst;
+  int64_t page_bytes;  // multiple of 16
+  const int32_t* src_ids;
+  const int32_t* dst_ids;
+  int n;
+  const int32_t* n_dev;
+  int64_t n_src, n_dst;
+};
+
+// Fetch of the selected pages of every KV head from host pages into device staging pages.
+struct FetchArgs {
+  const void* host_k;
+  const void* host_v;
+  int64_t host_pages;
+  const int32_t* host_table;  // [n_heads][host_tstride]: logical page -> host page
+  int64_t host_tstride;
+  void* k_pool;
+  void* v_pool;
+  int64_t dev_pages;
+  int32_t* table;             // [n_heads][tstride]: logical page -> device page (updated)
+  int64_t tstride;
+  const int32_t* sel;
+  int64_t sel_stride;
+  const int32_t* count;
+  const int32_t* stage;       // [n_heads][stage_stride]: device staging page of entry j
+  int64_t stage_stride;
+  int64_t n_logical;          // logical pages that may be selected (table widths)
+  int64_t page_bytes;
+  int n_heads;
+};
+
+hipError_t launch_copy_pages(const PageCopyArgs& a, hipStream_t s);
+hipError_t launch_add_pages(const PageCopyArgs& a, int zero_src, hipStream_t s);
+hipError_t launch_fetch_selected(const FetchArgs& a, hipStream_t s);
+
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_page_summarize(const SummarizeArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);

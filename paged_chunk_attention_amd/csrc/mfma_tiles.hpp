@@ -238,8 +238,6 @@ __device__ __forceinline__ int first_block(const Keys& k, int qpos) {
 // chunk L%16 of row r = 16i + 4w + L/16, whose logical chunk is (L%16) ^ swz(r). With
 // this row order swz(r) = 4(L/16) + w is the same for all four instructions of a lane,
 // so one column offset serves them all.
-// Rows that are not loaded keep their previous (finite) contents; every consumer
-// masks them (P = 0), so stale values never reach a result.
 __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
@@ -288,6 +286,10 @@ __device__ __forceinline__ void fill_pages(const Keys& k, int* spage, int win, i
   for (int e = win + tid; e < end; e += NT) spage[e - win] = k.phys(e);
 }
 
+// Four zero rows of keys in global memory: the source of every staged row that is not
+// an attended key (lane offsets stay below 4 rows). One copy per code object.
+static __device__ __attribute__((aligned(16))) uint16_t g_zero_rows[4 * D] = {};
+
 // Direct staging of a stage of ROWS attended keys (K and V rows) by NW wavefronts.
 // Instruction i of wave w fills LDS rows r0 = 4 (NW i + w) .. r0 + 3. Those four rows are
 // 4-aligned, so they lie in one page (pages hold >= 16 tokens): one broadcast page-id read
@@ -301,8 +303,6 @@ struct KeyStage {
   const Keys& k;
   const int* spage;  // LDS page ids of entries [win, win + CAP)
   int win;
-  const uint16_t* kp;
-  const uint16_t* vp;
   int lane_off;      // (L/16) D + 8 ((L%16) ^ swz)
 
   __device__ static int lane_offset(int wave, int lane) {
@@ -310,35 +310,12 @@ struct KeyStage {
   }
 
   // DMA the rows of stage st (attended keys st*ROWS ..) of one pool (K or V) into t.
-  __device__ __forceinline__ void issue_one(int st, const uint16_t* pool, uint16_t* t, int wave,
-                                            int lane) const {
-    // opaque per call: keeps the compiler from hoisting (and spilling) 64-bit lane pointers
-    int lo = lane_off;
-    asm volatile("" : "+v"(lo));
-    const int a0 = st * ROWS;
-    int ph[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int a = a0 + 4 * (NW * i + wave);
-      ph[i] = a < k.n_keys ? spage[(a >> k.log2p) - win] : -1;  // all reads, then one wait
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r0 = 4 * (NW * i + wave);
-      const int a = a0 + r0;
-      const int p = __builtin_amdgcn_readfirstlane(ph[i]);
-      if (p < 0) continue;
-      const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
-      if (k.in_seq(a + (lane >> 4))) lds_dma16(pool + base + lo, t + r0 * D);
-    }
-  }
-
-  // As issue_one, but every wave issues exactly NI DMA instructions with all lanes active,
-  // whatever the rows: a lane whose row does not exist, lies past the end of the
-  // sequence or has an invalid page copies the first rows of the pool instead (such rows
-  // are masked or, for invalid pages, documented as undefined). A fixed count per call
-  // lets the caller wait for all but its most recent batches with vmcnt(n). Split in
-  // two so that the page-id reads (LDS) can be issued well before the DMA needs them.
+  // Every wave issues exactly NI DMA instructions with all lanes active, whatever the
+  // rows: a lane whose row does not exist, lies past the end of the sequence or has an
+  // invalid page copies a zero row instead (such rows are masked; zeros keep them
+  // finite, since a masked P of 0 still multiplies them). A fixed count per call lets
+  // the caller wait for all but its most recent batches with vmcnt(n). Split in two so
+  // that the page-id reads (LDS) can be issued well before the DMA needs them.
   __device__ __forceinline__ void read_pages(int st, int wave, int (&ph)[NI]) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -361,7 +338,7 @@ struct KeyStage {
       const int p = __builtin_amdgcn_readfirstlane(ph[i]);
       const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
       const bool ok = p >= 0 && k.in_seq(a + (lane >> 4));
-      lds_dma16(pool + (ok ? base : 0) + lo, t + r0 * D);
+      lds_dma16((ok ? pool + base : g_zero_rows) + lo, t + r0 * D);
     }
   }
   __device__ __forceinline__ void issue_fixed(int st, const uint16_t* pool, uint16_t* t, int wave,
@@ -369,30 +346,6 @@ struct KeyStage {
     int ph[NI];
     read_pages(st, wave, ph);
     dma_fixed(st, pool, t, wave, lane, ph);
-  }
-
-  // DMA stage st (attended keys st*ROWS ..) into (kt, vt). Rows past the attended keys or
-  // past the end of the sequence, and rows of invalid pages, are not written.
-  __device__ __forceinline__ void issue(int st, uint16_t* kt, uint16_t* vt, int wave, int lane) const {
-    const int a0 = st * ROWS;
-    int ph[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int a = a0 + 4 * (NW * i + wave);
-      ph[i] = a < k.n_keys ? spage[(a >> k.log2p) - win] : -1;  // all reads, then one wait
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r0 = 4 * (NW * i + wave);
-      const int a = a0 + r0;
-      const int p = __builtin_amdgcn_readfirstlane(ph[i]);
-      if (p < 0) continue;
-      const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
-      if (k.in_seq(a + (lane >> 4))) {
-        lds_dma16(kp + base + lane_off, kt + r0 * D);
-        lds_dma16(vp + base + lane_off, vt + r0 * D);
-      }
-    }
   }
 };
 

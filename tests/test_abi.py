@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "oomb.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(oomb_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(oomb_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -28,14 +28,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 4
+    assert lib.oomb_abi_version() == 5
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text

@@ -59,6 +59,22 @@ def test_chunk_parity_mfma_fixed_splits(kw, n, monkeypatch):
     run_chunk_parity(_w(**dict(kw, name=f"{kw['name']}_splits{n}")))
 
 
+@pytest.mark.parametrize("kw", [
+    dict(name="mfma_nan_page0_dense"),
+    dict(name="mfma_nan_page0_sparse", chunk=333, total=2597 + 333, top_k=5, needles=3),
+])
+def test_padding_rows_come_from_zeros(kw):
+    """Physical page 0 is never mapped and holds NaN: the rows staged for block tails,
+    slots past the end of the sequence and invalid pages come from zeros, not from the
+    pool, so nothing the attention does not attend reaches a result (a masked P of 0
+    times a NaN row would be NaN)."""
+    w = _w(**kw)
+    x = wl.make_inputs(w)
+    x["table"] = x["table"] + 1      # pages 1 .. N; page 0 keeps the NaN sentinel
+    x["gtable"] = x["gtable"] + 1
+    run_chunk_parity(w, x)
+
+
 # local attention (the sparse layers of sparse-native models): a window of W positions
 @pytest.mark.parametrize("kw", [
     dict(name="mfma_window5", window=5),                              # inside one key block

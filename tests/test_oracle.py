@@ -553,3 +553,72 @@ def test_sparse_sweep_selects_and_matches_masked_sdpa():
     for g in range(w.hkv):
         dk = orc.gather(r["dk_pool"], x["gtable"], g, range(w.pages_per_head))
         assert torch.allclose(dk, k.grad[g], atol=1e-12, rtol=0)
+
+
+# ----------------------------------------------------------------------------- page movement
+
+def test_copy_pages_round_trip_and_skips():
+    """Copying pages out and back restores them bitwise; ids outside either array are
+    skipped and every page not named keeps its value."""
+    src = _rand((12, 4, 8), 21, torch.bfloat16)
+    host = torch.full((20, 4, 8), 7.0, dtype=torch.bfloat16)
+    src_ids = [3, 0, 11, -1, 5, 40]
+    dst_ids = [19, 2, 7, 4, -3, 1]
+    orc.copy_pages(src, host, src_ids, dst_ids)
+    for s, d in ((3, 19), (0, 2), (11, 7)):
+        assert torch.equal(host[d], src[s])
+    untouched = [i for i in range(20) if i not in (19, 2, 7)]
+    assert bool((host[untouched] == 7.0).all())
+    back = torch.zeros_like(src)
+    orc.copy_pages(host, back, [19, 2, 7], [3, 0, 11])
+    assert torch.equal(back[[3, 0, 11]], src[[3, 0, 11]])
+    orc.copy_pages(src, back, [1, 2], [1, 2], n=1)  # n limits the list
+    assert torch.equal(back[1], src[1]) and bool((back[2] == 0).all())
+
+
+def test_add_pages_identities():
+    """Adding zero pages changes nothing bitwise; adding into zero pages copies; the sum
+    is the correctly rounded one (integers below 2^24 add exactly); zero_src clears."""
+    x = _rand((6, 4, 8), 22, torch.float32)
+    acc = x.clone()
+    zeros = torch.zeros_like(x)
+    orc.add_pages(zeros, acc, range(6), range(6))
+    assert torch.equal(acc, x)
+    dst = torch.zeros_like(x)
+    orc.add_pages(x, dst, [0, 1], [4, 5])
+    assert torch.equal(dst[4], x[0]) and torch.equal(dst[5], x[1])
+    a = torch.full((2, 4, 8), 3.0e6)
+    b = torch.full((2, 4, 8), 1234567.0)
+    orc.add_pages(b, a, [0, 1], [1, 0], zero_src=True)
+    assert bool((a == 4234567.0).all()) and bool((b == 0).all())
+    # one rounding: 1 + 2^-24 rounds to 1 in fp32 (ties to even), 1 + 3 * 2^-24 does not
+    c = torch.ones(1, 1, 4)
+    d = torch.tensor([[[2.0 ** -24, 3 * 2.0 ** -24, 0.0, -1.0]]])
+    orc.add_pages(d, c, [0], [0])
+    assert c.flatten().tolist() == [1.0, 1.0 + 2.0 ** -22, 1.0, 0.0]
+
+
+def test_fetch_selected_then_gather_equals_host_pages():
+    """After the fetch, gathering the selected logical pages through the updated table
+    from the device pool gives the host's pages bitwise, for every KV head; unselected
+    entries of the table are unchanged; out-of-range selections are skipped."""
+    hkv, P, D, n_logical = 2, 4, 8, 10
+    host_k = _rand((hkv * n_logical, P, D), 23, torch.bfloat16)
+    host_v = _rand((hkv * n_logical, P, D), 24, torch.bfloat16)
+    host_table = _table(hkv, n_logical, 25)
+    k_pool = torch.zeros(16, P, D, dtype=torch.bfloat16)
+    v_pool = torch.zeros_like(k_pool)
+    table = torch.full((hkv, n_logical), -1, dtype=torch.int32)
+    sel = torch.tensor([[1, 4, 8, 12], [0, 9, -2, 3]], dtype=torch.int32)
+    count = torch.tensor([3, 4], dtype=torch.int32)
+    stage = torch.tensor([[10, 11, 12, 13], [2, 3, 4, 5]], dtype=torch.int32)
+    orc.fetch_selected(k_pool, v_pool, table, host_k, host_v, host_table, sel, count, stage,
+                       n_logical)
+    for g, chosen in ((0, [1, 4, 8]), (1, [0, 9, 3])):
+        assert torch.equal(orc.gather(k_pool, table, g, chosen),
+                           orc.gather(host_k, host_table, g, chosen))
+        assert torch.equal(orc.gather(v_pool, table, g, chosen),
+                           orc.gather(host_v, host_table, g, chosen))
+        rest = [lp for lp in range(n_logical) if lp not in chosen]
+        assert bool((table[g, rest] == -1).all())
+
