@@ -134,6 +134,224 @@ def cpu_baseline(w, x, table_cpu, sel_cpu, rows: int):
                       f"{pairs} pairs, {dt:.1f} s"}
 
 
+PEAK_PCIE_GBS = 64.0  # PCIe 5.0 x16 host link, per direction
+
+
+def offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step, reps=10):
+    """The CPU offload of one sparse layer-chunk (explainer 2.C), timed with HIP events:
+    fetch of the selected pages from pinned host pages into another layer's device pool,
+    offload of the chunk's new pages to the host, and write-back of the attended
+    gradient pages into a pinned fp32 host pool; a copy-engine transfer of 256 MiB as
+    the link reference; and the overlap: the attention step alone against the same step
+    with the next layer's transfers on a second stream."""
+    P, C, t0, D = w.page, w.chunk, w.t0, w.d
+    esize = 2 if w.dtype == torch.bfloat16 else 4
+    page_b = P * D * esize
+    hkv = w.hkv
+    n_cand = t0 // P
+    first_local = n_cand
+    n_local = (t0 + C - 1) // P - first_local + 1
+    k = sel.shape[1]
+    dev = "cuda"
+    side = torch.cuda.Stream()
+    # host copies of the layer's prior pages: contents do not matter for timing, so a
+    # pool of 1024 pages stands in for the whole layer (logical pages map onto it)
+    n_host = 1024
+    host_k = torch.empty(n_host, P, D, dtype=w.dtype, pin_memory=True)
+    host_v = torch.empty_like(host_k, pin_memory=True)
+    host_table = ((torch.arange(hkv * n_cand, dtype=torch.int64) % n_host).to(torch.int32)
+                  .reshape(hkv, n_cand).to(dev))
+    # the next layer's device pool: its local pages plus one staging page per selection
+    nxt = pca.PagedPool(hkv * (k + n_local), P, D, w.hq, hkv, w.dtype, dev, with_summary=False,
+                        with_grad=False)
+    nxt_table = torch.zeros(hkv, first_local + n_local, dtype=torch.int32, device=dev)
+    stage = torch.arange(hkv * k, dtype=torch.int32, device=dev).reshape(hkv, k)
+    # the chunk's new pages (K and V of every head) to host slots
+    local_phys = table[:, first_local:first_local + n_local].contiguous().flatten()
+    host_new_k = torch.empty(hkv * n_local, P, D, dtype=w.dtype, pin_memory=True)
+    host_new_v = torch.empty_like(host_new_k, pin_memory=True)
+    new_ids = torch.arange(hkv * n_local, dtype=torch.int32, device=dev)
+    # the attended pages' gradients (selected + local) into a pinned fp32 host pool
+    att = torch.cat([sel.to(torch.int64), torch.arange(first_local, first_local + n_local,
+                                                        device=dev).expand(hkv, -1)], 1)
+    g_ids = torch.gather(gtable.to(torch.int64), 1, att).to(torch.int32).flatten().contiguous()
+    host_dk = torch.zeros(g_ids.numel(), P, D, dtype=torch.float32, pin_memory=True)
+    host_dv = torch.zeros_like(host_dk, pin_memory=True)
+    host_g_ids = torch.arange(g_ids.numel(), dtype=torch.int32, device=dev)
+
+    moves = {
+        "fetch_selected": (lambda st: pca.oomb_fetch_selected(nxt, nxt_table, host_k, host_v,
+                                                              host_table, sel, count, stage,
+                                                              n_logical=n_cand, stream=st),
+                           hkv * k * 2 * page_b, "host -> device",
+                           f"{hkv} x {k} selected pages, K and V"),
+        "offload_new_pages": (lambda st: (pca.oomb_copy_pages(pool.k, host_new_k, local_phys, new_ids,
+                                                              stream=st),
+                                          pca.oomb_copy_pages(pool.v, host_new_v, local_phys, new_ids,
+                                                              stream=st)),
+                              hkv * n_local * 2 * page_b, "device -> host",
+                              f"{hkv} x {n_local} chunk pages, K and V"),
+        "grad_write_back": (lambda st: (pca.oomb_add_pages_f32(pool.dk, host_dk, g_ids, host_g_ids,
+                                                               stream=st),
+                                        pca.oomb_add_pages_f32(pool.dv, host_dv, g_ids, host_g_ids,
+                                                               stream=st)),
+                            2 * g_ids.numel() * P * D * 4, "device -> host (read + write host)",
+                            f"{g_ids.numel()} attended gradient pages, dK and dV, added into the host pool"),
+    }
+
+    # the same moves on the copy engines, with page lists the host holds: the selection
+    # read back once (a small copy and one wait), the table and gradient table too
+    sel_h = sel.cpu()
+    cnt_h = count.cpu()
+    tab_h = table.cpu()
+    gtab_h = gtable.cpu()
+    hts_h = host_table.cpu()
+    f_src, f_dst = [], []
+    for g in range(hkv):
+        for j in range(int(cnt_h[g])):
+            f_src.append(int(hts_h[g, int(sel_h[g, j])]))
+            f_dst.append(int(stage[g, j]))
+    n_src_ids = tab_h[:, first_local:first_local + n_local].flatten().tolist()
+    att_h = torch.cat([sel_h.to(torch.int64),
+                       torch.arange(first_local, first_local + n_local).expand(hkv, -1)], 1)
+    g_src = torch.gather(gtab_h.to(torch.int64), 1, att_h).flatten().tolist()
+    dev_g_stage = torch.empty(len(g_src), P, D, dtype=torch.float32, device=dev)
+    g_stage_ids = list(range(len(g_src)))
+    sdma_moves = {
+        "fetch_selected_sdma": (lambda st: (pca.oomb_copy_pages_sdma(host_k, nxt.k, f_src, f_dst, stream=st),
+                                            pca.oomb_copy_pages_sdma(host_v, nxt.v, f_src, f_dst, stream=st)),
+                                hkv * k * 2 * page_b, "host -> device", "as fetch_selected"),
+        "offload_new_pages_sdma": (lambda st: (pca.oomb_copy_pages_sdma(pool.k, host_new_k, n_src_ids,
+                                                                        list(range(len(n_src_ids))), stream=st),
+                                               pca.oomb_copy_pages_sdma(pool.v, host_new_v, n_src_ids,
+                                                                        list(range(len(n_src_ids))), stream=st)),
+                                   hkv * n_local * 2 * page_b, "device -> host", "as offload_new_pages"),
+        # gradients: the host pool's pages come in, are added to on the device (a
+        # device-only kernel), and go back: twice the link bytes, in both directions
+        "grad_round_trip_sdma": (lambda st: (pca.oomb_copy_pages_sdma(host_dk, dev_g_stage, g_stage_ids,
+                                                                      g_stage_ids, stream=st),
+                                             pca.oomb_add_pages_f32(pool.dk, dev_g_stage, g_ids,
+                                                                    host_g_ids, stream=st),
+                                             pca.oomb_copy_pages_sdma(dev_g_stage, host_dk, g_stage_ids,
+                                                                      g_stage_ids, stream=st),
+                                             pca.oomb_copy_pages_sdma(host_dv, dev_g_stage, g_stage_ids,
+                                                                      g_stage_ids, stream=st),
+                                             pca.oomb_add_pages_f32(pool.dv, dev_g_stage, g_ids,
+                                                                    host_g_ids, stream=st),
+                                             pca.oomb_copy_pages_sdma(dev_g_stage, host_dv, g_stage_ids,
+                                                                      g_stage_ids, stream=st)),
+                                 2 * 2 * len(g_src) * P * D * 4, "both directions",
+                                 f"{len(g_src)} attended gradient pages, dK and dV: in, added on the "
+                                 f"device, out"),
+    }
+
+    def timed(fn, stream):
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(stream)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        return times[len(times) // 2]
+
+    out = {"peak_GBps": PEAK_PCIE_GBS, "link": "PCIe 5.0 x16, per direction"}
+    for name, (fn, nbytes, direction, what) in list(moves.items()) + list(sdma_moves.items()):
+        fn(side)
+        torch.cuda.synchronize()
+        ms = timed(fn, side)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "bytes": nbytes, "GBps": gbs, "frac": gbs / PEAK_PCIE_GBS,
+                     "direction": direction, "work": what}
+    # copy-engine reference: 256 MiB pinned -> device and back
+    hbuf = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dbuf = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    for name, fn in (("copy_engine_h2d", lambda st: dbuf.copy_(hbuf, non_blocking=True)),
+                     ("copy_engine_d2h", lambda st: hbuf.copy_(dbuf, non_blocking=True))):
+        def run(st, fn=fn):
+            with torch.cuda.stream(st):
+                fn(st)
+        run(side)
+        torch.cuda.synchronize()
+        ms = timed(run, side)
+        gbs = (256 << 20) / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "bytes": 256 << 20, "GBps": gbs, "frac": gbs / PEAK_PCIE_GBS}
+
+    # overlap: the attention step (forward + backward) alone, then with the next layer's
+    # fetch, this chunk's page offload and the gradient write-back on a second stream
+    main = torch.cuda.current_stream()
+
+    def step_alone():
+        attn_step()
+
+    def step_with_transfers():
+        side.wait_stream(main)
+        for fn, _, _, _ in moves.values():
+            fn(side)
+        attn_step()
+        main.wait_stream(side)
+
+    def step_with_sdma_transfers():
+        side.wait_stream(main)
+        for fn, _, _, _ in sdma_moves.values():
+            fn(side)
+        attn_step()
+        main.wait_stream(side)
+
+    res = {}
+    for name, fn in (("alone", step_alone), ("with_transfers", step_with_transfers),
+                     ("with_sdma_transfers", step_with_sdma_transfers), ("alone_again", step_alone)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t) * 1e3 / reps
+    # the same byte volumes moved by the copy engines (contiguous buffers, no CUs)
+    ce_h2d = [(torch.empty(nb, dtype=torch.uint8, device=dev),
+               torch.empty(nb, dtype=torch.uint8, pin_memory=True))
+              for nb in (moves["fetch_selected"][1], moves["grad_write_back"][1] // 2)]
+    ce_d2h = [(torch.empty(nb, dtype=torch.uint8, pin_memory=True),
+               torch.empty(nb, dtype=torch.uint8, device=dev))
+              for nb in (moves["offload_new_pages"][1], moves["grad_write_back"][1] // 2)]
+
+    def step_with_copy_engine():
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            for d_, s_ in ce_h2d + ce_d2h:
+                d_.copy_(s_, non_blocking=True)
+        attn_step()
+        main.wait_stream(side)
+
+    for _ in range(2):
+        step_with_copy_engine()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        step_with_copy_engine()
+    torch.cuda.synchronize()
+    res["with_copy_engine"] = (time.perf_counter() - t) * 1e3 / reps
+    base = 0.5 * (res["alone"] + res["alone_again"])
+    out["overlap"] = {"attention_ms": base, "attention_with_transfers_ms": res["with_transfers"],
+                      "overhead": res["with_transfers"] / base - 1.0,
+                      "attention_with_sdma_page_lists_ms": res["with_sdma_transfers"],
+                      "overhead_sdma_page_lists": res["with_sdma_transfers"] / base - 1.0,
+                      "sdma_transfer_bytes": sum(v[1] for v in sdma_moves.values()),
+                      "attention_with_copy_engine_ms": res["with_copy_engine"],
+                      "overhead_copy_engine": res["with_copy_engine"] / base - 1.0,
+                      "transfer_bytes": sum(v[1] for v in moves.values()),
+                      "what": "forward + backward of the chunk on one stream; on a second "
+                              "stream, started with it: the three kernel page moves above "
+                              "(overhead), the three copy-engine page-list moves "
+                              "(overhead_sdma_page_lists), or contiguous copy-engine transfers of "
+                              "the same bytes (overhead_copy_engine)"}
+    return out
+
+
 def context_build(pca, torch, pool, table, x, w, reps):
     """Write the whole prior context into the pool (kv_append) and summarise its pages
     (page_summarize), each timed on its own stream with HIP events after evicting the
@@ -215,6 +433,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="chunk queries in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the CPU-offload measurements (sparse workloads)")
     ap.add_argument("--hbm-reps", type=int, default=3,
                     help="cold-cache repetitions of the whole-context append and summarize")
     args = ap.parse_args()
@@ -344,6 +564,18 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": None, "traffic": None, "ms_per_launch": dom_ms}
 
+    offload = None
+    if sparse and not args.no_offload:
+        def attn_step():
+            pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, sel, count, w.scale, o=o, lse=lse,
+                                          workspace=ws_fwd)
+            pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, sel, count, o, do, lse,
+                                          w.scale, dq=dq, workspace=ws_bwd)
+        log("[bench] offload leg ...")
+        offload = offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step)
+        log(f"[bench] offload: fetch {offload['fetch_selected']['GBps']:.1f} GB/s, overlap "
+            f"overhead {100 * offload['overlap']['overhead']:.1f} %")
+
     cpu = None
     if not args.no_cpu_baseline:
         x_cpu = {"k": x["k"], "v": x["v"], "q": x["q"], "do": x["do"]}
@@ -366,6 +598,7 @@ def main():
         "roofline": roof,
         "kernels": breakdown,
         "hbm_kernels": hbm,
+        "offload": offload,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

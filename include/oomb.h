@@ -231,6 +231,17 @@ int oomb_copy_pages(const void* src, void* dst, int64_t page_bytes, int64_t n_sr
                     int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
                     int32_t n, const int32_t* n_dev, void* stream);
 
+/* As oomb_copy_pages, on the copy engines (SDMA) instead of compute units, for lists the
+ * host knows: src_ids / dst_ids are HOST int32 arrays, read during the call; runs of
+ * consecutive pages on both sides become one transfer each, enqueued on `stream`.
+ * page_bytes > 0. While attention kernels run on other streams, transfers
+ * by the copy engines leave them at full speed; copies by kernels (oomb_copy_pages,
+ * oomb_fetch_selected) share the compute units' memory path and slow them by ~10%, in
+ * exchange for device-side lists. */
+int oomb_copy_pages_sdma(const void* src, void* dst, int64_t page_bytes, int64_t n_src_pages,
+                         int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
+                         int32_t n, void* stream);
+
 /* fp32 pages of page_elems floats (a multiple of 4): dst page dst_ids[i] += src page
  * src_ids[i] (one fp32 rounding per element), then, if zero_src, src page src_ids[i]
  * = 0; for i < n (or min(n, *n_dev)). For moving key/value gradient pages into an fp32

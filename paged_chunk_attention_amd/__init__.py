@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     bwd_workspace_bytes,
     oomb_add_pages_f32,
     oomb_copy_pages,
+    oomb_copy_pages_sdma,
     oomb_fetch_selected,
     fwd_workspace_bytes,
     kernel_timer,

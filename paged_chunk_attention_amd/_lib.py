@@ -51,6 +51,8 @@ SIGNATURES = {
     "oomb_bwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64, c_int32]),
     "oomb_copy_pages": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                 c_int32, c_void_p, c_void_p]),
+    "oomb_copy_pages_sdma": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p,
+                                     c_void_p, c_int32, c_void_p]),
     "oomb_add_pages_f32": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p,
                                    c_void_p, c_int32, c_void_p, c_int32, c_void_p]),
     "oomb_fetch_selected": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_void_p, c_int64,

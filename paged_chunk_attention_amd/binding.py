@@ -265,6 +265,23 @@ def oomb_copy_pages(src: torch.Tensor, dst: torch.Tensor, src_ids: torch.Tensor,
          _stream(stream))
 
 
+def oomb_copy_pages_sdma(src: torch.Tensor, dst: torch.Tensor, src_ids, dst_ids,
+                         stream=None) -> None:
+    """As oomb_copy_pages, by the copy engines, for id lists the host holds (sequences of
+    ints or int32 CPU tensors)."""
+    _pages(src, "src")
+    _pages(dst, "dst")
+    if src.dtype != dst.dtype or src.shape[1:] != dst.shape[1:]:
+        raise ValueError("src and dst pages differ in dtype or shape")
+    s_ids = torch.as_tensor(src_ids, dtype=torch.int32).contiguous()
+    d_ids = torch.as_tensor(dst_ids, dtype=torch.int32).contiguous()
+    if s_ids.is_cuda or d_ids.is_cuda or s_ids.numel() != d_ids.numel():
+        raise ValueError("id lists must be host int32 lists of equal length")
+    page_bytes = src[0].numel() * src.element_size()
+    call("oomb_copy_pages_sdma", _ptr(src), _ptr(dst), page_bytes, src.shape[0], dst.shape[0],
+         _ptr(s_ids), _ptr(d_ids), s_ids.numel(), _stream(stream))
+
+
 def oomb_add_pages_f32(src: torch.Tensor, dst: torch.Tensor, src_ids: torch.Tensor,
                        dst_ids: torch.Tensor, n: Optional[int] = None,
                        n_dev: Optional[torch.Tensor] = None, zero_src: bool = False,

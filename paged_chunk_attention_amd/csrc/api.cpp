@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "launch.hpp"
 #include "oomb.h"
@@ -498,6 +499,49 @@ int oomb_copy_pages(const void* src, void* dst, int64_t page_bytes, int64_t n_sr
   if (st) return st;
   if (n == 0) return OOMB_OK;
   return hip_status(oomb::launch_copy_pages(a, static_cast<hipStream_t>(stream)), "copy_pages");
+}
+
+int oomb_copy_pages_sdma(const void* src, void* dst, int64_t page_bytes, int64_t n_src_pages,
+                         int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
+                         int32_t n, void* stream) {
+  if (page_bytes <= 0) return fail(OOMB_ERR_INVALID, "page size must be positive");
+  if (n < 0) return fail(OOMB_ERR_INVALID, "n must be >= 0 (got %d)", n);
+  if (n_src_pages <= 0 || n_dst_pages <= 0) return fail(OOMB_ERR_INVALID, "page counts must be positive");
+  if (n > 0 && (src_ids == nullptr || dst_ids == nullptr))
+    return fail(OOMB_ERR_INVALID, "id lists are NULL");
+  const void* s_dev = nullptr;
+  const void* d_dev = nullptr;
+  int st;
+  // both ends must be device memory or pinned host memory (pageable memory would make
+  // the copy synchronous); the copies themselves use the pointers as given
+  if ((st = device_address(src, 1, "src", &s_dev))) return st;
+  if ((st = device_address(static_cast<const void*>(dst), 1, "dst", &d_dev))) return st;
+  // runs of consecutive pages on both sides become one copy each
+  std::vector<void*> dsts, srcs;
+  std::vector<size_t> sizes;
+  for (int32_t i = 0; i < n;) {
+    const int64_t s0 = src_ids[i], d0 = dst_ids[i];
+    if (s0 < 0 || s0 >= n_src_pages || d0 < 0 || d0 >= n_dst_pages) {
+      ++i;
+      continue;
+    }
+    int32_t len = 1;
+    while (i + len < n && src_ids[i + len] == s0 + len && dst_ids[i + len] == d0 + len &&
+           s0 + len < n_src_pages && d0 + len < n_dst_pages)
+      ++len;
+    srcs.push_back(const_cast<char*>(static_cast<const char*>(src)) + s0 * page_bytes);
+    dsts.push_back(static_cast<char*>(dst) + d0 * page_bytes);
+    sizes.push_back(static_cast<size_t>(len) * page_bytes);
+    i += len;
+  }
+  // One asynchronous copy per run (the batched-copy call needs a newer HIP runtime than
+  // the one PyTorch loads).
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (size_t r = 0; r < dsts.size(); ++r) {
+    const hipError_t e = hipMemcpyAsync(dsts[r], srcs[r], sizes[r], hipMemcpyDefault, hs);
+    if (e != hipSuccess) return hip_status(e, "copy_pages_sdma");
+  }
+  return OOMB_OK;
 }
 
 int oomb_add_pages_f32(const float* src, float* dst, int64_t page_elems, int64_t n_src_pages,

@@ -63,6 +63,29 @@ def test_copy_pages_device_host_round_trip(dtype):
     assert torch.equal(bits(again), bits(want_again))
 
 
+def test_copy_pages_sdma_runs_and_skips():
+    """The copy-engine path: host id lists with runs (coalesced into one transfer each),
+    single pages and invalid ids, both directions, bitwise as the oracle."""
+    log("[case copy_pages_sdma]")
+    dev_cpu = _rand((64, 16, 128), 4, torch.bfloat16)
+    dev = dev_cpu.to(DEV)
+    host = _pinned((80, 16, 128), torch.bfloat16)
+    fill_sentinel(host)
+    want = host.clone()
+    src = [10, 11, 12, 13, 40, 41, 7, -1, 5, 63, 70]
+    dst = [20, 21, 22, 23, 50, 60, 0, 3, 79, 78, 1]
+    pca.oomb_copy_pages_sdma(dev, host, src, dst)
+    torch.cuda.synchronize()
+    orc.copy_pages(dev_cpu, want, src, dst)
+    assert torch.equal(bits(host), bits(want)), "device -> host (copy engine) differs"
+    back = torch.zeros(64, 16, 128, dtype=torch.bfloat16, device=DEV)
+    want_back = torch.zeros(64, 16, 128, dtype=torch.bfloat16)
+    pca.oomb_copy_pages_sdma(host, back, dst, src)
+    orc.copy_pages(want, want_back, dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(back), bits(want_back)), "host -> device (copy engine) differs"
+
+
 def test_add_pages_into_pinned_host():
     """Gradient pages added into a pinned fp32 pool (one rounding per element, as the
     oracle), the source pages cleared afterwards; pages not named unchanged."""
