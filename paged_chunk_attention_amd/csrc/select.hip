@@ -21,27 +21,69 @@ namespace oomb {
 
 constexpr int kQBlock = 64;
 
-// Block partial sums: grid (nb, Hkv), one thread per head dimension.
+// Block partial sums. Thread t of the grid owns block b = t / (D/8) of 64 consecutive
+// rows of KV head blockIdx.y and head dimensions 8 (t % (D/8)) .. +7: one 16-byte load
+// per row (issued in groups of 16), each dimension summed strictly in row order.
 template <bool kBf16>
-__global__ __launch_bounds__(128) void qbar_partial_kernel(SelectArgs a) {
-  const int d = threadIdx.x;
-  const int b = blockIdx.x, g = blockIdx.y;
+__global__ __launch_bounds__(256) void qbar_partial_kernel(SelectArgs a) {
   const int D = a.pool.D;
-  if (d >= D) return;
+  const int lanes_per_block = D / 8;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int b = t / lanes_per_block, d0 = 8 * (t % lanes_per_block);
+  const int g = blockIdx.y;
+  if (b >= a.nb) return;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int M = G * a.n_q;
   const int m0 = b * kQBlock;
   const int m1 = (m0 + kQBlock < M) ? m0 + kQBlock : M;
-  float s = 0.0f;
-  for (int m = m0; m < m1; ++m) {
-    const int h = g * G + m / a.n_q, i = m % a.n_q;
-    const int64_t off = h * a.q_hs + i * a.q_ts + d;
-    float x;
-    if (kBf16) x = to_f32(reinterpret_cast<const bf16_t*>(a.q)[off]);
-    else x = reinterpret_cast<const float*>(a.q)[off];
-    s = s + x;
+  constexpr int kGroup = 16;
+  float s[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s[c] = 0.0f;
+  // (head, query) of row m, stepped row by row (no division per row). The body is
+  // branch-free (rows past the block's end load its first row and count as zero): a
+  // branch per row would make each load wait for the previous one.
+  const int h0 = g * G + m0 / a.n_q, i0 = m0 % a.n_q;
+  int h = h0, i = i0;
+  for (int mg = m0; mg < m1; mg += kGroup) {
+    float x[kGroup][8];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const bool live = mg + u < m1;
+      const int64_t off = (live ? h * a.q_hs + static_cast<int64_t>(i) * a.q_ts
+                                : h0 * a.q_hs + static_cast<int64_t>(i0) * a.q_ts) + d0;
+      const int in = i + 1;
+      const bool wrap = in == a.n_q;
+      i = wrap ? 0 : in;
+      h += wrap ? 1 : 0;
+      if (kBf16) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.q) + off);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[u][2 * c] = live ? __uint_as_float(w[c] << 16) : 0.0f;
+          x[u][2 * c + 1] = live ? __uint_as_float(w[c] & 0xFFFF0000u) : 0.0f;
+        }
+      } else {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.q) + off);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.q) + off + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[u][c] = live ? lo[c] : 0.0f;
+          x[u][4 + c] = live ? hi[c] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      if (mg + u < m1) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = s[c] + x[u][c];
+      }
+    }
   }
-  a.partial[(static_cast<int64_t>(g) * a.nb + b) * D + d] = s;
+  float* dst = a.partial + (static_cast<int64_t>(g) * a.nb + b) * D + d0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dst[c] = s[c];
 }
 
 // Pairwise tree over the block sums of one (head dimension, KV head).
@@ -113,31 +155,48 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+// Candidates whose keys are kept in LDS (128 KiB plus one padding word per 32, so that
+// threads scanning contiguous ranges of 32 hit distinct banks); longer lists are read
+// from memory on every pass.
+constexpr int kTopkLds = 32768;
+__device__ __forceinline__ int key_slot(int j) { return j + (j >> 5); }
 
-// Exclusive prefix count of a per-thread flag over the workgroup; returns the
-// prefix and writes the total. Uses wave ballots plus one LDS pass over 16 waves.
-__device__ __forceinline__ int block_exclusive_count(bool flag, int* s_wave, int* total) {
+// Exclusive prefix sum of one int per thread over the workgroup (ids in thread order);
+// writes the total. Wave scans by shuffles, then one pass over the wave totals.
+__device__ __forceinline__ int block_exclusive_sum(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long ball = __ballot(flag);
-  const int in_wave = __popcll(ball & ((1ull << lane) - 1ull));
-  if (lane == 0) s_wave[wave] = __popcll(ball);
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wave[wave] = incl;
   __syncthreads();
   int before = 0, sum = 0;
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
     const int c = s_wave[w];
     before += (w < wave) ? c : 0;
     sum += c;
   }
   __syncthreads();
   *total = sum;
-  return before + in_wave;
+  return before + incl - v;
 }
 
 // One workgroup per KV head: radix select of the k-th largest (score, -id) key over
-// 4 digits of 8 bits, then an ordered compaction that emits ids ascending.
+// 4 digits of 8 bits, then an ordered compaction that emits ids ascending. The keys
+// are made once (into LDS when they fit); each digit is picked by one wavefront from
+// suffix sums of the histogram; in the compaction each thread owns a contiguous range
+// of ids, so the ties taken (the lowest ids) and the output order come from two
+// workgroup-wide prefix sums.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
+  extern __shared__ uint32_t s_keys[];  // min(n, kTopkLds) keys
   __shared__ int s_hist[256];
-  __shared__ int s_wave[kTopkThreads / 64];
+  __shared__ int s_whist[kTopkWaves][256];  // per-wave histograms: no contention across waves
+  __shared__ int s_wave[kTopkWaves];
   __shared__ uint32_t s_prefix;
   __shared__ int s_krem;
   const int g = blockIdx.x;
@@ -154,45 +213,88 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
     if (threadIdx.x == 0) a.count[g] = 0;
     return;
   }
+  const bool in_lds = n <= kTopkLds;
+  if (in_lds)
+    for (int j = threadIdx.x; j < n; j += kTopkThreads) s_keys[key_slot(j)] = score_key(sc[j]);
+  auto key = [&](int j) -> uint32_t { return in_lds ? s_keys[key_slot(j)] : score_key(sc[j]); };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t prefix = 0, mask = 0;
   int krem = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kTopkThreads) s_hist[i] = 0;
+    for (int i = lane; i < 256; i += 64) s_whist[wave][i] = 0;
     __syncthreads();
     for (int j = threadIdx.x; j < n; j += kTopkThreads) {
-      const uint32_t u = score_key(sc[j]);
-      if ((u & mask) == prefix) atomicAdd(&s_hist[(u >> shift) & 255], 1);
+      const uint32_t u = key(j);
+      if ((u & mask) == prefix) atomicAdd(&s_whist[wave][(u >> shift) & 255], 1);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int above = 0, digit = 255;
-      for (; digit > 0; --digit) {
-        if (above + s_hist[digit] >= krem) break;
-        above += s_hist[digit];
+    for (int i = threadIdx.x; i < 256; i += kTopkThreads) {
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; ++w) c += s_whist[w][i];
+      s_hist[i] = c;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds digits 4l .. 4l + 3; count(digit >= d) is a suffix sum, and the
+      // digit sought is the largest d with count(digit >= d) >= krem
+      int c[4], lsum = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        c[t] = s_hist[4 * lane + t];
+        lsum += c[t];
       }
-      s_prefix = prefix | (static_cast<uint32_t>(digit) << shift);
-      s_krem = krem - above;
+      int incl = lsum;  // sum over lanes >= lane
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(incl, off, 64);
+        if (lane + off < 64) incl += o;
+      }
+      int above = incl - lsum;  // keys with a digit above this lane's four
+      int found = -1, rem = 0;
+#pragma unroll
+      for (int t = 3; t >= 0; --t) {
+        if (found < 0 && above + c[t] >= krem) {
+          found = 4 * lane + t;
+          rem = krem - above;
+        }
+        above += c[t];
+      }
+      const unsigned long long ball = __ballot(found >= 0);
+      const int top = 63 - __builtin_clzll(ball);  // digit 0 always qualifies: ball != 0
+      if (lane == top) {
+        s_prefix = prefix | (static_cast<uint32_t>(found) << shift);
+        s_krem = rem;
+      }
     }
     __syncthreads();
     prefix = s_prefix;
     krem = s_krem;
     mask |= 255u << shift;
-    __syncthreads();
   }
-  // prefix = key of the k-th largest score; krem = how many keys equal to it to take.
-  int base_eq = 0, base_sel = 0;
-  for (int start = 0; start < n; start += kTopkThreads) {
-    const int j = start + threadIdx.x;
-    const uint32_t u = j < n ? score_key(sc[j]) : 0u;
-    const bool gt = j < n && u > prefix;
-    const bool eq = j < n && u == prefix;
-    int n_eq, n_take;
-    const int eq_rank = base_eq + block_exclusive_count(eq, s_wave, &n_eq);
-    const bool take = gt || (eq && eq_rank < krem);
-    const int pos = base_sel + block_exclusive_count(take, s_wave, &n_take);
-    if (take) out[pos] = j;
-    base_eq += n_eq;
-    base_sel += n_take;
+  // prefix = key of the k-th largest score; krem = how many keys equal to it to take
+  // (the lowest ids among them). Thread t owns ids [t * per, (t + 1) * per).
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int j0 = threadIdx.x * per, j1 = min(n, j0 + per);
+  int n_eq_mine = 0, n_gt_mine = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t u = key(j);
+    n_eq_mine += u == prefix;
+    n_gt_mine += u > prefix;
+  }
+  int tot;
+  const int eq_before = block_exclusive_sum(n_eq_mine, s_wave, &tot);
+  const int eq_take = max(0, min(n_eq_mine, krem - eq_before));  // my lowest-id ties taken
+  const int pos0 = block_exclusive_sum(n_gt_mine + eq_take, s_wave, &tot);
+  int pos = pos0, eq_seen = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t u = key(j);
+    const bool eq = u == prefix;
+    if (u > prefix || (eq && eq_seen < eq_take)) {
+      if (pos < k) out[pos] = j;  // pos < k always; the bound guards the row
+      ++pos;
+    }
+    eq_seen += eq;
   }
   if (threadIdx.x == 0) a.count[g] = k;
 }
@@ -200,9 +302,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
 static void launch_scores(const SelectArgs& a, hipStream_t s) {
   const bool bf = a.pool.dtype == 0;
   const int D = a.pool.D;
-  dim3 g1(a.nb, a.pool.Hkv);
-  if (bf) OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<true>, g1, dim3(128), 0, s, a);
-  else OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<false>, g1, dim3(128), 0, s, a);
+  dim3 g1((a.nb * (D / 8) + 255) / 256, a.pool.Hkv);
+  if (bf) OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<true>, g1, dim3(256), 0, s, a);
+  else OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<false>, g1, dim3(256), 0, s, a);
   int n2 = 1;
   while (n2 < a.nb) n2 <<= 1;
   OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
@@ -217,7 +319,9 @@ static void launch_scores(const SelectArgs& a, hipStream_t s) {
 // k = 0 or k >= n_cand; the query summary and scores are also diagnostics).
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (a.n_cand > 0) launch_scores(a, s);
-  OOMB_LAUNCH("topk", topk_kernel, dim3(a.pool.Hkv), dim3(kTopkThreads), 0, s, a);
+  const int n_lds = a.n_cand <= kTopkLds ? a.n_cand + (a.n_cand >> 5) + 1 : 0;
+  OOMB_LAUNCH("topk", topk_kernel, dim3(a.pool.Hkv), dim3(kTopkThreads),
+              static_cast<size_t>(n_lds) * sizeof(uint32_t), s, a);
   return hipGetLastError();
 }
 
