@@ -352,6 +352,69 @@ def offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step
     return out
 
 
+def mean_selector_leg(pca, torch, w, pool, table, q, sel, count, needles, reps=3):
+    """The selector variant (mean-key page representatives): its whole-context summary
+    timed with cold caches and its selection timed warm, both against HBM; then how far
+    it agrees with the min/max selection of the step, and each one's recall of the
+    needle pages."""
+    P, C, t0, D = w.page, w.chunk, w.t0, w.d
+    esize = 2 if w.dtype == torch.bfloat16 else 4
+    n_pages = t0 // P
+    n_cand = n_pages
+    kmean = torch.zeros(pool.k.shape[0], D, dtype=torch.float32, device="cuda")
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, cold):
+        times = []
+        for _ in range(reps):
+            if cold:
+                scratch.fill_(1)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        return times[len(times) // 2]
+
+    out = {}
+    ms = timed(lambda: pca.oomb_page_summarize_mean(pool, table, 0, n_pages, t0, kmean), True)
+    nbytes = w.hkv * t0 * D * esize + w.hkv * n_pages * D * 4
+    out["page_summarize_mean"] = {"ms": ms, "algorithmic_bytes": nbytes,
+                                  "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+                                  "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                  "peak_GBps": PEAK_HBM_GBS, "cache": "cold",
+                                  "work": f"{w.hkv} x {n_pages} pages of {P} tokens, fp32 means"}
+    pca.oomb_page_summarize_mean(pool, table, 0, (t0 + C - 1) // P + 1, t0 + C, kmean)
+    sel_m = torch.zeros_like(sel)
+    cnt_m = torch.zeros_like(count)
+    ws = torch.empty(pca.select_workspace_bytes(pool, C, t0), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: pca.oomb_select_pages_mean(pool, table, q, t0, w.top_k, kmean, sel=sel_m,
+                                                  count=cnt_m, workspace=ws), False)
+    nbytes = w.hq * C * D * esize + w.hkv * n_cand * D * 4
+    out["select_pages_mean"] = {"ms": ms, "algorithmic_bytes": nbytes,
+                                "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+                                "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                "peak_GBps": PEAK_HBM_GBS, "cache": "warm",
+                                "work": f"{w.hkv} x {n_cand} candidate pages, {w.hq} x {C} queries"}
+    a = [set(sel[g, :int(count[g])].tolist()) for g in range(w.hkv)]
+    b = [set(sel_m[g, :int(cnt_m[g])].tolist()) for g in range(w.hkv)]
+    nd = set(int(j) for j in needles)
+    k = max(1, sum(len(s_) for s_ in a))
+    out["overlap"] = sum(len(a[g] & b[g]) for g in range(w.hkv)) / k
+    out["needle_recall_minmax"] = (sum(len(a[g] & nd) for g in range(w.hkv)) /
+                                   max(1, w.hkv * len(nd)))
+    out["needle_recall_mean"] = (sum(len(b[g] & nd) for g in range(w.hkv)) /
+                                 max(1, w.hkv * len(nd)))
+    out["what"] = ("pages chosen by both selectors over pages chosen (overlap), and the share "
+                   "of the needle pages each selection contains, summed over KV heads")
+    del scratch
+    return out
+
+
 def context_build(pca, torch, pool, table, x, w, reps):
     """Write the whole prior context into the pool (kv_append) and summarise its pages
     (page_summarize), each timed on its own stream with HIP events after evicting the
@@ -564,6 +627,14 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": None, "traffic": None, "ms_per_launch": dom_ms}
 
+    selector = None
+    if sparse:
+        selector = mean_selector_leg(pca, torch, w, pool, table, q, sel, count, x["needles"])
+        hbm["page_summarize_mean"] = selector.pop("page_summarize_mean")
+        hbm["select_pages_mean"] = selector.pop("select_pages_mean")
+        log(f"[bench] selectors agree on {100 * selector['overlap']:.1f} % of pages; needle recall "
+            f"min/max {selector['needle_recall_minmax']:.2f}, mean {selector['needle_recall_mean']:.2f}")
+
     offload = None
     if sparse and not args.no_offload:
         def attn_step():
@@ -599,6 +670,7 @@ def main():
         "kernels": breakdown,
         "hbm_kernels": hbm,
         "offload": offload,
+        "selector_variants": selector,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

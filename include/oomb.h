@@ -138,6 +138,26 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
                       float* score_out, int64_t score_stride, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Selector variant: the page representative read as a plain average of the page's keys
+ * (the explainer's "representative vector average", 2.D, read the other way).
+ * oomb_page_summarize_mean writes kmean[phys] (fp32 [N][D], 16-byte aligned, caller
+ * owned) for logical pages [first_page, first_page + n_pages) of every KV head: the
+ * keys widened to fp32 and summed from +0 in token order over the tokens below
+ * seq_len, then multiplied by fp32(1 / n_valid) (reciprocal in fp64); pages with no
+ * such token are left unchanged. oomb_select_pages_mean is oomb_select_pages with
+ *   score_j = stride-halving tree over d of fp32(qbar[d] * kmean[phys_j][d])
+ * (same qbar, same tree, same top-k rule, same workspace size); k_summary is not
+ * used. */
+int oomb_page_summarize_mean(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                             int64_t first_page, int64_t n_pages, int64_t seq_len, float* kmean,
+                             void* stream);
+int oomb_select_pages_mean(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                           const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                           int32_t n_q, int64_t t0, int32_t top_k, const float* kmean,
+                           int32_t* sel, int64_t sel_stride, int32_t* count, float* qbar_out,
+                           float* score_out, int64_t score_stride, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Chunk attention forward (explainer 2.A/2.B/2.D). Query i of the chunk sits at
  * position t0 + i; q head h uses KV head g = h / (Hq/Hkv). It attends to key t iff
  *   t <= t0 + i  and  page(t) is in  Sel_g U Local  (and t > t0 + i - window),

@@ -49,6 +49,7 @@ __all__ = [
     "query_summary", "page_scores", "top_k_pages", "select_pages",
     "attended_pages", "key_positions", "fwd", "bwd", "sweep",
     "copy_pages", "add_pages", "fetch_selected",
+    "summarize_mean", "page_scores_mean", "select_pages_mean",
 ]
 
 
@@ -185,6 +186,43 @@ def page_scores(qbar: np.ndarray, summary: torch.Tensor, table: torch.Tensor, g:
     return a[:, 0].copy()
 
 
+def summarize_mean(k_pool, table, kmean: np.ndarray, first_page: int, n_pages: int,
+                   seq_len: int) -> None:
+    """Mean-key summary (the other plain reading of the page representative, explainer
+    2.D: an average of the page's keys) of logical pages [first_page, first_page +
+    n_pages) of every KV head, into kmean[phys] (float32 [N, D]): the keys widened to
+    float32 and summed from +0 in token order, one float32 rounding per addition, then
+    multiplied by float32(1 / n_valid) (the reciprocal taken in float64). Pages with no
+    token below seq_len are left unchanged."""
+    P = k_pool.shape[1]
+    for g in range(table.shape[0]):
+        for lp in range(first_page, first_page + n_pages):
+            n_valid = min(P, seq_len - lp * P)
+            if n_valid <= 0:
+                continue
+            ph = int(table[g, lp])
+            rows = _as_f32(k_pool[ph, :n_valid])          # [n_valid, D] float32
+            s = np.zeros(rows.shape[1], np.float32)
+            for t in range(n_valid):
+                s = (s + rows[t]).astype(np.float32)
+            kmean[ph] = (s * np.float32(1.0 / n_valid)).astype(np.float32)
+
+
+def page_scores_mean(qbar: np.ndarray, kmean: np.ndarray, table: torch.Tensor, g: int,
+                     n_cand: int) -> np.ndarray:
+    """score_j = sum_d float32(qbar_d * kmean_jd) for logical pages j < n_cand, summed
+    by the same stride-halving tree over d as page_scores."""
+    if n_cand == 0:
+        return np.zeros(0, np.float32)
+    phys = table[g, :n_cand].long().numpy()
+    a = (qbar.astype(np.float32)[None, :] * kmean[phys].astype(np.float32)).astype(np.float32)
+    s = a.shape[1] // 2
+    while s >= 1:
+        a[:, :s] = a[:, :s] + a[:, s:2 * s]
+        s //= 2
+    return a[:, 0].copy()
+
+
 def top_k_pages(scores: np.ndarray, k: int) -> List[int]:
     """The k best pages by (score descending, logical id ascending), in ascending id
     order. Scores compare as IEEE values (-0 equals +0). k >= n keeps every page."""
@@ -202,6 +240,17 @@ def select_pages(q, summary, table, t0: int, page: int, group: int, top_k: int):
     for g in range(table.shape[0]):
         qb = query_summary(q, g, group)
         sc = page_scores(qb, summary, table, g, n_cand)
+        out.append((qb, sc, top_k_pages(sc, top_k)))
+    return out
+
+
+def select_pages_mean(q, kmean: np.ndarray, table, t0: int, page: int, group: int, top_k: int):
+    """As select_pages, with the scores of page_scores_mean."""
+    n_cand = t0 // page
+    out = []
+    for g in range(table.shape[0]):
+        qb = query_summary(q, g, group)
+        sc = page_scores_mean(qb, kmean, table, g, n_cand)
         out.append((qb, sc, top_k_pages(sc, top_k)))
     return out
 

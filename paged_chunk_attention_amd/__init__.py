@@ -17,9 +17,11 @@ from .binding import (  # noqa: F401
     kernel_timer,
     oomb_kv_append,
     oomb_page_summarize,
+    oomb_page_summarize_mean,
     oomb_paged_chunk_attn_bwd,
     oomb_paged_chunk_attn_fwd,
     oomb_select_pages,
+    oomb_select_pages_mean,
     select_workspace_bytes,
 )
 from ._lib import LIB_PATH, OombError, lib  # noqa: F401

@@ -42,6 +42,12 @@ SIGNATURES = {
     "oomb_select_pages": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32,
                                   c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p,
                                   c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
+    "oomb_page_summarize_mean": (c_int, [P_pool, c_void_p, c_int64, c_int64, c_int64, c_int64,
+                                         c_void_p, c_void_p]),
+    "oomb_select_pages_mean": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64,
+                                       c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int64,
+                                       c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_size_t,
+                                       c_void_p]),
     "oomb_paged_chunk_attn_fwd": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64,
                                           c_int32, c_int64, c_void_p, c_int64, c_void_p, c_int32,
                                           c_float,

@@ -161,6 +161,45 @@ def oomb_select_pages(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0:
     return sel, count
 
 
+def oomb_page_summarize_mean(pool: PagedPool, table: torch.Tensor, first_page: int, n_pages: int,
+                             seq_len: int, kmean: torch.Tensor, stream=None) -> None:
+    """Mean-key summaries (fp32 [num_pages, head_dim]) of the listed logical pages."""
+    _check_table(table, pool, "table")
+    if (kmean.dtype != torch.float32 or kmean.device != pool.device or not kmean.is_contiguous()
+            or tuple(kmean.shape) != (pool.num_pages, pool.head_dim)):
+        raise ValueError(f"kmean must be a contiguous fp32 [{pool.num_pages}, {pool.head_dim}] "
+                         f"tensor on {pool.device}")
+    call("oomb_page_summarize_mean", pool.ref(), _ptr(table), table.stride(0), first_page, n_pages,
+         seq_len, _ptr(kmean), _stream(stream))
+
+
+def oomb_select_pages_mean(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0: int,
+                           top_k: int, kmean: torch.Tensor, sel: Optional[torch.Tensor] = None,
+                           count: Optional[torch.Tensor] = None,
+                           qbar_out: Optional[torch.Tensor] = None,
+                           score_out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """As oomb_select_pages, scoring pages by qbar . kmean (the mean-key summaries)."""
+    _check_table(table, pool, "table")
+    hs, ts = _view(q, pool, pool.num_q_heads, "q")
+    if kmean.dtype != torch.float32 or kmean.device != pool.device or not kmean.is_contiguous():
+        raise ValueError("kmean must be a contiguous fp32 tensor on the pool's device")
+    n_q = q.shape[1]
+    n_cand = t0 // pool.page_size
+    k = max(0, min(top_k, n_cand))
+    if sel is None:
+        sel = torch.full((pool.num_kv_heads, max(k, 1)), -1, dtype=torch.int32, device=q.device)
+    if count is None:
+        count = torch.zeros(pool.num_kv_heads, dtype=torch.int32, device=q.device)
+    ws = _workspace(select_workspace_bytes(pool, n_q, t0), q.device, workspace)
+    score_stride = 0 if score_out is None else score_out.stride(0)
+    call("oomb_select_pages_mean", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts, n_q,
+         t0, top_k, _ptr(kmean), _ptr(sel), sel.stride(0), _ptr(count), _ptr(qbar_out),
+         _ptr(score_out), score_stride, _ptr(ws), ws.numel(), _stream(stream))
+    return sel, count
+
+
 def oomb_paged_chunk_attn_fwd(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0: int,
                               sel: Optional[torch.Tensor] = None,
                               count: Optional[torch.Tensor] = None,

@@ -268,7 +268,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 5; }
+int oomb_abi_version(void) { return 6; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -331,14 +331,17 @@ size_t oomb_select_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t
   return total;
 }
 
-int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
-                      const void* q, int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q,
-                      int64_t t0, int32_t top_k, int32_t* sel, int64_t sel_stride,
-                      int32_t* count, float* qbar_out, float* score_out, int64_t score_stride,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+// Page selection from min/max summaries (kmean == nullptr) or mean-key summaries.
+static int select_common(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                         const void* q, int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q,
+                         int64_t t0, int32_t top_k, const float* kmean, int32_t* sel,
+                         int64_t sel_stride, int32_t* count, float* qbar_out, float* score_out,
+                         int64_t score_stride, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   oomb::SelectArgs a{};
-  int st = check_pool(pool, &a.pool, true, false);
+  int st = check_pool(pool, &a.pool, kmean == nullptr, false);
   if (st) return st;
+  a.kmean = kmean;
   ChunkGeom cg;
   if ((st = check_chunk(a.pool, n_q, t0, &cg))) return st;
   if (top_k < 0) return fail(OOMB_ERR_INVALID, "top_k must be >= 0");
@@ -377,6 +380,51 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
   a.nb = static_cast<int>(nb);
   a.inv = static_cast<float>(1.0 / (static_cast<double>(G) * n_q));
   return hip_status(oomb::launch_select(a, static_cast<hipStream_t>(stream)), "select_pages");
+}
+
+int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                      const void* q, int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q,
+                      int64_t t0, int32_t top_k, int32_t* sel, int64_t sel_stride,
+                      int32_t* count, float* qbar_out, float* score_out, int64_t score_stride,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, top_k,
+                       nullptr, sel, sel_stride, count, qbar_out, score_out, score_stride,
+                       workspace, workspace_bytes, stream);
+}
+
+int oomb_select_pages_mean(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                           const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                           int32_t n_q, int64_t t0, int32_t top_k, const float* kmean,
+                           int32_t* sel, int64_t sel_stride, int32_t* count, float* qbar_out,
+                           float* score_out, int64_t score_stride, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (kmean == nullptr || (reinterpret_cast<uintptr_t>(kmean) & 3u))
+    return fail(OOMB_ERR_INVALID, "kmean must be a 4-byte aligned device pointer");
+  return select_common(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, top_k,
+                       kmean, sel, sel_stride, count, qbar_out, score_out, score_stride, workspace,
+                       workspace_bytes, stream);
+}
+
+int oomb_page_summarize_mean(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                             int64_t first_page, int64_t n_pages, int64_t seq_len, float* kmean,
+                             void* stream) {
+  oomb::SummarizeArgs a{};
+  int st = check_pool(pool, &a.pool, false, false);
+  if (st) return st;
+  if (kmean == nullptr || !aligned16(kmean))
+    return fail(OOMB_ERR_INVALID, "kmean must be a 16-byte aligned device pointer");
+  if (first_page < 0 || n_pages < 0 || seq_len < 0 || seq_len > kMaxPos)
+    return fail(OOMB_ERR_INVALID, "first_page / n_pages / seq_len out of range");
+  if (n_pages > 0x7FFFFFFF) return fail(OOMB_ERR_INVALID, "n_pages too large");
+  if (n_pages == 0) return ok();
+  if ((st = check_table(table, table_stride, first_page + n_pages, "table"))) return st;
+  a.table = table;
+  a.tstride = table_stride;
+  a.first_page = first_page;
+  a.n_pages = n_pages;
+  a.seq_len = seq_len;
+  a.kmean = kmean;
+  return hip_status(oomb::launch_page_mean(a, static_cast<hipStream_t>(stream)), "page_summarize_mean");
 }
 
 // Forward workspace: (matrix-core path, when query tiles are split into key ranges)

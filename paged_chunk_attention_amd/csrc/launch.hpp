@@ -39,6 +39,7 @@ struct SummarizeArgs {
   const int32_t* table;
   int64_t tstride;
   int64_t first_page, n_pages, seq_len;
+  float* kmean;     // mean-key summaries [N][D] fp32 (page_mean only)
 };
 
 struct SelectArgs {
@@ -60,6 +61,7 @@ struct SelectArgs {
   int n_cand;
   int nb;           // query blocks of 64 rows
   float inv;        // fp32(1 / (G * n_q)), rounded once from fp64
+  const float* kmean;  // mean-key summaries [N][D] (score = qbar . kmean), or nullptr (min/max)
 };
 
 struct AttnArgs {
@@ -136,6 +138,7 @@ hipError_t launch_fetch_selected(const FetchArgs& a, hipStream_t s);
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_page_summarize(const SummarizeArgs& a, hipStream_t s);
+hipError_t launch_page_mean(const SummarizeArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
 // Scalar kernels: any supported dtype / head_dim / page size.

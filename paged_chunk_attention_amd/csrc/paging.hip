@@ -5,7 +5,8 @@
 // Gradient Management": the cache is a pool of fixed-size pages and grows by
 // filling page slots, never by reallocating or copying what is already stored.
 // The min/max summary is the per-page representative for top-k retrieval
-// (explainer 2.D), in the form used by Quest (cited by the paper).
+// (explainer 2.D), in the form used by Quest (cited by the paper); the mean-key
+// summary is the other plain reading of that representative (an average).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "profiling.hpp"
@@ -156,6 +157,82 @@ __global__ __launch_bounds__(256) void page_summarize_kernel(SummarizeArgs a) {
       reinterpret_cast<uint32_t*>(out)[D + d] = static_cast<uint32_t>(order_key_f32(static_cast<uint32_t>(hi)));
     }
   }
+}
+
+// Mean-key summary of a page (the other reading of the page representative, a plain
+// average): kmean[ph][d] = fp32(sum) * fp32(1 / n_valid), the sum taken in fp32 from
+// +0 over the page's valid tokens in slot order, 1 / n_valid rounded once from fp64.
+// Thread t of the grid owns page blockIdx.x * 16 + t / (D / 8) of KV head blockIdx.y
+// and head dimensions 8 (t % (D / 8)) .. +7: one 16-byte load per token, sixteen
+// issued together (branch-free, so that no load waits for the previous one), each
+// dimension summed strictly in token order.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void page_mean_kernel(SummarizeArgs a) {
+  const int D = a.pool.D;
+  const int lpp = D / 8;  // threads per page
+  const int64_t lp = a.first_page + static_cast<int64_t>(blockIdx.x) * (256 / lpp) + threadIdx.x / lpp;
+  const int d0 = 8 * (threadIdx.x % lpp);
+  const int g = blockIdx.y;
+  if (lp >= a.first_page + a.n_pages) return;
+  const int P = a.pool.P;
+  const int64_t n_valid64 = a.seq_len - (lp << a.pool.log2p);
+  if (n_valid64 <= 0) return;
+  const int n_valid = n_valid64 < P ? static_cast<int>(n_valid64) : P;
+  const int64_t ph = a.table[g * a.tstride + lp];
+  if (ph < 0 || ph >= a.pool.N) return;
+  const int64_t page0 = (ph << a.pool.log2p) * D + d0;  // element offset of token 0
+  constexpr int kGroup = 16;
+  float s[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s[c] = 0.0f;
+  for (int t0 = 0; t0 < n_valid; t0 += kGroup) {
+    float x[kGroup][8];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const bool live = t0 + u < n_valid;
+      const int64_t off = page0 + static_cast<int64_t>(live ? t0 + u : 0) * D;
+      if (kBf16) {
+        const u32x4 w = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.pool.k_pool) + off));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[u][2 * c] = live ? __uint_as_float(w[c] << 16) : 0.0f;
+          x[u][2 * c + 1] = live ? __uint_as_float(w[c] & 0xFFFF0000u) : 0.0f;
+        }
+      } else {
+        const float* src = static_cast<const float*>(a.pool.k_pool) + off;
+        const f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+        const f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + 4));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[u][c] = live ? lo[c] : 0.0f;
+          x[u][4 + c] = live ? hi[c] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      if (t0 + u < n_valid) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c] = s[c] + x[u][c];
+      }
+    }
+  }
+  const float inv = static_cast<float>(1.0 / static_cast<double>(n_valid));
+  float* dst = a.kmean + ph * D + d0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dst[c] = s[c] * inv;
+}
+
+hipError_t launch_page_mean(const SummarizeArgs& a, hipStream_t s) {
+  if (a.n_pages <= 0) return hipSuccess;
+  const int pages_per_block = 256 / (a.pool.D / 8);
+  dim3 grid(static_cast<unsigned>((a.n_pages + pages_per_block - 1) / pages_per_block), a.pool.Hkv);
+  if (a.pool.dtype == 0)
+    OOMB_LAUNCH("page_mean", page_mean_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    OOMB_LAUNCH("page_mean", page_mean_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_page_summarize(const SummarizeArgs& a, hipStream_t s) {

@@ -146,6 +146,38 @@ __global__ __launch_bounds__(256) void page_score_kernel(SelectArgs a) {
   if (lane == 0) a.score[g * a.score_stride + j] = score;
 }
 
+// Mean-key scores: score_j = sum_d fp32(qbar_d * kmean_jd), the products rounded to
+// fp32 and summed by the same stride-halving tree over d as the min/max scores.
+template <int D>
+__global__ __launch_bounds__(256) void page_score_mean_kernel(SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int g = blockIdx.y;
+  if (j >= a.n_cand) return;
+  const int64_t ph = a.table[g * a.tstride + j];
+  float score;
+  if (ph < 0 || ph >= a.pool.N) {
+    score = -__builtin_inff();
+  } else {
+    constexpr int R = D / 64;
+    float e[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int d = lane + 64 * r;
+      e[r] = a.qbar[g * D + d] * a.kmean[ph * D + d];
+    }
+    float acc = e[0];
+    if (R == 2) acc = e[0] + e[1];  // tree level s = 64: a[d] + a[d + 64]
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+      const float other = __shfl_xor(acc, s, 64);
+      acc = acc + other;
+    }
+    score = acc;
+  }
+  if (lane == 0) a.score[g * a.score_stride + j] = score;
+}
+
 // Order-preserving unsigned key of an fp32 score (-0 folded onto +0, NaN lowest).
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -309,6 +341,11 @@ static void launch_scores(const SelectArgs& a, hipStream_t s) {
   while (n2 < a.nb) n2 <<= 1;
   OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
   dim3 g3((a.n_cand + 3) / 4, a.pool.Hkv);
+  if (a.kmean != nullptr) {
+    if (D == 128) OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<128>, g3, dim3(256), 0, s, a);
+    else OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<64>, g3, dim3(256), 0, s, a);
+    return;
+  }
   if (bf && D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<true, 128>), g3, dim3(256), 0, s, a);
   else if (bf) OOMB_LAUNCH("page_score", (page_score_kernel<true, 64>), g3, dim3(256), 0, s, a);
   else if (D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<false, 128>), g3, dim3(256), 0, s, a);

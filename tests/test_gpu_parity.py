@@ -5,9 +5,12 @@ seconds that still span several tiles and ragged tails.
 Bars: bit-exact for pages, summaries, query summaries, scores and selections;
 max-abs 2e-2 and relative-L2 1e-2 for bf16 outputs (O, dQ, dK, dV), 1e-5 for fp32.
 """
+import numpy as np
 import pytest
 import torch
 
+import oracle as orc
+import paged_chunk_attention_amd as pca
 import workloads as wl
 from tests.gpu_harness import DEV, bits, compare, log, run_chunk_parity
 
@@ -200,3 +203,54 @@ def test_strided_views_match_contiguous():
     assert torch.equal(s1, s2) and torch.equal(c1, c2)
     assert torch.equal(bits(o1), bits(o2.contiguous())) and torch.equal(l1, l2)
     assert torch.equal(d1, d2)
+
+
+# selector variant: mean-key page representatives
+@pytest.mark.parametrize("kw", [
+    dict(name="mean_sel_k5", chunk=333, total=2597 + 333, top_k=5, needles=3),
+    dict(name="mean_sel_page16", hq=4, hkv=2, page=16, chunk=200, total=900, top_k=6),
+    dict(name="mean_sel_f32", hq=4, hkv=2, page=32, chunk=70, total=70 + 300, top_k=4,
+         dtype=torch.float32),
+    dict(name="mean_sel_d64", hq=6, hkv=2, d=64, page=16, chunk=50, total=50 + 400, top_k=7),
+])
+def test_mean_selector_bit_exact(kw):
+    """Mean-key summaries bit-exact on every page written (NaN sentinels elsewhere
+    untouched), then query summary, scores and selection bit-exact against the oracle,
+    and the forward with that selection within the bar."""
+    from tests.gpu_harness import GpuLayer, oracle_layer
+    w = _w(**kw)
+    x = wl.make_inputs(w)
+    t0, C, P = w.t0, w.chunk, w.page
+    log(f"[case {w.name}] mean-key selector hq={w.hq} hkv={w.hkv} d={w.d} page={P} t0={t0} "
+        f"top_k={w.top_k} dtype={w.dtype}")
+    L = GpuLayer(w, x)
+    L.append(x["k"][:, :t0 + C], x["v"][:, :t0 + C], 0)
+    n_pages = -(-(t0 + C) // P)
+    N = L.pool.k.shape[0]
+    kmean = torch.full((N, w.d), float("nan"), dtype=torch.float32, device=DEV)
+    pca.oomb_page_summarize_mean(L.pool, L.table, 0, n_pages, t0 + C, kmean)
+    q = x["q"].to(DEV)
+    n_cand = t0 // P
+    qbar = torch.empty(w.hkv, w.d, dtype=torch.float32, device=DEV)
+    score = torch.empty(w.hkv, max(n_cand, 1), dtype=torch.float32, device=DEV)
+    sel, count = pca.oomb_select_pages_mean(L.pool, L.table, q, t0, w.top_k, kmean, qbar_out=qbar,
+                                            score_out=score)
+    o, lse = pca.oomb_paged_chunk_attn_fwd(L.pool, L.table, q, t0, sel, count, w.scale)
+    torch.cuda.synchronize()
+
+    kp, vp, _ = oracle_layer(w, x, t0 + C)
+    ref_mean = np.full((kp.shape[0], w.d), np.nan, np.float32)
+    orc.summarize_mean(kp, x["table"], ref_mean, 0, n_pages, t0 + C)
+    got_mean = kmean.cpu().numpy()[:kp.shape[0]]
+    assert np.array_equal(got_mean.view(np.int32), ref_mean.view(np.int32)), "mean summaries differ"
+    ref = orc.select_pages_mean(x["q"], ref_mean, x["table"], t0, P, w.group, w.top_k)
+    osel = []
+    for g, (qb, sc, chosen) in enumerate(ref):
+        assert torch.equal(bits(qbar[g]), torch.from_numpy(qb).view(torch.int32)), f"qbar head {g}"
+        assert torch.equal(bits(score[g, :n_cand]), torch.from_numpy(sc).view(torch.int32)), \
+            f"scores head {g}"
+        assert int(count[g]) == len(chosen) and sel[g, :len(chosen)].tolist() == chosen, f"head {g}"
+        osel.append(chosen)
+    log(f"    mean summaries + selection bit-exact ({[len(s) for s in osel]} pages per head)")
+    O, _ = orc.fwd(x["q"], kp, vp, x["table"], t0, osel, w.scale)
+    compare("O", o, O, w.dtype)

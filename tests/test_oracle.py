@@ -622,3 +622,43 @@ def test_fetch_selected_then_gather_equals_host_pages():
         rest = [lp for lp in range(n_logical) if lp not in chosen]
         assert bool((table[g, rest] == -1).all())
 
+
+# ----------------------------------------------------------------------------- mean-key selector
+
+def test_summarize_mean_order_and_closed_forms():
+    """The mean-key summary sums in token order: 1 + 2^-24 + 2^-24 stays 1 in fp32 (ties
+    to even twice), so the mean of those three keys is fp32(1/3) exactly, where any
+    other order would give more. Constant keys average to themselves; a partial page
+    counts only tokens below seq_len; pages with none stay unchanged."""
+    P, D = 4, 8
+    k_pool = torch.zeros(3, P, D, dtype=torch.float32)
+    k_pool[0, 0, 0], k_pool[0, 1, 0], k_pool[0, 2, 0] = 1.0, 2.0 ** -24, 2.0 ** -24
+    k_pool[1] = 0.75
+    k_pool[2] = 5.0
+    table = torch.tensor([[0, 1, 2]], dtype=torch.int32)
+    kmean = np.full((3, D), -7.0, np.float32)
+    orc.summarize_mean(k_pool, table, kmean, 0, 1, seq_len=3)      # page 0: 3 valid tokens
+    orc.summarize_mean(k_pool, table, kmean, 1, 2, seq_len=2 * P)  # page 1 full, page 2 none
+    assert kmean[0, 0] == np.float32(1.0 / 3.0)
+    assert kmean[0, 0] < np.float32(1.0 + 2.0 ** -23) * np.float32(1.0 / 3.0)
+    assert bool((kmean[1] == np.float32(0.75)).all())  # 4 tokens of 0.75 (page 1 full)
+    assert bool((kmean[2] == np.float32(-7.0)).all())  # page 2 starts at seq_len: unchanged
+
+
+def test_page_scores_mean_equals_minmax_with_equal_bounds():
+    """With kmin = kmax = kmean the min/max score takes the same products through the
+    same tree, so the two score functions agree bitwise (pinning the mean score to the
+    golden-pinned min/max one); constant means give qbar_0 * c exactly."""
+    rng = np.random.default_rng(5)
+    D, n = 64, 37
+    qbar = rng.standard_normal(D).astype(np.float32)
+    kmean = rng.standard_normal((n, D)).astype(np.float32)
+    table = torch.arange(n, dtype=torch.int32)[None]
+    summ = torch.from_numpy(np.stack([kmean, kmean], 1))
+    assert np.array_equal(orc.page_scores_mean(qbar, kmean, table, 0, n),
+                          orc.page_scores(qbar, summ, table, 0, n))
+    cm = np.zeros((3, D), np.float32)
+    cm[:, 0] = [0.5, -2.0, 3.0]
+    got = orc.page_scores_mean(qbar, cm, torch.arange(3, dtype=torch.int32)[None], 0, 3)
+    assert got.tolist() == [qbar[0] * np.float32(c) for c in (0.5, -2.0, 3.0)]
+
