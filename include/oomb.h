@@ -138,6 +138,19 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
                       float* score_out, int64_t score_stride, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Rotary position embedding of a chunk's queries or keys by their absolute positions
+ * pos0 + i (the chunk-recurrent layer keeps every token's global position, explainer
+ * 2.A). x and y are [n_heads][n_tok][head_dim] views (element strides; y may equal x)
+ * of dtype OOMB_DTYPE_BF16 or _FP32; head_dim even. Pairs (d, d + head_dim/2):
+ *   y_d = x_d cos a - x_{d+h} sin a,  y_{d+h} = x_{d+h} cos a + x_d sin a,
+ *   a = (pos0 + i) * theta^(-2d/head_dim)   (h = head_dim/2; inverse != 0: a -> -a,
+ * the transpose, which is what the backward applies to gradients). Angles in fp64,
+ * rotation in fp32, one rounding to the dtype. */
+int oomb_rope(const void* x, int64_t x_head_stride, int64_t x_tok_stride, void* y,
+              int64_t y_head_stride, int64_t y_tok_stride, int32_t n_heads, int32_t n_tok,
+              int32_t head_dim, int32_t dtype, int64_t pos0, float theta, int32_t inverse,
+              void* stream);
+
 /* Selector variant: the page representative read as a plain average of the page's keys
  * (the explainer's "representative vector average", 2.D, read the other way).
  * oomb_page_summarize_mean writes kmean[phys] (fp32 [N][D], 16-byte aligned, caller

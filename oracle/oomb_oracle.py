@@ -49,7 +49,7 @@ __all__ = [
     "query_summary", "page_scores", "top_k_pages", "select_pages",
     "attended_pages", "key_positions", "fwd", "bwd", "sweep",
     "copy_pages", "add_pages", "fetch_selected",
-    "summarize_mean", "page_scores_mean", "select_pages_mean",
+    "summarize_mean", "page_scores_mean", "select_pages_mean", "rope",
 ]
 
 
@@ -479,4 +479,26 @@ def fetch_selected(k_pool, v_pool, table, host_k, host_v, host_table, sel, count
             k_pool[s] = host_k[hp]
             v_pool[s] = host_v[hp]
             table[g, lp] = s
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding of the chunk-recurrent layer (positions are global: a
+# chunk's tokens keep their absolute positions, explainer 2.A).
+# ---------------------------------------------------------------------------
+
+def rope(x: torch.Tensor, pos0: int, theta: float = 10000.0, inverse: bool = False) -> torch.Tensor:
+    """float64 rotation of x [heads, tokens, D] by a = (pos0 + i) * theta^(-2d/D) on the
+    pairs (d, d + D/2): y_d = x_d cos a - x_{d+D/2} sin a, y_{d+D/2} = x_{d+D/2} cos a
+    + x_d sin a; inverse rotates by -a."""
+    H, n, D = x.shape
+    half = D // 2
+    d = torch.arange(half, dtype=torch.float64)
+    inv_freq = torch.tensor(float(theta), dtype=torch.float64) ** (-2.0 * d / D)
+    ang = (pos0 + torch.arange(n, dtype=torch.float64))[:, None] * inv_freq[None, :]
+    c, s = torch.cos(ang), torch.sin(ang)
+    if inverse:
+        s = -s
+    xd = x.to(torch.float64)
+    lo, hi = xd[..., :half], xd[..., half:]
+    return torch.cat([lo * c - hi * s, hi * c + lo * s], dim=-1)
 

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     oomb_page_summarize_mean,
     oomb_paged_chunk_attn_bwd,
     oomb_paged_chunk_attn_fwd,
+    oomb_rope,
     oomb_select_pages,
     oomb_select_pages_mean,
     select_workspace_bytes,

@@ -161,6 +161,23 @@ def oomb_select_pages(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0:
     return sel, count
 
 
+def oomb_rope(x: torch.Tensor, pos0: int, theta: float = 10000.0, inverse: bool = False,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Rotary embedding of x [heads, tokens, head_dim] (bf16 or fp32, on the GPU) at
+    positions pos0 .. pos0 + tokens - 1; out may be x (in place)."""
+    if x.dim() != 3 or x.stride(2) != 1 or not x.is_cuda or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be a [heads, tokens, head_dim] bf16/fp32 GPU tensor, last dim contiguous")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.shape != x.shape or out.dtype != x.dtype or out.stride(2) != 1:
+        raise ValueError("out must match x")
+    dt = OOMB_DTYPE_BF16 if x.dtype == torch.bfloat16 else OOMB_DTYPE_FP32
+    call("oomb_rope", _ptr(x), x.stride(0), x.stride(1), _ptr(out), out.stride(0), out.stride(1),
+         x.shape[0], x.shape[1], x.shape[2], dt, pos0, float(theta), int(bool(inverse)),
+         _stream(stream))
+    return out
+
+
 def oomb_page_summarize_mean(pool: PagedPool, table: torch.Tensor, first_page: int, n_pages: int,
                              seq_len: int, kmean: torch.Tensor, stream=None) -> None:
     """Mean-key summaries (fp32 [num_pages, head_dim]) of the listed logical pages."""

@@ -268,7 +268,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 6; }
+int oomb_abi_version(void) { return 7; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -536,6 +536,29 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   float* dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dq);
   return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, oomb::dq_splits(a), dq_part, s),
                     "paged_chunk_attn_bwd");
+}
+
+int oomb_rope(const void* x, int64_t x_head_stride, int64_t x_tok_stride, void* y,
+              int64_t y_head_stride, int64_t y_tok_stride, int32_t n_heads, int32_t n_tok,
+              int32_t head_dim, int32_t dtype, int64_t pos0, float theta, int32_t inverse,
+              void* stream) {
+  if (dtype != OOMB_DTYPE_BF16 && dtype != OOMB_DTYPE_FP32)
+    return fail(OOMB_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 1024)
+    return fail(OOMB_ERR_INVALID, "head_dim %d must be even and at most 1024", head_dim);
+  if (n_heads < 0 || n_tok < 0) return fail(OOMB_ERR_INVALID, "negative sizes");
+  if (pos0 < 0 || pos0 + n_tok > kMaxPos) return fail(OOMB_ERR_INVALID, "positions out of range");
+  if (!(theta > 1.0f) || theta > 1e30f) return fail(OOMB_ERR_INVALID, "theta must be > 1 and finite");
+  if (x == nullptr || y == nullptr) return fail(OOMB_ERR_INVALID, "x or y is NULL");
+  const int es = dtype == OOMB_DTYPE_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) % es)
+    return fail(OOMB_ERR_INVALID, "x / y misaligned");
+  if (x_head_stride < 0 || x_tok_stride < 0 || y_head_stride < 0 || y_tok_stride < 0)
+    return fail(OOMB_ERR_INVALID, "negative strides");
+  if (n_heads == 0 || n_tok == 0) return ok();
+  oomb::RopeArgs a{x, x_head_stride, x_tok_stride, y, y_head_stride, y_tok_stride,
+                   n_heads, n_tok, head_dim, dtype, pos0, theta, inverse != 0};
+  return hip_status(oomb::launch_rope(a, static_cast<hipStream_t>(stream)), "rope");
 }
 
 int oomb_copy_pages(const void* src, void* dst, int64_t page_bytes, int64_t n_src_pages,

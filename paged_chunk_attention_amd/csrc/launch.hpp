@@ -136,6 +136,20 @@ hipError_t launch_copy_pages(const PageCopyArgs& a, hipStream_t s);
 hipError_t launch_add_pages(const PageCopyArgs& a, int zero_src, hipStream_t s);
 hipError_t launch_fetch_selected(const FetchArgs& a, hipStream_t s);
 
+// Rotary embedding of n_tok tokens of n_heads heads ([head][token][D] views x, y; y may
+// alias x), positions pos0 .. pos0 + n_tok - 1.
+struct RopeArgs {
+  const void* x;
+  int64_t x_hs, x_ts;
+  void* y;
+  int64_t y_hs, y_ts;
+  int n_heads, n_tok, D, dtype;
+  int64_t pos0;
+  float theta;
+  int inverse;
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
+
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_page_summarize(const SummarizeArgs& a, hipStream_t s);
 hipError_t launch_page_mean(const SummarizeArgs& a, hipStream_t s);

@@ -28,14 +28,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 6
+    assert lib.oomb_abi_version() == 7
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text

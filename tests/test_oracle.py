@@ -662,3 +662,27 @@ def test_page_scores_mean_equals_minmax_with_equal_bounds():
     got = orc.page_scores_mean(qbar, cm, torch.arange(3, dtype=torch.int32)[None], 0, 3)
     assert got.tolist() == [qbar[0] * np.float32(c) for c in (0.5, -2.0, 3.0)]
 
+
+# ----------------------------------------------------------------------------- rotary embedding
+
+def test_rope_closed_forms_and_invariants():
+    """Position 0 is the identity; a hand-computed rotation (D = 4, theta = 100: angles
+    p and p / 10); pair norms are kept; the inverse undoes the forward; dot products
+    depend on positions only through their difference."""
+    x = _rand((3, 5, 8), 31)
+    assert torch.allclose(orc.rope(x[:, :1], 0), x[:, :1].double(), atol=0, rtol=0)
+    v = torch.tensor([[[1.0, 2.0, 3.0, 4.0]]], dtype=F64)
+    got = orc.rope(v, 2, theta=100.0)[0, 0]
+    want = torch.tensor([1 * math.cos(2) - 3 * math.sin(2), 2 * math.cos(0.2) - 4 * math.sin(0.2),
+                         3 * math.cos(2) + 1 * math.sin(2), 4 * math.cos(0.2) + 2 * math.sin(0.2)],
+                        dtype=F64)
+    assert torch.allclose(got, want, atol=1e-14, rtol=0)
+    y = orc.rope(x, 12345)
+    pair = lambda t: t[..., :4] ** 2 + t[..., 4:] ** 2
+    assert torch.allclose(pair(y), pair(x.double()), atol=1e-12, rtol=0)
+    assert torch.allclose(orc.rope(y, 12345, inverse=True), x.double(), atol=1e-12, rtol=0)
+    q, k = _rand((1, 1, 8), 32), _rand((1, 1, 8), 33)
+    d1 = (orc.rope(q, 40) * orc.rope(k, 17)).sum()
+    d2 = (orc.rope(q, 1040) * orc.rope(k, 1017)).sum()
+    assert abs(float(d1 - d2)) < 1e-11
+
