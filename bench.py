@@ -415,6 +415,52 @@ def mean_selector_leg(pca, torch, w, pool, table, q, sel, count, needles, reps=3
     return out
 
 
+def layer_leg(pca, torch, tokens=65536, reps=2):
+    """One chunk-recurrent attention layer (paged_chunk_attention_amd.layer) at the
+    attention shape of the pages' model (hidden 3584, 28 query / 4 KV heads of 128,
+    rotary theta 1e6), chunks of 4096, pages of 128: forward and backward over `tokens`
+    tokens, dense and top-64. Reports the time of one layer step, tokens per second and
+    the share of it spent in the library's kernels (the rest is the projection GEMMs and
+    PyTorch glue)."""
+    from paged_chunk_attention_amd.layer import ChunkRecurrentAttention
+    hidden, hq, hkv, d, chunk, page = 3584, 28, 4, 128, 4096, 128
+    out = {}
+    for mode, top_k in (("dense", None), ("top64", 64)):
+        layer = ChunkRecurrentAttention(hidden, hq, hkv, d, page, chunk, tokens, top_k=top_k,
+                                        dtype=torch.bfloat16, device="cuda", seed=1)
+        g = torch.Generator(device="cuda").manual_seed(2)
+        x = torch.randn(tokens, hidden, generator=g, device="cuda").to(torch.bfloat16)
+        x.requires_grad_()
+        dy = torch.randn(tokens, hidden, generator=g, device="cuda").to(torch.bfloat16)
+
+        def step():
+            x.grad = None
+            for p_ in layer.parameters():
+                p_.grad = None
+            layer(x).backward(dy)
+
+        step()
+        torch.cuda.synchronize()
+        times, lib_ms = [], []
+        for _ in range(reps):
+            with pca.kernel_timer() as timer:
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                step()
+                torch.cuda.synchronize()
+                times.append((time.perf_counter() - t) * 1e3)
+            lib_ms.append(sum(ms for _, ms in timer.records))
+        ms = min(times)
+        out[mode] = {"ms_per_layer_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                     "library_kernel_ms": min(lib_ms), "library_share": min(lib_ms) / ms}
+        del layer, x, dy
+        torch.cuda.empty_cache()
+    out["what"] = (f"forward + backward of one attention layer over {tokens} tokens in chunks of "
+                   f"{chunk} (hidden {hidden}, {hq}/{hkv} heads of {d}, pages of {page}); "
+                   "library kernels timed with HIP events, the rest is GEMMs and glue")
+    return out
+
+
 def context_build(pca, torch, pool, table, x, w, reps):
     """Write the whole prior context into the pool (kv_append) and summarise its pages
     (page_summarize), each timed on its own stream with HIP events after evicting the
@@ -496,6 +542,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="chunk queries in the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layer", action="store_true",
+                    help="also time one chunk-recurrent attention layer (65,536 tokens)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offload measurements (sparse workloads)")
     ap.add_argument("--hbm-reps", type=int, default=3,
@@ -647,6 +695,13 @@ def main():
         log(f"[bench] offload: fetch {offload['fetch_selected']['GBps']:.1f} GB/s, overlap "
             f"overhead {100 * offload['overlap']['overhead']:.1f} %")
 
+    layer = None
+    if args.layer:
+        log("[bench] layer leg ...")
+        layer = layer_leg(pca, torch)
+        log(f"[bench] layer: dense {layer['dense']['tokens_per_s']:.0f} tok/s, top64 "
+            f"{layer['top64']['tokens_per_s']:.0f} tok/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         x_cpu = {"k": x["k"], "v": x["v"], "q": x["q"], "do": x["do"]}
@@ -671,6 +726,7 @@ def main():
         "hbm_kernels": hbm,
         "offload": offload,
         "selector_variants": selector,
+        "layer": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -34,6 +34,23 @@ from .binding import (
 )
 
 
+_MM_OUT_F32: Optional[bool] = None
+
+
+def _mm_f32(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """a @ b with bf16 operands, fp32 accumulation and an fp32 result (the plain bf16
+    product widened where the fp32-output form is not available). b is contiguous."""
+    global _MM_OUT_F32
+    if _MM_OUT_F32 is not False:
+        try:
+            c = torch.mm(a, b, out_dtype=torch.float32)
+            _MM_OUT_F32 = True
+            return c
+        except (NotImplementedError, RuntimeError, TypeError):
+            _MM_OUT_F32 = False
+    return torch.mm(a, b).float()
+
+
 class ChunkRecurrentAttention(torch.nn.Module):
     """Grouped-query self-attention over `max_tokens` tokens, trained chunk by chunk.
 
@@ -73,7 +90,6 @@ class ChunkRecurrentAttention(torch.nn.Module):
         self.pool = PagedPool(num_kv_heads * pages_per_head, page, head_dim, num_q_heads,
                               num_kv_heads, dtype, device)
         self.sels: List[Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]] = []
-        self.lses: List[torch.Tensor] = []
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return _ChunkRecurrentFn.apply(x, self.wq, self.wk, self.wv, self.wo, self)
@@ -105,8 +121,8 @@ class ChunkRecurrentAttention(torch.nn.Module):
 
 class _ChunkRecurrentFn(torch.autograd.Function):
     """Forward: chunks in order, nothing saved but x and the weights (plus each chunk's
-    selection and LSE, a few bytes per query). Backward: chunks in reverse with
-    recomputation; key/value gradients accumulate in the paged pool in place."""
+    page selection, k ids per KV head). Backward: chunks in reverse with recomputation;
+    key/value gradients accumulate in the paged pool in place."""
 
     @staticmethod
     def forward(ctx, x, wq, wk, wv, wo, layer: ChunkRecurrentAttention):
@@ -114,7 +130,7 @@ class _ChunkRecurrentFn(torch.autograd.Function):
         if T % C or T > layer.max_tokens:
             raise ValueError(f"sequence of {T} tokens does not fit chunks of {C} up to "
                              f"{layer.max_tokens}")
-        layer.sels, layer.lses = [], []
+        layer.sels = []
         y = torch.empty(T, wo.shape[1], dtype=x.dtype, device=x.device)
         with torch.no_grad():
             for t0 in range(0, T, C):
@@ -125,9 +141,8 @@ class _ChunkRecurrentFn(torch.autograd.Function):
                 sel = count = None
                 if layer.top_k is not None:
                     sel, count = oomb_select_pages(layer.pool, layer.table, q, t0, layer.top_k)
-                o, lse = layer._attend(q, t0, sel, count)
+                o, _ = layer._attend(q, t0, sel, count)
                 layer.sels.append((sel, count))
-                layer.lses.append(lse)
                 y[t0:t0 + C] = o.transpose(0, 1).reshape(C, -1) @ wo
         ctx.layer = layer
         ctx.save_for_backward(x, wq, wk, wv, wo)
@@ -141,10 +156,13 @@ class _ChunkRecurrentFn(torch.autograd.Function):
         pool = layer.pool
         pool.dk.zero_()
         pool.dv.zero_()
-        f32 = torch.float32
+        f32, cdt = torch.float32, x.dtype
         dx = torch.empty(T, x.shape[1], dtype=f32, device=x.device)
         dwq, dwk, dwv, dwo = (torch.zeros(w.shape, dtype=f32, device=x.device)
                               for w in (wq, wk, wv, wo))
+        # transposed weights, contiguous, once: every right operand below is contiguous
+        wqT, wkT, wvT, woT = (w.t().contiguous() for w in (wq, wk, wv, wo))
+        mm = _mm_f32 if cdt == torch.bfloat16 else torch.mm
         n_pg = C // P
         gk = torch.empty(layer.hkv * n_pg, P, D, dtype=f32, device=x.device)
         gv = torch.empty_like(gk)
@@ -157,9 +175,10 @@ class _ChunkRecurrentFn(torch.autograd.Function):
                 # recompute the chunk's activations just before they are needed
                 q, _, _ = layer._qkv(xc, t0)
                 o, lse = layer._attend(q, t0, sel, count)
-                dyc = dy[t0:t0 + C].to(f32)
-                dwo += o.transpose(0, 1).reshape(C, -1).to(f32).T @ dyc
-                do = layer._heads((dyc @ wo.to(f32).T).to(x.dtype), layer.hq)
+                dyc = dy[t0:t0 + C].contiguous()
+                o2 = o.transpose(0, 1).reshape(C, -1)
+                dwo += mm(o2.t(), dyc)
+                do = layer._heads(dyc @ woT, layer.hq)
                 sstride = -1 if sel is None else sel.stride(0)
                 ws = torch.empty(bwd_workspace_bytes(pool, C, t0, sstride, layer.window),
                                  dtype=torch.uint8, device=x.device)
@@ -170,18 +189,16 @@ class _ChunkRecurrentFn(torch.autograd.Function):
                 rows = layer._chunk_rows(t0)
                 oomb_copy_pages(pool.dk, gk, rows, dst)
                 oomb_copy_pages(pool.dv, gv, rows, dst)
-                dk = gk.view(layer.hkv, C, D)
-                dv = gv.view(layer.hkv, C, D)
                 # through the rotary embedding (a rotation: its transpose is the inverse)
                 dq = oomb_rope(dq, t0, layer.theta, inverse=True)
-                dk = oomb_rope(dk.contiguous(), t0, layer.theta, inverse=True)
-                dq2 = dq.transpose(0, 1).reshape(C, -1)
-                dk2 = dk.transpose(0, 1).reshape(C, -1)
-                dv2 = dv.transpose(0, 1).reshape(C, -1)
-                xf = xc.to(f32)
-                dwq += xf.T @ dq2
-                dwk += xf.T @ dk2
-                dwv += xf.T @ dv2
-                dx[t0:t0 + C] = dq2 @ wq.to(f32).T + dk2 @ wk.to(f32).T + dv2 @ wv.to(f32).T
+                dk = oomb_rope(gk.view(layer.hkv, C, D), t0, layer.theta, inverse=True)
+                dq2 = dq.transpose(0, 1).reshape(C, -1).to(cdt)
+                dk2 = dk.transpose(0, 1).reshape(C, -1).to(cdt)
+                dv2 = gv.view(layer.hkv, C, D).transpose(0, 1).reshape(C, -1).to(cdt)
+                xt = xc.t()
+                dwq += mm(xt, dq2)
+                dwk += mm(xt, dk2)
+                dwv += mm(xt, dv2)
+                dx[t0:t0 + C] = mm(dq2, wqT) + mm(dk2, wkT) + mm(dv2, wvT)
         return (dx.to(x.dtype), dwq.to(wq.dtype), dwk.to(wk.dtype), dwv.to(wv.dtype),
                 dwo.to(wo.dtype), None)
