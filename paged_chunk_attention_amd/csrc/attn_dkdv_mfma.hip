@@ -53,6 +53,8 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   const int k0 = kb * KPW;
   if (kb >= nkb || k0 >= km.n_keys) return;  // uniform: block past this head's attended keys
   const float c2 = a.scale * kLog2e;
+  // Pairs with q - k >= wlim lie outside the window (none without one).
+  const int wlim = km.window > 0 ? km.window : 0x7FFFFFFF;
 
   // This lane's key (column of S = Q K^T) and its K (P wave) or V (D wave) fragments.
   const int kidx = k0 + 32 * kg + col;
@@ -124,11 +126,22 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
                                 : static_cast<const uint16_t*>(a.dout) + hq * a.do_hs;
     const int64_t ts = pwave ? a.q_ts : a.do_ts;
     uint16_t* dst = pwave ? qd : dd;
+    if (q0 + QTB <= a.n_q) {  // uniform: the whole tile is in range
+      const int64_t lo = static_cast<int64_t>(lane >> 4) * ts + c8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = 16 * i + 4 * kg;
-      const int qi = q0 + r0 + (lane >> 4);
-      if (qi < a.n_q) lds_dma16(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = 16 * i + 4 * kg;
+        lds_dma16(src + static_cast<int64_t>(q0 + r0) * ts + lo, dst + r0 * D);
+      }
+    } else {
+      // The last, partial tile: rows past the end reload the last row. Their data is
+      // finite and their LSE +inf, so their P (and dS) is exactly zero.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = 16 * i + 4 * kg;
+        const int qi = min(q0 + r0 + (lane >> 4), a.n_q - 1);
+        lds_dma16(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
+      }
     }
     if (kg == 0) {  // raw loads: arithmetic here would wait for the whole prefetch
       const int qi = q0 + lane;
@@ -163,7 +176,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
     const int q0 = (qt0 + u % tph) * QTB;
     // Some pair of this tile hidden for this lane's key (in its future, or past the end
     // of a window: q - kpos >= window, written so that kpos = INT_MAX cannot overflow)?
-    const bool wmask = __any(kpos > a.t0 + q0 || (km.window > 0 && a.t0 + q0 + QTB - 1 - kpos >= km.window));
+    const bool wmask = __any(kpos > a.t0 + q0 || a.t0 + q0 + QTB - 1 - kpos >= wlim);
     FragOffsets o = fo;
     o.opaque();
     // S = Q K^T for both 32-query halves, the two chains interleaved, fragments read one
@@ -178,24 +191,39 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
       sa[us] = mfma(fq, kvf[kk], sa[us]);
       fq = nq;
     }
+    // P = exp2(S c - LSE log2 e) in place; register 8s + j of half us holds query row
+    // rA + 8(j/4) + (j%4), j = 0..7, rA = 32us + 16s + 4h2.
+#pragma unroll
+    for (int us = 0; us < 2; ++us)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int rA = 32 * us + 16 * s + 4 * h2;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse + rA);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse + rA + 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          sa[us][8 * s + j] = fast_exp2(__builtin_fmaf(sa[us][8 * s + j], c2, -(j < 4 ? l0[j] : l1[j - 4])));
+      }
+    // One uniform branch per tile, branch-free inside: the masked pairs of tiles on the
+    // block's diagonal (or window edge) get P = 0.
+    if (wmask) {
+#pragma unroll
+      for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qpos = a.t0 + q0 + 32 * us + 16 * (r >> 3) + 4 * h2 + 8 * ((r >> 2) & 1) + (r & 3);
+          const bool hide = (kpos > qpos) | (qpos - kpos >= wlim);
+          sa[us][r] = hide ? 0.0f : sa[us][r];
+        }
+    }
     bf16x8 pb[2][2];
 #pragma unroll
     for (int us = 0; us < 2; ++us)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        // query rows rA + 8(j/4) + (j%4), j = 0..7, rA = 32us + 16s + 4h2
-        const int rA = 32 * us + 16 * s + 4 * h2;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse + rA);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse + rA + 8);
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float lse_r = j < 4 ? l0[j] : l1[j - 4];
-          float pv = fast_exp2(__builtin_fmaf(sa[us][8 * s + j], c2, -lse_r));
-          const int qpos = a.t0 + q0 + rA + 8 * (j >> 2) + (j & 3);
-          if (wmask && (kpos > qpos || (km.window > 0 && qpos - kpos >= km.window))) pv = 0.0f;
-          p[j] = pv;
-        }
+        for (int j = 0; j < 8; ++j) p[j] = sa[us][8 * s + j];
         pb[us][s] = pack8(p);
         f32x4* px = s_p + ((xp * 4 + kg) * 8 + 2 * (2 * us + s)) * 64 + lane;
         px[0] = f32x4{p[0], p[1], p[2], p[3]};

@@ -139,22 +139,26 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
           fk = nk;
           fv = nv;
         }
-        // dS^T = P^T (dP^T - Delta), P = exp2(S c - lse log2 e); masked keys give 0.
+        // dS^T = P^T (dP^T - Delta), P = exp2(S c - lse log2 e); masked keys give 0
+        // (one uniform branch, branch-free inside).
         bf16x8 ta[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) ta[db] = tr_frag_at(kt, 32 * sub, 0, o, db);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = fast_exp2(__builtin_fmaf(st[r], c2, -lse2));
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            st[r] = ((key > klim) | (key < klo)) ? 0.0f : st[r];
+          }
+        }
         bf16x8 dsb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           float ds[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = 8 * s + j;
-            float p = fast_exp2(__builtin_fmaf(st[r], c2, -lse2));
-            const int key = b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (mask && (key > klim || key < klo)) p = 0.0f;
-            ds[j] = p * (dpt[r] - delta);
-          }
+          for (int j = 0; j < 8; ++j) ds[j] = st[8 * s + j] * (dpt[8 * s + j] - delta);
           dsb[s] = pack8(ds);
         }
         // dQ^T += K^T dS^T, the second k-step's fragments read during the first's products.

@@ -177,7 +177,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (key > klim || key < klo) st[sub][r] = -__builtin_inff();
+          st[sub][r] = ((key > klim) | (key < klo)) ? -__builtin_inff() : st[sub][r];
         }
     }
     // Row maximum: four independent chains, then the other half-wave's rows.

@@ -197,9 +197,10 @@ struct Keys {
   __device__ __forceinline__ int pos_linear(int a) const {
     return (first_local << log2p) + (a - local0);
   }
-  // Does attended key a exist and lie before the end of the sequence?
+  // Does attended key a exist and lie before the end of the sequence? (Bitwise, so that
+  // per-lane uses compile to compares and selects, not branches.)
   __device__ __forceinline__ bool in_seq(int a) const {
-    return a < n_keys && (a < local0 || (first_local << log2p) + (a - local0) < kv_end);
+    return (a < n_keys) & ((a < local0) | ((first_local << log2p) + (a - local0) < kv_end));
   }
 };
 
@@ -337,7 +338,7 @@ struct KeyStage {
       const int a = st * ROWS + r0;
       const int p = __builtin_amdgcn_readfirstlane(ph[i]);
       const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
-      const bool ok = p >= 0 && k.in_seq(a + (lane >> 4));
+      const bool ok = (p >= 0) & k.in_seq(a + (lane >> 4));
       lds_dma16((ok ? pool + base : g_zero_rows) + lo, t + r0 * D);
     }
   }
