@@ -19,7 +19,10 @@ namespace mf {
 // Each wave carries half of the state of one owner of 32 keys, so two fit on a SIMD,
 // and the hardware overlaps one wave's softmax arithmetic with the other's products.
 // The D wave's order (dS and dK of the previous tile, then dP of this one) puts its
-// 32 products under the P wave's softmax. Query tiles arrive by DMA one tile ahead:
+// 32 products under the P wave's softmax, and it issues them at raised wave priority,
+// so that the SIMD's arbiter feeds the matrix core first whenever both waves are ready
+// (measured 4% faster than equal priorities; raising the P wave's products too gained
+// less). Query tiles arrive by DMA one tile ahead:
 // Q in three buffers (the D wave still reads the previous tile's), dO in two; the
 // buffers' roles are static in each sixth of the unrolled loop.
 constexpr int DKV_WAVES = 8;
@@ -272,6 +275,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         }
       // dK += dS^T Q (the scale is applied once, at the end).
       bf16x8 ft = tr_frag_at(qp, 0, 0, o, 0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int nb = i & 3, s = (i >> 2) & 1, us = i >> 3;
@@ -283,12 +287,14 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         acc[nb] = mfma(dsb[us][s], ft, acc[nb]);
         ft = nt;
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (cur) {
       // dP = dO V^T for both halves, interleaved, fragments one step ahead.
       dpa[0] = f32x16{};
       dpa[1] = f32x16{};
       bf16x8 fd = row_frag_at(dt, 0, o, 0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int us = i & 1, kk = i >> 1;
@@ -297,6 +303,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         dpa[us] = mfma(fd, kvf[kk], dpa[us]);
         fd = nd;
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
