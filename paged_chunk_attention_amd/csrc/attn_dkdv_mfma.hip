@@ -12,7 +12,7 @@ namespace mf {
 // A workgroup is 8 wavefronts that own 128 keys, 32 per key group kg = wave % 4. The
 // two wavefronts of a key group share a SIMD and split its work by role:
 //  * the P wave holds K (B operand over d) and dV: per 64-query tile it computes
-//    S = Q K^T, P = exp(S - LSE) (masked), hands P (fp32) to its partner through LDS,
+//    S = Q K^T, P = exp(S - LSE) (masked), hands P (fp16) to its partner through LDS,
 //    and adds P^T dO into dV;
 //  * the D wave holds V and dK: it computes dP = dO V^T of a tile, and one tile later,
 //    once that tile's P has arrived, dS = P (dP - Delta) and dK += dS^T Q.
@@ -37,8 +37,12 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   // LSE (x log2 e) and Delta of the rows of the tile in the Q buffer of the same index
   __shared__ __attribute__((aligned(16))) float s_lse0[QTB], s_lse1[QTB], s_lse2[QTB];
   __shared__ __attribute__((aligned(16))) float s_del0[QTB], s_del1[QTB], s_del2[QTB];
-  // P (fp32) of one tile for each key group: [tile parity][kg][8 (2us + s) + 4 (j/4)..][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 s_p[2 * 4 * 8 * 64];
+  // P (fp16) of one tile for each key group: [tile parity][kg][2us + s][lane], eight
+  // values (j = 0..7) per lane. fp16 keeps 11 significant bits for P in [0, 1] (bf16
+  // keeps 8): the dS that the D wave forms from it is rounded to bf16 anyway, so the
+  // exchange adds a small fraction of that rounding, at half the LDS traffic of fp32.
+  // (A bf16 exchange doubled dS's rounding and failed the dK bar.)
+  __shared__ __attribute__((aligned(16))) h16x8 s_p[2 * 4 * 4 * 64];
   __shared__ int64_t s_grow[KPW];  // gradient pool row (or partial row) of each key, -1 = skip
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -228,9 +232,10 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = sa[us][8 * s + j];
         pb[us][s] = pack8(p);
-        f32x4* px = s_p + ((xp * 4 + kg) * 8 + 2 * (2 * us + s)) * 64 + lane;
-        px[0] = f32x4{p[0], p[1], p[2], p[3]};
-        px[64] = f32x4{p[4], p[5], p[6], p[7]};
+        h16x8 ph;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ph[j] = static_cast<_Float16>(p[j]);
+        s_p[((xp * 4 + kg) * 4 + 2 * us + s) * 64 + lane] = ph;
       }
     // dV += P^T dO, transposed dO fragments read one step ahead.
     bf16x8 ft = tr_frag_at(dt, 0, 0, o, 0);
@@ -253,6 +258,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
                     const uint16_t* dt) __attribute__((always_inline)) {
     FragOffsets o = fo;
     o.opaque();
+    __builtin_amdgcn_s_setprio(1);
     if (prev) {
       bf16x8 dsb[2][2];
 #pragma unroll
@@ -262,20 +268,19 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
           const int rA = 32 * us + 16 * s + 4 * h2;
           const f32x4 d0 = *reinterpret_cast<const f32x4*>(delp + rA);
           const f32x4 d1 = *reinterpret_cast<const f32x4*>(delp + rA + 8);
-          const f32x4* px = s_p + ((xp * 4 + kg) * 8 + 2 * (2 * us + s)) * 64 + lane;
-          const f32x4 p0 = px[0], p1 = px[64];
+          const h16x8 ph = s_p[((xp * 4 + kg) * 4 + 2 * us + s) * 64 + lane];
           float ds[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float pv = j < 4 ? p0[j] : p1[j - 4];
+            const float pv = static_cast<float>(ph[j]);
             const float del_r = j < 4 ? d0[j] : d1[j - 4];
-            ds[j] = pv * (dpa[us][8 * s + j] - del_r);
+            // an fma with the fp16 operand widened in the instruction (v_fma_mix)
+            ds[j] = __builtin_fmaf(pv, dpa[us][8 * s + j] - del_r, 0.0f);
           }
           dsb[us][s] = pack8(ds);
         }
       // dK += dS^T Q (the scale is applied once, at the end).
       bf16x8 ft = tr_frag_at(qp, 0, 0, o, 0);
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int nb = i & 3, s = (i >> 2) & 1, us = i >> 3;
@@ -287,14 +292,12 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         acc[nb] = mfma(dsb[us][s], ft, acc[nb]);
         ft = nt;
       }
-      __builtin_amdgcn_s_setprio(0);
     }
     if (cur) {
       // dP = dO V^T for both halves, interleaved, fragments one step ahead.
       dpa[0] = f32x16{};
       dpa[1] = f32x16{};
       bf16x8 fd = row_frag_at(dt, 0, o, 0);
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int us = i & 1, kk = i >> 1;
@@ -303,8 +306,8 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
         dpa[us] = mfma(fd, kvf[kk], dpa[us]);
         fd = nd;
       }
-      __builtin_amdgcn_s_setprio(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Iteration it (0 .. n_it): DMA of tile it + 1 into set (qn, dn, lsen, deln); the P

@@ -38,6 +38,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 // Pack two fp32 into one dword of two bf16 (lo = a, hi = b), round to nearest even:
 // a single v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
