@@ -138,7 +138,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r0 = 16 * i + 4 * kg;
-        lds_dma16(src + static_cast<int64_t>(q0 + r0) * ts + lo, dst + r0 * D);
+        lds_dma16<true>(src + static_cast<int64_t>(q0 + r0) * ts + lo, dst + r0 * D);
       }
     } else {
       // The last, partial tile: rows past the end reload the last row. Their data is
@@ -147,7 +147,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
       for (int i = 0; i < 4; ++i) {
         const int r0 = 16 * i + 4 * kg;
         const int qi = min(q0 + r0 + (lane >> 4), a.n_q - 1);
-        lds_dma16(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
+        lds_dma16<true>(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
       }
     }
     if (kg == 0) {  // raw loads: arithmetic here would wait for the whole prefetch

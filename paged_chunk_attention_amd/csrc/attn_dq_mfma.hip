@@ -28,7 +28,7 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_v1[KB * D];
   __shared__ int s_page[PCAP];
   constexpr int NT = 64 * DQ_WAVES;
-  using Stage = KeyStage<KB, DQ_WAVES>;
+  using Stage = KeyStage<KB, DQ_WAVES, PCAP, true>;  // DMA from assembly
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, col = lane & 31;
