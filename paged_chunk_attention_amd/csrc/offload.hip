@@ -9,13 +9,14 @@
 // whatever its length, the page ids (a selection, a table) are read on the device with
 // no host round trip, and pinned host memory is read or written directly through its
 // device mapping. Each workgroup moves one page at a time with every lane holding four
-// 16-byte loads in flight before it stores, and 16 workgroups are enough to keep the
-// host link busy (~55 GB/s host to device). Transfers run beside attention kernels on
-// other streams, so they are made light for them: few workgroups (one per page slowed
-// a concurrent attention step by a third), few registers, and non-temporal accesses
-// that stream through the caches instead of evicting the attention's tiles (measured
-// overhead on a concurrent forward + backward: 32% -> ~3%). Ids outside their pool
-// are skipped.
+// 16-byte loads in flight before it stores, and 8 workgroups are enough to keep the
+// host link busy for plain copies (~55 GB/s host to device, ~50 device to host; 16
+// measured the same, and added into host memory 45 GB/s against 36). Transfers run
+// beside attention kernels on other streams, so they are made light for them: few
+// workgroups (one per page slowed a concurrent attention step by a third; 16 cost it
+// 7%, 8 cost 3%), few registers, and non-temporal accesses that stream through the
+// caches instead of evicting the attention's tiles. Ids outside their pool are
+// skipped.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "profiling.hpp"
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void fetch_selected_kernel(FetchArgs a) {
 
 // Workgroups for a list of n items: one per item up to kMaxBlocks (grid-stride loops
 // take the rest).
-constexpr int kMaxBlocks = 16;
+constexpr int kMaxBlocks = 8;
 unsigned list_grid(int64_t n) {
   return static_cast<unsigned>(n < kMaxBlocks ? (n > 0 ? n : 1) : kMaxBlocks);
 }
