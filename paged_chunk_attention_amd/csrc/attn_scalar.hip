@@ -106,6 +106,39 @@ __global__ __launch_bounds__(256) void delta_kernel(AttnArgs a) {
   if (lane == 0) a.delta[static_cast<int64_t>(h) * a.n_q + i] = s;
 }
 
+// The same with 16-byte loads: L = D * sizeof(T) / 16 lanes per row, 64 / L rows per
+// wave (bf16, D = 128: 16 lanes, 4 rows). Used when the rows are 16-byte aligned.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_vec_kernel(AttnArgs a) {
+  constexpr int EPL = 16 / static_cast<int>(sizeof(T));  // elements per lane
+  constexpr int L = D / EPL;
+  constexpr int RPW = 64 / L;
+  static_assert(L >= 1 && L <= 64 && 64 % L == 0, "row split");
+  const int lane = threadIdx.x & 63;
+  const int i = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / L;
+  const int h = blockIdx.y;
+  const int c = (lane % L) * EPL;
+  float s = 0.0f;
+  if (i < a.n_q) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + h * a.do_hs +
+                                                   static_cast<int64_t>(i) * a.do_ts + c);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.o) + h * a.o_hs +
+                                                   static_cast<int64_t>(i) * a.o_ts + c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (sizeof(T) == 2) {  // bf16: two values per word
+        s += __uint_as_float(x[k] << 16) * __uint_as_float(y[k] << 16);
+        s += __uint_as_float(x[k] & 0xFFFF0000u) * __uint_as_float(y[k] & 0xFFFF0000u);
+      } else {
+        s += __uint_as_float(x[k]) * __uint_as_float(y[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);  // within the row's L lanes
+  if (lane % L == 0 && i < a.n_q) a.delta[static_cast<int64_t>(h) * a.n_q + i] = s;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dq_scalar_kernel(AttnArgs a) {
   constexpr int R = D / 64;
@@ -217,17 +250,18 @@ __global__ __launch_bounds__(256) void dkdv_scalar_kernel(AttnArgs a) {
   }
 }
 
-#define OOMB_DISPATCH(KERNEL, GRID)                                                       \
+#define OOMB_DISPATCH_NAMED(NAME, KERNEL, GRID)                                           \
   do {                                                                                    \
     if (a.pool.dtype == 0 && a.pool.D == 128)                                             \
-      OOMB_LAUNCH(#KERNEL, (KERNEL<bf16_t, 128>), GRID, dim3(256), 0, s, a);                \
+      OOMB_LAUNCH(NAME, (KERNEL<bf16_t, 128>), GRID, dim3(256), 0, s, a);                   \
     else if (a.pool.dtype == 0)                                                           \
-      OOMB_LAUNCH(#KERNEL, (KERNEL<bf16_t, 64>), GRID, dim3(256), 0, s, a);                 \
+      OOMB_LAUNCH(NAME, (KERNEL<bf16_t, 64>), GRID, dim3(256), 0, s, a);                    \
     else if (a.pool.D == 128)                                                             \
-      OOMB_LAUNCH(#KERNEL, (KERNEL<float, 128>), GRID, dim3(256), 0, s, a);                 \
+      OOMB_LAUNCH(NAME, (KERNEL<float, 128>), GRID, dim3(256), 0, s, a);                    \
     else                                                                                  \
-      OOMB_LAUNCH(#KERNEL, (KERNEL<float, 64>), GRID, dim3(256), 0, s, a);                  \
+      OOMB_LAUNCH(NAME, (KERNEL<float, 64>), GRID, dim3(256), 0, s, a);                     \
   } while (0)
+#define OOMB_DISPATCH(KERNEL, GRID) OOMB_DISPATCH_NAMED(#KERNEL, KERNEL, GRID)
 
 hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.n_q + 3) / 4, a.pool.Hq);
@@ -236,8 +270,19 @@ hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_delta(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((a.n_q + 3) / 4, a.pool.Hq);
-  OOMB_DISPATCH(delta_kernel, grid);
+  // 16-byte rows (bases and strides) take the vector kernel
+  const int64_t epl = a.pool.dtype == 0 ? 8 : 4;
+  const bool vec = (reinterpret_cast<uintptr_t>(a.o) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(a.dout) % 16 == 0) && a.o_hs % epl == 0 &&
+                   a.o_ts % epl == 0 && a.do_hs % epl == 0 && a.do_ts % epl == 0;
+  if (vec) {
+    const int64_t rows_per_block = 4 * (64 / (a.pool.D / epl));
+    dim3 grid(static_cast<unsigned>((a.n_q + rows_per_block - 1) / rows_per_block), a.pool.Hq);
+    OOMB_DISPATCH_NAMED("delta_kernel", delta_vec_kernel, grid);
+  } else {
+    dim3 grid((a.n_q + 3) / 4, a.pool.Hq);
+    OOMB_DISPATCH(delta_kernel, grid);
+  }
   return hipGetLastError();
 }
 
