@@ -89,27 +89,11 @@ __global__ __launch_bounds__(256) void fwd_scalar_kernel(AttnArgs a) {
   if (lane == 0) a.lse[static_cast<int64_t>(h) * a.n_q + i] = (mx + __log2f(l)) * kLn2;
 }
 
-// Delta_i = sum_d dO_i[d] * O_i[d] in fp32; one wavefront per row.
+// Delta_i = sum_d dO_i[d] * O_i[d] in fp32, with 16-byte loads: L = D * sizeof(T) / 16 lanes per row, 64 / L
+// rows per wave (bf16, D = 128: 16 lanes, 4 rows). The boundary guarantees 16-byte
+// aligned rows (aligned pointers, strides in multiples of 16 bytes).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(AttnArgs a) {
-  constexpr int R = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int h = blockIdx.y;
-  if (i >= a.n_q) return;
-  float s = 0.0f;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    s += ld<T>(a.dout, h * a.do_hs + i * a.do_ts + lane + 64 * r) *
-         ld<T>(a.o, h * a.o_hs + i * a.o_ts + lane + 64 * r);
-  s = wave_sum(s);
-  if (lane == 0) a.delta[static_cast<int64_t>(h) * a.n_q + i] = s;
-}
-
-// The same with 16-byte loads: L = D * sizeof(T) / 16 lanes per row, 64 / L rows per
-// wave (bf16, D = 128: 16 lanes, 4 rows). Used when the rows are 16-byte aligned.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_vec_kernel(AttnArgs a) {
   constexpr int EPL = 16 / static_cast<int>(sizeof(T));  // elements per lane
   constexpr int L = D / EPL;
   constexpr int RPW = 64 / L;
@@ -250,18 +234,17 @@ __global__ __launch_bounds__(256) void dkdv_scalar_kernel(AttnArgs a) {
   }
 }
 
-#define OOMB_DISPATCH_NAMED(NAME, KERNEL, GRID)                                           \
+#define OOMB_DISPATCH(KERNEL, GRID)                                                       \
   do {                                                                                    \
     if (a.pool.dtype == 0 && a.pool.D == 128)                                             \
-      OOMB_LAUNCH(NAME, (KERNEL<bf16_t, 128>), GRID, dim3(256), 0, s, a);                   \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<bf16_t, 128>), GRID, dim3(256), 0, s, a);                \
     else if (a.pool.dtype == 0)                                                           \
-      OOMB_LAUNCH(NAME, (KERNEL<bf16_t, 64>), GRID, dim3(256), 0, s, a);                    \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<bf16_t, 64>), GRID, dim3(256), 0, s, a);                 \
     else if (a.pool.D == 128)                                                             \
-      OOMB_LAUNCH(NAME, (KERNEL<float, 128>), GRID, dim3(256), 0, s, a);                    \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<float, 128>), GRID, dim3(256), 0, s, a);                 \
     else                                                                                  \
-      OOMB_LAUNCH(NAME, (KERNEL<float, 64>), GRID, dim3(256), 0, s, a);                     \
+      OOMB_LAUNCH(#KERNEL, (KERNEL<float, 64>), GRID, dim3(256), 0, s, a);                  \
   } while (0)
-#define OOMB_DISPATCH(KERNEL, GRID) OOMB_DISPATCH_NAMED(#KERNEL, KERNEL, GRID)
 
 hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.n_q + 3) / 4, a.pool.Hq);
@@ -270,19 +253,10 @@ hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_delta(const AttnArgs& a, hipStream_t s) {
-  // 16-byte rows (bases and strides) take the vector kernel
-  const int64_t epl = a.pool.dtype == 0 ? 8 : 4;
-  const bool vec = (reinterpret_cast<uintptr_t>(a.o) % 16 == 0) &&
-                   (reinterpret_cast<uintptr_t>(a.dout) % 16 == 0) && a.o_hs % epl == 0 &&
-                   a.o_ts % epl == 0 && a.do_hs % epl == 0 && a.do_ts % epl == 0;
-  if (vec) {
-    const int64_t rows_per_block = 4 * (64 / (a.pool.D / epl));
-    dim3 grid(static_cast<unsigned>((a.n_q + rows_per_block - 1) / rows_per_block), a.pool.Hq);
-    OOMB_DISPATCH_NAMED("delta_kernel", delta_vec_kernel, grid);
-  } else {
-    dim3 grid((a.n_q + 3) / 4, a.pool.Hq);
-    OOMB_DISPATCH(delta_kernel, grid);
-  }
+  const int elems_per_lane = a.pool.dtype == 0 ? 8 : 4;
+  const int rows_per_block = 4 * (64 / (a.pool.D / elems_per_lane));
+  dim3 grid((a.n_q + rows_per_block - 1) / rows_per_block, a.pool.Hq);
+  OOMB_DISPATCH(delta_kernel, grid);
   return hipGetLastError();
 }
 
