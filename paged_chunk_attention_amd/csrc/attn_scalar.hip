@@ -89,9 +89,9 @@ __global__ __launch_bounds__(256) void fwd_scalar_kernel(AttnArgs a) {
   if (lane == 0) a.lse[static_cast<int64_t>(h) * a.n_q + i] = (mx + __log2f(l)) * kLn2;
 }
 
-// Delta_i = sum_d dO_i[d] * O_i[d] in fp32, with 16-byte loads: L = D * sizeof(T) / 16 lanes per row, 64 / L
-// rows per wave (bf16, D = 128: 16 lanes, 4 rows). The boundary guarantees 16-byte
-// aligned rows (aligned pointers, strides in multiples of 16 bytes).
+// Delta_i = sum_d dO_i[d] * O_i[d] in fp32, with 16-byte loads: L = D * sizeof(T) / 16
+// lanes per row, 64 / L rows per wave (bf16, D = 128: 16 lanes, 4 rows). The boundary
+// guarantees 16-byte aligned rows (aligned pointers, strides in multiples of 16 bytes).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(AttnArgs a) {
   constexpr int EPL = 16 / static_cast<int>(sizeof(T));  // elements per lane
