@@ -19,12 +19,13 @@ namespace mf {
 // Each wave carries half of the state of one owner of 32 keys, so two fit on a SIMD,
 // and the hardware overlaps one wave's softmax arithmetic with the other's products.
 // The D wave's order (dS and dK of the previous tile, then dP of this one) puts its
-// 32 products under the P wave's softmax, and it issues them at raised wave priority,
-// so that the SIMD's arbiter feeds the matrix core first whenever both waves are ready
-// (measured 4% faster than equal priorities; raising the P wave's products too gained
-// less). Query tiles arrive by DMA one tile ahead:
-// Q in three buffers (the D wave still reads the previous tile's), dO in two; the
-// buffers' roles are static in each sixth of the unrolled loop.
+// 32 products under the P wave's softmax, and it runs its tile at raised wave
+// priority, so that the SIMD's arbiter feeds the matrix core first whenever both waves
+// are ready (measured 4-5% faster than equal priorities; raising the P wave's products
+// too gained less). Query tiles arrive by DMA one tile ahead: Q in three buffers (the
+// D wave still reads the previous tile's), dO in two; the buffers' roles are static in
+// each sixth of the unrolled loop. P has to be exactly 0 for masked pairs and at most
+// about 1 elsewhere (it is exp(S - LSE) with the forward's LSE), which fp16 holds.
 constexpr int DKV_WAVES = 8;
 
 __global__ __launch_bounds__(64 * DKV_WAVES) __attribute__((amdgpu_waves_per_eu(2)))

@@ -1,11 +1,13 @@
 // Matrix-core backward of paged chunk attention, dQ pass: recompute P from the saved
 // log-sum-exp and dP = dO V^T per key block, then dQ^T += K^T dS^T.
 //
-// A workgroup is 4 wavefronts and owns 128 queries of one head (32 per wavefront, Q and
-// dO fragments held in registers); two workgroups share a CU, so each SIMD interleaves
-// two independent wavefronts. Key blocks of 64 rows (K and V) are copied global -> LDS
-// by DMA one block ahead, a fixed number of instructions per wave, into double buffers
-// whose roles are static in each half of the unrolled loop. The page ids a DMA needs
+// A workgroup is 8 wavefronts and owns 256 queries of one head (32 per wavefront, Q and
+// dO fragments held in registers), one workgroup per CU, two wavefronts per SIMD. The
+// key blocks are staged once for all 256 queries: LDS writes cost more than their share
+// of LDS bytes, and two 4-wave workgroups per CU (each staging its own blocks) ran 5%
+// slower. Key blocks of 64 rows (K and V) are copied global -> LDS by DMA one block
+// ahead, a fixed number of instructions per wave, into double buffers whose roles are
+// static in each half of the unrolled loop. The page ids a DMA needs
 // are read from LDS one block before it is issued, so the read has left the LDS queue
 // by then. Fragment reads are software-pipelined one step ahead of the products.
 //
@@ -17,7 +19,7 @@
 namespace oomb {
 namespace mf {
 
-constexpr int DQ_WAVES = 4;
+constexpr int DQ_WAVES = 8;
 constexpr int DQ_Q = 32 * DQ_WAVES;  // queries per workgroup
 
 __global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
@@ -219,9 +221,9 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, con
 // Key ranges per query tile of the dQ pass, chosen for load balance: a tile's work is
 // its key blocks (prior keys plus the chunk keys its last query sees). The ranges are
 // halved while the largest is more than a quarter of the average work per workgroup
-// slot (two per CU, 256 CUs, fixed so the choice and the result bits do not depend on
-// the device) and would stay at least 64 blocks, below which the partials' traffic and
-// each workgroup's start-up outweigh the balance gained.
+// slot (one per CU, 256 CUs, fixed so the choice and the result bits do not depend on
+// the device) and would stay at least 128 blocks, below which the partials' traffic and
+// each workgroup's start-up outweigh the balance gained (as in the forward).
 int dq_splits(const AttnArgs& a) {
   if (const int n = split_override("OOMB_DQ_SPLITS")) return n;
   const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
@@ -231,9 +233,9 @@ int dq_splits(const AttnArgs& a) {
     total += blocks;
     largest = blocks > largest ? blocks : largest;
   }
-  const double per_slot = total * a.pool.Hq / 512.0;
+  const double per_slot = total * a.pool.Hq / 256.0;
   int nk = 1;
-  while (nk < 4 && largest / nk > per_slot / 4.0 && largest / (2 * nk) >= 64.0) nk *= 2;
+  while (nk < 4 && largest / nk > per_slot / 4.0 && largest / (2 * nk) >= 128.0) nk *= 2;
   return nk;
 }
 
