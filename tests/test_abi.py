@@ -142,6 +142,29 @@ def test_fwd_workspace(lib):
     assert _fwd(lib, p, ws=0xA00010, wsb=need, **kw) == L.OOMB_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("name,n_q,t0,sel_stride,splits", [
+    ("sparse 1M", 4096, 1048576, 64, (1, 1, 4)),
+    ("dense 128K", 4096, 126976, -1, (4, 4, 1)),
+    ("sparse 4M", 8192, 4186112, 128, (2, 2, 2)),
+])
+def test_split_counts_at_the_workloads(lib, name, n_q, t0, sel_stride, splits):
+    """The host's load-balance rule picks, at the three benchmark workloads, the split
+    counts (forward key ranges, dQ key ranges, dK/dV query-stream splits) that measured
+    fastest; they show in the workspace sizes, which are a function of them alone."""
+    p = _pool()
+    n_fwd, n_dq, n_kv = splits
+    hq, hkv, d, page = 28, 4, 128, 128
+    n_cand = t0 // page
+    pages = (n_cand if sel_stride < 0 else min(sel_stride, n_cand)) + (-(-(t0 + n_q) // page) - n_cand)
+    keys = pages * page
+    a256 = lambda x: (x + 255) // 256 * 256
+    fwd = 0 if n_fwd == 1 else n_fwd * hq * n_q * (d + 2) * 4
+    bwd = (a256(hq * n_q * 4) + a256(0 if n_kv == 1 else n_kv * hkv * keys * 2 * d * 4)
+           + a256(0 if n_dq == 1 else n_dq * hq * n_q * d * 4))
+    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), n_q, t0, sel_stride, 0) == fwd, name
+    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), n_q, t0, sel_stride, 0) == bwd, name
+
+
 def test_window_arguments(lib):
     """A window is local attention: negative windows and windows combined with a page
     selection are rejected before any launch; the workspace queries reject them too."""
