@@ -31,6 +31,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # forward = S and PV; the dK/dV pass = S, dP (recomputed), dV, dK; the dQ pass is
 # credited with dQ only (its S and dP are recomputation).
 FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 2}
+# what each pass executes on the matrix cores (the dQ pass recomputes S and dP)
+HW_FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 6}
 
 
 def log(*a):
@@ -461,6 +463,78 @@ def layer_leg(pca, torch, tokens=65536, reps=2):
     return out
 
 
+def other_workload(pca, torch, name, steps=5, warmup=2):
+    """The same step (append, summarize, select when sparse, forward, backward) on another
+    benchmark workload, briefly: ms per step, model TFLOP/s, and each matrix-core pass's
+    time and hardware FLOP rate against the bf16 peak."""
+    import workloads as wl
+    w = wl.WORKLOADS[name]
+    P, C, t0 = w.page, w.chunk, w.t0
+    x = wl.make_inputs(w, device="cuda")
+    table, gtable = x["table"].to("cuda"), x["gtable"].to("cuda")
+    pool = pca.PagedPool(w.pool_pages, P, w.d, w.hq, w.hkv, w.dtype, "cuda")
+    pca.oomb_kv_append(pool, table, x["k"][:, :t0], x["v"][:, :t0], 0)
+    pca.oomb_page_summarize(pool, table, 0, t0 // P, t0)
+    k_new = x["k"][:, t0:t0 + C].contiguous()
+    v_new = x["v"][:, t0:t0 + C].contiguous()
+    q, do = x["q"], x["do"]
+    first_local = t0 // P
+    n_local = (t0 + C - 1) // P - first_local + 1
+    sparse = w.top_k is not None
+    k = max(0, min(w.top_k, t0 // P)) if sparse else 0
+    sel = torch.zeros(w.hkv, max(k, 1), dtype=torch.int32, device="cuda")
+    count = torch.zeros(w.hkv, dtype=torch.int32, device="cuda")
+    sstride = sel.stride(0) if sparse else -1
+    ws_sel = torch.empty(pca.select_workspace_bytes(pool, C, t0), dtype=torch.uint8, device="cuda")
+    ws_fwd = torch.empty(max(256, pca.fwd_workspace_bytes(pool, C, t0, sstride, w.window)),
+                         dtype=torch.uint8, device="cuda")
+    ws_bwd = torch.empty(pca.bwd_workspace_bytes(pool, C, t0, sstride, w.window),
+                         dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(w.hq, C, dtype=torch.float32, device="cuda")
+    dq = torch.empty(w.hq, C, w.d, dtype=torch.float32, device="cuda")
+
+    def step():
+        pca.oomb_kv_append(pool, table, k_new, v_new, t0)
+        pca.oomb_page_summarize(pool, table, first_local, n_local, t0 + C)
+        s_, c_ = (None, None)
+        if sparse:
+            s_, c_ = pca.oomb_select_pages(pool, table, q, t0, w.top_k, sel=sel, count=count,
+                                           workspace=ws_sel)
+        pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, s_, c_, w.scale, o=o, lse=lse,
+                                      workspace=ws_fwd, window=w.window)
+        pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, s_, c_, o, do, lse, w.scale,
+                                      dq=dq, workspace=ws_bwd, window=w.window)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    with pca.kernel_timer() as timer:
+        t_start = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    ms = elapsed * 1e3 / steps
+    pairs = attended_pairs(w, count.cpu().tolist() if sparse else None)
+    value = 14 * w.d * pairs / (ms * 1e-3) / 1e12
+    per = {}
+    for kname, kms in timer.records:
+        tot, n = per.get(kname, (0.0, 0))
+        per[kname] = (tot + kms, n + 1)
+    passes = {}
+    for kname, hw in HW_FLOP_PER_PAIR_D.items():
+        if kname in per:
+            kms = per[kname][0] / per[kname][1]
+            tf = hw * w.d * pairs / (kms * 1e-3) / 1e12
+            passes[kname] = {"ms_per_launch": kms, "hardware_TFLOPs": tf,
+                             "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
+    del pool, x
+    return {"ms_per_step": ms, "value": value, "unit": "TFLOP/s",
+            "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS, "steps": steps,
+            "attended_pairs": pairs, "passes": passes}
+
+
 def context_build(pca, torch, pool, table, x, w, reps):
     """Write the whole prior context into the pool (kv_append) and summarise its pages
     (page_summarize), each timed on its own stream with HIP events after evicting the
@@ -546,6 +620,8 @@ def main():
                     help="also time one chunk-recurrent attention layer (65,536 tokens)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offload measurements (sparse workloads)")
+    ap.add_argument("--also", default="dense128k",
+                    help="comma-separated other workloads to time briefly ('none' for none)")
     ap.add_argument("--hbm-reps", type=int, default=3,
                     help="cold-cache repetitions of the whole-context append and summarize")
     args = ap.parse_args()
@@ -702,6 +778,16 @@ def main():
         log(f"[bench] layer: dense {layer['dense']['tokens_per_s']:.0f} tok/s, top64 "
             f"{layer['top64']['tokens_per_s']:.0f} tok/s")
 
+    others = {}
+    for name in [n_ for n_ in args.also.split(",") if n_ not in ("", "none", w.name)]:
+        if name not in wl.WORKLOADS:
+            print(f"unknown workload {name!r} in --also", file=sys.stderr)
+            sys.exit(2)
+        log(f"[bench] {name} step ...")
+        others[name] = other_workload(pca, torch, name)
+        log(f"[bench] {name}: {others[name]['ms_per_step']:.3f} ms/step, "
+            f"{others[name]['value']:.1f} TFLOP/s ({others[name]['pct_mfma_peak']:.1f}% of peak)")
+
     cpu = None
     if not args.no_cpu_baseline:
         x_cpu = {"k": x["k"], "v": x["v"], "q": x["q"], "do": x["do"]}
@@ -727,6 +813,7 @@ def main():
         "offload": offload,
         "selector_variants": selector,
         "layer": layer,
+        "other_workloads": others or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
