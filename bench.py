@@ -77,38 +77,36 @@ def attended_pairs(w, counts):
     return total
 
 
-def cpu_baseline(w, x, table_cpu, sel_cpu, rows: int):
-    """The oracle (fp64 CPU) on a bounded sample of the same step: KV head 0, its
-    query heads, the last `rows` queries of the chunk, over exactly the keys those
-    queries attend in the full chunk."""
+def _oracle_sample_head(w, x, sel_head, g: int, rows: int):
+    """Oracle fwd+bwd for KV head g's query heads over the last `rows` chunk queries and
+    exactly the keys they attend in the full chunk; returns (seconds, pairs)."""
     import torch
     import oracle as orc
 
     P, C, t0, G = w.page, w.chunk, w.t0, w.group
-    rows = min(rows, C)
     t0s = t0 + C - rows
     shift = 0
     if w.window > 0:
         # local attention depends on positions only through p - t: renumber the pages
         # from the first one the sample's windows reach, so the oracle scans no others
         shift = max(0, t0s - w.window + 1) // P * P
-    sel0 = list(sel_cpu[0]) if sel_cpu is not None else list(range(shift // P, t0 // P))
+    sel0 = list(sel_head) if sel_head is not None else list(range(shift // P, t0 // P))
     # the chunk's own pages before the sample are selected pages for the sample
     sel_s = sorted(set(sel0) | set(range(t0 // P, t0s // P)))
     pages = orc.attended_pages(t0s, rows, P, sel_s)
-    # compact oracle pool holding only the attended pages of head 0
+    # compact oracle pool holding only the attended pages of this head
     tab = torch.zeros(1, (t0 + C) // P + 1, dtype=torch.int32)
     for i, lp in enumerate(pages):
         tab[0, lp] = i
     kp = torch.zeros(len(pages), P, w.d, dtype=w.dtype)
     vp = torch.zeros_like(kp)
-    kh, vh = x["k"][0:1], x["v"][0:1]
+    kh, vh = x["k"][g:g + 1], x["v"][g:g + 1]
     for lp in pages:
         a, b = lp * P, min((lp + 1) * P, t0 + C)
         orc.append(kp, tab, kh[:, a:b].cpu(), a)
         orc.append(vp, tab, vh[:, a:b].cpu(), a)
-    q = x["q"][0:G, C - rows:].cpu()
-    do = x["do"][0:G, C - rows:].cpu()
+    q = x["q"][g * G:(g + 1) * G, C - rows:].cpu()
+    do = x["do"][g * G:(g + 1) * G, C - rows:].cpu()
     pairs = 0
     for i in range(rows):
         p = t0s + i
@@ -116,7 +114,6 @@ def cpu_baseline(w, x, table_cpu, sel_cpu, rows: int):
         pairs += sum(max(0, min(P, p - lp * P + 1) - max(0, lo - lp * P)) for lp in pages
                      if lp * P <= p)
     pairs *= G
-    threads = torch.get_num_threads()
     t = time.perf_counter()
     if w.window > 0:
         # the same computation with every position moved down by `shift` (dense call)
@@ -128,12 +125,42 @@ def cpu_baseline(w, x, table_cpu, sel_cpu, rows: int):
     else:
         orc.fwd(q, kp, vp, tab, t0s, [sel_s], w.scale)
         orc.bwd(q, kp, vp, tab, t0s, [sel_s], w.scale, do)
-    dt = time.perf_counter() - t
+    return time.perf_counter() - t, pairs
+
+
+def cpu_baseline(w, x, sel_cpu, rows: int, max_pairs: float):
+    """The oracle (fp64 CPU) on a bounded sample of the same step: the last `rows`
+    queries of the chunk for as many KV heads (with their query heads) as fit in
+    about `max_pairs` attended pairs, halving `rows` when one head alone exceeds it,
+    each over exactly the keys those queries attend in the full chunk."""
+    import torch
+
+    P, C, t0, G = w.page, w.chunk, w.t0, w.group
+    rows = min(rows, C)
+
+    def est(g, r):  # upper bound on one head's pairs: every attended prior key plus the chunk
+        n_prior = len(sel_cpu[g]) * P if sel_cpu is not None else t0
+        if w.window > 0:
+            n_prior = min(n_prior, w.window)
+        return G * r * (n_prior + C)
+
+    while rows > 64 and est(0, rows) > max_pairs:
+        rows //= 2
+    heads, total = 0, 0
+    while heads < w.hkv and (heads == 0 or total + est(heads, rows) <= max_pairs):
+        total += est(heads, rows)
+        heads += 1
+    threads = torch.get_num_threads()
+    dt, pairs = 0.0, 0
+    for g in range(heads):
+        s, p = _oracle_sample_head(w, x, sel_cpu[g] if sel_cpu is not None else None, g, rows)
+        dt += s
+        pairs += p
     flop = 14 * w.d * pairs
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"KV head 0 of {w.hkv} ({G} query heads), last {rows} of {C} chunk queries "
-                      f"over the same {len(pages)} attended pages; oracle fwd+bwd in fp64; "
-                      f"{pairs} pairs, {dt:.1f} s"}
+            "sample": f"KV heads 0..{heads - 1} of {w.hkv} ({heads * G} query heads), last {rows} "
+                      f"of {C} chunk queries, each head over the keys its queries attend; oracle "
+                      f"fwd+bwd in fp64; {pairs} pairs, {dt:.1f} s"}
 
 
 PEAK_PCIE_GBS = 64.0  # PCIe 5.0 x16 host link, per direction
@@ -613,8 +640,10 @@ def main():
                     choices=["sparse1m", "dense128k", "sparse4m", "local1m"])
     ap.add_argument("--window", type=int, default=None,
                     help="local-attention window overriding the workload's (dense workloads)")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
-                    help="chunk queries in the oracle's CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="chunk queries per KV head in the oracle's CPU-baseline sample")
+    ap.add_argument("--cpu-pairs", type=float, default=1.5e9,
+                    help="bound on the attended pairs of the CPU-baseline sample (~13 s on 16 threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layer", action="store_true",
                     help="also time one chunk-recurrent attention layer (65,536 tokens)")
@@ -793,7 +822,7 @@ def main():
         x_cpu = {"k": x["k"], "v": x["v"], "q": x["q"], "do": x["do"]}
         sel_cpu = [sel[g, :counts[g]].tolist() for g in range(w.hkv)] if sparse else None
         log("[bench] timing the oracle on the CPU sample ...")
-        cpu = cpu_baseline(w, x_cpu, x["table"], sel_cpu, args.cpu_rows)
+        cpu = cpu_baseline(w, x_cpu, sel_cpu, args.cpu_rows, args.cpu_pairs)
         log(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 
     out = {
