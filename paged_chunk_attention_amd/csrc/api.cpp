@@ -431,7 +431,7 @@ int oomb_page_summarize_mean(const oomb_pool* pool, const int32_t* table, int64_
 // the ranges' fp32 partials.
 static size_t fwd_workspace(const oomb::AttnArgs& a) {
   if (!use_mfma(a.pool)) return 0;
-  return align256(oomb::fwd_partial_bytes(a, oomb::fwd_splits(a)));
+  return align256(oomb::fwd_partial_bytes(a, oomb::fwd_plan(a)));
 }
 
 size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
@@ -467,7 +467,7 @@ int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64
     return fail(OOMB_ERR_WORKSPACE, "fwd needs %zu bytes of 256-byte aligned workspace", need);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!use_mfma(a.pool)) return hip_status(oomb::launch_fwd_scalar(a, s), "paged_chunk_attn_fwd");
-  return hip_status(oomb::launch_fwd_mfma(a, oomb::fwd_splits(a), static_cast<float*>(workspace), s),
+  return hip_status(oomb::launch_fwd_mfma(a, oomb::fwd_plan(a), static_cast<float*>(workspace), s),
                     "paged_chunk_attn_fwd");
 }
 
@@ -480,7 +480,7 @@ static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part, size_t* o
   *off_dq = delta;
   if (!use_mfma(a.pool)) return delta;
   *off_dq = delta + align256(oomb::dkdv_partial_bytes(a, oomb::dkdv_splits(a)));
-  return *off_dq + align256(oomb::dq_partial_bytes(a, oomb::dq_splits(a)));
+  return *off_dq + align256(oomb::dq_partial_bytes(a, oomb::dq_plan(a)));
 }
 
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
@@ -534,7 +534,7 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   if (!use_mfma(a.pool)) return hip_status(oomb::launch_bwd_scalar(a, s), "paged_chunk_attn_bwd");
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
   float* dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dq);
-  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, oomb::dq_splits(a), dq_part, s),
+  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, oomb::dq_plan(a), dq_part, s),
                     "paged_chunk_attn_bwd");
 }
 

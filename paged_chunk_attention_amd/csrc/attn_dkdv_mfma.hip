@@ -443,11 +443,11 @@ size_t dkdv_partial_bytes(const AttnArgs& a, int n_split) {
   return static_cast<size_t>(n_split) * a.pool.Hkv * keys * 2 * mf::D * sizeof(float);
 }
 
-hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, int n_ks, float* dq_part,
-                           hipStream_t s) {
+hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, SplitPlan dq,
+                           float* dq_part, hipStream_t s) {
   hipError_t err = launch_delta(a, s);
   if (err != hipSuccess) return err;
-  err = launch_dq_mfma(a, n_ks, dq_part, s);
+  err = launch_dq_mfma(a, dq, dq_part, s);
   if (err != hipSuccess) return err;
   const int nkb = (a.max_att_pages * a.pool.P + mf::KPW - 1) / mf::KPW;
   const int part_keys = a.max_att_pages * a.pool.P;

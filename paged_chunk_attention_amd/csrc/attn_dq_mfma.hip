@@ -13,7 +13,9 @@
 //
 // A query tile's key blocks may be cut into n_ks equal ranges, one workgroup each, for
 // load balance (the tiles' work differs, and there are few of them per CU); each range
-// then writes an fp32 partial dQ and a merge kernel adds them in range order.
+// then writes an fp32 partial dQ and a merge kernel adds them in range order. With
+// `whole` > 0 only the tiles after the first `whole` of each KV head (in longest-first
+// order) are cut; the first ones run whole and write dQ directly.
 #include "mfma_tiles.hpp"
 
 namespace oomb {
@@ -23,7 +25,7 @@ constexpr int DQ_WAVES = 8;
 constexpr int DQ_Q = 32 * DQ_WAVES;  // queries per workgroup
 
 __global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
+void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D];
@@ -36,18 +38,20 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + DQ_Q - 1) / DQ_Q;
-  // A KV head's units: latest query tiles (most local keys, the longest) first, then
-  // the group's heads, then the key ranges of one tile.
+  // A KV head's units: tiles j in longest-first order (latest query tiles, with the most
+  // local keys, first; then the group's heads), the first `whole` whole, each later
+  // one as n_ks consecutive key ranges.
   const HeadUnit hu = head_unit(blockIdx.x, gridDim.x, a.pool.Hkv);
-  const int g = hu.head, kr = hu.unit % n_ks;
-  const int hh = (hu.unit / n_ks) % G, qt = n_qt - 1 - hu.unit / (n_ks * G);
+  const TileRange tr = tile_range(hu.unit, whole, n_ks);
+  const int g = hu.head, kr = tr.range, n_rng = tr.n_ranges;
+  const int hh = tr.tile % G, qt = n_qt - 1 - tr.tile / G;
   const int h = g * G + hh;
   const Keys km = make_keys(a, g);
   const int q0 = qt * DQ_Q;
   const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);
   const int blo_tile = first_block(km, a.t0 + q0);  // 0 without a window
   const int span = max(0, nblk - blo_tile);
-  const int b0 = blo_tile + span * kr / n_ks, b1 = blo_tile + span * (kr + 1) / n_ks;  // this workgroup's blocks
+  const int b0 = blo_tile + span * kr / n_rng, b1 = blo_tile + span * (kr + 1) / n_rng;  // this workgroup's blocks
   const float c2 = a.scale * kLog2e;
   // One wave of each SIMD (waves w and w + 4 share one) runs its blocks at raised
   // priority: it wins the matrix core when both are ready, and the other drifts behind
@@ -190,7 +194,7 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
 
   if (i < a.n_q) {
     // the whole dQ row, or this key range's partial of it
-    float* drow = n_ks == 1 ? a.dq + h * a.dq_hs + static_cast<int64_t>(i) * a.dq_ts
+    float* drow = n_rng == 1 ? a.dq + h * a.dq_hs + static_cast<int64_t>(i) * a.dq_ts
                             : part + ((static_cast<int64_t>(kr) * a.pool.Hq + h) * a.n_q + i) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -206,11 +210,13 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, float* part) {
 
 // dQ = the sum of the key ranges' partials, in range order. One thread per 4 columns
 // of a row.
-__global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, const float* part) {
+__global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, int whole,
+                                                       const float* part) {
   const int64_t rows = static_cast<int64_t>(a.pool.Hq) * a.n_q;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= rows * (D / 4)) return;
   const int64_t row = idx / (D / 4);
+  if (!row_was_split(a, row, DQ_Q, whole)) return;  // its tile ran whole and wrote dQ
   const int c = static_cast<int>(idx % (D / 4)) * 4;
   f32x4 s = *reinterpret_cast<const f32x4*>(part + row * D + c);
   for (int k = 1; k < n_ks; ++k) {
@@ -229,35 +235,41 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, con
 // halved while the largest is more than a quarter of the average work per workgroup
 // slot (one per CU, 256 CUs, fixed so the choice and the result bits do not depend on
 // the device) and would stay at least 128 blocks, below which the partials' traffic and
-// each workgroup's start-up outweigh the balance gained (as in the forward).
-int dq_splits(const AttnArgs& a) {
-  if (const int n = split_override("OOMB_DQ_SPLITS")) return n;
+// each workgroup's start-up outweigh the balance gained (as in the forward). When the
+// tiles are cut and their count is not a multiple of the CU count, mixed_plan cuts
+// only those beyond a whole number per CU (see launch.hpp).
+SplitPlan dq_plan(const AttnArgs& a) {
   const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
-  double total = 0.0, largest = 0.0;
+  const int G = a.pool.Hq / a.pool.Hkv;
+  SplitPlan forced;
+  if (plan_override("OOMB_DQ_SPLITS", "OOMB_DQ_WHOLE", G * n_qt, &forced)) return forced;
+  double total = 0.0, largest = 0.0, smallest = 1e300;
   for (int qt = 0; qt < n_qt; ++qt) {
     const double blocks = static_cast<double>(tile_key_blocks(a, qt * mf::DQ_Q, mf::DQ_Q, mf::KB));
     total += blocks;
     largest = blocks > largest ? blocks : largest;
+    smallest = blocks < smallest ? blocks : smallest;
   }
   const double per_slot = total * a.pool.Hq / 256.0;
   int nk = 1;
   while (nk < 4 && largest / nk > per_slot / 4.0 && largest / (2 * nk) >= 128.0) nk *= 2;
-  return nk;
+  return mixed_plan(G * n_qt, a.pool.Hkv, smallest, nk);
 }
 
-size_t dq_partial_bytes(const AttnArgs& a, int n_ks) {
-  if (n_ks <= 1) return 0;
-  return static_cast<size_t>(n_ks) * a.pool.Hq * a.n_q * mf::D * sizeof(float);
+size_t dq_partial_bytes(const AttnArgs& a, SplitPlan p) {
+  if (p.n_ks <= 1) return 0;
+  return static_cast<size_t>(p.n_ks) * a.pool.Hq * a.n_q * mf::D * sizeof(float);
 }
 
-hipError_t launch_dq_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s) {
+hipError_t launch_dq_mfma(const AttnArgs& a, SplitPlan p, float* part, hipStream_t s) {
   const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
-  OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, dim3(a.pool.Hq * n_qt * n_ks), dim3(64 * mf::DQ_WAVES), 0,
-              s, a, n_ks, part);
-  if (n_ks > 1) {
+  const int G = a.pool.Hq / a.pool.Hkv;
+  OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, dim3(a.pool.Hkv * plan_units(p, G * n_qt)),
+              dim3(64 * mf::DQ_WAVES), 0, s, a, p.n_ks, p.whole, part);
+  if (p.n_ks > 1) {
     const int64_t threads = static_cast<int64_t>(a.pool.Hq) * a.n_q * (mf::D / 4);
     OOMB_LAUNCH("dq_merge", mf::dq_merge_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
-                dim3(256), 0, s, a, n_ks, part);
+                dim3(256), 0, s, a, p.n_ks, p.whole, part);
   }
   return hipGetLastError();
 }

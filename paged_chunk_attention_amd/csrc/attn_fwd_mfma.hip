@@ -14,7 +14,9 @@
 //
 // A query tile's key blocks may be cut into n_ks equal ranges, one workgroup each, for
 // load balance; each range then writes its unnormalised fp32 O with its running
-// maximum and sum, and a merge kernel combines them in range order.
+// maximum and sum, and a merge kernel combines them in range order. With `whole` > 0
+// only the tiles after the first `whole` of each KV head (in longest-first order) are
+// cut; the first ones run whole and write O directly.
 #include <type_traits>
 
 #include "mfma_tiles.hpp"
@@ -31,7 +33,7 @@ constexpr int FWD_CAP = 8192;
 
 template <int CAP, bool SLIDE>
 __global__ __launch_bounds__(64 * FWD_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
+void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_ml) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k2[KB * D];
@@ -46,11 +48,13 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + FWD_Q - 1) / FWD_Q;
-  // A KV head's units: latest query tiles (most local keys, the longest) first, then
-  // the group's heads, then the key ranges of one tile.
+  // A KV head's units: tiles j in longest-first order (latest query tiles, with the most
+  // local keys, first; then the group's heads), the first `whole` whole, each later
+  // one as n_ks consecutive key ranges.
   const HeadUnit hu = head_unit(blockIdx.x, gridDim.x, a.pool.Hkv);
-  const int g = hu.head, krange = hu.unit % n_ks;
-  const int hh = (hu.unit / n_ks) % G, qt = n_qt - 1 - hu.unit / (n_ks * G);
+  const TileRange tr = tile_range(hu.unit, whole, n_ks);
+  const int g = hu.head, krange = tr.range, n_rng = tr.n_ranges;
+  const int hh = tr.tile % G, qt = n_qt - 1 - tr.tile / G;
   const int h = g * G + hh;
   const Keys km = make_keys(a, g);
   const int q0 = qt * FWD_Q;
@@ -61,7 +65,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
   const int span = max(0, nb_tile - blo_tile);
   // This workgroup's blocks are b0 .. b0 + nb - 1; below, block indices are relative
   // to b0 and made absolute (b0 + .) wherever keys are addressed or masked.
-  const int b0 = blo_tile + span * krange / n_ks, nb = blo_tile + span * (krange + 1) / n_ks - b0;
+  const int b0 = blo_tile + span * krange / n_rng, nb = blo_tile + span * (krange + 1) / n_rng - b0;
   const float c2 = a.scale * kLog2e;
 
   // This wave's queries: blocks past its last query, or (with a window) before its
@@ -298,7 +302,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; or this key range's partial.
   const float lt = add_halves(l_run);
-  if (n_ks > 1) {
+  if (n_rng > 1) {
     if (i < a.n_q) {
       const int64_t row = (static_cast<int64_t>(krange) * a.pool.Hq + h) * a.n_q + i;
       float* prow = part + row * D;
@@ -335,13 +339,14 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, float* part, float* part_ml) {
 // units), w_r = 2^(m_r - M), O = sum_r w_r O_r / sum_r w_r l_r and
 // LSE = (M + log2 sum_r w_r l_r) ln 2, the ranges taken in order. One thread per 4
 // columns of a row.
-__global__ __launch_bounds__(256) void fwd_merge_kernel(AttnArgs a, int n_ks, const float* part,
-                                                        const float* part_ml) {
+__global__ __launch_bounds__(256) void fwd_merge_kernel(AttnArgs a, int n_ks, int whole,
+                                                        const float* part, const float* part_ml) {
   const int64_t rows = static_cast<int64_t>(a.pool.Hq) * a.n_q;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= rows * (D / 4)) return;
   const int64_t row = idx / (D / 4);
   const int c = static_cast<int>(idx % (D / 4)) * 4;
+  if (!row_was_split(a, row, FWD_Q, whole)) return;  // its tile ran whole and wrote O
   float mx = -__builtin_inff();
   for (int k = 0; k < n_ks; ++k) mx = fmaxf(mx, part_ml[2 * (k * rows + row)]);
   float l = 0.0f;
@@ -372,42 +377,48 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(AttnArgs a, int n_ks, co
 // result bits do not depend on the device) and would stay at least 128 blocks: a CU
 // runs one forward workgroup at a time, so each one's start-up (query fragments, page
 // list, first key blocks) is exposed, and shorter ranges cost more than they balance.
-int fwd_splits(const AttnArgs& a) {
-  if (const int n = split_override("OOMB_FWD_SPLITS")) return n;
+// When the tiles are cut and their count is not a multiple of the CU count,
+// mixed_plan cuts only those beyond a whole number per CU (see launch.hpp).
+SplitPlan fwd_plan(const AttnArgs& a) {
   const int n_qt = (a.n_q + mf::FWD_Q - 1) / mf::FWD_Q;
-  double total = 0.0, largest = 0.0;
+  const int G = a.pool.Hq / a.pool.Hkv;
+  SplitPlan forced;
+  if (plan_override("OOMB_FWD_SPLITS", "OOMB_FWD_WHOLE", G * n_qt, &forced)) return forced;
+  double total = 0.0, largest = 0.0, smallest = 1e300;
   for (int qt = 0; qt < n_qt; ++qt) {
     const double blocks = static_cast<double>(tile_key_blocks(a, qt * mf::FWD_Q, mf::FWD_Q, mf::KB));
     total += blocks;
     largest = blocks > largest ? blocks : largest;
+    smallest = blocks < smallest ? blocks : smallest;
   }
   const double per_cu = total * a.pool.Hq / 256.0;
   int nk = 1;
   while (nk < 4 && largest / nk > per_cu / 4.0 && largest / (2 * nk) >= 128.0) nk *= 2;
-  return nk;
+  return mixed_plan(G * n_qt, a.pool.Hkv, smallest, nk);
 }
 
-size_t fwd_partial_bytes(const AttnArgs& a, int n_ks) {
-  if (n_ks <= 1) return 0;
-  return static_cast<size_t>(n_ks) * a.pool.Hq * a.n_q * (mf::D + 2) * sizeof(float);
+size_t fwd_partial_bytes(const AttnArgs& a, SplitPlan p) {
+  if (p.n_ks <= 1) return 0;
+  return static_cast<size_t>(p.n_ks) * a.pool.Hq * a.n_q * (mf::D + 2) * sizeof(float);
 }
 
-hipError_t launch_fwd_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s) {
+hipError_t launch_fwd_mfma(const AttnArgs& a, SplitPlan p, float* part, hipStream_t s) {
   const int n_qt = (a.n_q + mf::FWD_Q - 1) / mf::FWD_Q;
-  const dim3 grid(a.pool.Hq * n_qt * n_ks), block(64 * mf::FWD_WAVES);
+  const int G = a.pool.Hq / a.pool.Hkv;
+  const dim3 grid(a.pool.Hkv * plan_units(p, G * n_qt)), block(64 * mf::FWD_WAVES);
   // partial O [n_ks][Hq][n_q][D], then (m, l) [n_ks][Hq][n_q][2]
-  float* part_ml = part ? part + static_cast<size_t>(n_ks) * a.pool.Hq * a.n_q * mf::D : nullptr;
+  float* part_ml = part ? part + static_cast<size_t>(p.n_ks) * a.pool.Hq * a.n_q * mf::D : nullptr;
   if (a.max_att_pages <= mf::FWD_CAP) {
-    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::FWD_CAP, false>), grid, block, 0, s, a, n_ks,
-                part, part_ml);
+    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::FWD_CAP, false>), grid, block, 0, s, a, p.n_ks,
+                p.whole, part, part_ml);
   } else {
-    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::PCAP, true>), grid, block, 0, s, a, n_ks, part,
-                part_ml);
+    OOMB_LAUNCH("fwd_mfma", (mf::fwd_mfma_kernel<mf::PCAP, true>), grid, block, 0, s, a, p.n_ks,
+                p.whole, part, part_ml);
   }
-  if (n_ks > 1) {
+  if (p.n_ks > 1) {
     const int64_t threads = static_cast<int64_t>(a.pool.Hq) * a.n_q * (mf::D / 4);
     OOMB_LAUNCH("fwd_merge", mf::fwd_merge_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
-                dim3(256), 0, s, a, n_ks, part, part_ml);
+                dim3(256), 0, s, a, p.n_ks, p.whole, part, part_ml);
   }
   return hipGetLastError();
 }

@@ -112,4 +112,16 @@ __device__ __forceinline__ HeadUnit head_unit(int i, int n, int n_heads) {
   return {x / x_per_head, local * x_per_head + x % x_per_head};
 }
 
+// Unit u of one KV head under a split plan: the head's first `whole` tiles (in its
+// longest-first tile order) are one unit each; every later tile is n_ks consecutive
+// units, one per key range.
+struct TileRange {
+  int tile, range, n_ranges;
+};
+__device__ __forceinline__ TileRange tile_range(int u, int whole, int n_ks) {
+  if (u < whole) return {u, 0, 1};
+  const int v = u - whole;
+  return {whole + v / n_ks, v % n_ks, n_ks};
+}
+
 }  // namespace oomb

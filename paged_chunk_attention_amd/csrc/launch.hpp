@@ -159,21 +159,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_fwd_scalar(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_scalar(const AttnArgs& a, hipStream_t s);
 // Matrix-core kernels: bf16, head_dim 128, page size >= 16.
-// n_ks > 1 splits each query tile's key blocks into ranges; `part` then holds
-// fwd_partial_bytes(a, n_ks) bytes of fp32 partials.
-hipError_t launch_fwd_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s);
-int fwd_splits(const AttnArgs& a);
-size_t fwd_partial_bytes(const AttnArgs& a, int n_ks);
-// n_split > 1 splits the dK/dV pass over the query stream; `part` then holds
-// dkdv_partial_bytes(a, n_split) bytes of fp32 partials. n_ks > 1 splits the dQ pass
-// over key ranges; `dq_part` then holds dq_partial_bytes(a, n_ks) bytes.
-hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, int n_ks, float* dq_part,
-                           hipStream_t s);
-// dQ pass of the matrix-core backward (launched by launch_bwd_mfma after Delta).
-hipError_t launch_dq_mfma(const AttnArgs& a, int n_ks, float* part, hipStream_t s);
+
 // The split counts below are chosen for load balance; OOMB_FWD_SPLITS, OOMB_DQ_SPLITS
-// and OOMB_DKDV_SPLITS (1..16) fix them instead, read at every call, so the workspace
-// query and the call agree while the variable does not change. Every count gives the
+// and OOMB_DKDV_SPLITS (1..16) fix them instead (with OOMB_FWD_WHOLE and OOMB_DQ_WHOLE
+// for the tiles per KV head that stay whole), read at every call, so the workspace
+// query and the call agree while the variables do not change. Every choice gives the
 // same results up to rounding order; the variables exist so that each code path can
 // be tested at small sizes. Returns 0 when the variable is unset or out of range.
 inline int split_override(const char* var) {
@@ -181,6 +171,55 @@ inline int split_override(const char* var) {
   if (v == nullptr) return 0;
   const int n = atoi(v);
   return n >= 1 && n <= 16 ? n : 0;
+}
+// How the forward and dQ passes cut query tiles into key ranges: per KV head, the
+// first `whole` tiles in longest-first order run whole, every later one as n_ks
+// ranges (whole = 0: all tiles cut; n_ks = 1: none). Partials are laid out for n_ks
+// ranges of every row; rows of whole tiles never use theirs.
+struct SplitPlan {
+  int n_ks;
+  int whole;
+};
+// Workgroups per KV head under plan p with `tiles` query tiles per head.
+inline int plan_units(SplitPlan p, int tiles) {
+  return p.n_ks <= 1 ? tiles : p.whole + (tiles - p.whole) * p.n_ks;
+}
+// The plan fixed by the environment: `var_n` as in split_override, and `var_whole`
+// (default 0, clamped to the tiles per head) for the tiles that stay whole.
+inline bool plan_override(const char* var_n, const char* var_whole, int tiles, SplitPlan* out) {
+  const int n = split_override(var_n);
+  if (n == 0) return false;
+  int w = 0;
+  if (const char* v = getenv(var_whole)) w = atoi(v);
+  w = w < 0 ? 0 : (w > tiles ? tiles : w);
+  *out = SplitPlan{n, n > 1 ? w : 0};
+  return true;
+}
+// Refines a uniform cut into n_uniform > 1 key ranges. When the Hkv * tiles tiles are
+// not a multiple of the 256 CUs (one workgroup per CU), cutting every tile is more
+// than balance needs: the longest 256 * floor(T / 256) tiles run whole (the same number
+// on every CU) and only the remaining r = T mod 256 are cut, into n ranges with n in
+// {2, 4, 8} minimising the rounds ceil(r n / 256) / n the pieces take (smaller n on
+// ties; ranges of at least 16 key blocks), so the pieces spread over all CUs and
+// fewer rows need partials and a merge. Needs 256 % Hkv == 0, so that every head has a
+// whole number of whole tiles; otherwise (or with no gain) the uniform cut stays.
+inline SplitPlan mixed_plan(int tiles, int hkv, double smallest_blocks, int n_uniform) {
+  const SplitPlan uniform{n_uniform, 0};
+  const int T = tiles * hkv;
+  if (n_uniform <= 1 || 256 % hkv != 0 || T <= 256 || T % 256 == 0) return uniform;
+  const int r = T % 256;
+  int best = 0;
+  double best_rounds = 1.0;  // the remainder left whole: one more round of whole tiles
+  for (int n = 2; n <= 8; n *= 2) {
+    if (smallest_blocks / n < 16.0) break;
+    const double rounds = static_cast<double>((r * n + 255) / 256) / n;
+    if (rounds < best_rounds - 1e-9) {
+      best = n;
+      best_rounds = rounds;
+    }
+  }
+  if (best == 0) return uniform;
+  return SplitPlan{best, (T / 256) * 256 / hkv};
 }
 // Key blocks (of kb keys) that the query tile [q_first, q_first + len) visits: from
 // the block its first query's window starts in (block 0 without a window) to the one
@@ -199,10 +238,22 @@ inline int64_t tile_key_blocks(const AttnArgs& a, int q_first, int len, int kb) 
   }
   return hi / kb - lo / kb + 1;
 }
+// Matrix-core forward. A plan with n_ks > 1 cuts query tiles into key ranges; `part`
+// then holds fwd_partial_bytes(a, plan) bytes of fp32 partials.
+hipError_t launch_fwd_mfma(const AttnArgs& a, SplitPlan p, float* part, hipStream_t s);
+SplitPlan fwd_plan(const AttnArgs& a);
+size_t fwd_partial_bytes(const AttnArgs& a, SplitPlan p);
+// n_split > 1 splits the dK/dV pass over the query stream; `part` then holds
+// dkdv_partial_bytes(a, n_split) bytes of fp32 partials. A dQ plan with n_ks > 1 cuts
+// query tiles into key ranges; `dq_part` then holds dq_partial_bytes(a, plan) bytes.
+hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, SplitPlan dq,
+                           float* dq_part, hipStream_t s);
+// dQ pass of the matrix-core backward (launched by launch_bwd_mfma after Delta).
+hipError_t launch_dq_mfma(const AttnArgs& a, SplitPlan p, float* part, hipStream_t s);
 int dkdv_splits(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, int n_split);
-int dq_splits(const AttnArgs& a);
-size_t dq_partial_bytes(const AttnArgs& a, int n_ks);
+SplitPlan dq_plan(const AttnArgs& a);
+size_t dq_partial_bytes(const AttnArgs& a, SplitPlan p);
 // Delta_i = dO_i . O_i, shared by both backward paths.
 hipError_t launch_delta(const AttnArgs& a, hipStream_t s);
 

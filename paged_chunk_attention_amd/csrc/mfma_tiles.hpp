@@ -50,6 +50,17 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int KPW = 128;      // keys per workgroup in the dK/dV pass (32 per wavefront)
 constexpr int QTB = 64;       // queries per staged tile in the dK/dV pass
 
+// Whether attention row `row` (= h * n_q + i) belongs to a query tile (of `tileq`
+// queries) that a split plan cut into key ranges: its tile index in the KV head's
+// longest-first order is at least `whole`.
+__device__ __forceinline__ bool row_was_split(const AttnArgs& a, int64_t row, int tileq, int whole) {
+  if (whole <= 0) return true;
+  const int G = a.pool.Hq / a.pool.Hkv;
+  const int h = static_cast<int>(row / a.n_q), i = static_cast<int>(row % a.n_q);
+  const int n_qt = (a.n_q + tileq - 1) / tileq;
+  return (n_qt - 1 - i / tileq) * G + h % G >= whole;
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

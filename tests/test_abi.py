@@ -127,11 +127,12 @@ def test_summarize_and_select_errors(lib):
 
 def test_fwd_workspace(lib):
     """The forward's workspace: sized by oomb_fwd_workspace_bytes (empty for a short
-    prior context; for a dense 4096-query chunk after 126,976 tokens the query tiles are
-    split into key ranges, so it is not), and a missing, short or misaligned one is
-    rejected before any launch."""
+    prior context and for a first chunk, whose tiles are too short to cut; for a dense
+    4096-query chunk after 126,976 tokens the query tiles are split into key ranges, so
+    it is not), and a missing, short or misaligned one is rejected before any launch."""
     p = _pool()
     assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, 4096, -1, 0) == 0
+    assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, 0, -1, 0) == 0
     assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 0, 4096, -1, 0) == 0
     t0 = 126976
     need = lib.oomb_fwd_workspace_bytes(ctypes.byref(p), 4096, t0, -1, 0)
@@ -150,7 +151,9 @@ def test_fwd_workspace(lib):
 def test_split_counts_at_the_workloads(lib, name, n_q, t0, sel_stride, splits):
     """The host's load-balance rule picks, at the three benchmark workloads, the split
     counts (forward key ranges, dQ key ranges, dK/dV query-stream splits) that measured
-    fastest; they show in the workspace sizes, which are a function of them alone."""
+    fastest; they show in the workspace sizes, which are a function of them alone.
+    (Where the forward and dQ cut tiles, dense 128K and sparse 4M, only the tiles
+    beyond a whole number per CU are cut; the partials keep the uniform layout.)"""
     p = _pool()
     n_fwd, n_dq, n_kv = splits
     hq, hkv, d, page = 28, 4, 128, 128

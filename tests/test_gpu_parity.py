@@ -78,6 +78,22 @@ def test_padding_rows_come_from_zeros(kw):
     run_chunk_parity(w, x)
 
 
+@pytest.mark.parametrize("n,whole", [(3, 5), (2, 13), (4, 14)])
+@pytest.mark.parametrize("kw", [
+    dict(name="mfma_gqa7_mixed_sparse", hq=28, hkv=4, chunk=333, total=2597 + 333, top_k=5, needles=3),
+    dict(name="mfma_gqa7_mixed_window", hq=28, hkv=4, chunk=333, total=2597 + 333, window=300),
+])
+def test_chunk_parity_mfma_mixed_plans(kw, n, whole, monkeypatch):
+    """Mixed split plans fixed through the environment: per KV head the first `whole`
+    of its 14 query tiles (longest first) run whole and write O and dQ directly, the
+    rest as n key ranges merged in order (whole = 14: every tile whole although the
+    partials are laid out), so the merges must leave the whole tiles' rows alone."""
+    for var, val in (("OOMB_FWD_SPLITS", n), ("OOMB_DQ_SPLITS", n), ("OOMB_FWD_WHOLE", whole),
+                     ("OOMB_DQ_WHOLE", whole)):
+        monkeypatch.setenv(var, str(val))
+    run_chunk_parity(_w(**dict(kw, name=f"{kw['name']}_n{n}_w{whole}")))
+
+
 # local attention (the sparse layers of sparse-native models): a window of W positions
 @pytest.mark.parametrize("kw", [
     dict(name="mfma_window5", window=5),                              # inside one key block
