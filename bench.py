@@ -562,6 +562,96 @@ def other_workload(pca, torch, name, steps=5, warmup=2):
             "attended_pairs": pairs, "passes": passes}
 
 
+def sweep_workload(pca, torch, name, reps=2, warmup=1):
+    """The chunk-recurrent sweep of a whole sequence (explainer 2.A): forward over the
+    chunks in order (append, summarize, select when sparse, forward), then in reverse
+    order the forward again and the backward, dK/dV accumulating in the paged fp32 pool
+    (zeroed first). Outputs and workspaces are allocated before timing. Returns ms per
+    sweep, model TFLOP/s (14 D per attended pair, recomputation not counted) and each
+    matrix-core pass's total time and hardware FLOP rate."""
+    import types
+    import workloads as wl
+    w = wl.WORKLOADS[name]
+    P, C, S, D = w.page, w.chunk, w.n_chunks, w.d
+    x = wl.make_inputs(w, device="cuda")
+    table, gtable = x["table"].to("cuda"), x["gtable"].to("cuda")
+    pool = pca.PagedPool(w.pool_pages, P, D, w.hq, w.hkv, w.dtype, "cuda")
+    sparse = w.top_k is not None
+    q_all, do_all, k_all, v_all = x["q"], x["do"], x["k"], x["v"]
+    o_all = torch.empty_like(q_all)
+    lse_all = torch.empty(S, w.hq, C, dtype=torch.float32, device="cuda")
+    dq_all = torch.empty(w.hq, w.total, D, dtype=torch.float32, device="cuda")
+    k = max(1, w.top_k or 1)
+    sel = torch.zeros(S, w.hkv, k, dtype=torch.int32, device="cuda")
+    count = torch.zeros(S, w.hkv, dtype=torch.int32, device="cuda")
+    sstride = k if sparse else -1
+    nbytes = lambda f: max(256, max(f(c * C) for c in range(S)))
+    ws_sel = torch.empty(nbytes(lambda t0: pca.select_workspace_bytes(pool, C, t0)),
+                         dtype=torch.uint8, device="cuda")
+    ws_fwd = torch.empty(nbytes(lambda t0: pca.fwd_workspace_bytes(pool, C, t0, sstride)),
+                         dtype=torch.uint8, device="cuda")
+    ws_bwd = torch.empty(nbytes(lambda t0: pca.bwd_workspace_bytes(pool, C, t0, sstride)),
+                         dtype=torch.uint8, device="cuda")
+
+    def sweep():
+        pool.dk.zero_()
+        pool.dv.zero_()
+        for c in range(S):
+            t0, sl = c * C, slice(c * C, (c + 1) * C)
+            pca.oomb_kv_append(pool, table, k_all[:, sl], v_all[:, sl], t0)
+            pca.oomb_page_summarize(pool, table, t0 // P, (t0 + C - 1) // P - t0 // P + 1, t0 + C)
+            s_, c_ = (None, None)
+            if sparse:
+                s_, c_ = pca.oomb_select_pages(pool, table, q_all[:, sl], t0, w.top_k, sel=sel[c],
+                                               count=count[c], workspace=ws_sel)
+            pca.oomb_paged_chunk_attn_fwd(pool, table, q_all[:, sl], t0, s_, c_, w.scale,
+                                          o=o_all[:, sl], lse=lse_all[c], workspace=ws_fwd)
+        for c in reversed(range(S)):
+            t0, sl = c * C, slice(c * C, (c + 1) * C)
+            s_, c_ = (sel[c], count[c]) if sparse else (None, None)
+            pca.oomb_paged_chunk_attn_fwd(pool, table, q_all[:, sl], t0, s_, c_, w.scale,
+                                          o=o_all[:, sl], lse=lse_all[c], workspace=ws_fwd)
+            pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q_all[:, sl], t0, s_, c_,
+                                          o_all[:, sl], do_all[:, sl], lse_all[c], w.scale,
+                                          dq=dq_all[:, sl], workspace=ws_bwd)
+
+    for _ in range(warmup):
+        sweep()
+    torch.cuda.synchronize()
+    with pca.kernel_timer() as timer:
+        t_start = time.perf_counter()
+        for _ in range(reps):
+            sweep()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+    ms = elapsed * 1e3 / reps
+    counts = count.cpu().tolist()
+    pairs = 0
+    for c in range(S):
+        wc = types.SimpleNamespace(chunk=C, page=P, t0=c * C, window=0, hq=w.hq, hkv=w.hkv,
+                                   group=w.group)
+        pairs += attended_pairs(wc, counts[c] if sparse else None)
+    value = 14 * D * pairs / (ms * 1e-3) / 1e12
+    per = {}
+    for kname, kms in timer.records:
+        tot, n = per.get(kname, (0.0, 0))
+        per[kname] = (tot + kms, n + 1)
+    passes = {}
+    # per sweep: the forward runs twice per chunk (in order, then recomputed)
+    launches = {"fwd_mfma": 2 * S, "dkdv_mfma": S, "dq_mfma": S}
+    for kname, hw in HW_FLOP_PER_PAIR_D.items():
+        if kname in per:
+            kms = per[kname][0] / reps
+            tf = launches[kname] * hw * D * pairs / S / (kms * 1e-3) / 1e12
+            passes[kname] = {"ms_per_sweep": kms, "hardware_TFLOPs": tf,
+                             "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
+    del pool, x, o_all, dq_all
+    return {"ms_per_sweep": ms, "value": value, "unit": "TFLOP/s",
+            "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS, "sweeps": reps, "chunks": S,
+            "chunk": C, "tokens": w.total, "top_k": w.top_k, "attended_pairs": pairs,
+            "model_flop_per_sweep": 14 * D * pairs, "passes": passes}
+
+
 def context_build(pca, torch, pool, table, x, w, reps):
     """Write the whole prior context into the pool (kv_append) and summarise its pages
     (page_summarize), each timed on its own stream with HIP events after evicting the
@@ -649,7 +739,7 @@ def main():
                     help="also time one chunk-recurrent attention layer (65,536 tokens)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offload measurements (sparse workloads)")
-    ap.add_argument("--also", default="dense128k",
+    ap.add_argument("--also", default="dense128k,sweep256k,sweep256k_top64",
                     help="comma-separated other workloads to time briefly ('none' for none)")
     ap.add_argument("--hbm-reps", type=int, default=3,
                     help="cold-cache repetitions of the whole-context append and summarize")
@@ -812,6 +902,12 @@ def main():
         if name not in wl.WORKLOADS:
             print(f"unknown workload {name!r} in --also", file=sys.stderr)
             sys.exit(2)
+        if wl.WORKLOADS[name].sweep:
+            log(f"[bench] {name} sweep ...")
+            others[name] = sweep_workload(pca, torch, name)
+            log(f"[bench] {name}: {others[name]['ms_per_sweep']:.1f} ms/sweep, "
+                f"{others[name]['value']:.1f} TFLOP/s ({others[name]['pct_mfma_peak']:.1f}% of peak)")
+            continue
         log(f"[bench] {name} step ...")
         others[name] = other_workload(pca, torch, name)
         log(f"[bench] {name}: {others[name]['ms_per_step']:.3f} ms/step, "
