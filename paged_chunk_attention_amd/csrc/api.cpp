@@ -479,7 +479,7 @@ static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part, size_t* o
   *off_part = delta;
   *off_dq = delta;
   if (!use_mfma(a.pool)) return delta;
-  *off_dq = delta + align256(oomb::dkdv_partial_bytes(a, oomb::dkdv_splits(a)));
+  *off_dq = delta + align256(oomb::dkdv_partial_bytes(a, oomb::dkdv_plan(a)));
   return *off_dq + align256(oomb::dq_partial_bytes(a, oomb::dq_plan(a)));
 }
 
@@ -534,7 +534,7 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   if (!use_mfma(a.pool)) return hip_status(oomb::launch_bwd_scalar(a, s), "paged_chunk_attn_bwd");
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
   float* dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dq);
-  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_splits(a), part, oomb::dq_plan(a), dq_part, s),
+  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_plan(a), part, oomb::dq_plan(a), dq_part, s),
                     "paged_chunk_attn_bwd");
 }
 

@@ -6,8 +6,11 @@ namespace oomb {
 namespace mf {
 
 // ============================================================================ dK / dV
-// Grid: Hkv * (key blocks of 128) * n_split. With n_split > 1, split s writes its
-// partial dK/dV rows to part[((s * Hkv + g) * part_keys + key) * 2D + {0: dK, D: dV}].
+// Grid: Hkv * units; per KV head, the first `whole` key blocks of 128 (in block order)
+// are one unit each and add into the gradient pool directly, every later block is
+// n_split units over its query stream. Split s of such a block writes its partial
+// dK/dV rows to part[((s * Hkv + g) * part_keys + key) * 2D + {0: dK, D: dV}], and a
+// merge kernel adds them into the pool in split order.
 //
 // A workgroup is 8 wavefronts that own 128 keys, 32 per key group kg = wave % 4. The
 // two wavefronts of a key group share a SIMD and split its work by role:
@@ -29,7 +32,7 @@ namespace mf {
 constexpr int DKV_WAVES = 8;
 
 __global__ __launch_bounds__(64 * DKV_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
+void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_keys) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q0[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_q1[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_q2[QTB * D];
@@ -56,7 +59,8 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   // block only falls with the index (local blocks see fewer query tiles), so this is
   // longest first.
   const HeadUnit hu = head_unit(blockIdx.x, gridDim.x, a.pool.Hkv);
-  const int g = hu.head, split = hu.unit % n_split, kb = hu.unit / n_split;
+  const TileRange tr = tile_range(hu.unit, whole, n_split);
+  const int g = hu.head, split = tr.range, n_parts = tr.n_ranges, kb = tr.tile;
   const Keys km = make_keys(a, g);
   const int k0 = kb * KPW;
   if (kb >= nkb || k0 >= km.n_keys) return;  // uniform: block past this head's attended keys
@@ -80,7 +84,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   if (pwave && h2 == 0) {
     int64_t out = -1;
     if (krow >= 0) {
-      if (n_split > 1) {
+      if (n_parts > 1) {
         out = kidx;  // partial row index
       } else {
         const int64_t gp = a.gtable[g * a.gtstride + (kpos >> km.log2p)];
@@ -99,7 +103,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
 
   // Query tiles that can see some key of this block: every head of the group, from
   // the first query at or after the block's first key (with a window, up to the last
-  // query whose window still reaches the block's last key); cut into n_split parts.
+  // query whose window still reaches the block's last key); cut into n_parts parts.
   const int n_qt = (a.n_q + QTB - 1) / QTB;
   int qt0 = 0, qt_end = n_qt;
   if (!km.in_seq(k0)) {
@@ -114,8 +118,8 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   }
   const int tph = max(0, qt_end - qt0);
   const int n_tiles = G * tph;
-  const int u_begin = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / n_split);
-  const int u_end = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / n_split);
+  const int u_begin = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / n_parts);
+  const int u_end = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / n_parts);
   const int n_it = u_end - u_begin;
 
   f32x16 acc[4];  // dV (P wave) or dK (D wave): register r = key row, lane column = d
@@ -354,7 +358,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
     const int m = 8 * (r >> 2) + 4 * h2 + (r & 3);
     const int64_t out = s_grow[32 * kg + m];
     if (out < 0) continue;
-    if (n_split == 1) {
+    if (n_parts == 1) {
       float* row = (pwave ? a.pool.dv_pool : a.pool.dk_pool) + out * D;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) row[32 * nb + col] += acc[nb][r] * mul;
@@ -367,12 +371,13 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, float* part, int part_keys) {
   }
 }
 
-// Adds the split partials of every attended key row, in split order, into the
-// gradient pool. One wavefront per (key, KV head); lanes over d.
+// Adds the split partials of every attended key row from k_first on (the rows of the
+// split key blocks), in split order, into the gradient pool. One wavefront per (key,
+// KV head); lanes over d.
 __global__ __launch_bounds__(256) void dkdv_merge_kernel(AttnArgs a, int n_split, const float* part,
-                                                         int part_keys) {
+                                                         int part_keys, int k_first) {
   const int lane = threadIdx.x & 63;
-  const int kidx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int kidx = k_first + blockIdx.x * 4 + (threadIdx.x >> 6);
   const int g = blockIdx.y;
   const Keys km = make_keys(a, g);
   if (kidx >= part_keys || !km.in_seq(kidx)) return;
@@ -407,8 +412,11 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(AttnArgs a, int n_split
 // least 64 tiles, so that longest-first list scheduling over the CUs ends evenly. The
 // CU count is fixed at the MI355X's 256, which keeps the choice, and so the result
 // bits and the workspace size, independent of the device.
-int dkdv_splits(const AttnArgs& a) {
-  if (const int n = split_override("OOMB_DKDV_SPLITS")) return n;
+SplitPlan dkdv_plan(const AttnArgs& a) {
+  const int64_t n_kb = (static_cast<int64_t>(a.max_att_pages) * a.pool.P + mf::KPW - 1) / mf::KPW;
+  SplitPlan forced;
+  if (plan_override("OOMB_DKDV_SPLITS", "OOMB_DKDV_WHOLE", static_cast<int>(n_kb), &forced))
+    return forced;
   const int G = a.pool.Hq / a.pool.Hkv;
   const int n_qt = (a.n_q + mf::QTB - 1) / mf::QTB;
   const int64_t P = a.pool.P;
@@ -416,6 +424,7 @@ int dkdv_splits(const AttnArgs& a) {
   const int64_t local0 = static_cast<int64_t>(a.max_att_pages - a.n_local) * P;
   const int64_t nkb = (n_keys + mf::KPW - 1) / mf::KPW;
   double total = 0.0, largest = 0.0;
+  int64_t n_largest = 0;  // leading blocks (prior keys) that see every query tile
   for (int64_t kb = 0; kb < nkb; ++kb) {
     // the query tiles of key block kb, as the kernel bounds them
     const int64_t k0 = kb * mf::KPW;
@@ -429,21 +438,34 @@ int dkdv_splits(const AttnArgs& a) {
     }
     const double t = static_cast<double>(G) * (qt_end > qt0 ? qt_end - qt0 : 0);
     total += t;
-    largest = t > largest ? t : largest;
+    if (t > largest) {
+      largest = t;
+      n_largest = 0;
+    }
+    if (t == largest && n_largest == kb) ++n_largest;
   }
   const double per_cu = total * a.pool.Hkv / 256.0;
   int ns = 1;
   while (ns < 8 && largest / ns > per_cu / 4.0 && largest / (2 * ns) >= 64.0) ns *= 2;
-  return ns;
+  // Cutting every block is more than balance needs when the longest blocks (the prior
+  // keys, seen by every query tile) fill a whole number of rounds of the 256 CUs: those
+  // run whole, one per CU and round, adding into the pool with no partials, and only
+  // the rest (the chunk's own blocks, and prior blocks beyond whole rounds) are cut
+  // into ns parts, their pieces filling in behind. Without a window only.
+  int whole = 0;
+  if (ns > 1 && a.window <= 0 && 256 % a.pool.Hkv == 0)
+    whole = static_cast<int>((n_largest * a.pool.Hkv / 256) * 256 / a.pool.Hkv);
+  return SplitPlan{ns, whole};
 }
 
-size_t dkdv_partial_bytes(const AttnArgs& a, int n_split) {
+size_t dkdv_partial_bytes(const AttnArgs& a, SplitPlan p) {
+  const int n_split = p.n_ks;
   if (n_split <= 1) return 0;
   const size_t keys = static_cast<size_t>(a.max_att_pages) * a.pool.P;
   return static_cast<size_t>(n_split) * a.pool.Hkv * keys * 2 * mf::D * sizeof(float);
 }
 
-hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, SplitPlan dq,
+hipError_t launch_bwd_mfma(const AttnArgs& a, SplitPlan kv, float* part, SplitPlan dq,
                            float* dq_part, hipStream_t s) {
   hipError_t err = launch_delta(a, s);
   if (err != hipSuccess) return err;
@@ -451,13 +473,14 @@ hipError_t launch_bwd_mfma(const AttnArgs& a, int n_split, float* part, SplitPla
   if (err != hipSuccess) return err;
   const int nkb = (a.max_att_pages * a.pool.P + mf::KPW - 1) / mf::KPW;
   const int part_keys = a.max_att_pages * a.pool.P;
-  OOMB_LAUNCH("dkdv_mfma", mf::dkdv_mfma_kernel, dim3(a.pool.Hkv * nkb * n_split),
+  OOMB_LAUNCH("dkdv_mfma", mf::dkdv_mfma_kernel, dim3(a.pool.Hkv * plan_units(kv, nkb)),
               dim3(64 * mf::DKV_WAVES), 0, s,
-              a, n_split, part, part_keys);
-  if (n_split > 1) {
-    dim3 grid((part_keys + 3) / 4, a.pool.Hkv);
-    OOMB_LAUNCH("dkdv_merge", mf::dkdv_merge_kernel, grid, dim3(256), 0, s, a, n_split, part,
-                part_keys);
+              a, kv.n_ks, kv.whole, part, part_keys);
+  const int k_first = kv.whole * mf::KPW;  // keys of the blocks that ran whole are done
+  if (kv.n_ks > 1 && k_first < part_keys) {
+    dim3 grid((part_keys - k_first + 3) / 4, a.pool.Hkv);
+    OOMB_LAUNCH("dkdv_merge", mf::dkdv_merge_kernel, grid, dim3(256), 0, s, a, kv.n_ks, part,
+                part_keys, k_first);
   }
   return hipGetLastError();
 }

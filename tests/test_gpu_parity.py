@@ -87,9 +87,12 @@ def test_chunk_parity_mfma_mixed_plans(kw, n, whole, monkeypatch):
     """Mixed split plans fixed through the environment: per KV head the first `whole`
     of its 14 query tiles (longest first) run whole and write O and dQ directly, the
     rest as n key ranges merged in order (whole = 14: every tile whole although the
-    partials are laid out), so the merges must leave the whole tiles' rows alone."""
-    for var, val in (("OOMB_FWD_SPLITS", n), ("OOMB_DQ_SPLITS", n), ("OOMB_FWD_WHOLE", whole),
-                     ("OOMB_DQ_WHOLE", whole)):
+    partials are laid out), so the merges must leave the whole tiles' rows alone. The
+    dK/dV pass likewise: its first `whole` key blocks (of 8 with the selection, 23 with
+    the window) add into the pool directly, the others' query streams in n parts."""
+    for var, val in (("OOMB_FWD_SPLITS", n), ("OOMB_DQ_SPLITS", n), ("OOMB_DKDV_SPLITS", n),
+                     ("OOMB_FWD_WHOLE", whole), ("OOMB_DQ_WHOLE", whole),
+                     ("OOMB_DKDV_WHOLE", whole)):
         monkeypatch.setenv(var, str(val))
     run_chunk_parity(_w(**dict(kw, name=f"{kw['name']}_n{n}_w{whole}")))
 
