@@ -1,5 +1,5 @@
 // Matrix-core backward of paged chunk attention, dK/dV pass (race-free, one owner per
-// gradient row) and the launcher of the whole backward (Delta, dQ, dK/dV, merge).
+// gradient row) and the launcher of the whole backward (dQ with Delta, dK/dV, merges).
 #include "mfma_tiles.hpp"
 
 namespace oomb {
@@ -467,9 +467,8 @@ size_t dkdv_partial_bytes(const AttnArgs& a, SplitPlan p) {
 
 hipError_t launch_bwd_mfma(const AttnArgs& a, SplitPlan kv, float* part, SplitPlan dq,
                            float* dq_part, hipStream_t s) {
-  hipError_t err = launch_delta(a, s);
-  if (err != hipSuccess) return err;
-  err = launch_dq_mfma(a, dq, dq_part, s);
+  // The dQ pass also computes Delta and stores it for the dK/dV pass.
+  hipError_t err = launch_dq_mfma(a, dq, dq_part, s);
   if (err != hipSuccess) return err;
   const int nkb = (a.max_att_pages * a.pool.P + mf::KPW - 1) / mf::KPW;
   const int part_keys = a.max_att_pages * a.pool.P;

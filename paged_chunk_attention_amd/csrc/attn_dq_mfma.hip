@@ -1,5 +1,7 @@
 // Matrix-core backward of paged chunk attention, dQ pass: recompute P from the saved
-// log-sum-exp and dP = dO V^T per key block, then dQ^T += K^T dS^T.
+// log-sum-exp and dP = dO V^T per key block, then dQ^T += K^T dS^T. Each lane holds its
+// query's dO row anyway, so the pass also forms Delta = dO . O for its rows and stores
+// it for the dK/dV pass (no separate pre-pass).
 //
 // A workgroup is 8 wavefronts and owns 256 queries of one head (32 per wavefront, Q and
 // dO fragments held in registers), one workgroup per CU, two wavefronts per SIMD. The
@@ -67,23 +69,40 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   const int klim_w0 = km.klim(a.t0 + wq0);
   const int klo_wl = km.klo(a.t0 + wq_last);
 
-  // This lane's query (column of S^T and dP^T) with its Q and dO fragments.
+  // This lane's query (column of S^T and dP^T) with its Q and dO fragments; lanes col
+  // and col + 32 hold alternate 8-element groups of the row (h2 = 0, 1).
   const int i = wq0 + col;
   const int klim = km.klim(a.t0 + i), klo = km.klo(a.t0 + i);
+  const bool ok = i < a.n_q;
   bf16x8 qf[8], df[8];
+  u32x4 of[8];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + h * a.q_hs + static_cast<int64_t>(i) * a.q_ts;
     const uint16_t* drow = static_cast<const uint16_t*>(a.dout) + h * a.do_hs + static_cast<int64_t>(i) * a.do_ts;
-    const bool ok = i < a.n_q;
+    const uint16_t* orow = static_cast<const uint16_t*>(a.o) + h * a.o_hs + static_cast<int64_t>(i) * a.o_ts;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       qf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * h2) : u32x4{0u, 0u, 0u, 0u});
       df[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(drow + 16 * kk + 8 * h2) : u32x4{0u, 0u, 0u, 0u});
+      of[kk] = ok ? *reinterpret_cast<const u32x4*>(orow + 16 * kk + 8 * h2) : u32x4{0u, 0u, 0u, 0u};
     }
   }
   const int64_t rid = static_cast<int64_t>(h) * a.n_q + i;
-  const float lse2 = i < a.n_q ? a.lse_in[rid] * kLog2e : __builtin_inff();
-  const float delta = i < a.n_q ? a.delta[rid] : 0.0f;
+  const float lse2 = ok ? a.lse_in[rid] * kLog2e : __builtin_inff();
+  // Delta_i = dO_i . O_i in fp32: each lane sums its half of the row in element order,
+  // then the two halves are added (the same sum in both lanes, so every unit that holds
+  // the row gets the same bits). The first key range of each tile stores it for the
+  // dK/dV pass, which runs after this one on the same stream.
+  float delta = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 ob = as_bf16x8(of[kk]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      delta = __builtin_fmaf(static_cast<float>(df[kk][e]), static_cast<float>(ob[e]), delta);
+  }
+  delta += __shfl_xor(delta, 32, 64);
+  if (ok && kr == 0 && h2 == 0) a.delta[rid] = delta;
 
   f32x16 dqt[4];
 #pragma unroll

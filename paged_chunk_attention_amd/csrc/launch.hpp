@@ -249,7 +249,8 @@ size_t fwd_partial_bytes(const AttnArgs& a, SplitPlan p);
 // query tiles into key ranges; `dq_part` then holds dq_partial_bytes(a, plan) bytes.
 hipError_t launch_bwd_mfma(const AttnArgs& a, SplitPlan kv, float* part, SplitPlan dq,
                            float* dq_part, hipStream_t s);
-// dQ pass of the matrix-core backward (launched by launch_bwd_mfma after Delta).
+// dQ pass of the matrix-core backward, launched first by launch_bwd_mfma; it also
+// computes Delta = rowsum(dO * O) and stores it in a.delta for the dK/dV pass.
 hipError_t launch_dq_mfma(const AttnArgs& a, SplitPlan p, float* part, hipStream_t s);
 SplitPlan dkdv_plan(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, SplitPlan p);
