@@ -7,7 +7,8 @@
 // dO fragments held in registers), one workgroup per CU, two wavefronts per SIMD. The
 // key blocks are staged once for all 256 queries: LDS writes cost more than their share
 // of LDS bytes, and two 4-wave workgroups per CU (each staging its own blocks) ran 5%
-// slower. Key blocks of 64 rows (K and V) are copied global -> LDS by DMA one block
+// slower. Key blocks of 128 rows (K and V; 64-row blocks, with twice the barriers,
+// ran 1.2% slower) are copied global -> LDS by DMA one block
 // ahead, a fixed number of instructions per wave, into double buffers whose roles are
 // static in each half of the unrolled loop. The page ids a DMA needs
 // are read from LDS one block before it is issued, so the read has left the LDS queue
@@ -25,16 +26,28 @@ namespace mf {
 
 constexpr int DQ_WAVES = 8;
 constexpr int DQ_Q = 32 * DQ_WAVES;  // queries per workgroup
+constexpr int DQ_KB = 128;           // keys per staged block
+
+// Blocks of DQ_KB keys that queries up to position qmax_pos must visit, and the first
+// block a query at position qpos (or any later one) sees.
+__device__ __forceinline__ int dq_n_blocks(const Keys& k, int qmax_pos) {
+  const int last = k.klim(qmax_pos);
+  return last < 0 ? 0 : last / DQ_KB + 1;
+}
+__device__ __forceinline__ int dq_first_block(const Keys& k, int qpos) {
+  const int lo = k.klo(qpos);
+  return lo > 0 ? lo / DQ_KB : 0;
+}
 
 __global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v1[KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[DQ_KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[DQ_KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[DQ_KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[DQ_KB * D];
   __shared__ int s_page[PCAP];
   constexpr int NT = 64 * DQ_WAVES;
-  using Stage = KeyStage<KB, DQ_WAVES, PCAP, true>;  // DMA from assembly
+  using Stage = KeyStage<DQ_KB, DQ_WAVES, PCAP, true>;  // DMA from assembly
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, col = lane & 31;
@@ -50,8 +63,8 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   const int h = g * G + hh;
   const Keys km = make_keys(a, g);
   const int q0 = qt * DQ_Q;
-  const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);
-  const int blo_tile = first_block(km, a.t0 + q0);  // 0 without a window
+  const int nblk = dq_n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);
+  const int blo_tile = dq_first_block(km, a.t0 + q0);  // 0 without a window
   const int span = max(0, nblk - blo_tile);
   const int b0 = blo_tile + span * kr / n_rng, b1 = blo_tile + span * (kr + 1) / n_rng;  // this workgroup's blocks
   const float c2 = a.scale * kLog2e;
@@ -64,8 +77,8 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   // its first query need the mask.
   const int wq0 = q0 + 32 * wave;
   const int wq_last = min(a.n_q, wq0 + 32) - 1;
-  const int nblk_w = wq_last < wq0 ? 0 : n_blocks(km, a.t0 + wq_last);
-  const int blo_w = first_block(km, a.t0 + wq0);
+  const int nblk_w = wq_last < wq0 ? 0 : dq_n_blocks(km, a.t0 + wq_last);
+  const int blo_w = dq_first_block(km, a.t0 + wq0);
   const int klim_w0 = km.klim(a.t0 + wq0);
   const int klo_wl = km.klo(a.t0 + wq_last);
 
@@ -112,7 +125,7 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   fo.init(lane);
   const uint16_t* kpool = static_cast<const uint16_t*>(a.pool.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.pool.v_pool);
-  const int win0 = (b0 * KB) >> km.log2p;
+  const int win0 = (b0 * DQ_KB) >> km.log2p;
   Stage ks{km, s_page, win0, Stage::lane_offset(wave, lane)};
   fill_pages<NT>(km, s_page, win0, tid);
   wait_dma();  // the page-table loads are retired here, not at a later register reuse
@@ -131,9 +144,9 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   auto block = [&](int b, const uint16_t* kt, const uint16_t* vt, uint16_t* kn,
                    uint16_t* vn) __attribute__((always_inline)) {
     if (b + 1 < b1) {
-      const int last_e = ((b + 1) * KB + KB - 1) >> km.log2p;
+      const int last_e = ((b + 1) * DQ_KB + DQ_KB - 1) >> km.log2p;
       if (last_e >= ks.win + PCAP) {  // uniform over the workgroup: slide the page window
-        ks.win = ((b + 1) * KB) >> km.log2p;
+        ks.win = ((b + 1) * DQ_KB) >> km.log2p;
         fill_pages<NT>(km, s_page, ks.win, tid);
         wait_dma();
         __syncthreads();
@@ -142,7 +155,7 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
       ks.dma_fixed(b + 1, kpool, kn, wave, lane, pid);
       ks.dma_fixed(b + 1, vpool, vn, wave, lane, pid);
       if (b + 2 < b1) {
-        const int last2 = ((b + 2) * KB + KB - 1) >> km.log2p;
+        const int last2 = ((b + 2) * DQ_KB + DQ_KB - 1) >> km.log2p;
         if (last2 < ks.win + PCAP) ks.read_pages(b + 2, wave, pid);  // else after the slide
       }
     }
@@ -150,9 +163,9 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
       if (lead) __builtin_amdgcn_s_setprio(1);
       FragOffsets o = fo;
       o.opaque();
-      const bool mask = b * KB + KB - 1 > klim_w0 || b * KB < klo_wl;
+      const bool mask = b * DQ_KB + DQ_KB - 1 > klim_w0 || b * DQ_KB < klo_wl;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < DQ_KB / 32; ++sub) {
         // S^T = K Q^T and dP^T = V dO^T for 32 keys: two independent chains, fragment
         // reads one k-step ahead.
         f32x16 st = f32x16{}, dpt = f32x16{};
@@ -179,7 +192,7 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
         if (mask) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = b * KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            const int key = b * DQ_KB + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
             st[r] = ((key > klim) | (key < klo)) ? 0.0f : st[r];
           }
         }
