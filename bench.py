@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd paged chunk-attn TFLOP/s @1M ctx; % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # Algorithmic FLOP per attended (query, key) pair and head_dim unit, per kernel:
 # forward = S and PV; the dK/dV pass = S, dP (recomputed), dV, dK; the dQ pass is
@@ -632,10 +633,14 @@ def sweep_workload(pca, torch, name, reps=2, warmup=1):
                                    group=w.group)
         pairs += attended_pairs(wc, counts[c] if sparse else None)
     value = 14 * D * pairs / (ms * 1e-3) / 1e12
+    # bf16 runs on the matrix cores; fp32 (the tiny workload) on the scalar kernels,
+    # against the fp32 vector peak
+    peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_FP32_VECTOR_TFLOPS
     per = {}
     for kname, kms in timer.records:
         tot, n = per.get(kname, (0.0, 0))
         per[kname] = (tot + kms, n + 1)
+    kernels = {kname: tot / reps for kname, (tot, n) in per.items()}
     passes = {}
     # per sweep: the forward runs twice per chunk (in order, then recomputed)
     launches = {"fwd_mfma": 2 * S, "dkdv_mfma": S, "dq_mfma": S}
@@ -646,10 +651,11 @@ def sweep_workload(pca, torch, name, reps=2, warmup=1):
             passes[kname] = {"ms_per_sweep": kms, "hardware_TFLOPs": tf,
                              "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
     del pool, x, o_all, dq_all
-    return {"ms_per_sweep": ms, "value": value, "unit": "TFLOP/s",
-            "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS, "sweeps": reps, "chunks": S,
+    return {"ms_per_sweep": ms, "value": value, "unit": "TFLOP/s", "dtype": str(w.dtype)[6:],
+            "peak_TFLOPs": peak, "pct_peak": 100.0 * value / peak, "sweeps": reps, "chunks": S,
             "chunk": C, "tokens": w.total, "top_k": w.top_k, "attended_pairs": pairs,
-            "model_flop_per_sweep": 14 * D * pairs, "passes": passes}
+            "model_flop_per_sweep": 14 * D * pairs, "passes": passes,
+            "kernel_ms_per_sweep": kernels}
 
 
 def context_build(pca, torch, pool, table, x, w, reps):
@@ -739,7 +745,7 @@ def main():
                     help="also time one chunk-recurrent attention layer (65,536 tokens)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offload measurements (sparse workloads)")
-    ap.add_argument("--also", default="dense128k,sweep256k,sweep256k_top64",
+    ap.add_argument("--also", default="dense128k,sweep256k,sweep256k_top64,tiny",
                     help="comma-separated other workloads to time briefly ('none' for none)")
     ap.add_argument("--hbm-reps", type=int, default=3,
                     help="cold-cache repetitions of the whole-context append and summarize")
@@ -906,7 +912,8 @@ def main():
             log(f"[bench] {name} sweep ...")
             others[name] = sweep_workload(pca, torch, name)
             log(f"[bench] {name}: {others[name]['ms_per_sweep']:.1f} ms/sweep, "
-                f"{others[name]['value']:.1f} TFLOP/s ({others[name]['pct_mfma_peak']:.1f}% of peak)")
+                f"{others[name]['value']:.1f} TFLOP/s ({others[name]['pct_peak']:.1f}% of the "
+                f"{others[name]['dtype']} peak)")
             continue
         log(f"[bench] {name} step ...")
         others[name] = other_workload(pca, torch, name)
