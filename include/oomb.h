@@ -84,7 +84,7 @@ typedef struct oomb_pool {
 const char* oomb_status_string(int status);
 /* Description of the last error returned on the calling thread ("" if none). */
 const char* oomb_last_error(void);
-/* ABI version: bumped whenever a signature or a layout changes. */
+/* ABI version: bumped whenever a signature or a layout changes, or a call is added. */
 int oomb_abi_version(void);
 
 /* KV append - write a chunk's keys and values into their pages (explainer 2.B:
@@ -212,6 +212,18 @@ size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
  * Returns 0 for invalid arguments. */
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
                                 int64_t sel_stride, int32_t window);
+
+/* How the forward and backward calls of this geometry (arguments as for the workspace
+ * queries) spread their work over the GPU, for inspection and tests; the calls compute
+ * the same themselves. out[0], out[1]: key ranges per query tile of the forward, and
+ * query tiles per KV head (the longest first) that stay whole; out[2], out[3]: the same
+ * for the dQ pass; out[4], out[5]: parts of each key block's query stream in the dK/dV
+ * pass, and key blocks per KV head (in attended order) that stay whole. The scalar
+ * kernels (fp32, head_dim 64) do not split: 1, 0 for each pass. The choice depends on
+ * the geometry and the OOMB_*_SPLITS / OOMB_*_WHOLE environment variables only, never
+ * on the device. Returns OOMB_OK, or OOMB_ERR_INVALID (out untouched). */
+int oomb_split_plan(const oomb_pool* pool, int32_t n_q, int64_t t0, int64_t sel_stride,
+                    int32_t window, int32_t* out);
 
 /* Chunk attention backward, with the attention probabilities recomputed from the
  * saved LSE (explainer 2.A: activations are recomputed just before use) and the

@@ -24,5 +24,6 @@ from .binding import (  # noqa: F401
     oomb_select_pages,
     oomb_select_pages_mean,
     select_workspace_bytes,
+    split_plan,
 )
 from ._lib import LIB_PATH, OombError, lib  # noqa: F401

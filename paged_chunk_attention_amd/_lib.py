@@ -57,6 +57,7 @@ SIGNATURES = {
                                           c_size_t, c_void_p]),
     "oomb_fwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64, c_int32]),
     "oomb_bwd_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int64, c_int32]),
+    "oomb_split_plan": (c_int, [P_pool, c_int32, c_int64, c_int64, c_int32, ctypes.POINTER(c_int32)]),
     "oomb_copy_pages": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                 c_int32, c_void_p, c_void_p]),
     "oomb_copy_pages_sdma": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p,

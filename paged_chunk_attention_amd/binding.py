@@ -113,6 +113,15 @@ def oomb_page_summarize(pool: PagedPool, table: torch.Tensor, first_page: int, n
          seq_len, _stream(stream))
 
 
+def split_plan(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1, window: int = 0) -> dict:
+    """How the forward and backward calls of this geometry spread their work over the
+    GPU (oomb_split_plan): per pass, the key ranges or query-stream parts and the tiles
+    or key blocks per KV head that stay whole."""
+    out = (ctypes.c_int32 * 6)()
+    call("oomb_split_plan", pool.ref(), n_q, t0, sel_stride, window, out)
+    return {"fwd": (out[0], out[1]), "dq": (out[2], out[3]), "dkdv": (out[4], out[5])}
+
+
 def select_workspace_bytes(pool: PagedPool, n_q: int, t0: int) -> int:
     return int(lib().oomb_select_workspace_bytes(pool.ref(), n_q, t0))
 

@@ -268,7 +268,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 7; }
+int oomb_abi_version(void) { return 8; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -490,6 +490,26 @@ size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
   if (attn_geometry(a.pool, n_q, t0, sel_stride >= 0, sel_stride, window, &a) != OOMB_OK) return 0;
   size_t off, off_dq;
   return bwd_workspace(a, &off, &off_dq);
+}
+
+int oomb_split_plan(const oomb_pool* pool, int32_t n_q, int64_t t0, int64_t sel_stride,
+                    int32_t window, int32_t* out) {
+  oomb::AttnArgs a{};
+  int st = check_pool(pool, &a.pool, false, false);
+  if (st) return st;
+  if ((st = attn_geometry(a.pool, n_q, t0, sel_stride >= 0, sel_stride, window, &a))) return st;
+  if (out == nullptr) return fail(OOMB_ERR_INVALID, "out must hold 6 int32");
+  oomb::SplitPlan p[3] = {{1, 0}, {1, 0}, {1, 0}};
+  if (use_mfma(a.pool)) {
+    p[0] = oomb::fwd_plan(a);
+    p[1] = oomb::dq_plan(a);
+    p[2] = oomb::dkdv_plan(a);
+  }
+  for (int i = 0; i < 3; ++i) {
+    out[2 * i] = p[i].n_ks;
+    out[2 * i + 1] = p[i].n_ks > 1 ? p[i].whole : 0;
+  }
+  return OOMB_OK;
 }
 
 int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64_t table_stride,

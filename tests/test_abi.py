@@ -28,14 +28,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 7
+    assert lib.oomb_abi_version() == 8
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text
@@ -166,6 +166,41 @@ def test_split_counts_at_the_workloads(lib, name, n_q, t0, sel_stride, splits):
            + a256(0 if n_dq == 1 else n_dq * hq * n_q * d * 4))
     assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), n_q, t0, sel_stride, 0) == fwd, name
     assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), n_q, t0, sel_stride, 0) == bwd, name
+
+
+@pytest.mark.parametrize("name,n_q,t0,sel_stride,plan", [
+    # forward (ranges, whole tiles), dQ (ranges, whole tiles), dK/dV (parts, whole blocks)
+    ("sparse 1M", 4096, 1048576, 64, (1, 0, 1, 0, 4, 64)),
+    ("dense 128K", 4096, 126976, -1, (4, 64, 4, 64, 1, 0)),
+    ("sparse 4M", 8192, 4186112, 128, (2, 192, 2, 192, 2, 128)),
+])
+def test_split_plans_at_the_workloads(lib, name, n_q, t0, sel_stride, plan):
+    """The whole load-balance plan at the three benchmark workloads (448, 448 and 896
+    query tiles of 256 for the forward and dQ passes; 96, 1024 and 192 key blocks of 128
+    per KV head for dK/dV). Sparse 1M: the forward and dQ tiles too short to cut; dK/dV
+    keeps its 64 selected blocks per head whole (256, one per CU) and cuts the chunk's
+    32 in four. Dense 128K: 256 of the 448 tiles whole (64 per head), the rest in four
+    ranges; the 4,128 key blocks need no cut. Sparse 4M: 768 of 896 tiles whole, the
+    rest in two ranges; the 128 selected blocks per head whole (two per CU), the chunk's
+    64 in two parts."""
+    p = _pool()
+    out = (ctypes.c_int32 * 6)()
+    assert lib.oomb_split_plan(ctypes.byref(p), n_q, t0, sel_stride, 0, out) == L.OOMB_OK, name
+    assert tuple(out) == plan, name
+
+
+def test_split_plan_overrides_and_errors(lib, monkeypatch):
+    """The environment fixes a plan (whole clamped to the tiles or blocks per head; no
+    whole count when a pass is not cut), and a bad geometry is rejected."""
+    p = _pool()
+    out = (ctypes.c_int32 * 6)()
+    for var, val in (("OOMB_FWD_SPLITS", "3"), ("OOMB_FWD_WHOLE", "1000"), ("OOMB_DQ_SPLITS", "1"),
+                     ("OOMB_DQ_WHOLE", "5"), ("OOMB_DKDV_SPLITS", "2"), ("OOMB_DKDV_WHOLE", "7")):
+        monkeypatch.setenv(var, val)
+    assert lib.oomb_split_plan(ctypes.byref(p), 4096, 1048576, 64, 0, out) == L.OOMB_OK
+    assert tuple(out) == (3, 7 * 16, 1, 0, 2, 7)  # 16 tiles of 256 for each of 7 query heads
+    assert lib.oomb_split_plan(ctypes.byref(p), 0, 4096, -1, 0, out) == L.OOMB_ERR_INVALID
+    assert lib.oomb_split_plan(ctypes.byref(p), 4096, 4096, -1, 0, None) == L.OOMB_ERR_INVALID
 
 
 def test_window_arguments(lib):
