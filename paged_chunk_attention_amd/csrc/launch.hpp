@@ -161,11 +161,12 @@ hipError_t launch_bwd_scalar(const AttnArgs& a, hipStream_t s);
 // Matrix-core kernels: bf16, head_dim 128, page size >= 16.
 
 // The split counts below are chosen for load balance; OOMB_FWD_SPLITS, OOMB_DQ_SPLITS
-// and OOMB_DKDV_SPLITS (1..16) fix them instead (with OOMB_FWD_WHOLE, OOMB_DQ_WHOLE and
-// OOMB_DKDV_WHOLE for the tiles or key blocks per KV head that stay whole), read at every call, so the workspace
-// query and the call agree while the variables do not change. Every choice gives the
-// same results up to rounding order; the variables exist so that each code path can
-// be tested at small sizes. Returns 0 when the variable is unset or out of range.
+// and OOMB_DKDV_SPLITS (1..16) fix them instead (with OOMB_FWD_WHOLE, OOMB_DQ_WHOLE
+// and OOMB_DKDV_WHOLE for the tiles or key blocks per KV head that stay whole), read
+// at every call, so the workspace query and the call agree while the variables do not
+// change. Every choice gives the same results up to rounding order; the variables
+// exist so that each code path can be tested at small sizes. Returns 0 when the
+// variable is unset or out of range.
 inline int split_override(const char* var) {
   const char* v = getenv(var);
   if (v == nullptr) return 0;
@@ -245,8 +246,8 @@ SplitPlan fwd_plan(const AttnArgs& a);
 size_t fwd_partial_bytes(const AttnArgs& a, SplitPlan p);
 // A dK/dV plan with n_ks > 1 splits key blocks' query streams (per KV head the first
 // `whole` blocks stay whole); `part` then holds dkdv_partial_bytes(a, plan) bytes of
-// fp32 partials. A dQ plan with n_ks > 1 cuts
-// query tiles into key ranges; `dq_part` then holds dq_partial_bytes(a, plan) bytes.
+// fp32 partials. A dQ plan with n_ks > 1 cuts query tiles into key ranges; `dq_part`
+// then holds dq_partial_bytes(a, plan) bytes.
 hipError_t launch_bwd_mfma(const AttnArgs& a, SplitPlan kv, float* part, SplitPlan dq,
                            float* dq_part, hipStream_t s);
 // dQ pass of the matrix-core backward, launched first by launch_bwd_mfma; it also
@@ -256,7 +257,7 @@ SplitPlan dkdv_plan(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, SplitPlan p);
 SplitPlan dq_plan(const AttnArgs& a);
 size_t dq_partial_bytes(const AttnArgs& a, SplitPlan p);
-// Delta_i = dO_i . O_i, shared by both backward paths.
+// Delta_i = dO_i . O_i for the scalar backward (the matrix-core dQ pass forms its own).
 hipError_t launch_delta(const AttnArgs& a, hipStream_t s);
 
 }  // namespace oomb
