@@ -49,9 +49,9 @@ COMMON = [
 ]
 
 
-# Sources of the matrix-core attention kernels, whose hash tags measured profiles.
-# the kernels, the headers they include, and launch.hpp, which also holds the host rules
-# that decide how the passes split their work
+# Sources of the matrix-core attention kernels, whose hash tags measured profiles: the
+# kernels, the headers they include, and launch.hpp, which also holds the host rules that
+# decide how the passes split their work.
 MFMA_SOURCES = ["device_common.hpp", "launch.hpp", "mfma_tiles.hpp", "attn_fwd_mfma.hip",
                 "attn_dq_mfma.hip", "attn_dkdv_mfma.hip"]
 
