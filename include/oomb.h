@@ -10,7 +10,7 @@
  *     "Chunk-Recurrent Training with Activation Recomputation";
  *   - paged K/V and paged K/V gradients, in-place accumulation, no autograd:
  *     explainer 2.B "Paged KV Cache and Gradient Management"; the mlsanity page's
- *     abstract ("a paged memory manager for both the KV cache and its gradients");
+ *     abstract (pages managed for the key/value cache and for its gradients alike);
  *   - top-k page retrieval: explainer 2.D "Page-Level Sparse Attention".
  *
  * Conventions shared by every call
@@ -99,8 +99,9 @@ int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_st
                    int64_t tok_stride, int32_t n_tok, int64_t start_pos, void* stream);
 
 /* Page summarize - per-page key summary used to rank pages (explainer 2.D retrieves
- * pages "based on a representative vector"; the min/max form follows Quest, cited
- * by the paper). For KV head g and logical page j in [first_page, first_page+n_pages):
+ * pages by scoring them against an averaged stand-in vector; the min/max form follows
+ * Quest, cited by the paper). For KV head g and logical page j in
+ * [first_page, first_page+n_pages):
  *   k_summary[phys][0][d] = min, k_summary[phys][1][d] = max of K[t][d] over the
  *   page's tokens t with t < seq_len,
  * under the total order of values in which -0 < +0 (result independent of the
@@ -152,7 +153,7 @@ int oomb_rope(const void* x, int64_t x_head_stride, int64_t x_tok_stride, void* 
               void* stream);
 
 /* Selector variant: the page representative read as a plain average of the page's keys
- * (the explainer's "representative vector average", 2.D, read the other way).
+ * (the explainer's averaged stand-in vector, 2.D, read the other way).
  * oomb_page_summarize_mean writes kmean[phys] (fp32 [N][D], 16-byte aligned, caller
  * owned) for logical pages [first_page, first_page + n_pages) of every KV head: the
  * keys widened to fp32 and summed from +0 in token order over the tokens below

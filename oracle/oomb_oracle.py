@@ -10,7 +10,7 @@ Sources (the OOMB pages; "explainer" = the gist.science explainer of arXiv 2602.
     Training with Activation Recomputation"; mlsanity page, "Abstract (arXiv)".
   * paged KV cache and paged KV gradients, in-place accumulation: explainer, 2.B
     "Paged KV Cache and Gradient Management"; mlsanity abstract.
-  * top-K page retrieval from a representative vector: explainer, 2.D "Page-Level
+  * top-K page retrieval scored through an averaged stand-in vector: explainer, 2.D "Page-Level
     Sparse Attention".
   * CPU offload of pages and gradient pages: explainer, 2.C "Asynchronous KV Cache CPU
     Offloading" (moving pages is a copy; moving gradient pages adds them in).
@@ -121,7 +121,7 @@ def summarize(k_pool, table, summary, first_page: int, n_pages: int, seq_len: in
 
 # ---------------------------------------------------------------------------
 # Page selection (explainer 2.D "Top-K Page Retrieval": keep the K most relevant key
-# pages, judged from a representative vector average). Float32, fixed order.
+# pages, scored through an averaged stand-in vector). Float32, fixed order.
 # ---------------------------------------------------------------------------
 
 BLOCK = 64  # queries summed sequentially before the pairwise stage

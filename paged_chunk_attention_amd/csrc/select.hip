@@ -1,6 +1,6 @@
 // Top-k page retrieval for gfx950 (gist.science explainer of OOMB, 2.D
 // "Page-Level Sparse Attention": per chunk, keep only the K most relevant prior
-// key pages, judged from a representative vector). The rule is Quest-style:
+// key pages, scored through an averaged stand-in vector). The rule is Quest-style:
 //   qbar   = mean of the chunk's queries over the KV head's query-head group;
 //   score  = sum_d max(qbar_d * kmax_d, qbar_d * kmin_d) with per-page key min/max;
 //   keep the top-k scores, ties to the lower logical page id, ascending output.
