@@ -727,6 +727,29 @@ def context_build(pca, torch, pool, table, x, w, reps):
     return out
 
 
+def gemm_reference(torch, n=8192, reps=10):
+    """Secondary reference for the matrix-core roofline: the rate a library bf16 GEMM
+    (torch.matmul, i.e. hipBLASLt) reaches on this GPU for n x n x n, fp32 accumulation."""
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"TFLOPs": tf, "ms": ms, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+            "what": f"bf16 GEMM {n} x {n} x {n} through torch.matmul (hipBLASLt), "
+                    "achievable-peak reference"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -866,8 +889,12 @@ def main():
     if dom in FLOP_PER_PAIR_D:
         ach = FLOP_PER_PAIR_D[dom] * w.d * pairs / (dom_ms * 1e-3) / 1e12
         tr = measured_traffic(w.name, dom)
+        gemm = gemm_reference(torch)
+        log(f"[bench] bf16 GEMM reference: {gemm['TFLOPs']:.0f} TFLOP/s "
+            f"({100 * gemm['frac_of_peak']:.1f}% of peak)")
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "reference_gemm": gemm, "frac_of_reference_gemm": ach / gemm["TFLOPs"],
                 "traffic": None if tr is None else tr["bytes"],
                 "traffic_detail": tr,
                 "algorithmic_flop_per_launch": FLOP_PER_PAIR_D[dom] * w.d * pairs,
