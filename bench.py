@@ -727,27 +727,33 @@ def context_build(pca, torch, pool, table, x, w, reps):
     return out
 
 
-def gemm_reference(torch, n=8192, reps=10):
-    """Secondary reference for the matrix-core roofline: the rate a library bf16 GEMM
-    (torch.matmul, i.e. hipBLASLt) reaches on this GPU for n x n x n, fp32 accumulation."""
-    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
-    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
-    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
-    for _ in range(3):
-        torch.matmul(a, b, out=c)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        torch.matmul(a, b, out=c)
-    e1.record()
-    e1.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-    del a, b, c
-    return {"TFLOPs": tf, "ms": ms, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
-            "what": f"bf16 GEMM {n} x {n} x {n} through torch.matmul (hipBLASLt), "
-                    "achievable-peak reference"}
+def gemm_reference(torch, sizes=(4096, 8192, 16384), reps=10):
+    """Secondary reference for the matrix-core roofline: the best rate a library bf16
+    GEMM (torch.matmul, i.e. hipBLASLt) reaches on this GPU over n x n x n for the given
+    sizes, fp32 accumulation."""
+    best = None
+    for n in sizes:
+        a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        del a, b, c
+        if best is None or tf > best["TFLOPs"]:
+            best = {"TFLOPs": tf, "ms": ms, "n": n}
+    best.update({"frac_of_peak": best["TFLOPs"] / PEAK_BF16_TFLOPS,
+                 "what": f"best bf16 GEMM n x n x n over n in {list(sizes)} through torch.matmul "
+                         "(hipBLASLt), achievable-peak reference"})
+    return best
 
 
 def main():
