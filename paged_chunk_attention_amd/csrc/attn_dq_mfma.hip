@@ -68,10 +68,8 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   const int span = max(0, nblk - blo_tile);
   const int b0 = blo_tile + span * kr / n_rng, b1 = blo_tile + span * (kr + 1) / n_rng;  // this workgroup's blocks
   const float c2 = a.scale * kLog2e;
-  // One wave of each SIMD (waves w and w + 4 share one) runs its blocks at raised
-  // priority: it wins the matrix core when both are ready, and the other drifts behind
-  // into the first one's exp/dS arithmetic (1-1.5% faster than equal priorities).
-  const bool lead = wave < DQ_WAVES / 2;
+  // (Both waves of a SIMD run at the same priority: with blocks of 128 keys, raising one
+  // of them, which helped at 64, measured 0-0.5% slower.)
 
   // This wave's queries: blocks past its last query are skipped; blocks reaching past
   // its first query need the mask.
@@ -160,7 +158,6 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
       }
     }
     if (b < nblk_w && b >= blo_w) {
-      if (lead) __builtin_amdgcn_s_setprio(1);
       FragOffsets o = fo;
       o.opaque();
       const bool mask = b * DQ_KB + DQ_KB - 1 > klim_w0 || b * DQ_KB < klo_wl;
@@ -214,7 +211,6 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
         for (int db = 0; db < 4; ++db) dqt[db] = mfma(tb[db], dsb[1], dqt[db]);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
     wait_vm<0>();     // block b + 1 has landed (this wave's part) ...
     phase_barrier();  // ... everyone's, and nobody reads block b any more
   };
