@@ -28,7 +28,7 @@ template <bool kBf16>
 __global__ __launch_bounds__(256) void qbar_partial_kernel(SelectArgs a) {
   const int D = a.pool.D;
   const int lanes_per_block = D / 8;
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int b = t / lanes_per_block, d0 = 8 * (t % lanes_per_block);
   const int g = blockIdx.y;
   if (b >= a.nb) return;
@@ -334,9 +334,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
 static void launch_scores(const SelectArgs& a, hipStream_t s) {
   const bool bf = a.pool.dtype == 0;
   const int D = a.pool.D;
-  dim3 g1((a.nb * (D / 8) + 255) / 256, a.pool.Hkv);
-  if (bf) OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<true>, g1, dim3(256), 0, s, a);
-  else OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<false>, g1, dim3(256), 0, s, a);
+  // one wavefront per workgroup: the few hundred threads per KV head spread over all CUs
+  dim3 g1((a.nb * (D / 8) + 63) / 64, a.pool.Hkv);
+  if (bf) OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<true>, g1, dim3(64), 0, s, a);
+  else OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<false>, g1, dim3(64), 0, s, a);
   int n2 = 1;
   while (n2 < a.nb) n2 <<= 1;
   OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
