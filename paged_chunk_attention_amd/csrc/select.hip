@@ -250,9 +250,43 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
     for (int j = threadIdx.x; j < n; j += kTopkThreads) s_keys[key_slot(j)] = score_key(sc[j]);
   auto key = [&](int j) -> uint32_t { return in_lds ? s_keys[key_slot(j)] : score_key(sc[j]); };
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The keys' range: a leading digit on which the smallest and the largest key agree
+  // (with every digit above it) is that of every key, so its histogram pass would only
+  // confirm it. Page scores are close together, so this usually skips the first pass.
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int j = threadIdx.x; j < n; j += kTopkThreads) {
+    const uint32_t u = key(j);
+    lo = u < lo ? u : lo;
+    hi = u > hi ? u : hi;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t ol = __shfl_xor(lo, off, 64), oh = __shfl_xor(hi, off, 64);
+    lo = ol < lo ? ol : lo;
+    hi = oh > hi ? oh : hi;
+  }
+  if (lane == 0) {
+    s_whist[wave][0] = static_cast<int>(lo);
+    s_whist[wave][1] = static_cast<int>(hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t wl = static_cast<uint32_t>(s_whist[w][0]), wh = static_cast<uint32_t>(s_whist[w][1]);
+    lo = wl < lo ? wl : lo;
+    hi = wh > hi ? wh : hi;
+  }
+  __syncthreads();
   uint32_t prefix = 0, mask = 0;
   int krem = k;
+  bool leading = true;  // every pass so far was skipped
   for (int shift = 24; shift >= 0; shift -= 8) {
+    if (leading && ((lo ^ hi) >> shift) == 0u) {  // uniform: every key has this digit
+      prefix |= lo & (255u << shift);
+      mask |= 255u << shift;
+      continue;
+    }
+    leading = false;
     for (int i = lane; i < 256; i += 64) s_whist[wave][i] = 0;
     __syncthreads();
     for (int j = threadIdx.x; j < n; j += kTopkThreads) {
