@@ -103,47 +103,74 @@ __global__ __launch_bounds__(256) void qbar_final_kernel(SelectArgs a) {
   if (threadIdx.x == 0) a.qbar[g * D + d] = s_tree[0] * a.inv;
 }
 
-// One wavefront per candidate page; 4 pages per workgroup.
+// D / 8 lanes per candidate page (64 / (D / 8) pages per wavefront, 4 wavefronts per
+// workgroup): lane l of a page holds dimensions 8l .. 8l + 7, loaded as one 16-byte
+// row piece of kmin and of kmax (bf16). The stride-halving tree over d keeps its order:
+// the levels s = D/2 .. 8 pair lane l with lane l ^ (s / 8) (same slot), the levels
+// s = 4, 2, 1 pair slots within the lane, each sum a[d] + a[d + s] as in the definition.
 template <bool kBf16, int D>
 __global__ __launch_bounds__(256) void page_score_kernel(SelectArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int LP = D / 8;        // lanes per page
+  constexpr int PW = 64 / LP;      // pages per wavefront
+  const int lane = threadIdx.x & 63, sub = lane % LP;
+  const int j = (blockIdx.x * 4 + (threadIdx.x >> 6)) * PW + lane / LP;
   const int g = blockIdx.y;
-  if (j >= a.n_cand) return;
-  const int64_t ph = a.table[g * a.tstride + j];
-  float score;
-  if (ph < 0 || ph >= a.pool.N) {
-    score = -__builtin_inff();
-  } else {
-    constexpr int R = D / 64;
-    float e[R];
+  const bool cand = j < a.n_cand;
+  const int64_t ph = cand ? a.table[g * a.tstride + j] : -1;
+  const bool ok = ph >= 0 && ph < a.pool.N;
+  const int d0 = 8 * sub;
+  float e[8];
+  {
+    float qb[8], kmin[8], kmax[8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int d = lane + 64 * r;
-      const float qb = a.qbar[g * D + d];
-      float kmin, kmax;
-      if (kBf16) {
-        const bf16_t* sm = reinterpret_cast<const bf16_t*>(a.pool.k_summary) + ph * 2 * D;
-        kmin = to_f32(sm[d]);
-        kmax = to_f32(sm[D + d]);
-      } else {
-        const float* sm = reinterpret_cast<const float*>(a.pool.k_summary) + ph * 2 * D;
-        kmin = sm[d];
-        kmax = sm[D + d];
+    for (int c = 0; c < 8; ++c) qb[c] = a.qbar[g * D + d0 + c];  // qbar_out may be 4-byte aligned only
+    const int64_t row = ok ? ph * 2 * D : 0;  // invalid pages read page 0 and are discarded
+    if (kBf16) {
+      const bf16_t* sm = reinterpret_cast<const bf16_t*>(a.pool.k_summary) + row + d0;
+      const u32x4 wmin = *reinterpret_cast<const u32x4*>(sm);
+      const u32x4 wmax = *reinterpret_cast<const u32x4*>(sm + D);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kmin[2 * c] = __uint_as_float(wmin[c] << 16);
+        kmin[2 * c + 1] = __uint_as_float(wmin[c] & 0xFFFF0000u);
+        kmax[2 * c] = __uint_as_float(wmax[c] << 16);
+        kmax[2 * c + 1] = __uint_as_float(wmax[c] & 0xFFFF0000u);
       }
-      const float hi = qb * kmax, lo = qb * kmin;
-      e[r] = hi > lo ? hi : lo;
-    }
-    float acc = e[0];
-    if (R == 2) acc = e[0] + e[1];  // tree level s = 64: a[d] + a[d + 64]
+    } else {
+      const float* sm = reinterpret_cast<const float*>(a.pool.k_summary) + row + d0;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float other = __shfl_xor(acc, s, 64);  // lane d < s receives a[d + s]
-      acc = acc + other;
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(sm + 4 * h);
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(sm + D + 4 * h);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kmin[4 * h + c] = n4[c];
+          kmax[4 * h + c] = x4[c];
+        }
+      }
     }
-    score = acc;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float hi = qb[c] * kmax[c], lo = qb[c] * kmin[c];
+      e[c] = hi > lo ? hi : lo;
+    }
   }
-  if (lane == 0) a.score[g * a.score_stride + j] = score;
+  // levels s = D/2 .. 8: lane l (dimension block l) receives the block s / 8 lanes on
+  // (only the lanes still in the lower half keep a meaningful sum, as in the tree)
+#pragma unroll
+  for (int s = D / 2; s >= 8; s >>= 1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) e[c] = e[c] + __shfl_xor(e[c], s / 8, 64);
+  }
+  // levels s = 4, 2, 1 inside the lane
+  e[0] = e[0] + e[4];
+  e[1] = e[1] + e[5];
+  e[2] = e[2] + e[6];
+  e[3] = e[3] + e[7];
+  e[0] = e[0] + e[2];
+  e[1] = e[1] + e[3];
+  e[0] = e[0] + e[1];
+  if (cand && sub == 0) a.score[g * a.score_stride + j] = ok ? e[0] : -__builtin_inff();
 }
 
 // Mean-key scores: score_j = sum_d fp32(qbar_d * kmean_jd), the products rounded to
@@ -375,16 +402,19 @@ static void launch_scores(const SelectArgs& a, hipStream_t s) {
   int n2 = 1;
   while (n2 < a.nb) n2 <<= 1;
   OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
-  dim3 g3((a.n_cand + 3) / 4, a.pool.Hkv);
+  dim3 g3((a.n_cand + 3) / 4, a.pool.Hkv);  // mean scores: one wavefront per page
+  // min/max scores: 64 / (D / 8) pages per wavefront, 4 wavefronts per workgroup
+  const int per_wg = 4 * (64 / (D / 8));
+  dim3 g4((a.n_cand + per_wg - 1) / per_wg, a.pool.Hkv);
   if (a.kmean != nullptr) {
     if (D == 128) OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<128>, g3, dim3(256), 0, s, a);
     else OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<64>, g3, dim3(256), 0, s, a);
     return;
   }
-  if (bf && D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<true, 128>), g3, dim3(256), 0, s, a);
-  else if (bf) OOMB_LAUNCH("page_score", (page_score_kernel<true, 64>), g3, dim3(256), 0, s, a);
-  else if (D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<false, 128>), g3, dim3(256), 0, s, a);
-  else OOMB_LAUNCH("page_score", (page_score_kernel<false, 64>), g3, dim3(256), 0, s, a);
+  if (bf && D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<true, 128>), g4, dim3(256), 0, s, a);
+  else if (bf) OOMB_LAUNCH("page_score", (page_score_kernel<true, 64>), g4, dim3(256), 0, s, a);
+  else if (D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<false, 128>), g4, dim3(256), 0, s, a);
+  else OOMB_LAUNCH("page_score", (page_score_kernel<false, 64>), g4, dim3(256), 0, s, a);
 }
 
 // Scores are always computed when there are candidates (the top-k needs them unless
