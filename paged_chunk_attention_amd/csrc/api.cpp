@@ -398,8 +398,8 @@ int oomb_select_pages_mean(const oomb_pool* pool, const int32_t* table, int64_t 
                            int32_t* sel, int64_t sel_stride, int32_t* count, float* qbar_out,
                            float* score_out, int64_t score_stride, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  if (kmean == nullptr || (reinterpret_cast<uintptr_t>(kmean) & 3u))
-    return fail(OOMB_ERR_INVALID, "kmean must be a 4-byte aligned device pointer");
+  if (kmean == nullptr || !aligned16(kmean))
+    return fail(OOMB_ERR_INVALID, "kmean must be a 16-byte aligned device pointer");
   return select_common(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, top_k,
                        kmean, sel, sel_stride, count, qbar_out, score_out, score_stride, workspace,
                        workspace_bytes, stream);

@@ -177,32 +177,39 @@ __global__ __launch_bounds__(256) void page_score_kernel(SelectArgs a) {
 // fp32 and summed by the same stride-halving tree over d as the min/max scores.
 template <int D>
 __global__ __launch_bounds__(256) void page_score_mean_kernel(SelectArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the min/max kernel's layout: D / 8 lanes per page, lane l holds dimensions
+  // 8l .. 8l + 7 (two 16-byte loads of the page's fp32 mean), the same tree order
+  constexpr int LP = D / 8;
+  constexpr int PW = 64 / LP;
+  const int lane = threadIdx.x & 63, sub = lane % LP;
+  const int j = (blockIdx.x * 4 + (threadIdx.x >> 6)) * PW + lane / LP;
   const int g = blockIdx.y;
-  if (j >= a.n_cand) return;
-  const int64_t ph = a.table[g * a.tstride + j];
-  float score;
-  if (ph < 0 || ph >= a.pool.N) {
-    score = -__builtin_inff();
-  } else {
-    constexpr int R = D / 64;
-    float e[R];
+  const bool cand = j < a.n_cand;
+  const int64_t ph = cand ? a.table[g * a.tstride + j] : -1;
+  const bool ok = ph >= 0 && ph < a.pool.N;
+  const int d0 = 8 * sub;
+  const float* km = a.kmean + (ok ? ph * D : 0) + d0;  // invalid pages read page 0, discarded
+  const f32x4 k0 = *reinterpret_cast<const f32x4*>(km);
+  const f32x4 k1 = *reinterpret_cast<const f32x4*>(km + 4);
+  float e[8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int d = lane + 64 * r;
-      e[r] = a.qbar[g * D + d] * a.kmean[ph * D + d];
-    }
-    float acc = e[0];
-    if (R == 2) acc = e[0] + e[1];  // tree level s = 64: a[d] + a[d + 64]
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float other = __shfl_xor(acc, s, 64);
-      acc = acc + other;
-    }
-    score = acc;
+  for (int c = 0; c < 4; ++c) {
+    e[c] = a.qbar[g * D + d0 + c] * k0[c];
+    e[4 + c] = a.qbar[g * D + d0 + 4 + c] * k1[c];
   }
-  if (lane == 0) a.score[g * a.score_stride + j] = score;
+#pragma unroll
+  for (int s = D / 2; s >= 8; s >>= 1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) e[c] = e[c] + __shfl_xor(e[c], s / 8, 64);
+  }
+  e[0] = e[0] + e[4];
+  e[1] = e[1] + e[5];
+  e[2] = e[2] + e[6];
+  e[3] = e[3] + e[7];
+  e[0] = e[0] + e[2];
+  e[1] = e[1] + e[3];
+  e[0] = e[0] + e[1];
+  if (cand && sub == 0) a.score[g * a.score_stride + j] = ok ? e[0] : -__builtin_inff();
 }
 
 // Order-preserving unsigned key of an fp32 score (-0 folded onto +0, NaN lowest).
@@ -402,13 +409,12 @@ static void launch_scores(const SelectArgs& a, hipStream_t s) {
   int n2 = 1;
   while (n2 < a.nb) n2 <<= 1;
   OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
-  dim3 g3((a.n_cand + 3) / 4, a.pool.Hkv);  // mean scores: one wavefront per page
-  // min/max scores: 64 / (D / 8) pages per wavefront, 4 wavefronts per workgroup
+  // 64 / (D / 8) pages per wavefront, 4 wavefronts per workgroup
   const int per_wg = 4 * (64 / (D / 8));
   dim3 g4((a.n_cand + per_wg - 1) / per_wg, a.pool.Hkv);
   if (a.kmean != nullptr) {
-    if (D == 128) OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<128>, g3, dim3(256), 0, s, a);
-    else OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<64>, g3, dim3(256), 0, s, a);
+    if (D == 128) OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<128>, g4, dim3(256), 0, s, a);
+    else OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<64>, g4, dim3(256), 0, s, a);
     return;
   }
   if (bf && D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<true, 128>), g4, dim3(256), 0, s, a);
