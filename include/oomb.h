@@ -161,7 +161,7 @@ int oomb_rope(const void* x, int64_t x_head_stride, int64_t x_tok_stride, void* 
  * such token are left unchanged. oomb_select_pages_mean is oomb_select_pages with
  *   score_j = stride-halving tree over d of fp32(qbar[d] * kmean[phys_j][d])
  * (same qbar, same tree, same top-k rule, same workspace size); k_summary is not
- * used. */
+ * used, and kmean must be the 16-byte aligned array the summary call writes. */
 int oomb_page_summarize_mean(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                              int64_t first_page, int64_t n_pages, int64_t seq_len, float* kmean,
                              void* stream);
