@@ -770,11 +770,11 @@ def main():
     ap.add_argument("--cpu-pairs", type=float, default=1.5e9,
                     help="bound on the attended pairs of the CPU-baseline sample (~13 s on 16 threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layer", action="store_true",
-                    help="also time one chunk-recurrent attention layer (65,536 tokens)")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip timing one chunk-recurrent attention layer (65,536 tokens)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offload measurements (sparse workloads)")
-    ap.add_argument("--also", default="dense128k,sweep256k,sweep256k_top64,tiny",
+    ap.add_argument("--also", default="dense128k,sparse4m,local1m,sweep256k,sweep256k_top64,tiny",
                     help="comma-separated other workloads to time briefly ('none' for none)")
     ap.add_argument("--hbm-reps", type=int, default=3,
                     help="cold-cache repetitions of the whole-context append and summarize")
@@ -930,7 +930,7 @@ def main():
             f"overhead {100 * offload['overlap']['overhead']:.1f} %")
 
     layer = None
-    if args.layer:
+    if not args.no_layer:
         log("[bench] layer leg ...")
         layer = layer_leg(pca, torch)
         log(f"[bench] layer: dense {layer['dense']['tokens_per_s']:.0f} tok/s, top64 "

@@ -49,7 +49,7 @@ __all__ = [
     "query_summary", "page_scores", "top_k_pages", "select_pages",
     "attended_pages", "key_positions", "fwd", "bwd", "sweep",
     "copy_pages", "add_pages", "fetch_selected",
-    "summarize_mean", "page_scores_mean", "select_pages_mean", "rope",
+    "summarize_mean", "page_scores_mean", "select_pages_mean", "rope", "layer_reference",
 ]
 
 
@@ -180,9 +180,10 @@ def page_scores(qbar: np.ndarray, summary: torch.Tensor, table: torch.Tensor, g:
     p_lo = qb * kmin
     a = np.where(p_hi > p_lo, p_hi, p_lo).astype(np.float32)
     s = a.shape[1] // 2
-    while s >= 1:
-        a[:, :s] = a[:, :s] + a[:, s:2 * s]
-        s //= 2
+    with np.errstate(invalid="ignore"):      # inf + -inf is NaN by IEEE rules: intended
+        while s >= 1:
+            a[:, :s] = a[:, :s] + a[:, s:2 * s]
+            s //= 2
     return a[:, 0].copy()
 
 
@@ -225,9 +226,17 @@ def page_scores_mean(qbar: np.ndarray, kmean: np.ndarray, table: torch.Tensor, g
 
 def top_k_pages(scores: np.ndarray, k: int) -> List[int]:
     """The k best pages by (score descending, logical id ascending), in ascending id
-    order. Scores compare as IEEE values (-0 equals +0). k >= n keeps every page."""
+    order. Scores compare as IEEE values (-0 equals +0). A NaN score (keys holding
+    infinities of both signs, say) ranks below every number, -inf included; NaN pages
+    tie with each other, so among them the lower ids come first. k >= n keeps every
+    page."""
     n = len(scores)
-    order = sorted(range(n), key=lambda j: (-float(scores[j]), j))
+
+    def rank(j):
+        x = float(scores[j])
+        return (1, 0.0, j) if math.isnan(x) else (0, -x, j)
+
+    order = sorted(range(n), key=rank)
     return sorted(order[:max(0, min(k, n))])
 
 
@@ -338,14 +347,16 @@ def fwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, row_block: int = 2
 
 
 def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
-        dk_pool=None, dv_pool=None, gtable=None, row_block: int = 256, window: int = 0):
+        dk_pool=None, dv_pool=None, gtable=None, row_block: int = 256, window: int = 0,
+        with_fwd: bool = False):
     """Analytic backward of fwd for the loss sum(dout * O), with O and LSE recomputed
     here (explainer 2.A: activations are recomputed just before the gradient).
 
     Returns dQ [Hq, C, D] float64. With dk_pool/dv_pool (float64 [Ng, P, D]) and
     gtable, adds dK/dV of every attended key into its gradient page (explainer 2.B:
     gradients accumulate in place in paged storage). Also returns the per-head
-    key-gradient arrays as a list of (positions, dK, dV).
+    key-gradient arrays as a list of (positions, dK, dV). with_fwd=True appends the
+    recomputed O and LSE (the same values fwd returns) to the result.
         Delta_i = dO_i . O_i
         dP_it   = dO_i . v_t
         dS_it   = P_it (dP_it - Delta_i)
@@ -359,6 +370,8 @@ def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
     G = hq // hkv
     P = k_pool.shape[1]
     dQ = torch.zeros(hq, C, D, dtype=torch.float64)
+    O = torch.zeros(hq, C, D, dtype=torch.float64) if with_fwd else None
+    L = torch.zeros(hq, C, dtype=torch.float64) if with_fwd else None
     per_head = []
     qpos_all = t0 + torch.arange(C)
     for g in range(hkv):
@@ -370,8 +383,11 @@ def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
         dV = torch.zeros_like(V)
         for i0, i1 in _rows(C, row_block):
             Qb, dOb = Qg[:, i0:i1], dOg[:, i0:i1]
-            Pm, _ = _probs(Qb, K, pos, qpos_all[i0:i1], scale, window)
+            Pm, lse = _probs(Qb, K, pos, qpos_all[i0:i1], scale, window)
             Ob = torch.matmul(Pm, V)
+            if with_fwd:
+                O[g * G:(g + 1) * G, i0:i1] = Ob
+                L[g * G:(g + 1) * G, i0:i1] = lse
             delta = (dOb * Ob).sum(dim=-1, keepdim=True)
             dP = torch.matmul(dOb, V.T)
             dS = Pm * (dP - delta)
@@ -383,6 +399,8 @@ def bwd(q, k_pool, v_pool, table, t0: int, sel, scale: float, dout,
             phys = gtable[g].long()[pos // P]
             dk_pool.index_put_((phys, pos % P), dK, accumulate=True)
             dv_pool.index_put_((phys, pos % P), dV, accumulate=True)
+    if with_fwd:
+        return dQ, per_head, O, L
     return dQ, per_head
 
 
@@ -502,3 +520,70 @@ def rope(x: torch.Tensor, pos0: int, theta: float = 10000.0, inverse: bool = Fal
     lo, hi = xd[..., :half], xd[..., half:]
     return torch.cat([lo * c - hi * s, hi * c + lo * s], dim=-1)
 
+
+
+# ---------------------------------------------------------------------------
+# One chunk-recurrent attention layer as a single full-sequence computation
+# (explainer 2.A: chunking with recomputation must give the gradients of the whole
+# sequence; 2.D: top-k layers attend the pages each chunk selected, local layers a
+# window).
+# ---------------------------------------------------------------------------
+
+def layer_reference(x, wq, wk, wv, wo, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                    page: int, chunk: int, scale: float, theta: float, dy,
+                    top_k: Optional[int] = None, window: int = 0,
+                    sel_dtype: torch.dtype = torch.bfloat16):
+    """y = o Wo with o = attention(q, k, v), q = rope(x Wq), k = rope(x Wk), v = x Wv
+    (positions 0..T-1), over the whole sequence at once in float64, and the gradients
+    of sum(dy * y) with respect to x, Wq, Wk, Wv, Wo by autograd.
+
+    Query i attends key t iff t <= i, and with a window also t > i - window; for a
+    top-k layer also iff page(t) is one of the pages the chunk holding i selected, or
+    one of that chunk's own pages. The selection of chunk c is select_pages applied to
+    the chunk's queries and the keys before it, each rounded once to sel_dtype (the
+    dtype the layer keeps its activations in), with the summaries of complete pages.
+
+    Returns (y, dx, [dWq, dWk, dWv, dWo], sels) with sels[c] = one list of selected
+    logical pages per KV head (None for layers without selection)."""
+    f64 = torch.float64
+    xs = x.detach().to("cpu", f64).requires_grad_()
+    ws = [w.detach().to("cpu", f64).requires_grad_() for w in (wq, wk, wv, wo)]
+    T = xs.shape[0]
+    hq, hkv, D = n_q_heads, n_kv_heads, head_dim
+    G = hq // hkv
+    q = rope((xs @ ws[0]).view(T, hq, D).transpose(0, 1), 0, theta)
+    k = rope((xs @ ws[1]).view(T, hkv, D).transpose(0, 1), 0, theta)
+    v = (xs @ ws[2]).view(T, hkv, D).transpose(0, 1)
+    pos = torch.arange(T)
+    allowed = pos[None, :] <= pos[:, None]
+    if window:
+        allowed = allowed & (pos[None, :] > pos[:, None] - window)
+    allowed = allowed[None].expand(hq, T, T).clone()
+    sels = [None] * (T // chunk)
+    if top_k is not None:
+        n_pages = -(-T // page)
+        ident = torch.arange(hkv * n_pages, dtype=torch.int32).reshape(hkv, n_pages)
+        kr = k.detach().to(sel_dtype)
+        kpool = torch.zeros(hkv * n_pages, page, D, dtype=sel_dtype)
+        append(kpool, ident, kr, 0)
+        summ = torch.zeros(hkv * n_pages, 2, D, dtype=sel_dtype)
+        summarize(kpool, ident, summ, 0, n_pages, T)
+        page_of = pos // page
+        for c in range(T // chunk):
+            t0 = c * chunk
+            qc = q.detach()[:, t0:t0 + chunk].to(sel_dtype)
+            chosen = [s_ for (_, _, s_) in select_pages(qc, summ, ident, t0, page, G, top_k)]
+            sels[c] = chosen
+            for h in range(hq):
+                ok = torch.zeros(n_pages, dtype=torch.bool)
+                ok[torch.as_tensor(chosen[h // G], dtype=torch.long)] = True
+                ok[t0 // page:] = True
+                allowed[h, t0:t0 + chunk] &= ok[page_of][None, :]
+    kk = k.repeat_interleave(G, dim=0)
+    vv = v.repeat_interleave(G, dim=0)
+    S = (q @ kk.transpose(1, 2)) * scale
+    S = S.masked_fill(~allowed, -math.inf)
+    o = torch.softmax(S, dim=-1) @ vv
+    y = o.transpose(0, 1).reshape(T, hq * D) @ ws[3]
+    (y * dy.detach().to("cpu", f64)).sum().backward()
+    return y.detach(), xs.grad, [w.grad for w in ws], (sels if top_k is not None else None)

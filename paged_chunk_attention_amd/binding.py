@@ -2,7 +2,15 @@
 
 Each function has the C name, checks tensor devices/dtypes/shapes, allocates
 outputs and workspace with torch when the caller passes none, and calls the
-library on torch's current stream. No step of the computation happens here.
+library on the given stream (torch's current stream by default). What a function
+allocates or fills is allocated and filled on that same stream, so the fills are
+ordered before the library's kernels and the caching allocator reuses the memory
+only for later work on that stream. No step of the computation happens here.
+
+Setting OOMB_CHECK_TABLES=1 makes every call check, on the host, that the page
+tables it reads are injective over the pages the call touches and that selections
+are strictly ascending candidate ids (check_page_tables, check_selection). The
+check copies the tables to the host and synchronises, so it is for debugging.
 
 `PagedPool` owns one layer's page pool (K, V, key summaries, fp32 dK/dV) as torch
 tensors and describes it to the library. The page tables are plain int32 tensors
@@ -14,8 +22,10 @@ the autograd graph).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
-from typing import Optional, Tuple
+import os
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -32,6 +42,102 @@ def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(stream):
+    """Context in which the binding allocates and fills: the call's stream when one is
+    given (torch.cuda.stream makes it current), else torch's current stream as is."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _new(kind: str, shape, dtype, device, fill=None) -> torch.Tensor:
+    """Every tensor the binding creates for a call comes from here (inside _on)."""
+    if kind == "full":
+        return torch.full(shape, fill, dtype=dtype, device=device)
+    if kind == "zeros":
+        return torch.zeros(shape, dtype=dtype, device=device)
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _checks_on() -> bool:
+    return os.environ.get("OOMB_CHECK_TABLES", "0") not in ("", "0")
+
+
+def check_page_tables(table: torch.Tensor, pages, n_pages: int, name: str = "table") -> None:
+    """Raise ValueError unless the logical pages a call touches map to distinct physical
+    pages in [0, n_pages).
+
+    table: int32 [Hkv, stride]; pages: the number of leading logical pages in use per KV
+    head, or one list of logical ids per KV head. All the (head, page) entries together
+    must be distinct, since the KV heads share one page array. Two logical pages on one
+    physical page would make the forward count those keys twice and two backward
+    workgroups add into one gradient row at once."""
+    t = table.detach().to("cpu", torch.int64)
+    if isinstance(pages, int):
+        if pages > t.shape[1]:
+            raise ValueError(f"{name}: {pages} pages in use but only {t.shape[1]} columns")
+        ids = t[:, :pages].reshape(-1)
+    else:
+        rows = []
+        for g, lp in enumerate(pages):
+            lp = torch.as_tensor(list(lp), dtype=torch.int64)
+            if lp.numel() and (int(lp.min()) < 0 or int(lp.max()) >= t.shape[1]):
+                raise ValueError(f"{name}: logical page outside the table of KV head {g}")
+            rows.append(t[g, lp])
+        ids = torch.cat(rows) if rows else torch.zeros(0, dtype=torch.int64)
+    bad = (ids < 0) | (ids >= n_pages)
+    if bool(bad.any()):
+        raise ValueError(f"{name}: physical id {int(ids[bad][0])} outside [0, {n_pages})")
+    uniq, counts = torch.unique(ids, return_counts=True)
+    if bool((counts > 1).any()):
+        raise ValueError(f"{name}: physical page {int(uniq[counts > 1][0])} is mapped "
+                         f"{int(counts.max())} times")
+
+
+def check_selection(sel: torch.Tensor, count: torch.Tensor, n_cand: int) -> None:
+    """Raise ValueError unless, for every KV head g, sel[g, :count[g]] (count clamped to
+    the row length and to n_cand, as the kernels clamp it) are strictly ascending
+    candidate ids in [0, n_cand)."""
+    s = sel.detach().to("cpu", torch.int64)
+    c = count.detach().to("cpu", torch.int64)
+    for g in range(s.shape[0]):
+        row = s[g, :max(0, min(int(c[g]), s.shape[1], n_cand))]
+        if row.numel() and (int(row.min()) < 0 or int(row.max()) >= n_cand):
+            raise ValueError(f"selection of KV head {g}: id outside [0, {n_cand})")
+        if row.numel() > 1 and not bool((row[1:] > row[:-1]).all()):
+            raise ValueError(f"selection of KV head {g} is not strictly ascending")
+
+
+def attended_logical_pages(hkv: int, P: int, t0: int, n_q: int, sel=None, count=None,
+                           window: int = 0):
+    """Per KV head, the logical pages an attention call reads: the selected (or, dense,
+    all) prior pages, or with a window the prior pages it reaches, then the chunk's own."""
+    first_local, last_local = t0 // P, (t0 + max(n_q, 1) - 1) // P
+    local = list(range(first_local, last_local + 1))
+    if sel is not None:
+        s = sel.detach().to("cpu", torch.int64)
+        c = count.detach().to("cpu", torch.int64)
+        out = []
+        for g in range(hkv):
+            n = max(0, min(int(c[g]), s.shape[1], first_local))
+            out.append(sorted(set(s[g, :n].tolist())) + local)
+        return out
+    lo = 0 if window <= 0 else max(0, t0 - window + 1) // P
+    return [list(range(lo, first_local)) + local for _ in range(hkv)]
+
+
+def _debug_check(pool, table, t0: int, n_q: int, sel=None, count=None, window: int = 0,
+                 gtable=None) -> None:
+    """The OOMB_CHECK_TABLES checks of one attention call (no-op when unset)."""
+    if not _checks_on() or n_q == 0:
+        return
+    n_cand = t0 // pool.page_size
+    if sel is not None:
+        check_selection(sel, count, n_cand)
+    pages = attended_logical_pages(pool.num_kv_heads, pool.page_size, t0, n_q, sel, count, window)
+    check_page_tables(table, pages, pool.num_pages, "table")
+    if gtable is not None:
+        check_page_tables(gtable, pages, pool.dk.shape[0], "gtable")
 
 
 class PagedPool:
@@ -101,6 +207,11 @@ def oomb_kv_append(pool: PagedPool, table: torch.Tensor, k_new: torch.Tensor,
     hs, ts = _view(k_new, pool, pool.num_kv_heads, "k_new")
     if _view(v_new, pool, pool.num_kv_heads, "v_new") != (hs, ts) or v_new.shape != k_new.shape:
         raise ValueError("k_new and v_new must have the same shape and strides")
+    n = k_new.shape[1]
+    if _checks_on() and n > 0:
+        P = pool.page_size
+        written = list(range(start_pos // P, (start_pos + n - 1) // P + 1))
+        check_page_tables(table, [written] * pool.num_kv_heads, pool.num_pages, "table")
     call("oomb_kv_append", pool.ref(), _ptr(table), table.stride(0), _ptr(k_new), _ptr(v_new),
          hs, ts, k_new.shape[1], start_pos, _stream(stream))
 
@@ -140,7 +251,7 @@ def fwd_workspace_bytes(pool: PagedPool, n_q: int, t0: int, sel_stride: int = -1
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
     if ws is None:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = _new("empty", max(nbytes, 256), torch.uint8, device)
     if ws.numel() < nbytes or ws.data_ptr() % 256:
         raise ValueError(f"workspace must hold {nbytes} bytes at a 256-byte aligned address")
     return ws
@@ -158,15 +269,18 @@ def oomb_select_pages(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0:
     n_q = q.shape[1]
     n_cand = t0 // pool.page_size
     k = max(0, min(top_k, n_cand))
-    if sel is None:
-        sel = torch.full((pool.num_kv_heads, max(k, 1)), -1, dtype=torch.int32, device=q.device)
-    if count is None:
-        count = torch.zeros(pool.num_kv_heads, dtype=torch.int32, device=q.device)
-    ws = _workspace(select_workspace_bytes(pool, n_q, t0), q.device, workspace)
-    score_stride = 0 if score_out is None else score_out.stride(0)
-    call("oomb_select_pages", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts, n_q, t0,
-         top_k, _ptr(sel), sel.stride(0), _ptr(count), _ptr(qbar_out), _ptr(score_out),
-         score_stride, _ptr(ws), ws.numel(), _stream(stream))
+    with _on(stream):
+        if sel is None:
+            sel = _new("full", (pool.num_kv_heads, max(k, 1)), torch.int32, q.device, -1)
+        if count is None:
+            count = _new("zeros", pool.num_kv_heads, torch.int32, q.device)
+        ws = _workspace(select_workspace_bytes(pool, n_q, t0), q.device, workspace)
+        score_stride = 0 if score_out is None else score_out.stride(0)
+        if _checks_on():
+            check_page_tables(table, n_cand, pool.num_pages, "table")
+        call("oomb_select_pages", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts, n_q,
+             t0, top_k, _ptr(sel), sel.stride(0), _ptr(count), _ptr(qbar_out), _ptr(score_out),
+             score_stride, _ptr(ws), ws.numel(), _stream(stream))
     return sel, count
 
 
@@ -176,14 +290,15 @@ def oomb_rope(x: torch.Tensor, pos0: int, theta: float = 10000.0, inverse: bool 
     positions pos0 .. pos0 + tokens - 1; out may be x (in place)."""
     if x.dim() != 3 or x.stride(2) != 1 or not x.is_cuda or x.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("x must be a [heads, tokens, head_dim] bf16/fp32 GPU tensor, last dim contiguous")
-    if out is None:
-        out = torch.empty_like(x, memory_format=torch.contiguous_format)
-    if out.shape != x.shape or out.dtype != x.dtype or out.stride(2) != 1:
-        raise ValueError("out must match x")
-    dt = OOMB_DTYPE_BF16 if x.dtype == torch.bfloat16 else OOMB_DTYPE_FP32
-    call("oomb_rope", _ptr(x), x.stride(0), x.stride(1), _ptr(out), out.stride(0), out.stride(1),
-         x.shape[0], x.shape[1], x.shape[2], dt, pos0, float(theta), int(bool(inverse)),
-         _stream(stream))
+    with _on(stream):
+        if out is None:
+            out = _new("empty", x.shape, x.dtype, x.device)
+        if out.shape != x.shape or out.dtype != x.dtype or out.stride(2) != 1:
+            raise ValueError("out must match x")
+        dt = OOMB_DTYPE_BF16 if x.dtype == torch.bfloat16 else OOMB_DTYPE_FP32
+        call("oomb_rope", _ptr(x), x.stride(0), x.stride(1), _ptr(out), out.stride(0),
+             out.stride(1), x.shape[0], x.shape[1], x.shape[2], dt, pos0, float(theta),
+             int(bool(inverse)), _stream(stream))
     return out
 
 
@@ -214,15 +329,18 @@ def oomb_select_pages_mean(pool: PagedPool, table: torch.Tensor, q: torch.Tensor
     n_q = q.shape[1]
     n_cand = t0 // pool.page_size
     k = max(0, min(top_k, n_cand))
-    if sel is None:
-        sel = torch.full((pool.num_kv_heads, max(k, 1)), -1, dtype=torch.int32, device=q.device)
-    if count is None:
-        count = torch.zeros(pool.num_kv_heads, dtype=torch.int32, device=q.device)
-    ws = _workspace(select_workspace_bytes(pool, n_q, t0), q.device, workspace)
-    score_stride = 0 if score_out is None else score_out.stride(0)
-    call("oomb_select_pages_mean", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts, n_q,
-         t0, top_k, _ptr(kmean), _ptr(sel), sel.stride(0), _ptr(count), _ptr(qbar_out),
-         _ptr(score_out), score_stride, _ptr(ws), ws.numel(), _stream(stream))
+    with _on(stream):
+        if sel is None:
+            sel = _new("full", (pool.num_kv_heads, max(k, 1)), torch.int32, q.device, -1)
+        if count is None:
+            count = _new("zeros", pool.num_kv_heads, torch.int32, q.device)
+        ws = _workspace(select_workspace_bytes(pool, n_q, t0), q.device, workspace)
+        score_stride = 0 if score_out is None else score_out.stride(0)
+        if _checks_on():
+            check_page_tables(table, n_cand, pool.num_pages, "table")
+        call("oomb_select_pages_mean", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts,
+             n_q, t0, top_k, _ptr(kmean), _ptr(sel), sel.stride(0), _ptr(count), _ptr(qbar_out),
+             _ptr(score_out), score_stride, _ptr(ws), ws.numel(), _stream(stream))
     return sel, count
 
 
@@ -243,19 +361,21 @@ def oomb_paged_chunk_attn_fwd(pool: PagedPool, table: torch.Tensor, q: torch.Ten
     n_q = q.shape[1]
     if scale is None:
         scale = pool.head_dim ** -0.5
-    if o is None:
-        o = torch.empty_like(q, memory_format=torch.contiguous_format)
-    ohs, ots = _view(o, pool, pool.num_q_heads, "o")
-    if lse is None:
-        lse = torch.empty(pool.num_q_heads, n_q, dtype=torch.float32, device=q.device)
-    if not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
-        raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
-    sel_stride = 0 if sel is None else sel.stride(0)
-    need = fwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride, window)
-    ws = _workspace(need, q.device, workspace) if need > 0 or workspace is not None else None
-    call("oomb_paged_chunk_attn_fwd", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts,
-         n_q, t0, _ptr(sel), sel_stride, _ptr(count), int(window), float(scale), _ptr(o), ohs,
-         ots, _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    with _on(stream):
+        if o is None:
+            o = _new("empty", q.shape, q.dtype, q.device)
+        ohs, ots = _view(o, pool, pool.num_q_heads, "o")
+        if lse is None:
+            lse = _new("empty", (pool.num_q_heads, n_q), torch.float32, q.device)
+        if not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
+            raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
+        sel_stride = 0 if sel is None else sel.stride(0)
+        need = fwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride, window)
+        ws = _workspace(need, q.device, workspace) if need > 0 or workspace is not None else None
+        _debug_check(pool, table, t0, n_q, sel, count, window)
+        call("oomb_paged_chunk_attn_fwd", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs,
+             ts, n_q, t0, _ptr(sel), sel_stride, _ptr(count), int(window), float(scale), _ptr(o),
+             ohs, ots, _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     return o, lse
 
 
@@ -279,18 +399,20 @@ def oomb_paged_chunk_attn_bwd(pool: PagedPool, table: torch.Tensor, gtable: torc
         scale = pool.head_dim ** -0.5
     ohs, ots = _view(o, pool, pool.num_q_heads, "o")
     dhs, dts = _view(dout, pool, pool.num_q_heads, "dout")
-    if dq is None:
-        dq = torch.empty(pool.num_q_heads, n_q, pool.head_dim, dtype=torch.float32, device=q.device)
-    qhs, qts = _view(dq, pool, pool.num_q_heads, "dq", torch.float32)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (pool.num_q_heads, n_q):
         raise ValueError("lse must be a contiguous fp32 [Hq, n_q] tensor")
     sel_stride = 0 if sel is None else sel.stride(0)
-    ws = _workspace(bwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride, window),
-                    q.device, workspace)
-    call("oomb_paged_chunk_attn_bwd", pool.ref(), _ptr(table), table.stride(0), _ptr(gtable),
-         gtable.stride(0), _ptr(q), hs, ts, n_q, t0, _ptr(sel), sel_stride, _ptr(count),
-         int(window), float(scale), _ptr(o), ohs, ots, _ptr(dout), dhs, dts, _ptr(lse), _ptr(dq), qhs, qts,
-         _ptr(ws), ws.numel(), _stream(stream))
+    with _on(stream):
+        if dq is None:
+            dq = _new("empty", (pool.num_q_heads, n_q, pool.head_dim), torch.float32, q.device)
+        qhs, qts = _view(dq, pool, pool.num_q_heads, "dq", torch.float32)
+        ws = _workspace(bwd_workspace_bytes(pool, n_q, t0, -1 if sel is None else sel_stride,
+                                            window), q.device, workspace)
+        _debug_check(pool, table, t0, n_q, sel, count, window, gtable)
+        call("oomb_paged_chunk_attn_bwd", pool.ref(), _ptr(table), table.stride(0), _ptr(gtable),
+             gtable.stride(0), _ptr(q), hs, ts, n_q, t0, _ptr(sel), sel_stride, _ptr(count),
+             int(window), float(scale), _ptr(o), ohs, ots, _ptr(dout), dhs, dts, _ptr(lse),
+             _ptr(dq), qhs, qts, _ptr(ws), ws.numel(), _stream(stream))
     return dq
 
 

@@ -1,12 +1,22 @@
 """GPU parity at full workload sizes, in the launch configuration bench.py times,
-and the chunk-recurrent sweep.
+and the chunk-recurrent sweep at its full shape (32 chunks of 8192, 28/4 heads).
 
-Full sizes: page selection is compared bit for bit for every KV head; O, LSE and dQ
-on sampled query rows that the oracle evaluates one by one (each over exactly the
-keys that row attends); dK/dV elementwise for one whole KV group where the oracle
-can afford it (1M context), else through identities that hold at any size:
+Single chunks (1M, 4M, 128K): page selection bit for bit on every KV head; KV group 0
+(7 query heads) in full against the oracle: O, LSE and dQ on every row, dK and dV on
+every attended key; sampled rows of the other groups; and on every group the
+identities that hold at any size:
   sum_t dV_t = sum_{h in group, i} dO_hi      (rows of P sum to one)
   sum_t dK_t = 0                              (sum_t dS_it = dO_i.O_i - Delta_i = 0)
+
+Sweeps (the oracle cannot redo a whole 262,144-token sweep in the suite's time, so
+the sample is bounded, never skipped):
+  top-64: selections bit for bit for every chunk and KV head; KV group 0's last four
+    chunks in full (O, LSE, dQ of all their rows, and dK/dV of all their keys, which
+    no earlier chunk can attend, so the pool holds their final values after the
+    reverse pass); sampled rows of every other chunk and group; the identities over
+    the whole gradient pool.
+  dense: the last 256 queries of KV group 0 in full, and dK/dV of the 256 keys that
+    only those queries attend; sampled rows across the sequence; the identities.
 """
 import numpy as np
 import pytest
@@ -76,29 +86,74 @@ def _check_selection(w, x_cpu, kp, r):
     return out
 
 
-def _sampled_rows(w, x_cpu, kp, vp, osel, r, rows):
+def _sampled_rows(w, x_cpu, kp, vp, rows, go, glse, gdq, t0=None, sels=None, q_off=0):
     """O, LSE, dQ of single query rows (all heads of a group), each by an oracle call on
-    a one-query chunk whose selection includes the chunk pages before that query."""
-    P, t0, G = w.page, w.t0, w.group
-    go, glse, gdq = r["o"].cpu(), r["lse"].cpu(), r["dq"].cpu()
+    a one-query chunk at that query's position, whose selection is the chunk's
+    selection plus the chunk pages before the query (so it attends exactly the keys the
+    query attends in the chunk).
+
+    rows: (g, i) pairs, i the query's index in the chunk that starts at t0 (default
+    w.t0); sels: per-group selected prior pages of that chunk (None = dense). go, glse,
+    gdq: the GPU's outputs on CPU, indexed [head, q_off + i]."""
+    P, G = w.page, w.group
+    t0 = w.t0 if t0 is None else t0
     got_o, ref_o, got_q, ref_q, lse_err = [], [], [], [], 0.0
     for (g, i) in rows:
-        sel_g = list(range(t0 // P)) if osel is None else list(osel[g])
+        sel_g = list(range(t0 // P)) if sels is None else list(sels[g])
         sel_i = sorted(set(sel_g) | set(range(t0 // P, (t0 + i) // P)))
         hs = slice(g * G, (g + 1) * G)
-        q1 = x_cpu["q"][hs, i:i + 1]
-        O, L = orc.fwd(q1, kp, vp, x_cpu["table"][g:g + 1], t0 + i, [sel_i], w.scale)
-        dQ, _ = orc.bwd(q1, kp, vp, x_cpu["table"][g:g + 1], t0 + i, [sel_i], w.scale,
-                        x_cpu["do"][hs, i:i + 1])
-        got_o.append(go[hs, i])
+        q1 = x_cpu["q"][hs, q_off + i:q_off + i + 1]
+        d1 = x_cpu["do"][hs, q_off + i:q_off + i + 1]
+        dQ, _, O, L = orc.bwd(q1, kp, vp, x_cpu["table"][g:g + 1], t0 + i, [sel_i], w.scale, d1,
+                              with_fwd=True)
+        got_o.append(go[hs, q_off + i])
         ref_o.append(O[:, 0])
-        got_q.append(gdq[hs, i])
+        got_q.append(gdq[hs, q_off + i])
         ref_q.append(dQ[:, 0])
-        lse_err = max(lse_err, (glse[hs, i].double() - L[:, 0]).abs().max().item())
+        lse_err = max(lse_err, (glse[hs, q_off + i].double() - L[:, 0]).abs().max().item())
     compare("O(rows)", torch.stack(got_o), torch.stack(ref_o), w.dtype)
     compare("dQ(rows)", torch.stack(got_q), torch.stack(ref_q), w.dtype)
-    log(f"    LSE(rows) max_abs={lse_err:.3e}")
+    log(f"    LSE(rows) max_abs={lse_err:.3e} over {len(rows)} rows")
     assert lse_err <= 1e-2
+
+
+def _grad_rows(w, gtable_cpu, g, pos):
+    """Flat row indices of the gradient pool for KV head g's key positions."""
+    P = w.page
+    return gtable_cpu[g].long()[pos // P] * P + pos % P
+
+
+def _group_in_full(w, x_cpu, kp, vp, osel, r, g=0):
+    """KV group g against the oracle in full: O, LSE, dQ on every row of its query heads,
+    dK and dV on every key it attends (the pool was zero before this one backward)."""
+    G, P, t0, C = w.group, w.page, w.t0, w.chunk
+    hs = slice(g * G, (g + 1) * G)
+    gk = torch.zeros(kp.shape, dtype=torch.float64)
+    gv = torch.zeros(kp.shape, dtype=torch.float64)
+    sel_g = None if osel is None else [osel[g]]
+    log(f"    oracle: KV group {g} in full ...")
+    dQ, _, O, L = orc.bwd(x_cpu["q"][hs], kp, vp, x_cpu["table"][g:g + 1], t0, sel_g, w.scale,
+                          x_cpu["do"][hs], gk, gv, x_cpu["gtable"][g:g + 1], with_fwd=True)
+    compare(f"O(g{g})", r["o"][hs], O, w.dtype)
+    lse_err = (r["lse"][hs].cpu().double() - L).abs().max().item()
+    log(f"    LSE(g{g}) max_abs={lse_err:.3e}")
+    assert lse_err <= 1e-2
+    compare(f"dQ(g{g})", r["dq"][hs], dQ, w.dtype)
+    pages = orc.attended_pages(t0, C, P, None if osel is None else osel[g])
+    pos = orc.key_positions(pages, P, t0 + C)
+    rows = _grad_rows(w, x_cpu["gtable"], g, pos)
+    compare(f"dK(g{g})", r["pool"].dk.cpu().reshape(-1, w.d)[rows], gk.reshape(-1, w.d)[rows],
+            w.dtype)
+    compare(f"dV(g{g})", r["pool"].dv.cpu().reshape(-1, w.d)[rows], gv.reshape(-1, w.d)[rows],
+            w.dtype)
+
+
+def _invariant_check(w, g, dKg, dVg, sum_do):
+    ev = ((dVg.sum(0) - sum_do).norm() / sum_do.norm()).item()
+    ek = (dKg.sum(0).norm() / dKg.norm()).item()
+    log(f"    head {g}: |sum dV - sum dO|/|sum dO| = {ev:.2e}, |sum dK|/||dK|| = {ek:.2e}")
+    assert ev < 1e-2 and ek < 2e-2
+    assert torch.isfinite(dKg).all() and torch.isfinite(dVg).all()
 
 
 def _invariants(w, x_cpu, osel, r):
@@ -109,15 +164,10 @@ def _invariants(w, x_cpu, osel, r):
     for g in range(w.hkv):
         pages = orc.attended_pages(t0, C, P, None if osel is None else osel[g])
         pos = orc.key_positions(pages, P, t0 + C)
-        rows = x_cpu["gtable"][g].long()[pos // P] * P + pos % P
-        dKg = dk.reshape(-1, w.d)[rows].double()
-        dVg = dv.reshape(-1, w.d)[rows].double()
-        sum_do = x_cpu["do"][g * G:(g + 1) * G].double().sum((0, 1))
-        ev = ((dVg.sum(0) - sum_do).norm() / sum_do.norm()).item()
-        ek = (dKg.sum(0).norm() / dKg.norm()).item()
-        log(f"    head {g}: |sum dV - sum dO|/|sum dO| = {ev:.2e}, |sum dK|/||dK|| = {ek:.2e}")
-        assert ev < 1e-2 and ek < 2e-2
-        assert torch.isfinite(dKg).all() and torch.isfinite(dVg).all()
+        rows = _grad_rows(w, x_cpu["gtable"], g, pos)
+        _invariant_check(w, g, dk.reshape(-1, w.d)[rows].double(),
+                         dv.reshape(-1, w.d)[rows].double(),
+                         x_cpu["do"][g * G:(g + 1) * G].double().sum((0, 1)))
 
 
 def _sentinels(w, r, x_cpu, spare=3):
@@ -132,102 +182,70 @@ def _to_cpu(x):
     return {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in x.items()}
 
 
-def _row_sample(w, n_per_group=4):
-    C = w.chunk
+def _row_sample(w, n_per_group=4, groups=None, C=None):
+    C = w.chunk if C is None else C
     cand = [0, 1, C // 3, C // 2 + 17, C - 129, C - 1]
-    return [(g, cand[(g + j) % len(cand)]) for g in range(w.hkv) for j in range(n_per_group)]
+    groups = range(w.hkv) if groups is None else groups
+    return [(g, cand[(g + j) % len(cand)]) for g in groups for j in range(n_per_group)]
+
+
+def _single_chunk(name, check_determinism=False):
+    w = wl.WORKLOADS[name]
+    log(f"[case fullsize {name}] t0={w.t0} chunk={w.chunk} top_k={w.top_k}")
+    x = wl.make_inputs(w, device=DEV)
+    r = _gpu_step(w, x)
+    log("    gpu step done")
+    xc = _to_cpu(x)
+    kp, vp = _oracle_pool(w, xc)
+    osel = _check_selection(w, xc, kp, r) if w.top_k is not None else None
+    _sentinels(w, r, xc)
+    _group_in_full(w, xc, kp, vp, osel, r, g=0)
+    _sampled_rows(w, xc, kp, vp, _row_sample(w, 2, groups=range(1, w.hkv)), r["o"].cpu(),
+                  r["lse"].cpu(), r["dq"].cpu(), sels=osel)
+    _invariants(w, xc, osel, r)
+    return w, x, r
 
 
 def test_fullsize_sparse1m():
-    """1M prior tokens, top-64: selection bit-exact on all heads; KV group 0 checked
-    elementwise in full (O, LSE, dQ, dK, dV); invariants on all groups; determinism."""
-    w = wl.WORKLOADS["sparse1m"]
-    log(f"[case fullsize sparse1m] t0={w.t0} chunk={w.chunk}")
-    x = wl.make_inputs(w, device=DEV)
-    r = _gpu_step(w, x)
-    log("    gpu step done")
-    xc = _to_cpu(x)
-    kp, vp = _oracle_pool(w, xc)
-    osel = _check_selection(w, xc, kp, r)
-    _sentinels(w, r, xc)
-    # KV group 0 in full
-    G = w.group
-    O, L = orc.fwd(xc["q"][:G], kp, vp, xc["table"][:1], w.t0, osel[:1], w.scale)
-    compare("O(g0)", r["o"][:G], O, w.dtype)
-    assert (r["lse"][:G].cpu().double() - L).abs().max().item() <= 1e-2
-    gk = torch.zeros(kp.shape, dtype=torch.float64)
-    gv = torch.zeros(kp.shape, dtype=torch.float64)
-    dQ, _ = orc.bwd(xc["q"][:G], kp, vp, xc["table"][:1], w.t0, osel[:1], w.scale, xc["do"][:G],
-                    gk, gv, xc["gtable"][:1])
-    compare("dQ(g0)", r["dq"][:G], dQ, w.dtype)
-    pages = orc.attended_pages(w.t0, w.chunk, w.page, osel[0])
-    pos = orc.key_positions(pages, w.page, w.t0 + w.chunk)
-    rows = xc["gtable"][0].long()[pos // w.page] * w.page + pos % w.page
-    compare("dK(g0)", r["pool"].dk.cpu().reshape(-1, w.d)[rows], gk.reshape(-1, w.d)[rows], w.dtype)
-    compare("dV(g0)", r["pool"].dv.cpu().reshape(-1, w.d)[rows], gv.reshape(-1, w.d)[rows], w.dtype)
-    _sampled_rows(w, xc, kp, vp, osel, r, _row_sample(w, 2))
-    _invariants(w, xc, osel, r)
-    # run-twice determinism of the backward at full size
-    first = (r["dq"].clone(), r["pool"].dk.clone(), r["pool"].dv.clone())
-    r["pool"].zero_grad()
-    dq2 = pca.oomb_paged_chunk_attn_bwd(r["pool"], x["table"].to(DEV), x["gtable"].to(DEV),
-                                        x["q"], w.t0, r["sel"], r["count"], r["o"], x["do"],
-                                        r["lse"], w.scale)
-    torch.cuda.synchronize()
-    assert torch.equal(dq2, first[0])
-    r["pool"].dk.zero_()
-    r["pool"].dv.zero_()
-    # (pool was re-zeroed above: rerun once more into zeros and compare with a fresh zero run)
-    pca.oomb_paged_chunk_attn_bwd(r["pool"], x["table"].to(DEV), x["gtable"].to(DEV), x["q"],
-                                  w.t0, r["sel"], r["count"], r["o"], x["do"], r["lse"], w.scale)
-    dk_a, dv_a = r["pool"].dk.clone(), r["pool"].dv.clone()
-    r["pool"].zero_grad()
-    pca.oomb_paged_chunk_attn_bwd(r["pool"], x["table"].to(DEV), x["gtable"].to(DEV), x["q"],
-                                  w.t0, r["sel"], r["count"], r["o"], x["do"], r["lse"], w.scale)
-    torch.cuda.synchronize()
-    assert torch.equal(dk_a, r["pool"].dk) and torch.equal(dv_a, r["pool"].dv)
+    """1M prior tokens, top-64: selection bit-exact on all heads; KV group 0 in full;
+    sampled rows of the other groups; invariants; run-twice determinism."""
+    w, x, r = _single_chunk("sparse1m")
+    # run-twice determinism of the backward at full size (the pool re-zeroed each time)
+    table, gtable = x["table"].to(DEV), x["gtable"].to(DEV)
+    res = []
+    for _ in range(2):
+        r["pool"].zero_grad()
+        dq = pca.oomb_paged_chunk_attn_bwd(r["pool"], table, gtable, x["q"], w.t0, r["sel"],
+                                           r["count"], r["o"], x["do"], r["lse"], w.scale)
+        torch.cuda.synchronize()
+        res.append((dq.clone(), r["pool"].dk.clone(), r["pool"].dv.clone()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    assert torch.equal(res[0][0], r["dq"])
 
 
 def test_fullsize_sparse4m():
-    """4M-token context, top-128, chunk 8192: selection bit-exact on all heads, sampled
-    rows, invariants, sentinels."""
-    w = wl.WORKLOADS["sparse4m"]
-    log(f"[case fullsize sparse4m] t0={w.t0} chunk={w.chunk}")
-    x = wl.make_inputs(w, device=DEV)
-    r = _gpu_step(w, x)
-    log("    gpu step done")
-    xc = _to_cpu(x)
-    del x
-    kp, vp = _oracle_pool(w, xc)
-    osel = _check_selection(w, xc, kp, r)
-    _sentinels(w, r, xc)
-    _sampled_rows(w, xc, kp, vp, osel, r, _row_sample(w, 2))
-    _invariants(w, xc, osel, r)
+    """4M-token context, top-128, chunk 8192: selection bit-exact on all heads; KV group
+    0 in full; sampled rows of the other groups; invariants; sentinels."""
+    _single_chunk("sparse4m")
 
 
 def test_fullsize_dense128k():
-    """128K context, all 992 prior pages: sampled rows and invariants."""
-    w = wl.WORKLOADS["dense128k"]
-    log(f"[case fullsize dense128k] t0={w.t0} chunk={w.chunk}")
-    x = wl.make_inputs(w, device=DEV)
-    r = _gpu_step(w, x)
-    log("    gpu step done")
-    xc = _to_cpu(x)
-    kp, vp = _oracle_pool(w, xc)
-    _sentinels(w, r, xc)
-    _sampled_rows(w, xc, kp, vp, None, r, _row_sample(w, 3))
-    _invariants(w, xc, None, r)
+    """128K context, all 992 prior pages: KV group 0 in full; sampled rows of the other
+    groups; invariants; sentinels."""
+    _single_chunk("dense128k")
 
 
 def _gpu_sweep(w, x):
     """Chunk-recurrent sweep through the library: forward c = 0..S-1 (append, summarize,
-    select, fwd), then c = S-1..0 (fwd again, bwd)."""
+    select, fwd), then c = S-1..0 (fwd again, bwd). Returns the pool, O and LSE of the
+    forward pass, dQ of the reverse pass (all chunks) and the selections."""
     P, C = w.page, w.chunk
     pool = pca.PagedPool(w.pool_pages, P, w.d, w.hq, w.hkv, w.dtype, DEV)
     table, gtable = x["table"].to(DEV), x["gtable"].to(DEV)
     q_all, do_all = x["q"].to(DEV), x["do"].to(DEV)
     k_all, v_all = x["k"].to(DEV), x["v"].to(DEV)
-    sels, outs = [], []
+    sels, outs, lses = [], [], []
     for c in range(w.n_chunks):
         t0 = c * C
         pca.oomb_kv_append(pool, table, k_all[:, t0:t0 + C].contiguous(),
@@ -238,7 +256,9 @@ def _gpu_sweep(w, x):
         if w.top_k is not None:
             sc = pca.oomb_select_pages(pool, table, q, t0, w.top_k)
         sels.append(sc)
-        outs.append(pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, sc[0], sc[1], w.scale)[0])
+        o, lse = pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, sc[0], sc[1], w.scale)
+        outs.append(o)
+        lses.append(lse)
     dq = torch.zeros(w.hq, w.total, w.d, dtype=torch.float32, device=DEV)
     for c in reversed(range(w.n_chunks)):
         t0 = c * C
@@ -248,7 +268,7 @@ def _gpu_sweep(w, x):
         dq[:, t0:t0 + C] = pca.oomb_paged_chunk_attn_bwd(
             pool, table, gtable, q, t0, s_, c_, o, do_all[:, t0:t0 + C].contiguous(), lse, w.scale)
     torch.cuda.synchronize()
-    return pool, torch.cat(outs, dim=1), dq, sels
+    return pool, torch.cat(outs, dim=1), torch.cat(lses, dim=1), dq, sels
 
 
 @pytest.mark.parametrize("name,kw", [
@@ -262,7 +282,7 @@ def test_sweep_parity(name, kw):
     w = wl.custom(name, name=name + "_sweep", **kw) if kw else wl.WORKLOADS[name]
     log(f"[case sweep {w.name}] chunks={w.n_chunks} chunk={w.chunk} dtype={w.dtype} top_k={w.top_k}")
     x = wl.make_inputs(w)
-    pool, O, dq, sels = _gpu_sweep(w, x)
+    pool, O, _, dq, sels = _gpu_sweep(w, x)
     log("    gpu sweep done")
     ref = orc.sweep(x["q"], x["k"], x["v"], x["do"], x["table"], x["gtable"], w.pool_pages,
                     w.page, w.chunk, w.scale, top_k=w.top_k)
@@ -276,3 +296,109 @@ def test_sweep_parity(name, kw):
     mapped = x["gtable"].reshape(-1).long()
     compare("dK", pool.dk.cpu()[mapped], ref["dk_pool"][mapped], w.dtype)
     compare("dV", pool.dv.cpu()[mapped], ref["dv_pool"][mapped], w.dtype)
+
+
+def _sweep_invariants(w, x, pool):
+    """Over the whole sweep, per KV head: sum of dV over all its keys = sum of dO over
+    all its query rows of every chunk; sum of dK ~ 0."""
+    G, P = w.group, w.page
+    dk, dv = pool.dk.cpu().reshape(-1, w.d), pool.dv.cpu().reshape(-1, w.d)
+    pos = torch.arange(w.total)
+    for g in range(w.hkv):
+        rows = _grad_rows(w, x["gtable"], g, pos)
+        _invariant_check(w, g, dk[rows].double(), dv[rows].double(),
+                         x["do"][g * G:(g + 1) * G].double().sum((0, 1)))
+
+
+def _sweep_sampled_rows(w, x, kp, vp, chunks, sels, O, L, dq, n_per_group=1):
+    """Sampled rows of the listed chunks, every group (sels[c]: the oracle's selections
+    of chunk c per group, or None for dense)."""
+    C = w.chunk
+    go, glse, gdq = O.cpu(), L.cpu(), dq.cpu()
+    for c in chunks:
+        rows = [(g, i) for (g, i) in _row_sample(w, n_per_group)]
+        rows = [(g, (i + 97 * c) % C) for (g, i) in rows]
+        log(f"    chunk {c}:")
+        _sampled_rows(w, x, kp, vp, rows, go, glse, gdq, t0=c * C,
+                      sels=None if sels is None else sels[c], q_off=c * C)
+
+
+def test_fullsize_sweep_top64():
+    """The 262,144-token top-64 sweep at full shape (28/4 heads, 32 chunks of 8192):
+    selections bit for bit for every chunk and KV head; KV group 0's last four chunks
+    in full (O, LSE, dQ; dK/dV of all their keys); sampled rows of every other chunk;
+    the identities over the whole gradient pool."""
+    w = wl.WORKLOADS["sweep256k_top64"]
+    C, P, G = w.chunk, w.page, w.group
+    log(f"[case fullsize sweep {w.name}] chunks={w.n_chunks} chunk={C} top_k={w.top_k}")
+    x = wl.make_inputs(w)
+    pool, O, L, dq, gsels = _gpu_sweep(w, x)
+    log("    gpu sweep done")
+    kp, vp = _oracle_pool(w, x, spare=0)
+    summ = torch.zeros(kp.shape[0], 2, w.d, dtype=w.dtype)
+    # every page is complete by the time it is a candidate, so one summary of the
+    # whole context gives the scores each chunk saw
+    orc.summarize(kp, x["table"], summ, 0, w.pages_per_head, w.total)
+    osels = []
+    for c in range(w.n_chunks):
+        t0 = c * C
+        ref = orc.select_pages(x["q"][:, t0:t0 + C], summ, x["table"], t0, P, G, w.top_k)
+        s_, c_ = gsels[c]
+        s_, c_ = s_.cpu(), c_.cpu()
+        for g, (_, _, chosen) in enumerate(ref):
+            assert int(c_[g]) == len(chosen) and s_[g, :len(chosen)].tolist() == chosen, (c, g)
+        osels.append([chosen for (_, _, chosen) in ref])
+    log(f"    selections bit-exact: {w.n_chunks} chunks x {w.hkv} KV heads")
+    last = list(range(w.n_chunks - 4, w.n_chunks))
+    gk = torch.zeros(kp.shape, dtype=torch.float64)
+    gv = torch.zeros(kp.shape, dtype=torch.float64)
+    hs = slice(0, G)
+    for c in reversed(last):
+        t0 = c * C
+        log(f"    oracle: chunk {c}, KV group 0 in full ...")
+        dQ, _, Oc, Lc = orc.bwd(x["q"][hs, t0:t0 + C], kp, vp, x["table"][:1], t0,
+                                [osels[c][0]], w.scale, x["do"][hs, t0:t0 + C], gk, gv,
+                                x["gtable"][:1], with_fwd=True)
+        compare(f"O(c{c})", O[hs, t0:t0 + C], Oc, w.dtype)
+        lse_err = (L[hs, t0:t0 + C].cpu().double() - Lc).abs().max().item()
+        log(f"    LSE(c{c}) max_abs={lse_err:.3e}")
+        assert lse_err <= 1e-2
+        compare(f"dQ(c{c})", dq[hs, t0:t0 + C], dQ, w.dtype)
+    pos = torch.arange(last[0] * C, w.total)
+    rows = _grad_rows(w, x["gtable"], 0, pos)
+    compare("dK(last4)", pool.dk.cpu().reshape(-1, w.d)[rows], gk.reshape(-1, w.d)[rows], w.dtype)
+    compare("dV(last4)", pool.dv.cpu().reshape(-1, w.d)[rows], gv.reshape(-1, w.d)[rows], w.dtype)
+    _sweep_sampled_rows(w, x, kp, vp, range(0, w.n_chunks - 4), osels, O, L, dq)
+    _sweep_invariants(w, x, pool)
+
+
+def test_fullsize_sweep_dense():
+    """The 262,144-token dense sweep at full shape: the last 256 queries of KV group 0
+    in full (O, LSE, dQ) and dK/dV of the 256 keys only they attend; sampled rows of
+    chunks across the sequence; the identities over the whole gradient pool."""
+    w = wl.WORKLOADS["sweep256k"]
+    C, G, T = w.chunk, w.group, w.total
+    log(f"[case fullsize sweep {w.name}] chunks={w.n_chunks} chunk={C}")
+    x = wl.make_inputs(w)
+    pool, O, L, dq, _ = _gpu_sweep(w, x)
+    log("    gpu sweep done")
+    kp, vp = _oracle_pool(w, x, spare=0)
+    n_tail = 256
+    t0 = T - n_tail
+    hs = slice(0, G)
+    gk = torch.zeros(kp.shape, dtype=torch.float64)
+    gv = torch.zeros(kp.shape, dtype=torch.float64)
+    log(f"    oracle: last {n_tail} queries of KV group 0 over all {T} keys ...")
+    dQ, _, Ot, Lt = orc.bwd(x["q"][hs, t0:], kp, vp, x["table"][:1], t0, None, w.scale,
+                            x["do"][hs, t0:], gk, gv, x["gtable"][:1], with_fwd=True)
+    compare("O(tail)", O[hs, t0:], Ot, w.dtype)
+    lse_err = (L[hs, t0:].cpu().double() - Lt).abs().max().item()
+    log(f"    LSE(tail) max_abs={lse_err:.3e}")
+    assert lse_err <= 1e-2
+    compare("dQ(tail)", dq[hs, t0:], dQ, w.dtype)
+    rows = _grad_rows(w, x["gtable"], 0, torch.arange(t0, T))
+    compare("dK(tail)", pool.dk.cpu().reshape(-1, w.d)[rows], gk.reshape(-1, w.d)[rows], w.dtype)
+    compare("dV(tail)", pool.dv.cpu().reshape(-1, w.d)[rows], gv.reshape(-1, w.d)[rows], w.dtype)
+    n = w.n_chunks
+    _sweep_sampled_rows(w, x, kp, vp, sorted({0, 1, n // 2 - 3, n - 2}), None, O, L, dq)
+    _sweep_invariants(w, x, pool)

@@ -273,3 +273,92 @@ def test_mean_selector_bit_exact(kw):
     log(f"    mean summaries + selection bit-exact ({[len(s) for s in osel]} pages per head)")
     O, _ = orc.fwd(x["q"], kp, vp, x["table"], t0, osel, w.scale)
     compare("O", o, O, w.dtype)
+
+
+def _score_bits_equal(got: torch.Tensor, ref: np.ndarray) -> bool:
+    """Bit equality of fp32 scores, NaN matching any NaN (its sign and payload are the
+    arithmetic unit's choice, not part of the definition)."""
+    g = got.cpu().numpy()
+    nan_g, nan_r = np.isnan(g), np.isnan(ref)
+    if not np.array_equal(nan_g, nan_r):
+        return False
+    return np.array_equal(g[~nan_g].view(np.int32), ref[~nan_r].view(np.int32))
+
+
+def test_selection_signed_zero_inf_nan_scores():
+    """Scores of exactly +0 and -0 (all-zero keys, and zero keys signed against qbar so
+    that every product is -0) tie with each other and break to the lower logical id;
+    +inf ranks first, -inf below every number, NaN (keys with infinities of both signs)
+    below -inf with NaNs tied by id. qbar, every score and the selection against the
+    oracle, for several k around those boundaries."""
+    P, D = 128, 128
+    w = _w(name="score_edges", hq=4, hkv=1, chunk=128, total=128 * 20 + 128)
+    x = wl.make_inputs(w)
+    qbar = orc.query_summary(x["q"], 0, w.group)
+    sgn = torch.from_numpy(np.sign(qbar).astype(np.float32))
+    assert bool((sgn != 0).all())
+    k = x["k"].clone().float()
+    pg = lambda j: slice(j * P, (j + 1) * P)          # noqa: E731
+    for j, c in ((0, 0.01), (1, 0.02), (3, 0.03)):    # negative scores: -c * sum|qbar|
+        k[0, pg(j)] = -c * sgn
+    for j in (2, 7, 13):                               # all +0 keys: products +-0
+        k[0, pg(j)] = 0.0
+    for j in (4, 11):                                  # keys of sign -sgn: every product -0
+        k[0, pg(j)] = torch.where(sgn > 0, torch.tensor(-0.0), torch.tensor(0.0))
+    k[0, pg(8), 0] = float("inf") * sgn[0]             # +inf score
+    k[0, pg(9), 0] = -float("inf") * sgn[0]            # -inf score
+    for j in (5, 16):                                  # +inf in one dim, -inf in another: NaN
+        k[0, pg(j), 0] = float("inf") * sgn[0]
+        k[0, pg(j), 1] = -float("inf") * sgn[1]
+    x["k"] = k.to(w.dtype)
+    table = x["table"].to(DEV)
+    pool = pca.PagedPool(w.pool_pages, P, D, w.hq, w.hkv, w.dtype, DEV)
+    pca.oomb_kv_append(pool, table, x["k"].to(DEV), x["v"].to(DEV), 0)
+    pca.oomb_page_summarize(pool, table, 0, w.pages_per_head, w.total)
+    kp = torch.zeros(w.pool_pages, P, D, dtype=w.dtype)
+    orc.append(kp, x["table"], x["k"], 0)
+    summ = torch.zeros(w.pool_pages, 2, D, dtype=w.dtype)
+    orc.summarize(kp, x["table"], summ, 0, w.pages_per_head, w.total)
+    q = x["q"].to(DEV)
+    for top_k in (1, 9, 10, 11, 12, 15, 17, 18, 19, 20):
+        log(f"[case score_edges k={top_k}]")
+        qb = torch.empty(1, D, dtype=torch.float32, device=DEV)
+        sc = torch.empty(1, 20, dtype=torch.float32, device=DEV)
+        sel, cnt = pca.oomb_select_pages(pool, table, q, w.t0, top_k, qbar_out=qb, score_out=sc)
+        torch.cuda.synchronize()
+        (rq, rs, chosen), = orc.select_pages(x["q"], summ, x["table"], w.t0, P, w.group, top_k)
+        assert torch.equal(bits(qb[0]), torch.from_numpy(rq).view(torch.int32))
+        assert _score_bits_equal(sc[0], rs)
+        assert int(cnt[0]) == len(chosen) and sel[0, :len(chosen)].cpu().tolist() == chosen
+        if top_k == 12:   # +inf, the 8 positive pages, then 3 of the 5 tied zero pages
+            assert chosen == sorted([8, 6, 10, 12, 14, 15, 17, 18, 19, 2, 4, 7]), chosen
+            assert np.signbit(rs[4]) and rs[4] == 0 and rs[2] == 0
+        if top_k == 19:   # everything but the higher-id NaN page
+            assert chosen == [j for j in range(20) if j != 16]
+
+
+def test_side_stream_calls_match_default_stream():
+    """Select, forward and backward issued on a second stream (outputs, workspaces and
+    their fills made by the binding on that stream) give the default stream's results
+    bit for bit."""
+    w = _w(name="side_stream", hq=8, hkv=2, chunk=300, total=2000, top_k=6)
+    x = wl.make_inputs(w)
+    table = x["table"].to(DEV)
+    q, do = x["q"].to(DEV), x["do"].to(DEV)
+    outs = []
+    for use_side in (False, True):
+        log(f"[case side_stream {use_side}]")
+        pool = pca.PagedPool(w.pool_pages, w.page, w.d, w.hq, w.hkv, w.dtype, DEV)
+        pca.oomb_kv_append(pool, table, x["k"].to(DEV), x["v"].to(DEV), 0)
+        pca.oomb_page_summarize(pool, table, 0, w.pages_per_head, w.total)
+        st = torch.cuda.Stream() if use_side else None
+        if st is not None:
+            st.wait_stream(torch.cuda.current_stream())
+        sel, cnt = pca.oomb_select_pages(pool, table, q, w.t0, w.top_k, stream=st)
+        o, lse = pca.oomb_paged_chunk_attn_fwd(pool, table, q, w.t0, sel, cnt, stream=st)
+        dq = pca.oomb_paged_chunk_attn_bwd(pool, table, table, q, w.t0, sel, cnt, o, do, lse,
+                                           stream=st)
+        torch.cuda.synchronize()
+        outs.append((sel.cpu(), bits(o), lse.cpu(), dq.cpu(), pool.dk.cpu(), pool.dv.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

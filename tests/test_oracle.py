@@ -251,6 +251,36 @@ def test_top_k_matches_brute_force_with_ties():
             assert orc.top_k_pages(scores, k) == _brute_topk(list(scores), k)
 
 
+def _brute_topk_nan(scores, k):
+    """As _brute_topk, with NaN ranking below every number and NaNs tied (lower id
+    first): page i beats page j iff both are numbers and (s_i > s_j, or s_i == s_j and
+    i < j); or i is a number and j is NaN; or both are NaN and i < j."""
+    n = len(scores)
+
+    def beats(i, j):
+        ni, nj = math.isnan(scores[i]), math.isnan(scores[j])
+        if ni or nj:
+            return (not ni and nj) or (ni and nj and i < j)
+        return scores[i] > scores[j] or (scores[i] == scores[j] and i < j)
+
+    return [j for j in range(n) if sum(1 for i in range(n) if i != j and beats(i, j)) < k]
+
+
+def test_top_k_nan_ranks_lowest():
+    """NaN scores (possible when keys hold infinities) rank below -inf; among NaNs the
+    lower ids win; -0 and +0 still tie."""
+    rng = np.random.default_rng(5)
+    vals = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, 1.5, -1.5], np.float32)
+    for trial in range(40):
+        n = int(rng.integers(1, 40))
+        scores = vals[rng.integers(0, len(vals), size=n)]
+        for k in (0, 1, 3, n // 2, n, n + 2):
+            assert orc.top_k_pages(scores, k) == _brute_topk_nan(list(scores), k)
+    s = np.array([np.nan, -np.inf, np.nan, 2.0], np.float32)
+    assert orc.top_k_pages(s, 2) == [1, 3]
+    assert orc.top_k_pages(s, 3) == [0, 1, 3]
+
+
 def test_top_k_special_cases():
     s = np.zeros(10, np.float32)
     assert orc.top_k_pages(s, 4) == [0, 1, 2, 3]            # all equal -> lowest ids
@@ -314,9 +344,12 @@ def test_fwd_bwd_match_sdpa_autograd(sparse):
     gpool_k = torch.zeros(c["kp"].shape, dtype=F64)
     gpool_v = torch.zeros(c["vp"].shape, dtype=F64)
     gtable = _table(hkv, c["n_pages"], 99)
-    dQ, _ = orc.bwd(c["q"], c["kp"], c["vp"], c["table"], t0, sel, scale, c["do"],
-                    gpool_k, gpool_v, gtable)
+    dQ, _, O2, L2 = orc.bwd(c["q"], c["kp"], c["vp"], c["table"], t0, sel, scale, c["do"],
+                            gpool_k, gpool_v, gtable, with_fwd=True)
     assert torch.allclose(dQ, q.grad, atol=1e-12, rtol=0)
+    # the forward recomputed inside the backward is the forward (SDPA and fwd itself)
+    assert torch.allclose(O2, ref.detach(), atol=1e-13, rtol=0)
+    assert torch.equal(O2, O) and torch.equal(L2, L)
     for g in range(hkv):
         dk = orc.gather(gpool_k, gtable, g, range(c["n_pages"]))[:c["T"]]
         dv = orc.gather(gpool_v, gtable, g, range(c["n_pages"]))[:c["T"]]
@@ -686,3 +719,68 @@ def test_rope_closed_forms_and_invariants():
     d2 = (orc.rope(q, 1040) * orc.rope(k, 1017)).sum()
     assert abs(float(d1 - d2)) < 1e-11
 
+
+
+def _layer_by_chunks(x, ws, hq, hkv, D, page, chunk, scale, theta, dy, top_k, window):
+    """The same layer assembled chunk by chunk from the oracle's separately pinned
+    pieces: float64 projections and rotary embedding, the paged chunk sweep (keys and
+    values in fp32 pages, queries and dO in float64), then the chain rule through the
+    projections and the rotation (its transpose is the inverse rotation) by hand."""
+    X = x.double()
+    Wq, Wk, Wv, Wo = (w.double() for w in ws)
+    T = X.shape[0]
+    q = orc.rope((X @ Wq).view(T, hq, D).transpose(0, 1), 0, theta)
+    k = orc.rope((X @ Wk).view(T, hkv, D).transpose(0, 1), 0, theta)
+    v = (X @ Wv).view(T, hkv, D).transpose(0, 1)
+    dO = (dy.double() @ Wo.T).view(T, hq, D).transpose(0, 1)
+    n_pages = T // page
+    table = _table(hkv, n_pages, 3)
+    gtable = _table(hkv, n_pages, 4)
+    r = orc.sweep(q, k.float(), v.float(), dO, table, gtable, hkv * n_pages, page, chunk, scale,
+                  top_k=top_k, window=window)
+    O = r["O"].transpose(0, 1).reshape(T, hq * D)
+    dk = torch.stack([orc.gather(r["dk_pool"], gtable, g, range(n_pages)) for g in range(hkv)])
+    dv = torch.stack([orc.gather(r["dv_pool"], gtable, g, range(n_pages)) for g in range(hkv)])
+    dq_lin = orc.rope(r["dQ"], 0, theta, inverse=True).transpose(0, 1).reshape(T, hq * D)
+    dk_lin = orc.rope(dk, 0, theta, inverse=True).transpose(0, 1).reshape(T, hkv * D)
+    dv_lin = dv.transpose(0, 1).reshape(T, hkv * D)
+    y = O @ Wo
+    dX = dq_lin @ Wq.T + dk_lin @ Wk.T + dv_lin @ Wv.T
+    dW = [X.T @ dq_lin, X.T @ dk_lin, X.T @ dv_lin, O.T @ dy.double()]
+    return y, dX, dW, r["sels"]
+
+
+@pytest.mark.parametrize("top_k,window", [(None, 0), (None, 11), (2, 0)])
+def test_layer_reference_equals_chunk_by_chunk(top_k, window):
+    """The full-sequence layer reference (one masked softmax, autograd) equals the layer
+    computed chunk by chunk over the paged sweep with a hand-written backward, for a
+    dense, a local (window) and a top-k layer; the top-k layer's selections agree."""
+    hidden, hq, hkv, D, page, chunk, T = 24, 4, 2, 8, 8, 32, 128
+    g = torch.Generator().manual_seed(21)
+    x = torch.randn(T, hidden, generator=g)
+    ws = [torch.randn(a, b, generator=g) / math.sqrt(a)
+          for a, b in ((hidden, hq * D), (hidden, hkv * D), (hidden, hkv * D), (hq * D, hidden))]
+    dy = torch.randn(T, hidden, generator=g)
+    scale, theta = D ** -0.5, 100.0
+    y, dx, dw, sels = orc.layer_reference(x, *ws, hq, hkv, D, page, chunk, scale, theta, dy,
+                                          top_k=top_k, window=window, sel_dtype=torch.float32)
+    y2, dx2, dw2, sels2 = _layer_by_chunks(x, ws, hq, hkv, D, page, chunk, scale, theta, dy,
+                                           top_k, window)
+    if top_k is not None:
+        assert sels == sels2
+        assert any(len(s_[0]) == top_k for s_ in sels)          # selection really narrowed
+    else:
+        assert sels is None
+    assert torch.allclose(y, y2, rtol=1e-5, atol=1e-5)
+    assert torch.allclose(dx, dx2, rtol=1e-5, atol=1e-5)
+    for a, b in zip(dw, dw2):
+        assert torch.allclose(a, b, rtol=1e-5, atol=1e-5)
+    # and the dense layer's attention is plain causal attention (SDPA, GQA, no mask)
+    if top_k is None and window == 0:
+        X = x.double()
+        q = orc.rope((X @ ws[0].double()).view(T, hq, D).transpose(0, 1), 0, theta)
+        k = orc.rope((X @ ws[1].double()).view(T, hkv, D).transpose(0, 1), 0, theta)
+        v = (X @ ws[2].double()).view(T, hkv, D).transpose(0, 1)
+        o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale, enable_gqa=True)
+        assert torch.allclose(y, o.transpose(0, 1).reshape(T, hq * D) @ ws[3].double(),
+                              rtol=1e-10, atol=1e-10)
