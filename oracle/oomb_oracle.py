@@ -50,6 +50,7 @@ __all__ = [
     "attended_pages", "key_positions", "fwd", "bwd", "sweep",
     "copy_pages", "add_pages", "fetch_selected",
     "summarize_mean", "page_scores_mean", "select_pages_mean", "rope", "layer_reference",
+    "query_tiles", "select_pages_tiled", "tile_selection_row", "fwd_tiled", "bwd_tiled",
 ]
 
 
@@ -262,6 +263,79 @@ def select_pages_mean(q, kmean: np.ndarray, table, t0: int, page: int, group: in
         sc = page_scores_mean(qb, kmean, table, g, n_cand)
         out.append((qb, sc, top_k_pages(sc, top_k)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Finer selection granularity (explainer 2.D leaves the unit of selection open): the
+# chunk's queries are cut into tiles of `tile` consecutive queries (the last tile may
+# be shorter), and every (KV head, tile) pair selects its own top-k prior pages by the
+# same rule, from the mean of that tile's queries over the head group. The candidates
+# are still the complete pages before the chunk, and the chunk's own pages are still
+# attended by every query.
+# ---------------------------------------------------------------------------
+
+def query_tiles(n_q: int, tile: int) -> List[range]:
+    """Query index ranges of the tiles of a chunk of n_q queries."""
+    if tile <= 0:
+        raise ValueError("tile must be positive")
+    return [range(i0, min(n_q, i0 + tile)) for i0 in range(0, n_q, tile)]
+
+
+def select_pages_tiled(q, summary, table, t0: int, page: int, group: int, top_k: int,
+                       tile: int):
+    """out[g][j] = (qbar, scores, selected logical ids) of KV head g and query tile j:
+    select_pages' steps with qbar taken over the tile's queries only (the same fixed
+    order: blocks of 64 consecutive rows of the tile, head-major then query order, the
+    stride-halving tree, one multiply by fp32(1 / (group * tile length)))."""
+    n_cand = t0 // page
+    out = []
+    for g in range(table.shape[0]):
+        row = []
+        for r in query_tiles(q.shape[1], tile):
+            qb = query_summary(q[:, r.start:r.stop], g, group)
+            sc = page_scores(qb, summary, table, g, n_cand)
+            row.append((qb, sc, top_k_pages(sc, top_k)))
+        out.append(row)
+    return out
+
+
+def tile_selection_row(chosen: Sequence[int], t0: int, page: int, tile: int, j: int) -> List[int]:
+    """The pages that query tile j attends besides its own local pages, as one ascending
+    list: its chosen prior pages, then the chunk's pages that lie wholly before the
+    tile's first query (logical [t0 // page, (t0 + j * tile) // page)). Attention of the
+    tile is then the chunk attention of its queries, first position t0 + j * tile, with
+    this list as the selection."""
+    return sorted(int(c) for c in chosen) + list(range(t0 // page, (t0 + j * tile) // page))
+
+
+def fwd_tiled(q, k_pool, v_pool, table, t0: int, chosen, scale: float, tile: int):
+    """O, LSE of a chunk whose query tiles attend their own selections: chosen[g][j] are
+    tile j's prior pages for KV head g; each tile is fwd over its queries at t0 + j*tile
+    with tile_selection_row as its selection."""
+    hq, C, D = q.shape
+    P = k_pool.shape[1]
+    O = torch.zeros(hq, C, D, dtype=torch.float64)
+    L = torch.zeros(hq, C, dtype=torch.float64)
+    for j, r in enumerate(query_tiles(C, tile)):
+        sel = [tile_selection_row(chosen[g][j], t0, P, tile, j) for g in range(table.shape[0])]
+        O[:, r.start:r.stop], L[:, r.start:r.stop] = fwd(q[:, r.start:r.stop], k_pool, v_pool,
+                                                         table, t0 + r.start, sel, scale)
+    return O, L
+
+
+def bwd_tiled(q, k_pool, v_pool, table, t0: int, chosen, scale: float, tile: int, dout,
+              dk_pool=None, dv_pool=None, gtable=None):
+    """dQ of the tiled attention (tile by tile, as bwd), adding every tile's dK/dV into
+    the gradient pools when given."""
+    hq, C, D = q.shape
+    P = k_pool.shape[1]
+    dQ = torch.zeros(hq, C, D, dtype=torch.float64)
+    for j, r in enumerate(query_tiles(C, tile)):
+        sel = [tile_selection_row(chosen[g][j], t0, P, tile, j) for g in range(table.shape[0])]
+        dQ[:, r.start:r.stop], _ = bwd(q[:, r.start:r.stop], k_pool, v_pool, table,
+                                       t0 + r.start, sel, scale, dout[:, r.start:r.stop],
+                                       dk_pool, dv_pool, gtable)
+    return dQ
 
 
 # ---------------------------------------------------------------------------

@@ -10,11 +10,10 @@ identities that hold at any size:
 
 Sweeps (the oracle cannot redo a whole 262,144-token sweep in the suite's time, so
 the sample is bounded, never skipped):
-  top-64: selections bit for bit for every chunk and KV head; KV group 0's last four
-    chunks in full (O, LSE, dQ of all their rows, and dK/dV of all their keys, which
-    no earlier chunk can attend, so the pool holds their final values after the
-    reverse pass); sampled rows of every other chunk and group; the identities over
-    the whole gradient pool.
+  top-64: selections bit for bit for every chunk and KV head; KV group 0 in full
+    over all 32 chunks (O, LSE, dQ of every row; dK/dV of every key after the whole
+    reverse pass); sampled rows of the other groups in every chunk; the identities
+    over the whole gradient pool.
   dense: the last 256 queries of KV group 0 in full, and dK/dV of the 256 keys that
     only those queries attend; sampled rows across the sequence; the identities.
 """
@@ -325,9 +324,10 @@ def _sweep_sampled_rows(w, x, kp, vp, chunks, sels, O, L, dq, n_per_group=1):
 
 def test_fullsize_sweep_top64():
     """The 262,144-token top-64 sweep at full shape (28/4 heads, 32 chunks of 8192):
-    selections bit for bit for every chunk and KV head; KV group 0's last four chunks
-    in full (O, LSE, dQ; dK/dV of all their keys); sampled rows of every other chunk;
-    the identities over the whole gradient pool."""
+    selections bit for bit for every chunk and KV head; KV group 0 in full over all 32
+    chunks (O, LSE, dQ of every row; dK/dV of every key, accumulated over the whole
+    reverse pass); sampled rows of the other groups in every chunk; the identities over
+    the whole gradient pool."""
     w = wl.WORKLOADS["sweep256k_top64"]
     C, P, G = w.chunk, w.page, w.group
     log(f"[case fullsize sweep {w.name}] chunks={w.n_chunks} chunk={C} top_k={w.top_k}")
@@ -349,26 +349,34 @@ def test_fullsize_sweep_top64():
             assert int(c_[g]) == len(chosen) and s_[g, :len(chosen)].tolist() == chosen, (c, g)
         osels.append([chosen for (_, _, chosen) in ref])
     log(f"    selections bit-exact: {w.n_chunks} chunks x {w.hkv} KV heads")
-    last = list(range(w.n_chunks - 4, w.n_chunks))
+    # KV group 0, every chunk in the sweep's reverse order, gradients accumulated
     gk = torch.zeros(kp.shape, dtype=torch.float64)
     gv = torch.zeros(kp.shape, dtype=torch.float64)
     hs = slice(0, G)
-    for c in reversed(last):
+    o_ref = torch.zeros(G, w.total, w.d, dtype=torch.float64)
+    l_ref = torch.zeros(G, w.total, dtype=torch.float64)
+    q_ref = torch.zeros(G, w.total, w.d, dtype=torch.float64)
+    for c in reversed(range(w.n_chunks)):
         t0 = c * C
-        log(f"    oracle: chunk {c}, KV group 0 in full ...")
-        dQ, _, Oc, Lc = orc.bwd(x["q"][hs, t0:t0 + C], kp, vp, x["table"][:1], t0,
-                                [osels[c][0]], w.scale, x["do"][hs, t0:t0 + C], gk, gv,
-                                x["gtable"][:1], with_fwd=True)
-        compare(f"O(c{c})", O[hs, t0:t0 + C], Oc, w.dtype)
-        lse_err = (L[hs, t0:t0 + C].cpu().double() - Lc).abs().max().item()
-        log(f"    LSE(c{c}) max_abs={lse_err:.3e}")
-        assert lse_err <= 1e-2
-        compare(f"dQ(c{c})", dq[hs, t0:t0 + C], dQ, w.dtype)
-    pos = torch.arange(last[0] * C, w.total)
-    rows = _grad_rows(w, x["gtable"], 0, pos)
-    compare("dK(last4)", pool.dk.cpu().reshape(-1, w.d)[rows], gk.reshape(-1, w.d)[rows], w.dtype)
-    compare("dV(last4)", pool.dv.cpu().reshape(-1, w.d)[rows], gv.reshape(-1, w.d)[rows], w.dtype)
-    _sweep_sampled_rows(w, x, kp, vp, range(0, w.n_chunks - 4), osels, O, L, dq)
+        sl = slice(t0, t0 + C)
+        q_ref[:, sl], _, o_ref[:, sl], l_ref[:, sl] = orc.bwd(
+            x["q"][hs, sl], kp, vp, x["table"][:1], t0, [osels[c][0]], w.scale, x["do"][hs, sl],
+            gk, gv, x["gtable"][:1], with_fwd=True)
+        if c % 8 == 0:
+            log(f"    oracle: KV group 0 down to chunk {c}")
+    compare("O(g0)", O[hs], o_ref, w.dtype)
+    lse_err = (L[hs].cpu().double() - l_ref).abs().max().item()
+    log(f"    LSE(g0) max_abs={lse_err:.3e}")
+    assert lse_err <= 1e-2
+    compare("dQ(g0)", dq[hs], q_ref, w.dtype)
+    rows = _grad_rows(w, x["gtable"], 0, torch.arange(w.total))
+    compare("dK(g0)", pool.dk.cpu().reshape(-1, w.d)[rows], gk.reshape(-1, w.d)[rows], w.dtype)
+    compare("dV(g0)", pool.dv.cpu().reshape(-1, w.d)[rows], gv.reshape(-1, w.d)[rows], w.dtype)
+    # the other groups: sampled rows of every chunk
+    go, glse, gdq = O.cpu(), L.cpu(), dq.cpu()
+    for c in range(w.n_chunks):
+        rows_c = [(g, (i + 97 * c) % C) for (g, i) in _row_sample(w, 1, groups=range(1, w.hkv))]
+        _sampled_rows(w, x, kp, vp, rows_c, go, glse, gdq, t0=c * C, sels=osels[c], q_off=c * C)
     _sweep_invariants(w, x, pool)
 
 

@@ -784,3 +784,117 @@ def test_layer_reference_equals_chunk_by_chunk(top_k, window):
         o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale, enable_gqa=True)
         assert torch.allclose(y, o.transpose(0, 1).reshape(T, hq * D) @ ws[3].double(),
                               rtol=1e-10, atol=1e-10)
+
+
+# ----------------------------------------------------------------- tiled selection
+
+def _summ_case(hq=6, hkv=2, C=100, D=16, P=8, t0=203, seed=3, dtype=torch.float32):
+    c = _case(hq=hq, hkv=hkv, C=C, D=D, P=P, t0=t0, seed=seed, dtype=dtype)
+    summ = torch.zeros(c["kp"].shape[0], 2, D, dtype=dtype)
+    orc.summarize(c["kp"], c["table"], summ, 0, c["n_pages"], c["T"])
+    return c, summ
+
+
+def test_tiled_selection_one_tile_is_the_chunk_rule():
+    """A tile as long as the chunk reproduces the per-chunk selection bit for bit."""
+    c, summ = _summ_case()
+    G = c["q"].shape[0] // 2
+    ref = orc.select_pages(c["q"], summ, c["table"], c["t0"], c["P"], G, 5)
+    for tile in (100, 128, 1000):
+        got = orc.select_pages_tiled(c["q"], summ, c["table"], c["t0"], c["P"], G, 5, tile)
+        for g in range(2):
+            assert len(got[g]) == 1
+            qb, sc, ch = got[g][0]
+            assert np.array_equal(qb.view(np.int32), ref[g][0].view(np.int32))
+            assert np.array_equal(sc.view(np.int32), ref[g][1].view(np.int32))
+            assert ch == ref[g][2]
+
+
+def test_tiled_qbar_is_each_tiles_mean():
+    """Each tile's query summary is the mean of that tile's rows over the head group,
+    within the blocked-sum error bound; the last tile is the shorter one."""
+    c, summ = _summ_case(C=150)
+    G = 3
+    out = orc.select_pages_tiled(c["q"], summ, c["table"], c["t0"], c["P"], G, 4, 64)
+    assert [len(r) for r in out] == [3, 3]
+    for g in range(2):
+        for j, r in enumerate(orc.query_tiles(150, 64)):
+            rows = c["q"][g * G:(g + 1) * G, r.start:r.stop].to(F64).reshape(-1, 16)
+            exact = rows.mean(0).numpy()
+            n = rows.shape[0]
+            bound = (n + 10) * np.finfo(np.float32).eps * rows.abs().mean(0).numpy() + 1e-30
+            assert np.all(np.abs(out[g][j][0] - exact) <= bound)
+    assert orc.query_tiles(150, 64) == [range(0, 64), range(64, 128), range(128, 150)]
+
+
+def test_tiled_selection_follows_each_tiles_queries():
+    """Closed form: page 2 of each head holds keys along e0, page 5 along e1; the first
+    tile's queries point along e0, the second's along e1, so with k = 1 the tiles pick
+    pages 2 and 5, while the whole chunk (the mean of both) picks the larger one."""
+    hq, hkv, D, P, C, t0 = 2, 1, 8, 4, 8, 32
+    T = t0 + C
+    k = torch.zeros(1, T, D)
+    k[0, 2 * P:3 * P, 0] = 1.0
+    k[0, 5 * P:6 * P, 1] = 1.0
+    q = torch.zeros(hq, C, D)
+    q[:, :4, 0] = 1.0
+    q[:, 4:, 1] = 2.0
+    table = torch.arange(T // P, dtype=torch.int32)[None]
+    kp = torch.zeros(T // P, P, D)
+    orc.append(kp, table, k, 0)
+    summ = torch.zeros(T // P, 2, D)
+    orc.summarize(kp, table, summ, 0, T // P, T)
+    out = orc.select_pages_tiled(q, summ, table, t0, P, hq, 1, 4)
+    assert [ch for (_, _, ch) in out[0]] == [[2], [5]]
+    assert orc.select_pages(q, summ, table, t0, P, hq, 1)[0][2] == [5]
+    # the rows a tile attends: its pick, then the chunk's pages before its first query
+    assert orc.tile_selection_row([5], t0, P, 4, 1) == [5, 8]
+    assert orc.tile_selection_row([2], t0, P, 4, 0) == [2]
+
+
+@pytest.mark.parametrize("t0,C,tile", [(37, 24, 8), (40, 30, 16), (29, 17, 5)])
+def test_tiled_attention_matches_masked_sdpa(t0, C, tile):
+    """Tiled attention (each tile its own prior pages, the chunk's own pages for all)
+    equals SDPA whose mask gives every query row its tile's pages, with autograd
+    gradients, for unaligned chunk starts and tile edges and a short last tile."""
+    c = _case(C=C, t0=t0)
+    P, hkv, G = c["P"], 2, 2
+    n_prior = t0 // P
+    rng = np.random.default_rng(t0 + C)
+    tiles = orc.query_tiles(C, tile)
+    chosen = [[sorted(rng.choice(n_prior, size=int(rng.integers(0, n_prior + 1)),
+                                 replace=False).tolist()) for _ in tiles] for _ in range(hkv)]
+    scale = 0.3
+    O, L = orc.fwd_tiled(c["q"], c["kp"], c["vp"], c["table"], t0, chosen, scale, tile)
+    gk = torch.zeros(c["kp"].shape, dtype=F64)
+    gv = torch.zeros(c["vp"].shape, dtype=F64)
+    gtable = _table(hkv, c["n_pages"], 77)
+    dQ = orc.bwd_tiled(c["q"], c["kp"], c["vp"], c["table"], t0, chosen, scale, tile, c["do"],
+                       gk, gv, gtable)
+    # the reference mask, row by row: prior pages of the row's tile, or the chunk's pages
+    T = c["T"]
+    kpos = torch.arange(T)
+    mask = torch.zeros(4, C, T, dtype=torch.bool)
+    for h in range(4):
+        for j, r in enumerate(tiles):
+            ok = (kpos // P) >= t0 // P
+            for pg in chosen[h // G][j]:
+                ok |= (kpos // P) == pg
+            for i in r:
+                mask[h, i] = ok & (kpos <= t0 + i)
+    q = c["q"].clone().requires_grad_()
+    k = c["k"].clone().requires_grad_()
+    v = c["v"].clone().requires_grad_()
+    ref = F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=mask[None],
+                                         scale=scale, enable_gqa=True)[0]
+    (ref * c["do"]).sum().backward()
+    assert torch.allclose(O, ref.detach(), atol=1e-12, rtol=0)
+    assert torch.allclose(dQ, q.grad, atol=1e-12, rtol=0)
+    for g in range(hkv):
+        dk = orc.gather(gk, gtable, g, range(c["n_pages"]))[:T]
+        dv = orc.gather(gv, gtable, g, range(c["n_pages"]))[:T]
+        assert torch.allclose(dk, k.grad[g], atol=1e-12, rtol=0)
+        assert torch.allclose(dv, v.grad[g], atol=1e-12, rtol=0)
+    s = torch.logsumexp((scale * (c["q"] @ k.detach().repeat_interleave(2, 0).transpose(1, 2)))
+                        .masked_fill(~mask, -math.inf), dim=-1)
+    assert torch.allclose(L, s, atol=1e-12, rtol=0)
