@@ -125,7 +125,8 @@ size_t oomb_select_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t
  *      e[d] = qbar[d]*kmax[d] if that product is greater than qbar[d]*kmin[d],
  *      else qbar[d]*kmin[d]; score_j = stride-halving tree sum of e over d.
  *   3. Keep the min(top_k, t0/P) pages with the largest score, ties to the lower
- *      logical id (-0 and +0 compare equal), written in ascending id order to
+ *      logical id (-0 and +0 compare equal; a NaN score ranks below every number,
+ *      -inf included, NaNs tying with each other), written in ascending id order to
  *      sel[g*sel_stride + 0..count[g]).
  * The chunk's own pages (including one straddling t0) are never candidates: the
  * attention calls always add them. q: [Hq][n_q][D] view. sel_stride >=
