@@ -140,6 +140,22 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
                       float* score_out, int64_t score_stride, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Page select without any allocation, for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): oomb_select_pages with the same arguments and results, minus the
+ * workspace, which is instead a static device array of 8 MiB (8388608 bytes) inside
+ * the library, one per device, held until the process ends. The call needs the bytes
+ * oomb_select_workspace_bytes reports; above 8 MiB it returns OOMB_ERR_INVALID before
+ * any launch (the 4M-token chunk of 8192 queries with 28/4 heads of 128 needs
+ * 2.4 MiB). It calls no allocator. Every call on one device uses that device's array,
+ * so calls that may overlap on one device (different streams, no ordering between
+ * them) race on it: order them. Nothing in the array needs to be zero on entry. */
+int oomb_select_pages_noalloc(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                              const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                              int32_t n_q, int64_t t0, int32_t top_k, int32_t* sel,
+                              int64_t sel_stride, int32_t* count, float* qbar_out,
+                              float* score_out, int64_t score_stride, void* stream);
+
 /* Rotary position embedding of a chunk's queries or keys by their absolute positions
  * pos0 + i (the chunk-recurrent layer keeps every token's global position, explainer
  * 2.A). x and y are [n_heads][n_tok][head_dim] views (element strides; y may equal x)

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     oomb_rope,
     oomb_select_pages,
     oomb_select_pages_mean,
+    oomb_select_pages_noalloc,
     select_workspace_bytes,
     split_plan,
 )

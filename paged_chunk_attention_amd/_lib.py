@@ -42,6 +42,9 @@ SIGNATURES = {
     "oomb_select_pages": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32,
                                   c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p,
                                   c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
+    "oomb_select_pages_noalloc": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64,
+                                          c_int32, c_int64, c_int32, c_void_p, c_int64, c_void_p,
+                                          c_void_p, c_void_p, c_int64, c_void_p]),
     "oomb_rope": (c_int, [c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_int32, c_int32,
                           c_int32, c_int32, c_int64, c_float, c_int32, c_void_p]),
     "oomb_page_summarize_mean": (c_int, [P_pool, c_void_p, c_int64, c_int64, c_int64, c_int64,

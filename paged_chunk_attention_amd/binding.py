@@ -284,6 +284,26 @@ def oomb_select_pages(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0:
     return sel, count
 
 
+def oomb_select_pages_noalloc(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0: int,
+                              top_k: int, sel: torch.Tensor, count: torch.Tensor,
+                              qbar_out: Optional[torch.Tensor] = None,
+                              score_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """oomb_select_pages into the caller's sel [Hkv, >= k] and count [Hkv] (int32, on the
+    pool's device), with the library's static scratch instead of a workspace: nothing is
+    allocated, here or in the library."""
+    _check_table(table, pool, "table")
+    hs, ts = _view(q, pool, pool.num_q_heads, "q")
+    for name, t in (("sel", sel), ("count", count)):
+        if t.dtype != torch.int32 or t.device != pool.device:
+            raise ValueError(f"{name} must be an int32 tensor on {pool.device}")
+    if sel.dim() != 2 or sel.stride(1) != 1 or count.dim() != 1 or not count.is_contiguous():
+        raise ValueError("sel must be [Hkv, k] with contiguous rows, count [Hkv] contiguous")
+    score_stride = 0 if score_out is None else score_out.stride(0)
+    call("oomb_select_pages_noalloc", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts,
+         q.shape[1], t0, top_k, _ptr(sel), sel.stride(0), _ptr(count), _ptr(qbar_out),
+         _ptr(score_out), score_stride, _stream(stream))
+
+
 def oomb_rope(x: torch.Tensor, pos0: int, theta: float = 10000.0, inverse: bool = False,
               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Rotary embedding of x [heads, tokens, head_dim] (bf16 or fp32, on the GPU) at

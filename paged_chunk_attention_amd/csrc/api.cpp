@@ -11,6 +11,7 @@
 
 #include "launch.hpp"
 #include "oomb.h"
+#include "scratch.hpp"
 
 namespace {
 
@@ -268,7 +269,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 8; }
+int oomb_abi_version(void) { return 9; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -331,7 +332,60 @@ size_t oomb_select_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t
   return total;
 }
 
-// Page selection from min/max summaries (kmean == nullptr) or mean-key summaries.
+// Page selection from min/max summaries (kmean == nullptr) or mean-key summaries:
+// every argument check, and the fill of `a` except its workspace pointers; *total is
+// the workspace the call needs.
+static int select_prepare(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                          const void* q, int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q,
+                          int64_t t0, int32_t top_k, const float* kmean, int32_t* sel,
+                          int64_t sel_stride, int32_t* count, int64_t score_stride,
+                          bool has_score_out, oomb::SelectArgs* a, size_t* off_qbar,
+                          size_t* off_score, size_t* total) {
+  int st = check_pool(pool, &a->pool, kmean == nullptr, false);
+  if (st) return st;
+  a->kmean = kmean;
+  ChunkGeom cg;
+  if ((st = check_chunk(a->pool, n_q, t0, &cg))) return st;
+  if (top_k < 0) return fail(OOMB_ERR_INVALID, "top_k must be >= 0");
+  if ((st = check_table(table, table_stride, cg.n_cand, "table"))) return st;
+  if ((st = check_view(q, q_head_stride, q_tok_stride, elem_size(a->pool), "q"))) return st;
+  if (count == nullptr) return fail(OOMB_ERR_INVALID, "count is NULL");
+  const int k = top_k < cg.n_cand ? top_k : cg.n_cand;
+  if (k > 0 && (sel == nullptr || sel_stride < k))
+    return fail(OOMB_ERR_INVALID, "sel must hold min(top_k, t0/P) = %d ids per head", k);
+  if (has_score_out && score_stride < cg.n_cand)
+    return fail(OOMB_ERR_INVALID, "score_stride %lld < %d candidates", (long long)score_stride, cg.n_cand);
+  const int G = a->pool.Hq / a->pool.Hkv;
+  const int64_t nb = (static_cast<int64_t>(G) * n_q + 63) / 64;
+  if (nb > 16384) return fail(OOMB_ERR_INVALID, "G * n_q = %lld exceeds 1048576", (long long)G * n_q);
+  select_layout(a->pool.Hkv, a->pool.D, static_cast<int>(nb), cg.n_cand, off_qbar, off_score, total);
+  a->table = table;
+  a->tstride = table_stride;
+  a->q = q;
+  a->q_hs = q_head_stride;
+  a->q_ts = q_tok_stride;
+  a->n_q = n_q;
+  a->t0 = t0;
+  a->top_k = top_k;
+  a->sel = sel;
+  a->sel_stride = sel_stride;
+  a->count = count;
+  a->score_stride = has_score_out ? score_stride : (cg.n_cand > 0 ? cg.n_cand : 1);
+  a->n_cand = cg.n_cand;
+  a->nb = static_cast<int>(nb);
+  a->inv = static_cast<float>(1.0 / (static_cast<double>(G) * n_q));
+  return OOMB_OK;
+}
+
+// Launch a prepared selection with its workspace at `ws` (the caller's or the static one).
+static int select_launch(oomb::SelectArgs& a, char* ws, size_t off_qbar, size_t off_score,
+                         float* qbar_out, float* score_out, void* stream) {
+  a.partial = reinterpret_cast<float*>(ws);
+  a.qbar = qbar_out ? qbar_out : reinterpret_cast<float*>(ws + off_qbar);
+  a.score = score_out ? score_out : reinterpret_cast<float*>(ws + off_score);
+  return hip_status(oomb::launch_select(a, static_cast<hipStream_t>(stream)), "select_pages");
+}
+
 static int select_common(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                          const void* q, int64_t q_head_stride, int64_t q_tok_stride, int32_t n_q,
                          int64_t t0, int32_t top_k, const float* kmean, int32_t* sel,
@@ -339,47 +393,15 @@ static int select_common(const oomb_pool* pool, const int32_t* table, int64_t ta
                          int64_t score_stride, void* workspace, size_t workspace_bytes,
                          void* stream) {
   oomb::SelectArgs a{};
-  int st = check_pool(pool, &a.pool, kmean == nullptr, false);
-  if (st) return st;
-  a.kmean = kmean;
-  ChunkGeom cg;
-  if ((st = check_chunk(a.pool, n_q, t0, &cg))) return st;
-  if (top_k < 0) return fail(OOMB_ERR_INVALID, "top_k must be >= 0");
-  if ((st = check_table(table, table_stride, cg.n_cand, "table"))) return st;
-  if ((st = check_view(q, q_head_stride, q_tok_stride, elem_size(a.pool), "q"))) return st;
-  if (count == nullptr) return fail(OOMB_ERR_INVALID, "count is NULL");
-  const int k = top_k < cg.n_cand ? top_k : cg.n_cand;
-  if (k > 0 && (sel == nullptr || sel_stride < k))
-    return fail(OOMB_ERR_INVALID, "sel must hold min(top_k, t0/P) = %d ids per head", k);
-  if (score_out != nullptr && score_stride < cg.n_cand)
-    return fail(OOMB_ERR_INVALID, "score_stride %lld < %d candidates", (long long)score_stride, cg.n_cand);
-  const int G = a.pool.Hq / a.pool.Hkv;
-  const int64_t nb = (static_cast<int64_t>(G) * n_q + 63) / 64;
-  if (nb > 16384) return fail(OOMB_ERR_INVALID, "G * n_q = %lld exceeds 1048576", (long long)G * n_q);
   size_t off_qbar, off_score, total;
-  select_layout(a.pool.Hkv, a.pool.D, static_cast<int>(nb), cg.n_cand, &off_qbar, &off_score, &total);
+  int st = select_prepare(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0,
+                          top_k, kmean, sel, sel_stride, count, score_stride, score_out != nullptr,
+                          &a, &off_qbar, &off_score, &total);
+  if (st) return st;
   if (workspace == nullptr || workspace_bytes < total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(OOMB_ERR_WORKSPACE, "select needs %zu bytes of 256-byte aligned workspace", total);
-  char* ws = static_cast<char*>(workspace);
-  a.table = table;
-  a.tstride = table_stride;
-  a.q = q;
-  a.q_hs = q_head_stride;
-  a.q_ts = q_tok_stride;
-  a.n_q = n_q;
-  a.t0 = t0;
-  a.top_k = top_k;
-  a.sel = sel;
-  a.sel_stride = sel_stride;
-  a.count = count;
-  a.partial = reinterpret_cast<float*>(ws);
-  a.qbar = qbar_out ? qbar_out : reinterpret_cast<float*>(ws + off_qbar);
-  a.score = score_out ? score_out : reinterpret_cast<float*>(ws + off_score);
-  a.score_stride = score_out ? score_stride : (cg.n_cand > 0 ? cg.n_cand : 1);
-  a.n_cand = cg.n_cand;
-  a.nb = static_cast<int>(nb);
-  a.inv = static_cast<float>(1.0 / (static_cast<double>(G) * n_q));
-  return hip_status(oomb::launch_select(a, static_cast<hipStream_t>(stream)), "select_pages");
+  return select_launch(a, static_cast<char*>(workspace), off_qbar, off_score, qbar_out,
+                       score_out, stream);
 }
 
 int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
@@ -390,6 +412,30 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
   return select_common(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0, top_k,
                        nullptr, sel, sel_stride, count, qbar_out, score_out, score_stride,
                        workspace, workspace_bytes, stream);
+}
+
+int oomb_select_pages_noalloc(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                              const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                              int32_t n_q, int64_t t0, int32_t top_k, int32_t* sel,
+                              int64_t sel_stride, int32_t* count, float* qbar_out,
+                              float* score_out, int64_t score_stride, void* stream) {
+  oomb::SelectArgs a{};
+  size_t off_qbar, off_score, total;
+  int st = select_prepare(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0,
+                          top_k, nullptr, sel, sel_stride, count, score_stride,
+                          score_out != nullptr, &a, &off_qbar, &off_score, &total);
+  if (st) return st;
+  if (total > oomb::kSelectScratchBytes)
+    return fail(OOMB_ERR_INVALID,
+                "select_pages_noalloc: this call needs %zu bytes of scratch, the static scratch "
+                "holds %zu (use oomb_select_pages with a workspace)",
+                total, oomb::kSelectScratchBytes);
+  void* scratch_ptr = nullptr;
+  hipError_t e = oomb::select_scratch_address(&scratch_ptr);
+  if (e != hipSuccess)
+    return fail(OOMB_ERR_HIP, "select_pages_noalloc: scratch address: %s", hipGetErrorString(e));
+  return select_launch(a, static_cast<char*>(scratch_ptr), off_qbar, off_score, qbar_out,
+                       score_out, stream);
 }
 
 int oomb_select_pages_mean(const oomb_pool* pool, const int32_t* table, int64_t table_stride,

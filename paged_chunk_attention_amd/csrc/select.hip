@@ -13,9 +13,12 @@
 //         larger), a stride-halving tree over d (a wavefront butterfly).
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "profiling.hpp"
+#include "scratch.hpp"
 
 namespace oomb {
 
@@ -421,6 +424,32 @@ static void launch_scores(const SelectArgs& a, hipStream_t s) {
   else if (bf) OOMB_LAUNCH("page_score", (page_score_kernel<true, 64>), g4, dim3(256), 0, s, a);
   else if (D == 128) OOMB_LAUNCH("page_score", (page_score_kernel<false, 128>), g4, dim3(256), 0, s, a);
   else OOMB_LAUNCH("page_score", (page_score_kernel<false, 64>), g4, dim3(256), 0, s, a);
+}
+
+// Workspace of oomb_select_pages_noalloc, in static device memory: each device that
+// loads the library holds its own copy until the process ends. Host code must not pass
+// this name to a kernel (on the host it only stands for the symbol); it uses the device
+// address that select_scratch_address returns.
+static __device__ __align__(256) char scratch[kSelectScratchBytes];
+
+hipError_t select_scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // Scores are always computed when there are candidates (the top-k needs them unless

@@ -28,14 +28,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 8
+    assert lib.oomb_abi_version() == 9
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text
@@ -123,6 +123,32 @@ def test_summarize_and_select_errors(lib):
     assert sel(score=B, sstr=10) == L.OOMB_ERR_INVALID and b"score_stride" in lib.oomb_last_error()
     assert sel(wsb=ws - 1) == L.OOMB_ERR_WORKSPACE
     assert sel(ws=0xA00010) == L.OOMB_ERR_WORKSPACE
+
+
+def test_select_noalloc_host_checks(lib):
+    """The allocation-free selection checks every argument as oomb_select_pages does,
+    and rejects a call whose workspace would exceed its 8 MiB static scratch, all
+    before any HIP call (none is possible here)."""
+    p = _pool()
+
+    def sel(t0=4096, tstride=64, **kw):
+        a = dict(top_k=4, sel=B, sstride=4, count=B + 256, score=None, sstr=0)
+        a.update(kw)
+        return lib.oomb_select_pages_noalloc(ctypes.byref(p), T, tstride, Q, 4096 * 128, 128,
+                                             4096, t0, a["top_k"], a["sel"], a["sstride"],
+                                             a["count"], None, a["score"], a["sstr"], None)
+    assert sel(top_k=-1) == L.OOMB_ERR_INVALID and b"top_k" in lib.oomb_last_error()
+    assert sel(sstride=3) == L.OOMB_ERR_INVALID and b"sel must hold" in lib.oomb_last_error()
+    assert sel(count=None) == L.OOMB_ERR_INVALID
+    assert sel(tstride=10) == L.OOMB_ERR_INVALID
+    # 4 KV heads x 600,000 candidate pages of scores = 9.6 MB > 8 MiB
+    t0 = 128 * 600_000
+    need = lib.oomb_select_workspace_bytes(ctypes.byref(p), 4096, t0)
+    assert need > 8 * 2 ** 20
+    assert sel(t0=t0, tstride=600_000 + 32) == L.OOMB_ERR_INVALID
+    assert b"static scratch holds 8388608" in lib.oomb_last_error()
+    # the 4M-token chunk of 8192 queries fits
+    assert lib.oomb_select_workspace_bytes(ctypes.byref(p), 8192, 4_186_112) <= 8 * 2 ** 20
 
 
 def test_fwd_workspace(lib):
