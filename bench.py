@@ -23,6 +23,11 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+# Hardware queues per process (HIP's default is 4). The offload-schedule measurement
+# runs a compute stream and two copy streams beside the default one; with four queues
+# HIP can give a copy stream the compute stream's queue, where it waits behind the
+# kernels (measured 5-80% slower schedules). Set before HIP initialises.
+os.environ.setdefault("GPU_MAX_HW_QUEUES", "8")
 
 METRIC = "fwd+bwd paged chunk-attn TFLOP/s @1M ctx; % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -167,13 +172,12 @@ def cpu_baseline(w, x, sel_cpu, rows: int, max_pairs: float):
 PEAK_PCIE_GBS = 64.0  # PCIe 5.0 x16 host link, per direction
 
 
-def offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step, reps=10):
-    """The CPU offload of one sparse layer-chunk (explainer 2.C), timed with HIP events:
-    fetch of the selected pages from pinned host pages into another layer's device pool,
-    offload of the chunk's new pages to the host, and write-back of the attended
-    gradient pages into a pinned fp32 host pool; a copy-engine transfer of 256 MiB as
-    the link reference; and the overlap: the attention step alone against the same step
-    with the next layer's transfers on a second stream."""
+def offload_leg(pca, torch, w, pool, table, gtable, sel, count, reps=10):
+    """The page moves of the CPU offload of one sparse layer-chunk (explainer 2.C), each
+    timed alone with HIP events on a second stream: fetch of the selected pages from
+    pinned host pages into another layer's device pool, offload of the chunk's new pages
+    to the host, write-back of the attended gradient pages into a pinned fp32 host pool;
+    and copy-engine transfers of 256 MiB as the link reference."""
     P, C, t0, D = w.page, w.chunk, w.t0, w.d
     esize = 2 if w.dtype == torch.bfloat16 else 4
     page_b = P * D * esize
@@ -229,52 +233,6 @@ def offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step
                             f"{g_ids.numel()} attended gradient pages, dK and dV, added into the host pool"),
     }
 
-    # the same moves on the copy engines, with page lists the host holds: the selection
-    # read back once (a small copy and one wait), the table and gradient table too
-    sel_h = sel.cpu()
-    cnt_h = count.cpu()
-    tab_h = table.cpu()
-    gtab_h = gtable.cpu()
-    hts_h = host_table.cpu()
-    f_src, f_dst = [], []
-    for g in range(hkv):
-        for j in range(int(cnt_h[g])):
-            f_src.append(int(hts_h[g, int(sel_h[g, j])]))
-            f_dst.append(int(stage[g, j]))
-    n_src_ids = tab_h[:, first_local:first_local + n_local].flatten().tolist()
-    att_h = torch.cat([sel_h.to(torch.int64),
-                       torch.arange(first_local, first_local + n_local).expand(hkv, -1)], 1)
-    g_src = torch.gather(gtab_h.to(torch.int64), 1, att_h).flatten().tolist()
-    dev_g_stage = torch.empty(len(g_src), P, D, dtype=torch.float32, device=dev)
-    g_stage_ids = list(range(len(g_src)))
-    sdma_moves = {
-        "fetch_selected_sdma": (lambda st: (pca.oomb_copy_pages_sdma(host_k, nxt.k, f_src, f_dst, stream=st),
-                                            pca.oomb_copy_pages_sdma(host_v, nxt.v, f_src, f_dst, stream=st)),
-                                hkv * k * 2 * page_b, "host -> device", "as fetch_selected"),
-        "offload_new_pages_sdma": (lambda st: (pca.oomb_copy_pages_sdma(pool.k, host_new_k, n_src_ids,
-                                                                        list(range(len(n_src_ids))), stream=st),
-                                               pca.oomb_copy_pages_sdma(pool.v, host_new_v, n_src_ids,
-                                                                        list(range(len(n_src_ids))), stream=st)),
-                                   hkv * n_local * 2 * page_b, "device -> host", "as offload_new_pages"),
-        # gradients: the host pool's pages come in, are added to on the device (a
-        # device-only kernel), and go back: twice the link bytes, in both directions
-        "grad_round_trip_sdma": (lambda st: (pca.oomb_copy_pages_sdma(host_dk, dev_g_stage, g_stage_ids,
-                                                                      g_stage_ids, stream=st),
-                                             pca.oomb_add_pages_f32(pool.dk, dev_g_stage, g_ids,
-                                                                    host_g_ids, stream=st),
-                                             pca.oomb_copy_pages_sdma(dev_g_stage, host_dk, g_stage_ids,
-                                                                      g_stage_ids, stream=st),
-                                             pca.oomb_copy_pages_sdma(host_dv, dev_g_stage, g_stage_ids,
-                                                                      g_stage_ids, stream=st),
-                                             pca.oomb_add_pages_f32(pool.dv, dev_g_stage, g_ids,
-                                                                    host_g_ids, stream=st),
-                                             pca.oomb_copy_pages_sdma(dev_g_stage, host_dv, g_stage_ids,
-                                                                      g_stage_ids, stream=st)),
-                                 2 * 2 * len(g_src) * P * D * 4, "both directions",
-                                 f"{len(g_src)} attended gradient pages, dK and dV: in, added on the "
-                                 f"device, out"),
-    }
-
     def timed(fn, stream):
         times = []
         for _ in range(reps):
@@ -288,7 +246,7 @@ def offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step
         return times[len(times) // 2]
 
     out = {"peak_GBps": PEAK_PCIE_GBS, "link": "PCIe 5.0 x16, per direction"}
-    for name, (fn, nbytes, direction, what) in list(moves.items()) + list(sdma_moves.items()):
+    for name, (fn, nbytes, direction, what) in moves.items():
         fn(side)
         torch.cuda.synchronize()
         ms = timed(fn, side)
@@ -308,77 +266,91 @@ def offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step
         ms = timed(run, side)
         gbs = (256 << 20) / (ms * 1e-3) / 1e9
         out[name] = {"ms": ms, "bytes": 256 << 20, "GBps": gbs, "frac": gbs / PEAK_PCIE_GBS}
+    return out
 
-    # overlap: the attention step (forward + backward) alone, then with the next layer's
-    # fetch, this chunk's page offload and the gradient write-back on a second stream
-    main = torch.cuda.current_stream()
 
-    def step_alone():
-        attn_step()
+def offload_schedule_leg(pca, torch, name, n_layers, reps=3, steps=4, grads_on_host=True):
+    """The offload schedule end to end (explainer 2.C): one chunk step (forward through
+    `n_layers` attention layers, backward in reverse) of the named workload's geometry
+    with every layer's K/V cache and gradient pool in pinned host memory and the page
+    moves overlapped on a copy stream (paged_chunk_attention_amd.offload), against the
+    same step on all-resident caches, each timed over `steps` consecutive chunk steps.
+    Reports both times per step, the overhead and the bytes moved per step; the results
+    of the two runs are equal bit for bit (GPU test)."""
+    import workloads as wl
+    from paged_chunk_attention_amd.offload import OffloadedAttentionStack
+    w = wl.WORKLOADS[name]
+    C, P, t0 = w.chunk, w.page, w.t0
+    dev = "cuda"
+    stk = OffloadedAttentionStack(n_layers, w.hq, w.hkv, w.d, P, t0, C, top_k=w.top_k,
+                                  dtype=w.dtype, device=dev, grads_on_host=grads_on_host)
+    gen = torch.Generator(device=dev).manual_seed(11)
 
-    def step_with_transfers():
-        side.wait_stream(main)
-        for fn, _, _, _ in moves.values():
-            fn(side)
-        attn_step()
-        main.wait_stream(side)
+    def rnd(*shape):
+        return torch.randn(*shape, generator=gen, device=dev).to(w.dtype)
 
-    def step_with_sdma_transfers():
-        side.wait_stream(main)
-        for fn, _, _, _ in sdma_moves.values():
-            fn(side)
-        attn_step()
-        main.wait_stream(side)
+    for l in range(n_layers):
+        stk.load_prior(l, rnd(w.hkv, t0, w.d), rnd(w.hkv, t0, w.d))
+    q = [rnd(w.hq, C, w.d) for _ in range(n_layers)]
+    kn = [rnd(w.hkv, C, w.d) for _ in range(n_layers)]
+    vn = [rnd(w.hkv, C, w.d) for _ in range(n_layers)]
+    do = [rnd(w.hq, C, w.d) for _ in range(n_layers)]
+    o = [torch.empty(w.hq, C, w.d, dtype=w.dtype, device=dev) for _ in range(n_layers)]
+    lse = [torch.empty(w.hq, C, dtype=torch.float32, device=dev) for _ in range(n_layers)]
+    dq = [torch.empty(w.hq, C, w.d, dtype=torch.float32, device=dev) for _ in range(n_layers)]
+    pools = stk.resident_pools()
+
+    def resident():
+        for _ in range(steps):
+            for p_ in pools:
+                p_.zero_grad()
+            stk.resident_step(pools, q, kn, vn, do, o, lse, dq)
+
+    def offloaded():
+        for s_ in range(steps):   # consecutive chunk steps: one's tail overlaps the next's head
+            stk.step(q, kn, vn, do, o, lse, dq, join=s_ == steps - 1)
 
     res = {}
-    for name, fn in (("alone", step_alone), ("with_transfers", step_with_transfers),
-                     ("with_sdma_transfers", step_with_sdma_transfers), ("alone_again", step_alone)):
-        for _ in range(2):
-            fn()
+    for label, fn in (("resident", resident), ("offloaded", offloaded), ("resident_again", resident),
+                      ("offloaded_again", offloaded)):
+        fn()
         torch.cuda.synchronize()
-        t = time.perf_counter()
+        times = []
         for _ in range(reps):
+            t = time.perf_counter()
             fn()
-        torch.cuda.synchronize()
-        res[name] = (time.perf_counter() - t) * 1e3 / reps
-    # the same byte volumes moved by the copy engines (contiguous buffers, no CUs)
-    ce_h2d = [(torch.empty(nb, dtype=torch.uint8, device=dev),
-               torch.empty(nb, dtype=torch.uint8, pin_memory=True))
-              for nb in (moves["fetch_selected"][1], moves["grad_write_back"][1] // 2)]
-    ce_d2h = [(torch.empty(nb, dtype=torch.uint8, pin_memory=True),
-               torch.empty(nb, dtype=torch.uint8, device=dev))
-              for nb in (moves["offload_new_pages"][1], moves["grad_write_back"][1] // 2)]
-
-    def step_with_copy_engine():
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            for d_, s_ in ce_h2d + ce_d2h:
-                d_.copy_(s_, non_blocking=True)
-        attn_step()
-        main.wait_stream(side)
-
-    for _ in range(2):
-        step_with_copy_engine()
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    for _ in range(reps):
-        step_with_copy_engine()
-    torch.cuda.synchronize()
-    res["with_copy_engine"] = (time.perf_counter() - t) * 1e3 / reps
-    base = 0.5 * (res["alone"] + res["alone_again"])
-    out["overlap"] = {"attention_ms": base, "attention_with_transfers_ms": res["with_transfers"],
-                      "overhead": res["with_transfers"] / base - 1.0,
-                      "attention_with_sdma_page_lists_ms": res["with_sdma_transfers"],
-                      "overhead_sdma_page_lists": res["with_sdma_transfers"] / base - 1.0,
-                      "sdma_transfer_bytes": sum(v[1] for v in sdma_moves.values()),
-                      "attention_with_copy_engine_ms": res["with_copy_engine"],
-                      "overhead_copy_engine": res["with_copy_engine"] / base - 1.0,
-                      "transfer_bytes": sum(v[1] for v in moves.values()),
-                      "what": "forward + backward of the chunk on one stream; on a second "
-                              "stream, started with it: the three kernel page moves above "
-                              "(overhead), the three copy-engine page-list moves "
-                              "(overhead_sdma_page_lists), or contiguous copy-engine transfers of "
-                              "the same bytes (overhead_copy_engine)"}
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t) * 1e3 / steps)
+        res[label] = times
+    base = min(res["resident"] + res["resident_again"])
+    off = min(res["offloaded"] + res["offloaded_again"])
+    esize = 2 if w.dtype == torch.bfloat16 else 4
+    page_b = P * w.d * esize
+    grad_page_b = 2 * P * w.d * 4 if grads_on_host else 0   # dK and dV, fp32
+    if w.top_k is None:
+        # K/V: prior pages (forward) and every page (backward, but the last layer's);
+        # gradients: every page in and out
+        h2d = (n_layers * w.hkv * stk.n_prior + (n_layers - 1) * w.hkv * stk.npph) * 2 * page_b \
+            + n_layers * w.hkv * stk.npph * grad_page_b
+        d2h = n_layers * w.hkv * (stk.n_local * 2 * page_b + stk.npph * grad_page_b)
+    else:
+        # K/V: the selected pages twice, the local pages once; gradients: added into the
+        # host pool (read and written there by the add kernel)
+        h2d = (n_layers * w.hkv * 2 * stk.k_sel + (n_layers - 1) * w.hkv * stk.n_local) * 2 * page_b \
+            + n_layers * w.hkv * (stk.k_sel + stk.n_local) * grad_page_b
+        d2h = n_layers * w.hkv * (stk.n_local * 2 * page_b + (stk.k_sel + stk.n_local) * grad_page_b)
+    out = {"layers": n_layers, "steps_timed": steps, "gradients_on_host": grads_on_host,
+           "resident_ms": base, "offloaded_ms": off,
+           "all_ms": {k_: [round(v_, 3) for v_ in t_] for k_, t_ in res.items()},
+           "overhead": off / base - 1.0, "bytes_host_to_device": h2d,
+           "bytes_device_to_host": d2h,
+           "what": (f"one {C}-query chunk after {t0} tokens ({w.name} geometry, "
+                    f"{'top-' + str(w.top_k) if w.top_k else 'dense'}), forward through "
+                    f"{n_layers} layers then backward, caches and gradients in pinned host "
+                    "memory with the next layer's pages fetched and the gradient pages written "
+                    "back on a copy stream, against the same step on resident caches")}
+    del stk, pools
+    torch.cuda.empty_cache()
     return out
 
 
@@ -774,6 +746,8 @@ def main():
                     help="skip timing one chunk-recurrent attention layer (65,536 tokens)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offload measurements (sparse workloads)")
+    ap.add_argument("--offload-layers", type=int, default=4,
+                    help="layers of the offload schedule measurement (dense 128K and sparse 1M)")
     ap.add_argument("--also", default="dense128k,sparse4m,local1m,sweep256k,sweep256k_top64,tiny",
                     help="comma-separated other workloads to time briefly ('none' for none)")
     ap.add_argument("--hbm-reps", type=int, default=3,
@@ -919,15 +893,20 @@ def main():
 
     offload = None
     if sparse and not args.no_offload:
-        def attn_step():
-            pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, sel, count, w.scale, o=o, lse=lse,
-                                          workspace=ws_fwd)
-            pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, sel, count, o, do, lse,
-                                          w.scale, dq=dq, workspace=ws_bwd)
         log("[bench] offload leg ...")
-        offload = offload_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, attn_step)
-        log(f"[bench] offload: fetch {offload['fetch_selected']['GBps']:.1f} GB/s, overlap "
-            f"overhead {100 * offload['overlap']['overhead']:.1f} %")
+        offload = offload_leg(pca, torch, w, pool, table, gtable, sel, count)
+        log(f"[bench] offload: fetch {offload['fetch_selected']['GBps']:.1f} GB/s")
+        sched = {}
+        for label, sname, on_host in (("dense128k", "dense128k", True),
+                                      ("dense128k_grads_on_device", "dense128k", False),
+                                      ("sparse1m", "sparse1m", True)):
+            log(f"[bench] offload schedule {label}, {args.offload_layers} layers ...")
+            sched[label] = offload_schedule_leg(pca, torch, sname, args.offload_layers,
+                                                grads_on_host=on_host)
+            log(f"[bench] offload schedule {label}: resident {sched[label]['resident_ms']:.2f} ms, "
+                f"offloaded {sched[label]['offloaded_ms']:.2f} ms, overhead "
+                f"{100 * sched[label]['overhead']:.1f} %")
+        offload["schedule"] = sched
 
     layer = None
     if not args.no_layer:

@@ -295,12 +295,16 @@ int oomb_copy_pages(const void* src, void* dst, int64_t page_bytes, int64_t n_sr
                     int32_t n, const int32_t* n_dev, void* stream);
 
 /* As oomb_copy_pages, on the copy engines (SDMA) instead of compute units, for lists the
- * host knows: src_ids / dst_ids are HOST int32 arrays, read during the call; runs of
- * consecutive pages on both sides become one transfer each, enqueued on `stream`.
- * page_bytes > 0. While attention kernels run on other streams, transfers
- * by the copy engines leave them at full speed; copies by kernels (oomb_copy_pages,
- * oomb_fetch_selected) share the compute units' memory path and slow them by ~10%, in
- * exchange for device-side lists. */
+ * host knows that consist of long runs of consecutive pages (a whole layer's pages, a
+ * chunk's new pages): src_ids / dst_ids are HOST int32 arrays, read during the call;
+ * each run of consecutive pages on both sides becomes one transfer, enqueued on
+ * `stream`. page_bytes > 0. Every transfer has a fixed cost of several microseconds,
+ * so a list that breaks into more than max(16, n / 16) runs is refused with
+ * OOMB_ERR_INVALID before any HIP call: scattered pages go through oomb_copy_pages or
+ * oomb_fetch_selected, whose kernels gather them at the link's speed. While attention
+ * kernels run on other streams, copy-engine transfers leave them at full speed; copies
+ * by kernels share the compute units' memory path and slow them by ~10%, in exchange
+ * for device-side lists. */
 int oomb_copy_pages_sdma(const void* src, void* dst, int64_t page_bytes, int64_t n_src_pages,
                          int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
                          int32_t n, void* stream);

@@ -170,9 +170,37 @@ class PagedPool:
             dk_pool=self.dk.data_ptr() if with_grad else None,
             dv_pool=self.dv.data_ptr() if with_grad else None)
 
+    @classmethod
+    def from_tensors(cls, k: torch.Tensor, v: torch.Tensor, summary: Optional[torch.Tensor],
+                     dk: Optional[torch.Tensor], dv: Optional[torch.Tensor], num_q_heads: int,
+                     num_kv_heads: int, num_pages: Optional[int] = None) -> "PagedPool":
+        """A pool over existing tensors (nothing is allocated): k, v [N, P, D] in one dtype,
+        summary [>= num_pages, 2, D] or None, dk, dv fp32 [Ng, P, D] or None. num_pages
+        (default N) is what the descriptor declares; a larger value suits calls that only
+        read the summaries (the page selection), indexed by ids up to num_pages."""
+        if k.dtype not in _DTYPES or v.dtype != k.dtype or v.shape != k.shape or k.dim() != 3:
+            raise ValueError("k and v must be [pages, page_size, head_dim] tensors of one dtype")
+        self = cls.__new__(cls)
+        self.page_size, self.head_dim = k.shape[1], k.shape[2]
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.dtype, self.device = k.dtype, k.device
+        self.k, self.v, self.summary, self.dk, self.dv = k, v, summary, dk, dv
+        n = k.shape[0] if num_pages is None else num_pages
+        if summary is not None and summary.shape[0] < n:
+            raise ValueError("summary holds fewer pages than declared")
+        ng = 0 if dk is None else dk.shape[0]
+        self.desc = OombPool(
+            dtype=_DTYPES[k.dtype], page_size=k.shape[1], head_dim=k.shape[2],
+            num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, reserved=0,
+            num_pages=n, num_grad_pages=ng, k_pool=k.data_ptr(), v_pool=v.data_ptr(),
+            k_summary=None if summary is None else summary.data_ptr(),
+            dk_pool=None if dk is None else dk.data_ptr(),
+            dv_pool=None if dv is None else dv.data_ptr())
+        return self
+
     @property
     def num_pages(self) -> int:
-        return self.k.shape[0]
+        return int(self.desc.num_pages)
 
     def zero_grad(self):
         if self.dk is not None:

@@ -638,6 +638,11 @@ int oomb_copy_pages(const void* src, void* dst, int64_t page_bytes, int64_t n_sr
   return hip_status(oomb::launch_copy_pages(a, static_cast<hipStream_t>(stream)), "copy_pages");
 }
 
+// A copy-engine page list may break into at most max(kSdmaMaxShortRuns, n / kSdmaMinRun)
+// runs of consecutive pages: runs average at least kSdmaMinRun pages, or there are few.
+constexpr int64_t kSdmaMinRun = 16;
+constexpr int64_t kSdmaMaxShortRuns = 16;
+
 int oomb_copy_pages_sdma(const void* src, void* dst, int64_t page_bytes, int64_t n_src_pages,
                          int64_t n_dst_pages, const int32_t* src_ids, const int32_t* dst_ids,
                          int32_t n, void* stream) {
@@ -646,6 +651,21 @@ int oomb_copy_pages_sdma(const void* src, void* dst, int64_t page_bytes, int64_t
   if (n_src_pages <= 0 || n_dst_pages <= 0) return fail(OOMB_ERR_INVALID, "page counts must be positive");
   if (n > 0 && (src_ids == nullptr || dst_ids == nullptr))
     return fail(OOMB_ERR_INVALID, "id lists are NULL");
+  // Runs of consecutive pages on both sides become one copy-engine transfer each. Each
+  // transfer has a fixed cost of several microseconds, so a list that breaks into many
+  // short runs (scattered pages) would crawl: such lists belong to oomb_copy_pages,
+  // whose kernel gathers scattered pages at the link's speed. Refused before any HIP call.
+  {
+    int64_t runs = 0;
+    for (int32_t i = 0; i < n; ++i)
+      if (i == 0 || src_ids[i] != src_ids[i - 1] + 1 || dst_ids[i] != dst_ids[i - 1] + 1) ++runs;
+    const int64_t allowed = n / kSdmaMinRun > kSdmaMaxShortRuns ? n / kSdmaMinRun : kSdmaMaxShortRuns;
+    if (runs > allowed)
+      return fail(OOMB_ERR_INVALID,
+                  "copy_pages_sdma: %d pages in %lld runs (more than %lld); copy scattered pages "
+                  "with oomb_copy_pages", n, static_cast<long long>(runs),
+                  static_cast<long long>(allowed));
+  }
   const void* s_dev = nullptr;
   const void* d_dev = nullptr;
   int st;
@@ -653,7 +673,6 @@ int oomb_copy_pages_sdma(const void* src, void* dst, int64_t page_bytes, int64_t
   // the copy synchronous); the copies themselves use the pointers as given
   if ((st = device_address(src, 1, "src", &s_dev))) return st;
   if ((st = device_address(static_cast<const void*>(dst), 1, "dst", &d_dev))) return st;
-  // runs of consecutive pages on both sides become one copy each
   std::vector<void*> dsts, srcs;
   std::vector<size_t> sizes;
   for (int32_t i = 0; i < n;) {

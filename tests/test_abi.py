@@ -261,3 +261,19 @@ def test_bwd_errors(lib):
     assert bwd(p, gts=5) == L.OOMB_ERR_INVALID
     assert bwd(p, dqts=130) == L.OOMB_ERR_INVALID
     assert bwd(p, wsb=need - 4) == L.OOMB_ERR_WORKSPACE
+
+
+def test_copy_pages_sdma_refuses_scattered_lists(lib):
+    """The copy-engine page list is for long runs of consecutive pages: a list of 64
+    scattered pages (64 runs, more than max(16, 64 / 16)) is refused before any HIP call,
+    pointing to the gather kernel."""
+    n = 64
+    scattered = (ctypes.c_int32 * n)(*[3 * i for i in range(n)])
+    same = (ctypes.c_int32 * n)(*[3 * i for i in range(n)])
+    st = lib.oomb_copy_pages_sdma(0x100000, 0x200000, 32768, 4096, 4096, scattered, same, n, None)
+    assert st == L.OOMB_ERR_INVALID and b"oomb_copy_pages" in lib.oomb_last_error()
+    # 16 runs of 4 pages are still accepted by the run count (the call then checks the
+    # pointers, which here fails with a different message: no GPU, fake addresses)
+    runs = (ctypes.c_int32 * n)(*[16 * (i // 4) + i % 4 for i in range(n)])
+    st = lib.oomb_copy_pages_sdma(0x100000, 0x200000, 32768, 4096, 4096, runs, runs, n, None)
+    assert b"runs" not in lib.oomb_last_error()

@@ -197,3 +197,84 @@ def test_offload_cycle_then_attention(kw):
     gdv = L.pool.dv.cpu()[:n].double() - (L.grad_init[:n] * 0.5).double()
     compare("dK", gdk[touched], gpk[touched], w.dtype)
     compare("dV", gdv[touched], gpv[touched], w.dtype)
+
+
+@pytest.mark.parametrize("top_k,grads_on_host", [(None, True), (3, True), (None, False)])
+def test_offloaded_stack_matches_resident_and_oracle(top_k, grads_on_host):
+    """Three attention layers with their caches in pinned host memory, one chunk step
+    (forward through the layers, backward in reverse) with the transfers on a copy
+    stream: O, LSE, dQ, the selections, every host gradient page and the chunk's pages
+    written back to the host cache equal the all-resident run bit for bit; and each
+    layer matches the oracle (selection bit-exact, attention at the bf16 bar)."""
+    from paged_chunk_attention_amd.offload import OffloadedAttentionStack
+    L, hq, hkv, d, P, prior, C = 3, 8, 2, 128, 64, 64 * 12, 192
+    G = hq // hkv
+    log(f"[case offloaded stack top_k={top_k} grads_on_host={grads_on_host}] layers={L} "
+        f"prior={prior} chunk={C}")
+    stk = OffloadedAttentionStack(L, hq, hkv, d, P, prior, C, top_k=top_k, device=DEV,
+                                  grads_on_host=grads_on_host)
+    gen = lambda shape, seed: _rand(shape, seed, torch.bfloat16)      # noqa: E731
+    kp_in = [gen((hkv, prior, d), 100 + l) for l in range(L)]
+    vp_in = [gen((hkv, prior, d), 200 + l) for l in range(L)]
+    q = [gen((hq, C, d), 300 + l) for l in range(L)]
+    kn = [gen((hkv, C, d), 400 + l) for l in range(L)]
+    vn = [gen((hkv, C, d), 500 + l) for l in range(L)]
+    do = [gen((hq, C, d), 600 + l) for l in range(L)]
+    for l in range(L):
+        stk.load_prior(l, kp_in[l], vp_in[l])
+    stk.zero_grad()
+    qd, knd, vnd, dod = ([t.to(DEV) for t in ts] for ts in (q, kn, vn, do))
+    o = [torch.empty(hq, C, d, dtype=torch.bfloat16, device=DEV) for _ in range(L)]
+    lse = [torch.empty(hq, C, dtype=torch.float32, device=DEV) for _ in range(L)]
+    dq = [torch.empty(hq, C, d, dtype=torch.float32, device=DEV) for _ in range(L)]
+    stk.step(qd, knd, vnd, dod, o, lse, dq)
+    torch.cuda.synchronize()
+    log("    offloaded step done")
+    sels = None if top_k is None else [(s.clone(), c.clone()) for s, c in zip(stk.sel, stk.count)]
+    pools = stk.resident_pools()
+    o2 = [torch.empty_like(t) for t in o]
+    lse2 = [torch.empty_like(t) for t in lse]
+    dq2 = [torch.empty_like(t) for t in dq]
+    stk.resident_step(pools, qd, knd, vnd, dod, o2, lse2, dq2)
+    torch.cuda.synchronize()
+    log("    resident step done")
+    n_local = stk.n_local
+    for l in range(L):
+        assert torch.equal(bits(o[l]), bits(o2[l])), f"O layer {l}"
+        assert torch.equal(lse[l].cpu(), lse2[l].cpu()), f"LSE layer {l}"
+        assert torch.equal(dq[l].cpu(), dq2[l].cpu()), f"dQ layer {l}"
+        assert torch.equal(stk.hdk[l].cpu(), pools[l].dk.cpu()), f"dK pool layer {l}"
+        assert torch.equal(stk.hdv[l].cpu(), pools[l].dv.cpu()), f"dV pool layer {l}"
+        if sels is not None:
+            assert torch.equal(sels[l][0].cpu(), stk.sel[l].cpu()), f"selection layer {l}"
+            assert torch.equal(sels[l][1].cpu(), stk.count[l].cpu())
+        for g in range(hkv):   # the chunk's new pages reached the host cache
+            pg = g * stk.npph + stk.first_local
+            got_k = stk.hk[l][pg:pg + n_local].reshape(-1, d)[:C]
+            got_v = stk.hv[l][pg:pg + n_local].reshape(-1, d)[:C]
+            assert torch.equal(bits(got_k), bits(kn[l][g])) and torch.equal(bits(got_v), bits(vn[l][g]))
+    log("    offloaded == resident, bit for bit")
+    # the oracle, layer by layer, on its own pool (identity placement)
+    table = torch.arange(hkv * stk.npph, dtype=torch.int32).reshape(hkv, stk.npph)
+    for l in range(L):
+        kpo = torch.zeros(hkv * stk.npph, P, d, dtype=torch.bfloat16)
+        vpo = torch.zeros_like(kpo)
+        orc.append(kpo, table, torch.cat([kp_in[l], kn[l]], dim=1), 0)
+        orc.append(vpo, table, torch.cat([vp_in[l], vn[l]], dim=1), 0)
+        osel = None
+        if top_k is not None:
+            summ = torch.zeros(hkv * stk.npph, 2, d, dtype=torch.bfloat16)
+            orc.summarize(kpo, table, summ, 0, stk.npph, prior + C)
+            osel = [ch for (_, _, ch) in orc.select_pages(q[l], summ, table, prior, P, G, top_k)]
+            for g in range(hkv):
+                n = int(sels[l][1][g])
+                assert sels[l][0][g, :n].cpu().tolist() == osel[g], f"oracle selection layer {l}"
+        gk = torch.zeros(kpo.shape, dtype=torch.float64)
+        gv = torch.zeros(kpo.shape, dtype=torch.float64)
+        dQ, _, O, Lse = orc.bwd(q[l], kpo, vpo, table, prior, osel, stk.scale, do[l], gk, gv,
+                                table, with_fwd=True)
+        compare(f"O(l{l})", o[l], O, torch.bfloat16)
+        compare(f"dQ(l{l})", dq[l], dQ, torch.bfloat16)
+        assert (lse[l].cpu().double() - Lse).abs().max().item() <= 1e-2
+        compare(f"dK(l{l})", stk.hdk[l].cpu(), gk, torch.bfloat16)
+        compare(f"dV(l{l})", stk.hdv[l].cpu(), gv, torch.bfloat16)
