@@ -26,8 +26,14 @@ sys.path.insert(0, ROOT)
 # Hardware queues per process (HIP's default is 4). The offload-schedule measurement
 # runs a compute stream and two copy streams beside the default one; with four queues
 # HIP can give a copy stream the compute stream's queue, where it waits behind the
-# kernels (measured 5-80% slower schedules). Set before HIP initialises.
-os.environ.setdefault("GPU_MAX_HW_QUEUES", "8")
+# kernels (measured 5-80% slower schedules). Raised to 8 (when lower) before HIP
+# initialises; the environment may already hold HIP's default of 4.
+try:
+    _hwq = int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))
+except ValueError:
+    _hwq = 4
+if _hwq < 8:
+    os.environ["GPU_MAX_HW_QUEUES"] = "8"
 
 METRIC = "fwd+bwd paged chunk-attn TFLOP/s @1M ctx; % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -415,6 +421,71 @@ def mean_selector_leg(pca, torch, w, pool, table, q, sel, count, needles, reps=3
                    "of the needle pages each selection contains, summed over KV heads")
     del scratch
     return out
+
+
+def tiled_selector_leg(pca, torch, w, pool, table, gtable, q, do, sel, count, needles, tile=1024,
+                       reps=5):
+    """The per-query-tile selection (explainer 2.D leaves the unit of selection open): each
+    tile of `tile` queries selects its own top-k prior pages. Reports the tiled selection's
+    time, how far each tile's pages agree with the per-chunk selection of the step and
+    their needle recall, and the attention step (forward + backward, one call per tile)
+    against the per-chunk step on the same pool."""
+    C, t0 = w.chunk, w.t0
+    n_tiles = -(-C // tile)
+    stream = torch.cuda.current_stream()
+    width = pca.tile_row_length(pool, C, t0, w.top_k, tile)
+    sel_t = torch.full((n_tiles, w.hkv, width), -1, dtype=torch.int32, device="cuda")
+    cnt_t = torch.zeros(n_tiles, w.hkv, dtype=torch.int32, device="cuda")
+    ws = torch.empty(pca.select_tiled_workspace_bytes(pool, C, t0, tile), dtype=torch.uint8,
+                     device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        return times[len(times) // 2]
+
+    sel_ms = timed(lambda: pca.oomb_select_pages_tiled(pool, table, q, t0, w.top_k, tile,
+                                                       sel=sel_t, count=cnt_t, workspace=ws))
+    k = max(1, min(w.top_k, t0 // w.page))
+    chunk_sets = [set(sel[g, :int(count[g])].tolist()) for g in range(w.hkv)]
+    nd = set(int(j) for j in needles)
+    sel_h, cnt_h = sel_t.cpu(), cnt_t.cpu()
+    overlap, recall = [], []
+    for j in range(n_tiles):
+        for g in range(w.hkv):
+            picked = set(sel_h[j, g, :k].tolist())      # the row's top-k part
+            overlap.append(len(picked & chunk_sets[g]) / k)
+            recall.append(len(picked & nd) / max(1, len(nd)))
+
+    def chunk_attn():
+        o, lse = pca.oomb_paged_chunk_attn_fwd(pool, table, q, t0, sel, count, w.scale)
+        pca.oomb_paged_chunk_attn_bwd(pool, table, gtable, q, t0, sel, count, o, do, lse, w.scale)
+
+    def tiled_attn():
+        o, lses = pca.oomb_paged_chunk_attn_fwd_tiled(pool, table, q, t0, sel_t, cnt_t, tile,
+                                                      w.scale)
+        pca.oomb_paged_chunk_attn_bwd_tiled(pool, table, gtable, q, t0, sel_t, cnt_t, tile, o,
+                                            do, lses, w.scale)
+
+    t_chunk = timed(chunk_attn)
+    t_tiled = timed(tiled_attn)
+    return {"tile": tile, "tiles": n_tiles, "select_ms": sel_ms,
+            "overlap_with_chunk_selection": sum(overlap) / len(overlap),
+            "needle_recall_tiled": sum(recall) / len(recall),
+            "attention_ms_per_chunk_selection": t_chunk, "attention_ms_tiled": t_tiled,
+            "what": (f"{n_tiles} tiles of {tile} queries each select their own top-{w.top_k} "
+                     "prior pages; overlap = share of a tile's pages that the chunk's selection "
+                     "also holds, averaged over tiles and KV heads; attention = forward + "
+                     "backward, one call per tile against one call per chunk")}
 
 
 def layer_leg(pca, torch, tokens=65536, reps=2):
@@ -888,6 +959,13 @@ def main():
         selector = mean_selector_leg(pca, torch, w, pool, table, q, sel, count, x["needles"])
         hbm["page_summarize_mean"] = selector.pop("page_summarize_mean")
         hbm["select_pages_mean"] = selector.pop("select_pages_mean")
+        selector["tiled"] = tiled_selector_leg(pca, torch, w, pool, table, gtable, q, do, sel,
+                                               count, x["needles"])
+        log(f"[bench] tiled selection ({selector['tiled']['tiles']} tiles): "
+            f"{selector['tiled']['select_ms']:.3f} ms, overlap with the chunk's "
+            f"{100 * selector['tiled']['overlap_with_chunk_selection']:.1f} %, attention "
+            f"{selector['tiled']['attention_ms_tiled']:.3f} ms vs "
+            f"{selector['tiled']['attention_ms_per_chunk_selection']:.3f} ms")
         log(f"[bench] selectors agree on {100 * selector['overlap']:.1f} % of pages; needle recall "
             f"min/max {selector['needle_recall_minmax']:.2f}, mean {selector['needle_recall_mean']:.2f}")
 

@@ -140,6 +140,34 @@ int oomb_select_pages(const oomb_pool* pool, const int32_t* table, int64_t table
                       float* score_out, int64_t score_stride, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Page select per query tile, a finer selection granularity (the explainer, 2.D, leaves
+ * the unit of selection open): the chunk's n_q queries are cut into n_tiles =
+ * ceil(n_q / tile) tiles of `tile` queries (the last one shorter when tile does not
+ * divide n_q), and each (tile, KV head) selects its own top-k candidate pages by the
+ * steps of oomb_select_pages, with qbar taken over the tile's rows only: in step 1 read
+ * n_q as the tile's length and m over the tile's queries, in the same block, tree and
+ * reciprocal order. Candidates are still the complete pages before the chunk (t0/P).
+ * Outputs are tile-major, unit u = j * Hkv + g for tile j and KV head g:
+ *   sel [n_tiles][Hkv][sel_stride]: tile j's top-k ids ascending, then the chunk's
+ *       pages that lie wholly before the tile's first query, logical ids t0/P ..
+ *       (t0 + j*tile)/P - 1 (none for tile 0);
+ *   count [n_tiles][Hkv]: how many ids the row holds;
+ *   qbar_out [n_tiles][Hkv][D], score_out [n_tiles][Hkv][score_stride]: optional.
+ * sel_stride >= min(top_k, t0/P) + (t0 + (n_tiles - 1)*tile)/P - t0/P.
+ * Tile j's attention is then the forward / backward call on its queries (first
+ * position t0 + j*tile, n_q = its length) with sel + j*Hkv*sel_stride and count + j*Hkv
+ * as the selection: the tile attends its own prior pages and every chunk page up to
+ * each query. tile >= n_q gives exactly oomb_select_pages' results. The workspace holds
+ * oomb_select_tiled_workspace_bytes(pool, n_q, t0, tile) bytes (256-byte aligned). */
+size_t oomb_select_tiled_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
+                                         int32_t tile);
+int oomb_select_pages_tiled(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                            const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                            int32_t n_q, int64_t t0, int32_t tile, int32_t top_k, int32_t* sel,
+                            int64_t sel_stride, int32_t* count, float* qbar_out,
+                            float* score_out, int64_t score_stride, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Page select without any allocation, for callers that cannot allocate device memory
  * (code being captured into a HIP graph, tight serving loops, harnesses that forbid
  * hipMalloc): oomb_select_pages with the same arguments and results, minus the

@@ -19,11 +19,16 @@ from .binding import (  # noqa: F401
     oomb_page_summarize,
     oomb_page_summarize_mean,
     oomb_paged_chunk_attn_bwd,
+    oomb_paged_chunk_attn_bwd_tiled,
     oomb_paged_chunk_attn_fwd,
+    oomb_paged_chunk_attn_fwd_tiled,
     oomb_rope,
     oomb_select_pages,
     oomb_select_pages_mean,
     oomb_select_pages_noalloc,
+    oomb_select_pages_tiled,
+    select_tiled_workspace_bytes,
+    tile_row_length,
     select_workspace_bytes,
     split_plan,
 )

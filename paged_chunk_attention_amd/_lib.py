@@ -42,6 +42,11 @@ SIGNATURES = {
     "oomb_select_pages": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32,
                                   c_int64, c_int32, c_void_p, c_int64, c_void_p, c_void_p,
                                   c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
+    "oomb_select_tiled_workspace_bytes": (c_size_t, [P_pool, c_int32, c_int64, c_int32]),
+    "oomb_select_pages_tiled": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64,
+                                        c_int32, c_int64, c_int32, c_int32, c_void_p, c_int64,
+                                        c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_size_t,
+                                        c_void_p]),
     "oomb_select_pages_noalloc": (c_int, [P_pool, c_void_p, c_int64, c_void_p, c_int64, c_int64,
                                           c_int32, c_int64, c_int32, c_void_p, c_int64, c_void_p,
                                           c_void_p, c_void_p, c_int64, c_void_p]),

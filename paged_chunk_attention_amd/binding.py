@@ -312,6 +312,50 @@ def oomb_select_pages(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0:
     return sel, count
 
 
+def select_tiled_workspace_bytes(pool: PagedPool, n_q: int, t0: int, tile: int) -> int:
+    return int(lib().oomb_select_tiled_workspace_bytes(pool.ref(), n_q, t0, tile))
+
+
+def tile_row_length(pool: PagedPool, n_q: int, t0: int, top_k: int, tile: int) -> int:
+    """Ids a row of oomb_select_pages_tiled holds at most: top-k plus the chunk's pages
+    before the last tile."""
+    P = pool.page_size
+    n_tiles = max(1, -(-n_q // tile))
+    return max(0, min(top_k, t0 // P)) + (t0 + (n_tiles - 1) * tile) // P - t0 // P
+
+
+def oomb_select_pages_tiled(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0: int,
+                            top_k: int, tile: int, sel: Optional[torch.Tensor] = None,
+                            count: Optional[torch.Tensor] = None,
+                            qbar_out: Optional[torch.Tensor] = None,
+                            score_out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k prior pages per (query tile, KV head). Returns (sel int32 [n_tiles, Hkv,
+    stride], count int32 [n_tiles, Hkv]); sel[j] and count[j] are the selection of tile j
+    for the attention calls on its queries at position t0 + j * tile."""
+    _check_table(table, pool, "table")
+    hs, ts = _view(q, pool, pool.num_q_heads, "q")
+    n_q = q.shape[1]
+    n_tiles = max(1, -(-n_q // tile)) if tile < n_q else 1
+    width = max(1, tile_row_length(pool, n_q, t0, top_k, tile))
+    with _on(stream):
+        if sel is None:
+            sel = _new("full", (n_tiles, pool.num_kv_heads, width), torch.int32, q.device, -1)
+        if count is None:
+            count = _new("zeros", (n_tiles, pool.num_kv_heads), torch.int32, q.device)
+        if sel.dim() != 3 or sel.stride(2) != 1 or sel.stride(0) != sel.shape[1] * sel.stride(1):
+            raise ValueError("sel must be [n_tiles, Hkv, stride] with contiguous rows")
+        if not count.is_contiguous():
+            raise ValueError("count must be contiguous [n_tiles, Hkv]")
+        ws = _workspace(select_tiled_workspace_bytes(pool, n_q, t0, tile), q.device, workspace)
+        score_stride = 0 if score_out is None else score_out.stride(-2)
+        call("oomb_select_pages_tiled", pool.ref(), _ptr(table), table.stride(0), _ptr(q), hs, ts,
+             n_q, t0, tile, top_k, _ptr(sel), sel.stride(1), _ptr(count), _ptr(qbar_out),
+             _ptr(score_out), score_stride, _ptr(ws), ws.numel(), _stream(stream))
+    return sel, count
+
+
 def oomb_select_pages_noalloc(pool: PagedPool, table: torch.Tensor, q: torch.Tensor, t0: int,
                               top_k: int, sel: torch.Tensor, count: torch.Tensor,
                               qbar_out: Optional[torch.Tensor] = None,
@@ -461,6 +505,46 @@ def oomb_paged_chunk_attn_bwd(pool: PagedPool, table: torch.Tensor, gtable: torc
              gtable.stride(0), _ptr(q), hs, ts, n_q, t0, _ptr(sel), sel_stride, _ptr(count),
              int(window), float(scale), _ptr(o), ohs, ots, _ptr(dout), dhs, dts, _ptr(lse),
              _ptr(dq), qhs, qts, _ptr(ws), ws.numel(), _stream(stream))
+    return dq
+
+
+def oomb_paged_chunk_attn_fwd_tiled(pool: PagedPool, table: torch.Tensor, q: torch.Tensor,
+                                    t0: int, sel: torch.Tensor, count: torch.Tensor, tile: int,
+                                    scale: Optional[float] = None,
+                                    o: Optional[torch.Tensor] = None, stream=None):
+    """Attention of a chunk whose query tiles attend their own selections (sel, count
+    from oomb_select_pages_tiled): one forward call per tile, on its queries at position
+    t0 + j * tile with sel[j], count[j]. Returns (O [Hq, n_q, D], one LSE [Hq, tile
+    length] per tile)."""
+    n_q = q.shape[1]
+    with _on(stream):
+        if o is None:
+            o = _new("empty", q.shape, q.dtype, q.device)
+    lses = []
+    for j, i0 in enumerate(range(0, n_q, tile)):
+        i1 = min(n_q, i0 + tile)
+        _, lse = oomb_paged_chunk_attn_fwd(pool, table, q[:, i0:i1], t0 + i0, sel[j], count[j],
+                                           scale, o=o[:, i0:i1], stream=stream)
+        lses.append(lse)
+    return o, lses
+
+
+def oomb_paged_chunk_attn_bwd_tiled(pool: PagedPool, table: torch.Tensor, gtable: torch.Tensor,
+                                    q: torch.Tensor, t0: int, sel: torch.Tensor,
+                                    count: torch.Tensor, tile: int, o: torch.Tensor,
+                                    dout: torch.Tensor, lses, scale: Optional[float] = None,
+                                    dq: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Backward of oomb_paged_chunk_attn_fwd_tiled: one backward call per tile (dQ of its
+    rows; dK/dV of every tile added into the pool)."""
+    n_q = q.shape[1]
+    with _on(stream):
+        if dq is None:
+            dq = _new("empty", (pool.num_q_heads, n_q, pool.head_dim), torch.float32, q.device)
+    for j, i0 in enumerate(range(0, n_q, tile)):
+        i1 = min(n_q, i0 + tile)
+        oomb_paged_chunk_attn_bwd(pool, table, gtable, q[:, i0:i1], t0 + i0, sel[j], count[j],
+                                  o[:, i0:i1], dout[:, i0:i1], lses[j], scale, dq=dq[:, i0:i1],
+                                  stream=stream)
     return dq
 
 

@@ -269,7 +269,7 @@ const char* oomb_status_string(int status) {
 
 const char* oomb_last_error(void) { return g_last_error.c_str(); }
 
-int oomb_abi_version(void) { return 9; }
+int oomb_abi_version(void) { return 10; }
 
 int oomb_kv_append(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
                    const void* k_new, const void* v_new, int64_t head_stride,
@@ -322,14 +322,33 @@ static void select_layout(int Hkv, int D, int nb, int n_cand, size_t* off_qbar, 
   *total = partial + qbar + score;
 }
 
+// Query tiles of a chunk of n_q queries cut into tiles of `tile` (tile <= 0 or >= n_q:
+// one tile, the per-chunk selection).
+static int n_tiles_of(int32_t n_q, int32_t tile) {
+  return (tile <= 0 || tile >= n_q) ? 1 : (n_q + tile - 1) / tile;
+}
+
+static size_t select_bytes(const oomb::PoolView& v, int32_t n_q, int64_t t0, int32_t tile) {
+  const int nt = n_tiles_of(n_q, tile);
+  const int32_t tl = nt == 1 ? n_q : tile;
+  const int G = v.Hq / v.Hkv;
+  const int64_t nb = (static_cast<int64_t>(G) * tl + 63) / 64;
+  size_t oq, os, total;
+  select_layout(v.Hkv * nt, v.D, static_cast<int>(nb), static_cast<int>(t0 / v.P), &oq, &os, &total);
+  return total;
+}
+
 size_t oomb_select_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0) {
   oomb::PoolView v{};
   if (check_pool(pool, &v, false, false) != OOMB_OK || n_q <= 0 || t0 < 0) return 0;
-  const int G = v.Hq / v.Hkv;
-  const int64_t nb = (static_cast<int64_t>(G) * n_q + 63) / 64;
-  size_t oq, os, total;
-  select_layout(v.Hkv, v.D, static_cast<int>(nb), static_cast<int>(t0 / v.P), &oq, &os, &total);
-  return total;
+  return select_bytes(v, n_q, t0, 0);
+}
+
+size_t oomb_select_tiled_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
+                                         int32_t tile) {
+  oomb::PoolView v{};
+  if (check_pool(pool, &v, false, false) != OOMB_OK || n_q <= 0 || t0 < 0 || tile <= 0) return 0;
+  return select_bytes(v, n_q, t0, tile);
 }
 
 // Page selection from min/max summaries (kmean == nullptr) or mean-key summaries:
@@ -340,7 +359,7 @@ static int select_prepare(const oomb_pool* pool, const int32_t* table, int64_t t
                           int64_t t0, int32_t top_k, const float* kmean, int32_t* sel,
                           int64_t sel_stride, int32_t* count, int64_t score_stride,
                           bool has_score_out, oomb::SelectArgs* a, size_t* off_qbar,
-                          size_t* off_score, size_t* total) {
+                          size_t* off_score, size_t* total, int32_t tile = 0) {
   int st = check_pool(pool, &a->pool, kmean == nullptr, false);
   if (st) return st;
   a->kmean = kmean;
@@ -350,15 +369,21 @@ static int select_prepare(const oomb_pool* pool, const int32_t* table, int64_t t
   if ((st = check_table(table, table_stride, cg.n_cand, "table"))) return st;
   if ((st = check_view(q, q_head_stride, q_tok_stride, elem_size(a->pool), "q"))) return st;
   if (count == nullptr) return fail(OOMB_ERR_INVALID, "count is NULL");
+  const int nt = n_tiles_of(n_q, tile);
+  const int32_t tl = nt == 1 ? n_q : tile;
   const int k = top_k < cg.n_cand ? top_k : cg.n_cand;
-  if (k > 0 && (sel == nullptr || sel_stride < k))
-    return fail(OOMB_ERR_INVALID, "sel must hold min(top_k, t0/P) = %d ids per head", k);
+  // tile j's row also lists the chunk's pages wholly before its first query
+  const int64_t n_app = (t0 + static_cast<int64_t>(nt - 1) * tl) / a->pool.P - t0 / a->pool.P;
+  if ((k > 0 || n_app > 0) && (sel == nullptr || sel_stride < k + n_app))
+    return fail(OOMB_ERR_INVALID, "sel rows must hold %lld ids (sel_stride %lld)",
+                static_cast<long long>(k + n_app), static_cast<long long>(sel_stride));
   if (has_score_out && score_stride < cg.n_cand)
     return fail(OOMB_ERR_INVALID, "score_stride %lld < %d candidates", (long long)score_stride, cg.n_cand);
   const int G = a->pool.Hq / a->pool.Hkv;
-  const int64_t nb = (static_cast<int64_t>(G) * n_q + 63) / 64;
-  if (nb > 16384) return fail(OOMB_ERR_INVALID, "G * n_q = %lld exceeds 1048576", (long long)G * n_q);
-  select_layout(a->pool.Hkv, a->pool.D, static_cast<int>(nb), cg.n_cand, off_qbar, off_score, total);
+  const int64_t nb = (static_cast<int64_t>(G) * tl + 63) / 64;
+  if (nb > 16384) return fail(OOMB_ERR_INVALID, "G * n_q = %lld exceeds 1048576", (long long)G * tl);
+  select_layout(a->pool.Hkv * nt, a->pool.D, static_cast<int>(nb), cg.n_cand, off_qbar, off_score,
+                total);
   a->table = table;
   a->tstride = table_stride;
   a->q = q;
@@ -373,7 +398,10 @@ static int select_prepare(const oomb_pool* pool, const int32_t* table, int64_t t
   a->score_stride = has_score_out ? score_stride : (cg.n_cand > 0 ? cg.n_cand : 1);
   a->n_cand = cg.n_cand;
   a->nb = static_cast<int>(nb);
-  a->inv = static_cast<float>(1.0 / (static_cast<double>(G) * n_q));
+  a->n_tiles = nt;
+  a->tile = tl;
+  a->inv = static_cast<float>(1.0 / (static_cast<double>(G) * tl));
+  a->inv_last = static_cast<float>(1.0 / (static_cast<double>(G) * (n_q - (nt - 1) * tl)));
   return OOMB_OK;
 }
 
@@ -435,6 +463,25 @@ int oomb_select_pages_noalloc(const oomb_pool* pool, const int32_t* table, int64
   if (e != hipSuccess)
     return fail(OOMB_ERR_HIP, "select_pages_noalloc: scratch address: %s", hipGetErrorString(e));
   return select_launch(a, static_cast<char*>(scratch_ptr), off_qbar, off_score, qbar_out,
+                       score_out, stream);
+}
+
+int oomb_select_pages_tiled(const oomb_pool* pool, const int32_t* table, int64_t table_stride,
+                            const void* q, int64_t q_head_stride, int64_t q_tok_stride,
+                            int32_t n_q, int64_t t0, int32_t tile, int32_t top_k, int32_t* sel,
+                            int64_t sel_stride, int32_t* count, float* qbar_out,
+                            float* score_out, int64_t score_stride, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (tile <= 0) return fail(OOMB_ERR_INVALID, "tile must be positive (got %d)", tile);
+  oomb::SelectArgs a{};
+  size_t off_qbar, off_score, total;
+  int st = select_prepare(pool, table, table_stride, q, q_head_stride, q_tok_stride, n_q, t0,
+                          top_k, nullptr, sel, sel_stride, count, score_stride,
+                          score_out != nullptr, &a, &off_qbar, &off_score, &total, tile);
+  if (st) return st;
+  if (workspace == nullptr || workspace_bytes < total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(OOMB_ERR_WORKSPACE, "select needs %zu bytes of 256-byte aligned workspace", total);
+  return select_launch(a, static_cast<char*>(workspace), off_qbar, off_score, qbar_out,
                        score_out, stream);
 }
 

@@ -59,9 +59,17 @@ struct SelectArgs {
   float* score;     // [Hkv][score_stride]
   int64_t score_stride;
   int n_cand;
-  int nb;           // query blocks of 64 rows
-  float inv;        // fp32(1 / (G * n_q)), rounded once from fp64
+  int nb;           // query blocks of 64 rows (of one tile)
+  float inv;        // fp32(1 / (G * tile)), rounded once from fp64
   const float* kmean;  // mean-key summaries [N][D] (score = qbar . kmean), or nullptr (min/max)
+  // Query tiles: the chunk's queries in tiles of `tile` (the last one n_q - (n_tiles - 1)
+  // * tile long, whose reciprocal is inv_last); unit u = j * Hkv + g (tile j, KV head g)
+  // owns partial[u], qbar[u], score[u], sel[u] and count[u]. One tile of n_q queries is
+  // the per-chunk selection. After a tile's top-k ids its selection row lists the
+  // chunk's pages wholly before the tile's first query (none for tile 0).
+  int n_tiles;
+  int tile;
+  float inv_last;
 };
 
 struct AttnArgs {

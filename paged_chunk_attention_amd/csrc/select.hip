@@ -24,19 +24,26 @@ namespace oomb {
 
 constexpr int kQBlock = 64;
 
+// Queries in tile j of the chunk (the last tile may be shorter).
+__device__ __forceinline__ int tile_len(const SelectArgs& a, int j) {
+  return j + 1 < a.n_tiles ? a.tile : a.n_q - j * a.tile;
+}
+
 // Block partial sums. Thread t of the grid owns block b = t / (D/8) of 64 consecutive
-// rows of KV head blockIdx.y and head dimensions 8 (t % (D/8)) .. +7: one 16-byte load
-// per row (issued in groups of 16), each dimension summed strictly in row order.
+// rows of unit blockIdx.y (query tile j, KV head g) and head dimensions 8 (t % (D/8))
+// .. +7: one 16-byte load per row (issued in groups of 16), each dimension summed
+// strictly in row order.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void qbar_partial_kernel(SelectArgs a) {
   const int D = a.pool.D;
   const int lanes_per_block = D / 8;
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int b = t / lanes_per_block, d0 = 8 * (t % lanes_per_block);
-  const int g = blockIdx.y;
-  if (b >= a.nb) return;
+  const int u = blockIdx.y, tj = u / a.pool.Hkv, g = u % a.pool.Hkv;
   const int G = a.pool.Hq / a.pool.Hkv;
-  const int M = G * a.n_q;
+  const int nq = tile_len(a, tj), qoff = tj * a.tile;
+  const int M = G * nq;
+  if (b >= (M + kQBlock - 1) / kQBlock) return;
   const int m0 = b * kQBlock;
   const int m1 = (m0 + kQBlock < M) ? m0 + kQBlock : M;
   constexpr int kGroup = 16;
@@ -46,7 +53,7 @@ __global__ __launch_bounds__(256) void qbar_partial_kernel(SelectArgs a) {
   // (head, query) of row m, stepped row by row (no division per row). The body is
   // branch-free (rows past the block's end load its first row and count as zero): a
   // branch per row would make each load wait for the previous one.
-  const int h0 = g * G + m0 / a.n_q, i0 = m0 % a.n_q;
+  const int h0 = g * G + m0 / nq, i0 = qoff + m0 % nq;
   int h = h0, i = i0;
   for (int mg = m0; mg < m1; mg += kGroup) {
     float x[kGroup][8];
@@ -56,8 +63,8 @@ __global__ __launch_bounds__(256) void qbar_partial_kernel(SelectArgs a) {
       const int64_t off = (live ? h * a.q_hs + static_cast<int64_t>(i) * a.q_ts
                                 : h0 * a.q_hs + static_cast<int64_t>(i0) * a.q_ts) + d0;
       const int in = i + 1;
-      const bool wrap = in == a.n_q;
-      i = wrap ? 0 : in;
+      const bool wrap = in == qoff + nq;
+      i = wrap ? qoff : in;
       h += wrap ? 1 : 0;
       if (kBf16) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.q) + off);
@@ -84,26 +91,29 @@ __global__ __launch_bounds__(256) void qbar_partial_kernel(SelectArgs a) {
       }
     }
   }
-  float* dst = a.partial + (static_cast<int64_t>(g) * a.nb + b) * D + d0;
+  float* dst = a.partial + (static_cast<int64_t>(u) * a.nb + b) * D + d0;
 #pragma unroll
   for (int c = 0; c < 8; ++c) dst[c] = s[c];
 }
 
-// Pairwise tree over the block sums of one (head dimension, KV head).
+// Pairwise tree over the block sums of one (head dimension, unit), zero-padded to the
+// power of two of the unit's own block count.
 __global__ __launch_bounds__(256) void qbar_final_kernel(SelectArgs a) {
   extern __shared__ float s_tree[];
-  const int d = blockIdx.x, g = blockIdx.y;
+  const int d = blockIdx.x, u = blockIdx.y, tj = u / a.pool.Hkv;
   const int D = a.pool.D;
+  const int G = a.pool.Hq / a.pool.Hkv;
+  const int nb = (G * tile_len(a, tj) + kQBlock - 1) / kQBlock;
   int n2 = 1;
-  while (n2 < a.nb) n2 <<= 1;
+  while (n2 < nb) n2 <<= 1;
   for (int i = threadIdx.x; i < n2; i += 256)
-    s_tree[i] = i < a.nb ? a.partial[(static_cast<int64_t>(g) * a.nb + i) * D + d] : 0.0f;
+    s_tree[i] = i < nb ? a.partial[(static_cast<int64_t>(u) * a.nb + i) * D + d] : 0.0f;
   __syncthreads();
   for (int s = n2 >> 1; s >= 1; s >>= 1) {
     for (int i = threadIdx.x; i < s; i += 256) s_tree[i] = s_tree[i] + s_tree[i + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.qbar[g * D + d] = s_tree[0] * a.inv;
+  if (threadIdx.x == 0) a.qbar[u * D + d] = s_tree[0] * (tj + 1 < a.n_tiles ? a.inv : a.inv_last);
 }
 
 // D / 8 lanes per candidate page (64 / (D / 8) pages per wavefront, 4 wavefronts per
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(SelectArgs a) {
   constexpr int PW = 64 / LP;      // pages per wavefront
   const int lane = threadIdx.x & 63, sub = lane % LP;
   const int j = (blockIdx.x * 4 + (threadIdx.x >> 6)) * PW + lane / LP;
-  const int g = blockIdx.y;
+  const int u = blockIdx.y, g = u % a.pool.Hkv;  // unit (query tile, KV head)
   const bool cand = j < a.n_cand;
   const int64_t ph = cand ? a.table[g * a.tstride + j] : -1;
   const bool ok = ph >= 0 && ph < a.pool.N;
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(SelectArgs a) {
   {
     float qb[8], kmin[8], kmax[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qb[c] = a.qbar[g * D + d0 + c];  // qbar_out may be 4-byte aligned only
+    for (int c = 0; c < 8; ++c) qb[c] = a.qbar[u * D + d0 + c];  // qbar_out may be 4-byte aligned only
     const int64_t row = ok ? ph * 2 * D : 0;  // invalid pages read page 0 and are discarded
     if (kBf16) {
       const bf16_t* sm = reinterpret_cast<const bf16_t*>(a.pool.k_summary) + row + d0;
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(SelectArgs a) {
   e[0] = e[0] + e[2];
   e[1] = e[1] + e[3];
   e[0] = e[0] + e[1];
-  if (cand && sub == 0) a.score[g * a.score_stride + j] = ok ? e[0] : -__builtin_inff();
+  if (cand && sub == 0) a.score[u * a.score_stride + j] = ok ? e[0] : -__builtin_inff();
 }
 
 // Mean-key scores: score_j = sum_d fp32(qbar_d * kmean_jd), the products rounded to
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(256) void page_score_mean_kernel(SelectArgs a) {
   constexpr int PW = 64 / LP;
   const int lane = threadIdx.x & 63, sub = lane % LP;
   const int j = (blockIdx.x * 4 + (threadIdx.x >> 6)) * PW + lane / LP;
-  const int g = blockIdx.y;
+  const int u = blockIdx.y, g = u % a.pool.Hkv;  // unit (query tile, KV head)
   const bool cand = j < a.n_cand;
   const int64_t ph = cand ? a.table[g * a.tstride + j] : -1;
   const bool ok = ph >= 0 && ph < a.pool.N;
@@ -197,8 +207,8 @@ __global__ __launch_bounds__(256) void page_score_mean_kernel(SelectArgs a) {
   float e[8];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    e[c] = a.qbar[g * D + d0 + c] * k0[c];
-    e[4 + c] = a.qbar[g * D + d0 + 4 + c] * k1[c];
+    e[c] = a.qbar[u * D + d0 + c] * k0[c];
+    e[4 + c] = a.qbar[u * D + d0 + 4 + c] * k1[c];
   }
 #pragma unroll
   for (int s = D / 2; s >= 8; s >>= 1) {
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(256) void page_score_mean_kernel(SelectArgs a) {
   e[0] = e[0] + e[2];
   e[1] = e[1] + e[3];
   e[0] = e[0] + e[1];
-  if (cand && sub == 0) a.score[g * a.score_stride + j] = ok ? e[0] : -__builtin_inff();
+  if (cand && sub == 0) a.score[u * a.score_stride + j] = ok ? e[0] : -__builtin_inff();
 }
 
 // Order-preserving unsigned key of an fp32 score (-0 folded onto +0, NaN lowest).
@@ -268,18 +278,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   __shared__ int s_wave[kTopkWaves];
   __shared__ uint32_t s_prefix;
   __shared__ int s_krem;
-  const int g = blockIdx.x;
+  const int u = blockIdx.x;  // unit (query tile u / Hkv, KV head u % Hkv)
   const int n = a.n_cand;
   const int k = a.top_k < n ? a.top_k : n;
-  const float* sc = a.score + g * a.score_stride;
-  int32_t* out = a.sel + g * a.sel_stride;
+  const float* sc = a.score + u * a.score_stride;
+  int32_t* out = a.sel + u * a.sel_stride;
+  // after the k ids: the chunk's pages wholly before this tile's first query
+  const int tj = u / a.pool.Hkv;
+  const int first_local = static_cast<int>(a.t0 >> a.pool.log2p);
+  const int n_app = static_cast<int>((a.t0 + static_cast<int64_t>(tj) * a.tile) >> a.pool.log2p) - first_local;
+  for (int r = threadIdx.x; r < n_app; r += kTopkThreads) out[k + r] = first_local + r;
   if (k == n) {  // every candidate
     for (int j = threadIdx.x; j < n; j += kTopkThreads) out[j] = j;
-    if (threadIdx.x == 0) a.count[g] = n;
+    if (threadIdx.x == 0) a.count[u] = n + n_app;
     return;
   }
   if (k <= 0) {
-    if (threadIdx.x == 0) a.count[g] = 0;
+    if (threadIdx.x == 0) a.count[u] = n_app;
     return;
   }
   const bool in_lds = n <= kTopkLds;
@@ -399,22 +414,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
     }
     eq_seen += eq;
   }
-  if (threadIdx.x == 0) a.count[g] = k;
+  if (threadIdx.x == 0) a.count[u] = k + n_app;
 }
 
 static void launch_scores(const SelectArgs& a, hipStream_t s) {
   const bool bf = a.pool.dtype == 0;
   const int D = a.pool.D;
   // one wavefront per workgroup: the few hundred threads per KV head spread over all CUs
-  dim3 g1((a.nb * (D / 8) + 63) / 64, a.pool.Hkv);
+  const int units = a.pool.Hkv * a.n_tiles;
+  dim3 g1((a.nb * (D / 8) + 63) / 64, units);
   if (bf) OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<true>, g1, dim3(64), 0, s, a);
   else OOMB_LAUNCH("qbar_partial", qbar_partial_kernel<false>, g1, dim3(64), 0, s, a);
   int n2 = 1;
   while (n2 < a.nb) n2 <<= 1;
-  OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, a.pool.Hkv), dim3(256), n2 * sizeof(float), s, a);
+  OOMB_LAUNCH("qbar_final", qbar_final_kernel, dim3(D, units), dim3(256), n2 * sizeof(float), s, a);
   // 64 / (D / 8) pages per wavefront, 4 wavefronts per workgroup
   const int per_wg = 4 * (64 / (D / 8));
-  dim3 g4((a.n_cand + per_wg - 1) / per_wg, a.pool.Hkv);
+  dim3 g4((a.n_cand + per_wg - 1) / per_wg, units);
   if (a.kmean != nullptr) {
     if (D == 128) OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<128>, g4, dim3(256), 0, s, a);
     else OOMB_LAUNCH("page_score_mean", page_score_mean_kernel<64>, g4, dim3(256), 0, s, a);
@@ -457,7 +473,7 @@ hipError_t select_scratch_address(void** ptr) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (a.n_cand > 0) launch_scores(a, s);
   const int n_lds = a.n_cand <= kTopkLds ? a.n_cand + (a.n_cand >> 5) + 1 : 0;
-  OOMB_LAUNCH("topk", topk_kernel, dim3(a.pool.Hkv), dim3(kTopkThreads),
+  OOMB_LAUNCH("topk", topk_kernel, dim3(a.pool.Hkv * a.n_tiles), dim3(kTopkThreads),
               static_cast<size_t>(n_lds) * sizeof(uint32_t), s, a);
   return hipGetLastError();
 }

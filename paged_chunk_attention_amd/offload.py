@@ -156,7 +156,12 @@ class OffloadedAttentionStack:
                                           torch.arange(self.n_local, dtype=torch.int32)
                                           for g in range(hkv)])
         self.local_host_dev = self.local_host.to(dv)
+        # first host page of each KV head, for the write-back of selected gradient pages
+        self.head_base = (torch.arange(hkv, dtype=torch.int32) * self.npph)[:, None].to(dv)
         self.local_stage_dev = self.local_stage.to(dv)
+        # the id lists and tables above were written on the current stream; the step reads
+        # them on its own streams
+        torch.cuda.synchronize(dv)
 
     # ---- setup ------------------------------------------------------------------------
     def load_prior(self, layer: int, k: torch.Tensor, v: torch.Tensor) -> None:
@@ -233,9 +238,8 @@ class OffloadedAttentionStack:
         else:
             # selected pages: staging slot -> host page g * npph + selected id; the
             # chunk's own pages: fixed staging pages -> their host pages
-            base = (torch.arange(self.hkv, dtype=torch.int32, device=self.dev) * self.npph)[:, None]
             with torch.cuda.stream(stream):
-                sel_host = (self.sel[layer] + base).reshape(-1)
+                sel_host = (self.sel[layer] + self.head_base).reshape(-1)
                 src = torch.cat([self.stage_ids.reshape(-1), self.local_stage_dev])
                 dst = torch.cat([sel_host, self.local_host_dev])
         oomb_add_pages_f32(pool.dk, self.hdk[layer], src, dst, stream=stream)
@@ -368,8 +372,9 @@ class OffloadedAttentionStack:
                 gtable = self.ident
             elif sparse:
                 cs.wait_event(grads_out[b])
-                pool.dk.zero_()
-                pool.dv.zero_()
+                with torch.cuda.stream(cs):
+                    pool.dk.zero_()
+                    pool.dv.zero_()
             s_, c_ = (self.sel[i], self.count[i]) if sparse else (None, None)
             oomb_paged_chunk_attn_bwd(pool, table, gtable, q[i], self.t0, s_, c_, o[i],
                                       dout[i], lse[i], self.scale, dq=dq[i],

@@ -28,14 +28,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 9
+    assert lib.oomb_abi_version() == 10
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text
@@ -118,7 +118,7 @@ def test_summarize_and_select_errors(lib):
                                      a["top_k"], a["sel"], a["sstride"], a["count"], None,
                                      a["score"], a["sstr"], a["ws"], a["wsb"], None)
     assert sel(top_k=-1) == L.OOMB_ERR_INVALID and b"top_k" in lib.oomb_last_error()
-    assert sel(sstride=3) == L.OOMB_ERR_INVALID and b"sel must hold" in lib.oomb_last_error()
+    assert sel(sstride=3) == L.OOMB_ERR_INVALID and b"sel rows must hold" in lib.oomb_last_error()
     assert sel(count=None) == L.OOMB_ERR_INVALID
     assert sel(score=B, sstr=10) == L.OOMB_ERR_INVALID and b"score_stride" in lib.oomb_last_error()
     assert sel(wsb=ws - 1) == L.OOMB_ERR_WORKSPACE
@@ -138,7 +138,7 @@ def test_select_noalloc_host_checks(lib):
                                              4096, t0, a["top_k"], a["sel"], a["sstride"],
                                              a["count"], None, a["score"], a["sstr"], None)
     assert sel(top_k=-1) == L.OOMB_ERR_INVALID and b"top_k" in lib.oomb_last_error()
-    assert sel(sstride=3) == L.OOMB_ERR_INVALID and b"sel must hold" in lib.oomb_last_error()
+    assert sel(sstride=3) == L.OOMB_ERR_INVALID and b"sel rows must hold" in lib.oomb_last_error()
     assert sel(count=None) == L.OOMB_ERR_INVALID
     assert sel(tstride=10) == L.OOMB_ERR_INVALID
     # 4 KV heads x 600,000 candidate pages of scores = 9.6 MB > 8 MiB

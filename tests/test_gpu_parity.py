@@ -362,3 +362,102 @@ def test_side_stream_calls_match_default_stream():
         outs.append((sel.cpu(), bits(o), lse.cpu(), dq.cpu(), pool.dk.cpu(), pool.dv.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def _tiled_case(name, hq, hkv, page, chunk, t0, top_k, needles=0):
+    w = _w(name=name, hq=hq, hkv=hkv, page=page, chunk=chunk, total=t0 + chunk, top_k=top_k,
+           needles=needles)
+    x = wl.make_inputs(w)
+    table = x["table"].to(DEV)
+    pool = pca.PagedPool(w.pool_pages, page, w.d, hq, hkv, w.dtype, DEV)
+    pca.oomb_kv_append(pool, table, x["k"].to(DEV), x["v"].to(DEV), 0)
+    pca.oomb_page_summarize(pool, table, 0, w.pages_per_head, w.total)
+    kp = torch.zeros(w.pool_pages, page, w.d, dtype=w.dtype)
+    vp = torch.zeros_like(kp)
+    orc.append(kp, x["table"], x["k"], 0)
+    orc.append(vp, x["table"], x["v"], 0)
+    summ = torch.zeros(w.pool_pages, 2, w.d, dtype=w.dtype)
+    orc.summarize(kp, x["table"], summ, 0, w.pages_per_head, w.total)
+    return w, x, pool, table, kp, vp, summ
+
+
+@pytest.mark.parametrize("kw", [
+    dict(name="tiles_aligned", hq=8, hkv=2, page=64, chunk=512, t0=64 * 30, top_k=4, tile=128),
+    dict(name="tiles_ragged", hq=8, hkv=2, page=64, chunk=500, t0=64 * 30 + 17, top_k=5, tile=100),
+    dict(name="tiles_gqa7", hq=28, hkv=4, page=128, chunk=1024, t0=128 * 40, top_k=6, tile=256,
+         needles=5),
+    dict(name="tiles_k_exceeds", hq=4, hkv=1, page=32, chunk=96, t0=32 * 5, top_k=9, tile=40),
+])
+def test_tiled_selection_bit_exact(kw):
+    """Per-query-tile selection: every tile's qbar, scores and selection row (its top-k
+    ids, then the chunk's pages before the tile) and count against the oracle, bit for
+    bit; tiles not a multiple of the page size, a ragged last tile, k above the
+    candidate count."""
+    kw = dict(kw)
+    tile = kw.pop("tile")
+    w, x, pool, table, kp, vp, summ = _tiled_case(**kw)
+    log(f"[case {w.name}] t0={w.t0} chunk={w.chunk} tile={tile} top_k={w.top_k}")
+    n_tiles = -(-w.chunk // tile)
+    n_cand = w.t0 // w.page
+    qb = torch.empty(n_tiles, w.hkv, w.d, dtype=torch.float32, device=DEV)
+    sc = torch.empty(n_tiles, w.hkv, max(1, n_cand), dtype=torch.float32, device=DEV)
+    sel, cnt = pca.oomb_select_pages_tiled(pool, table, x["q"].to(DEV), w.t0, w.top_k, tile,
+                                           qbar_out=qb, score_out=sc)
+    torch.cuda.synchronize()
+    ref = orc.select_pages_tiled(x["q"], summ, x["table"], w.t0, w.page, w.group, w.top_k, tile)
+    sel, cnt, qb, sc = sel.cpu(), cnt.cpu(), qb.cpu(), sc.cpu()
+    for g in range(w.hkv):
+        for j in range(n_tiles):
+            rq, rs, chosen = ref[g][j]
+            assert torch.equal(bits(qb[j, g]), torch.from_numpy(rq).view(torch.int32)), (g, j)
+            assert torch.equal(bits(sc[j, g, :n_cand]), torch.from_numpy(rs).view(torch.int32)), (g, j)
+            row = orc.tile_selection_row(chosen, w.t0, w.page, tile, j)
+            assert int(cnt[j, g]) == len(row) and sel[j, g, :len(row)].tolist() == row, (g, j)
+    log(f"    {n_tiles} tiles x {w.hkv} heads bit-exact")
+
+
+def test_tiled_selection_one_tile_is_select_pages():
+    """A tile at least as long as the chunk gives oomb_select_pages' results bit for bit."""
+    w, x, pool, table, kp, vp, summ = _tiled_case("one_tile", 8, 2, 64, 300, 64 * 20, 4)
+    q = x["q"].to(DEV)
+    a_sel, a_cnt = pca.oomb_select_pages(pool, table, q, w.t0, w.top_k)
+    for tile in (300, 1000):
+        b_sel, b_cnt = pca.oomb_select_pages_tiled(pool, table, q, w.t0, w.top_k, tile)
+        torch.cuda.synchronize()
+        assert b_sel.shape[0] == 1
+        assert torch.equal(a_cnt.cpu(), b_cnt[0].cpu()) and torch.equal(a_sel.cpu(), b_sel[0].cpu())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(name="tiled_attn", hq=8, hkv=2, page=64, chunk=500, t0=64 * 30 + 17, top_k=5, tile=128),
+    dict(name="tiled_attn_gqa7", hq=28, hkv=4, page=128, chunk=768, t0=128 * 24, top_k=4, tile=256),
+])
+def test_tiled_attention_matches_oracle(kw):
+    """Attention with per-tile selections (one forward / backward call per tile) against
+    the oracle's tiled attention over its own tiled selection: O, LSE, dQ, and dK/dV
+    accumulated over the tiles, at the bf16 bar."""
+    kw = dict(kw)
+    tile = kw.pop("tile")
+    w, x, pool, table, kp, vp, summ = _tiled_case(**kw)
+    log(f"[case {w.name}] t0={w.t0} chunk={w.chunk} tile={tile} top_k={w.top_k}")
+    q, do = x["q"].to(DEV), x["do"].to(DEV)
+    gtable = x["gtable"].to(DEV)
+    sel, cnt = pca.oomb_select_pages_tiled(pool, table, q, w.t0, w.top_k, tile)
+    o, lses = pca.oomb_paged_chunk_attn_fwd_tiled(pool, table, q, w.t0, sel, cnt, tile)
+    dq = pca.oomb_paged_chunk_attn_bwd_tiled(pool, table, gtable, q, w.t0, sel, cnt, tile, o, do,
+                                             lses)
+    torch.cuda.synchronize()
+    ref = orc.select_pages_tiled(x["q"], summ, x["table"], w.t0, w.page, w.group, w.top_k, tile)
+    chosen = [[ch for (_, _, ch) in ref[g]] for g in range(w.hkv)]
+    O, L = orc.fwd_tiled(x["q"], kp, vp, x["table"], w.t0, chosen, w.scale, tile)
+    gk = torch.zeros(kp.shape, dtype=torch.float64)
+    gv = torch.zeros(kp.shape, dtype=torch.float64)
+    dQ = orc.bwd_tiled(x["q"], kp, vp, x["table"], w.t0, chosen, w.scale, tile, x["do"], gk, gv,
+                       x["gtable"])
+    compare("O", o, O, w.dtype)
+    lse = torch.cat([t.cpu() for t in lses], dim=1)
+    assert (lse.double() - L).abs().max().item() <= 1e-2
+    compare("dQ", dq, dQ, w.dtype)
+    mapped = x["gtable"].reshape(-1).long()
+    compare("dK", pool.dk.cpu()[mapped], gk[mapped], w.dtype)
+    compare("dV", pool.dv.cpu()[mapped], gv[mapped], w.dtype)
