@@ -322,23 +322,33 @@ def _sweep_sampled_rows(w, x, kp, vp, chunks, sels, O, L, dq, n_per_group=1):
                       sels=None if sels is None else sels[c], q_off=c * C)
 
 
-def test_fullsize_sweep_top64():
-    """The 262,144-token top-64 sweep at full shape (28/4 heads, 32 chunks of 8192):
-    selections bit for bit for every chunk and KV head; KV group 0 in full over all 32
-    chunks (O, LSE, dQ of every row; dK/dV of every key, accumulated over the whole
-    reverse pass); sampled rows of the other groups in every chunk; the identities over
-    the whole gradient pool."""
+_TOP64_PARTS = 4  # the oracle's reverse pass over KV group 0, a quarter of the chunks each
+
+
+@pytest.fixture(scope="module")
+def top64():
+    """The 262,144-token top-64 sweep at full shape (28/4 heads, 32 chunks of 8192), run
+    once on the GPU; the oracle's reverse pass over KV group 0 is added chunk by chunk
+    by the tests below, in their file order, so that no single test runs for minutes."""
     w = wl.WORKLOADS["sweep256k_top64"]
-    C, P, G = w.chunk, w.page, w.group
-    log(f"[case fullsize sweep {w.name}] chunks={w.n_chunks} chunk={C} top_k={w.top_k}")
+    log(f"[case fullsize sweep {w.name}] chunks={w.n_chunks} chunk={w.chunk} top_k={w.top_k}")
     x = wl.make_inputs(w)
     pool, O, L, dq, gsels = _gpu_sweep(w, x)
     log("    gpu sweep done")
     kp, vp = _oracle_pool(w, x, spare=0)
-    summ = torch.zeros(kp.shape[0], 2, w.d, dtype=w.dtype)
+    return dict(w=w, x=x, pool=pool, O=O, L=L, dq=dq, gsels=gsels, kp=kp, vp=vp, osels=None,
+                gk=torch.zeros(kp.shape, dtype=torch.float64),
+                gv=torch.zeros(kp.shape, dtype=torch.float64), parts_done=0)
+
+
+def test_fullsize_sweep_top64_selections(top64):
+    """Selections bit for bit for every chunk and KV head of the top-64 sweep."""
+    w, x, gsels = top64["w"], top64["x"], top64["gsels"]
+    C, P, G = w.chunk, w.page, w.group
+    summ = torch.zeros(top64["kp"].shape[0], 2, w.d, dtype=w.dtype)
     # every page is complete by the time it is a candidate, so one summary of the
     # whole context gives the scores each chunk saw
-    orc.summarize(kp, x["table"], summ, 0, w.pages_per_head, w.total)
+    orc.summarize(top64["kp"], x["table"], summ, 0, w.pages_per_head, w.total)
     osels = []
     for c in range(w.n_chunks):
         t0 = c * C
@@ -348,35 +358,51 @@ def test_fullsize_sweep_top64():
         for g, (_, _, chosen) in enumerate(ref):
             assert int(c_[g]) == len(chosen) and s_[g, :len(chosen)].tolist() == chosen, (c, g)
         osels.append([chosen for (_, _, chosen) in ref])
+    top64["osels"] = osels
     log(f"    selections bit-exact: {w.n_chunks} chunks x {w.hkv} KV heads")
-    # KV group 0, every chunk in the sweep's reverse order, gradients accumulated
-    gk = torch.zeros(kp.shape, dtype=torch.float64)
-    gv = torch.zeros(kp.shape, dtype=torch.float64)
+
+
+@pytest.mark.parametrize("part", range(_TOP64_PARTS))
+def test_fullsize_sweep_top64_chunks(top64, part):
+    """A quarter of the top-64 sweep's chunks, in the reverse pass's order (part 0 holds
+    the last chunks): KV group 0 in full (O, LSE and dQ of every row, the oracle's dK/dV
+    accumulated for the final check), sampled rows of the other groups."""
+    if top64["osels"] is None or top64["parts_done"] != part:
+        pytest.skip("needs the selections and the earlier parts of the same session")
+    w, x, osels = top64["w"], top64["x"], top64["osels"]
+    C, G = w.chunk, w.group
     hs = slice(0, G)
-    o_ref = torch.zeros(G, w.total, w.d, dtype=torch.float64)
-    l_ref = torch.zeros(G, w.total, dtype=torch.float64)
-    q_ref = torch.zeros(G, w.total, w.d, dtype=torch.float64)
-    for c in reversed(range(w.n_chunks)):
+    per = w.n_chunks // _TOP64_PARTS
+    chunks = list(reversed(range(w.n_chunks)))[part * per:(part + 1) * per]
+    go, glse, gdq = top64["O"].cpu(), top64["L"].cpu(), top64["dq"].cpu()
+    for c in chunks:
         t0 = c * C
         sl = slice(t0, t0 + C)
-        q_ref[:, sl], _, o_ref[:, sl], l_ref[:, sl] = orc.bwd(
-            x["q"][hs, sl], kp, vp, x["table"][:1], t0, [osels[c][0]], w.scale, x["do"][hs, sl],
-            gk, gv, x["gtable"][:1], with_fwd=True)
-        if c % 8 == 0:
-            log(f"    oracle: KV group 0 down to chunk {c}")
-    compare("O(g0)", O[hs], o_ref, w.dtype)
-    lse_err = (L[hs].cpu().double() - l_ref).abs().max().item()
-    log(f"    LSE(g0) max_abs={lse_err:.3e}")
-    assert lse_err <= 1e-2
-    compare("dQ(g0)", dq[hs], q_ref, w.dtype)
-    rows = _grad_rows(w, x["gtable"], 0, torch.arange(w.total))
-    compare("dK(g0)", pool.dk.cpu().reshape(-1, w.d)[rows], gk.reshape(-1, w.d)[rows], w.dtype)
-    compare("dV(g0)", pool.dv.cpu().reshape(-1, w.d)[rows], gv.reshape(-1, w.d)[rows], w.dtype)
-    # the other groups: sampled rows of every chunk
-    go, glse, gdq = O.cpu(), L.cpu(), dq.cpu()
-    for c in range(w.n_chunks):
+        dq_ref, _, o_ref, l_ref = orc.bwd(
+            x["q"][hs, sl], top64["kp"], top64["vp"], x["table"][:1], t0, [osels[c][0]],
+            w.scale, x["do"][hs, sl], top64["gk"], top64["gv"], x["gtable"][:1], with_fwd=True)
+        compare(f"O(g0, chunk {c})", go[hs, sl], o_ref, w.dtype)
+        lse_err = (glse[hs, sl].double() - l_ref).abs().max().item()
+        assert lse_err <= 1e-2, (c, lse_err)
+        compare(f"dQ(g0, chunk {c})", gdq[hs, sl], dq_ref, w.dtype)
         rows_c = [(g, (i + 97 * c) % C) for (g, i) in _row_sample(w, 1, groups=range(1, w.hkv))]
-        _sampled_rows(w, x, kp, vp, rows_c, go, glse, gdq, t0=c * C, sels=osels[c], q_off=c * C)
+        _sampled_rows(w, x, top64["kp"], top64["vp"], rows_c, go, glse, gdq, t0=t0,
+                      sels=osels[c], q_off=t0)
+    top64["parts_done"] = part + 1
+    log(f"    chunks {chunks[0]}..{chunks[-1]} done")
+
+
+def test_fullsize_sweep_top64_grads(top64):
+    """dK/dV of every key of KV group 0 after the whole reverse pass, and the identities
+    over the whole gradient pool."""
+    if top64["parts_done"] != _TOP64_PARTS:
+        pytest.skip("needs every chunk part of the same session")
+    w, x, pool = top64["w"], top64["x"], top64["pool"]
+    rows = _grad_rows(w, x["gtable"], 0, torch.arange(w.total))
+    compare("dK(g0)", pool.dk.cpu().reshape(-1, w.d)[rows], top64["gk"].reshape(-1, w.d)[rows],
+            w.dtype)
+    compare("dV(g0)", pool.dv.cpu().reshape(-1, w.d)[rows], top64["gv"].reshape(-1, w.d)[rows],
+            w.dtype)
     _sweep_invariants(w, x, pool)
 
 
