@@ -41,10 +41,30 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # Algorithmic FLOP per attended (query, key) pair and head_dim unit, per kernel:
 # forward = S and PV; the dK/dV pass = S, dP (recomputed), dV, dK; the dQ pass is
-# credited with dQ only (its S and dP are recomputation).
-FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 2}
-# what each pass executes on the matrix cores (the dQ pass recomputes S and dP)
-HW_FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 6}
+# credited with dQ only: dq_mfma recomputes S and dP, dqs_mfma reads the dS the dK/dV
+# pass spilled.
+FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 2, "dqs_mfma": 2}
+# what each pass executes on the matrix cores
+HW_FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 6, "dqs_mfma": 2}
+
+
+def spill_read_bytes(w, counts):
+    """Bytes of spilled dS the dQ-from-dS pass reads: for every query head and 64-query
+    tile, the 64-key stages up to the one holding the tile's last query's key, 64 x 64
+    bf16 each (the attended pairs plus the masked part of the diagonal stages)."""
+    C, P, t0 = w.chunk, w.page, w.t0
+    first_local = t0 // P
+    n_local = (t0 + C - 1) // P - first_local + 1
+    total = 0
+    for g in range(w.hkv):
+        n_sel = counts[g] if counts is not None else t0 // P
+        n_keys = (n_sel + n_local) * P
+        local0 = n_sel * P
+        for qt in range((C + 63) // 64):
+            qlast = t0 + min(C, 64 * qt + 64) - 1
+            klim = min(qlast - first_local * P + local0, n_keys - 1)
+            total += w.group * (klim // 64 + 1) * 64 * 64 * 2
+    return total
 
 
 def log(*a):
@@ -600,6 +620,11 @@ def other_workload(pca, torch, name, steps=5, warmup=2):
             tf = hw * w.d * pairs / (kms * 1e-3) / 1e12
             passes[kname] = {"ms_per_launch": kms, "hardware_TFLOPs": tf,
                              "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
+    if "dqs_mfma" in passes and w.window == 0:
+        rd = spill_read_bytes(w, count.cpu().tolist() if sparse else None)
+        gbs = rd / (passes["dqs_mfma"]["ms_per_launch"] * 1e-3) / 1e9
+        passes["dqs_mfma"].update(spill_read_bytes=rd, spill_read_GBps=gbs,
+                                  frac_of_hbm_peak=gbs / PEAK_HBM_GBS)
     del pool, x
     return {"ms_per_step": ms, "value": value, "unit": "TFLOP/s",
             "pct_mfma_peak": 100.0 * value / PEAK_BF16_TFLOPS, "steps": steps,
@@ -686,13 +711,14 @@ def sweep_workload(pca, torch, name, reps=2, warmup=1):
     kernels = {kname: tot / reps for kname, (tot, n) in per.items()}
     passes = {}
     # per sweep: the forward runs twice per chunk (in order, then recomputed)
-    launches = {"fwd_mfma": 2 * S, "dkdv_mfma": S, "dq_mfma": S}
+    launches = {"fwd_mfma": 2 * S, "dkdv_mfma": S, "dq_mfma": S, "dqs_mfma": S}
     for kname, hw in HW_FLOP_PER_PAIR_D.items():
         if kname in per:
             kms = per[kname][0] / reps
-            tf = launches[kname] * hw * D * pairs / S / (kms * 1e-3) / 1e12
-            passes[kname] = {"ms_per_sweep": kms, "hardware_TFLOPs": tf,
-                             "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}
+            passes[kname] = {"ms_per_sweep": kms, "launches_per_sweep": per[kname][1] / reps}
+            if per[kname][1] == launches[kname] * reps:  # ran for every chunk
+                tf = launches[kname] * hw * D * pairs / S / (kms * 1e-3) / 1e12
+                passes[kname].update(hardware_TFLOPs=tf, frac_of_bf16_peak=tf / PEAK_BF16_TFLOPS)
     del pool, x, o_all, dq_all
     return {"ms_per_sweep": ms, "value": value, "unit": "TFLOP/s", "dtype": str(w.dtype)[6:],
             "peak_TFLOPs": peak, "pct_peak": 100.0 * value / peak, "sweeps": reps, "chunks": S,

@@ -566,14 +566,20 @@ int oomb_paged_chunk_attn_fwd(const oomb_pool* pool, const int32_t* table, int64
 
 // Backward workspace: Delta [Hq][n_q] fp32, then (matrix-core path) the fp32 partials
 // of the dK/dV pass when it is split over the query stream, then those of the dQ pass
-// when it is split over key ranges.
-static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part, size_t* off_dq) {
+// when it is split over key ranges, then the bf16 dS spill when it is used.
+static size_t bwd_workspace(const oomb::AttnArgs& a, size_t* off_part, size_t* off_dq,
+                            size_t* off_ds) {
   const size_t delta = align256(static_cast<size_t>(a.pool.Hq) * a.n_q * sizeof(float));
   *off_part = delta;
   *off_dq = delta;
+  *off_ds = 0;
   if (!use_mfma(a.pool)) return delta;
   *off_dq = delta + align256(oomb::dkdv_partial_bytes(a, oomb::dkdv_plan(a)));
-  return *off_dq + align256(oomb::dq_partial_bytes(a, oomb::dq_plan(a)));
+  const size_t end = *off_dq + align256(oomb::dq_partial_bytes(a, oomb::dq_plan(a)));
+  const size_t ds = oomb::ds_spill_bytes(a);
+  if (ds == 0) return end;
+  *off_ds = end;
+  return end + align256(ds);
 }
 
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
@@ -581,8 +587,8 @@ size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
   oomb::AttnArgs a{};
   if (check_pool(pool, &a.pool, false, false) != OOMB_OK) return 0;
   if (attn_geometry(a.pool, n_q, t0, sel_stride >= 0, sel_stride, window, &a) != OOMB_OK) return 0;
-  size_t off, off_dq;
-  return bwd_workspace(a, &off, &off_dq);
+  size_t off, off_dq, off_ds;
+  return bwd_workspace(a, &off, &off_dq, &off_ds);
 }
 
 int oomb_split_plan(const oomb_pool* pool, int32_t n_q, int64_t t0, int64_t sel_stride,
@@ -625,8 +631,8 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(OOMB_ERR_INVALID, "lse must be a 4-byte aligned device pointer");
   if (!(scale > 0.0f) || scale > 1e30f) return fail(OOMB_ERR_INVALID, "scale must be positive and finite");
-  size_t off_part = 0, off_dq = 0;
-  const size_t need = bwd_workspace(a, &off_part, &off_dq);
+  size_t off_part = 0, off_dq = 0, off_ds = 0;
+  const size_t need = bwd_workspace(a, &off_part, &off_dq, &off_ds);
   if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(OOMB_ERR_WORKSPACE, "bwd needs %zu bytes of 256-byte aligned workspace", need);
   a.gtable = gtable;
@@ -647,7 +653,8 @@ int oomb_paged_chunk_attn_bwd(const oomb_pool* pool, const int32_t* table, int64
   if (!use_mfma(a.pool)) return hip_status(oomb::launch_bwd_scalar(a, s), "paged_chunk_attn_bwd");
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_part);
   float* dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + off_dq);
-  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_plan(a), part, oomb::dq_plan(a), dq_part, s),
+  uint16_t* ds = off_ds ? reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + off_ds) : nullptr;
+  return hip_status(oomb::launch_bwd_mfma(a, oomb::dkdv_plan(a), part, oomb::dq_plan(a), dq_part, ds, s),
                     "paged_chunk_attn_bwd");
 }
 

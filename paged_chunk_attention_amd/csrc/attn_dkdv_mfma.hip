@@ -29,10 +29,32 @@ namespace mf {
 // D wave still reads the previous tile's), dO in two; the buffers' roles are static in
 // each sixth of the unrolled loop. P has to be exactly 0 for masked pairs and at most
 // about 1 elsewhere (it is exp(S - LSE) with the forward's LSE), which fp16 holds.
+//
+// With SPILL the D wave also writes every dS tile it forms to ds, for the dQ pass to use
+// instead of recomputing S and dP. The dQ product contracts over keys, so it wants dS
+// with a lane per query and keys along the operand, the transpose of what the D wave
+// holds (a lane per key). Two products with 0/1 matrices transpose a tile exactly on
+// the matrix core: with A = the D wave's dS^T operand of one 32-query half (32 keys x 16
+// queries, twice) and B = the selection of those queries, C = dS^T lands in C layout,
+// lane = query, register r = key 8 (r / 4) + 4 h2 + r % 4, every value a single bf16
+// times 1 (exact). Packed to bf16 that is the B operand of dQ^T += K^T dS^T for k-step
+// sp = r / 8, in the row order of the transposed K fragment. Per (query head, key
+// block, 64-query tile, key group) the record block of DS_REC values is [us][sp][lane][8]
+// (query half us, k-step sp): four 16-byte stores per lane and tile, each a contiguous
+// 1 KiB. Masked pairs store exact zeros (P = 0); the tiles the pass never visits (query
+// tiles wholly before a chunk key block) are never read.
+//
+// The D wave never waits for its stores: with SPILL the P waves stage both the Q and
+// the dO tiles (and load the rows' LSE and Delta), so a D wave issues no load in the
+// loop, and the loop's barrier carries no memory fence (every wave that staged or wrote
+// LDS waits for that itself before it). Waiting at each barrier for the stores cost the
+// pass up to half its time.
 constexpr int DKV_WAVES = 8;
 
+template <bool SPILL>
 __global__ __launch_bounds__(64 * DKV_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_keys) {
+void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_keys,
+                      uint16_t* ds) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q0[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_q1[QTB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_q2[QTB * D];
@@ -131,13 +153,9 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
   // the D waves. The LSE (wave 0) and Delta (wave 4) of the tile's rows take a small
   // register path, stored once the tile has landed.
   float r_row = 0.0f;
-  auto issue_tile = [&](int u, uint16_t* qd, uint16_t* dd) {
-    const int hq = g * G + u / tph, q0 = (qt0 + u % tph) * QTB;
+  // Rows 16 i + 4 kg .. +3 (i = 0..3) of one tile of `src` into dst.
+  auto stage_rows = [&](const uint16_t* src, int64_t ts, int q0, uint16_t* dst) {
     const int c8 = dma_col(kg, lane);
-    const uint16_t* src = pwave ? static_cast<const uint16_t*>(a.q) + hq * a.q_hs
-                                : static_cast<const uint16_t*>(a.dout) + hq * a.do_hs;
-    const int64_t ts = pwave ? a.q_ts : a.do_ts;
-    uint16_t* dst = pwave ? qd : dd;
     if (q0 + QTB <= a.n_q) {  // uniform: the whole tile is in range
       const int64_t lo = static_cast<int64_t>(lane >> 4) * ts + c8;
 #pragma unroll
@@ -155,18 +173,28 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
         lds_dma16<true>(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
       }
     }
-    if (kg == 0) {  // raw loads: arithmetic here would wait for the whole prefetch
+  };
+  // Wave kg of each role stages its rows of the tile (SPILL: the P waves stage both);
+  // the LSE (P wave 0) and Delta (wave 4, or P wave 1 with SPILL) take a small register
+  // path, stored once the tile has landed.
+  const bool lse_wave = pwave && kg == 0;
+  const bool del_wave = SPILL ? (pwave && kg == 1) : (!pwave && kg == 0);
+  auto issue_tile = [&](int u, uint16_t* qd, uint16_t* dd) {
+    const int hq = g * G + u / tph, q0 = (qt0 + u % tph) * QTB;
+    const uint16_t* qsrc = static_cast<const uint16_t*>(a.q) + hq * a.q_hs;
+    const uint16_t* dsrc = static_cast<const uint16_t*>(a.dout) + hq * a.do_hs;
+    if (pwave) stage_rows(qsrc, a.q_ts, q0, qd);
+    if (SPILL ? pwave : !pwave) stage_rows(dsrc, a.do_ts, q0, dd);
+    if (lse_wave || del_wave) {  // raw loads: arithmetic here would wait for the whole prefetch
       const int qi = q0 + lane;
       const int64_t rid = static_cast<int64_t>(hq) * a.n_q + qi;
-      if (pwave) r_row = qi < a.n_q ? a.lse_in[rid] : __builtin_inff();
+      if (lse_wave) r_row = qi < a.n_q ? a.lse_in[rid] : __builtin_inff();
       else r_row = qi < a.n_q ? a.delta[rid] : 0.0f;
     }
   };
   auto store_rows = [&](float* lse, float* del) {
-    if (kg == 0) {
-      if (pwave) lse[lane] = r_row * kLog2e;
-      else del[lane] = r_row;
-    }
+    if (lse_wave) lse[lane] = r_row * kLog2e;
+    else if (del_wave) del[lane] = r_row;
   };
 
   FragOffsets fo;
@@ -260,7 +288,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
   // D wave: dS and dK of the previous tile (qp, delp, P parity xp), if any, then dP of
   // tile dt, if any.
   auto d_tile = [&](bool prev, const uint16_t* qp, const float* delp, int xp, bool cur,
-                    const uint16_t* dt) __attribute__((always_inline)) {
+                    const uint16_t* dt, int u_prev) __attribute__((always_inline)) {
     FragOffsets o = fo;
     o.opaque();
     __builtin_amdgcn_s_setprio(1);
@@ -274,16 +302,44 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
           const f32x4 d0 = *reinterpret_cast<const f32x4*>(delp + rA);
           const f32x4 d1 = *reinterpret_cast<const f32x4*>(delp + rA + 8);
           const h16x8 ph = s_p[((xp * 4 + kg) * 4 + 2 * us + s) * 64 + lane];
-          float ds[8];
+          float dsv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float pv = static_cast<float>(ph[j]);
             const float del_r = j < 4 ? d0[j] : d1[j - 4];
             // an fma with the fp16 operand widened in the instruction (v_fma_mix)
-            ds[j] = __builtin_fmaf(pv, dpa[us][8 * s + j] - del_r, 0.0f);
+            dsv[j] = __builtin_fmaf(pv, dpa[us][8 * s + j] - del_r, 0.0f);
           }
-          dsb[us][s] = pack8(ds);
+          dsb[us][s] = pack8(dsv);
         }
+      if constexpr (SPILL) {
+        const int hq = g * G + u_prev / tph, qt = qt0 + u_prev % tph;
+        uint16_t* rec = ds + ((((static_cast<int64_t>(hq) * nkb + kb) * n_qt + qt) * 4 + kg) * DS_REC) +
+                        8 * lane;
+        // The 0/1 operands: element e of lane (h2, j) stands for query 16 s + 4 h2 +
+        // 8 (e / 4) + e % 4 of the half (the k order of the dS^T operand) and is 1 where
+        // that query is column j.
+        bf16x8 sel01[2];
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          float e01[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) e01[e] = (16 * sh + 4 * h2 + 8 * (e >> 2) + (e & 3)) == col ? 1.0f : 0.0f;
+          sel01[sh] = pack8(e01);
+        }
+#pragma unroll
+        for (int us = 0; us < 2; ++us) {
+          f32x16 t = mfma(dsb[us][0], sel01[0], f32x16{});
+          t = mfma(dsb[us][1], sel01[1], t);
+#pragma unroll
+          for (int sp = 0; sp < 2; ++sp) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = t[8 * sp + j];
+            *reinterpret_cast<u32x4*>(rec + (2 * us + sp) * 512) = __builtin_bit_cast(u32x4, pack8(v));
+          }
+        }
+      }
       // dK += dS^T Q (the scale is applied once, at the end).
       bf16x8 ft = tr_frag_at(qp, 0, 0, o, 0);
 #pragma unroll
@@ -326,11 +382,18 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
     if constexpr (decltype(is_p)::value) {
       if (it < n_it) p_tile(u_begin + it, qc, dc, lsec, it & 1);
     } else {
-      d_tile(it > 0, qp, delp, (it + 1) & 1, it < n_it, dc);
+      d_tile(it > 0, qp, delp, (it + 1) & 1, it < n_it, dc, u_begin + it - 1);
     }
-    wait_dma();  // the next tile has landed (this wave's part); P is written
-    if (it + 1 < n_it) store_rows(lsen, deln);
-    __syncthreads();
+    if (SPILL && !decltype(is_p)::value) {
+      // A D wave staged nothing and writes no LDS; its LDS reads fed its products.
+      // It leaves its dS stores in flight.
+      phase_barrier();
+    } else {
+      wait_dma();  // the next tile has landed (this wave's part); P is written
+      if (it + 1 < n_it) store_rows(lsen, deln);
+      if constexpr (SPILL) phase_barrier();
+      else __syncthreads();
+    }
   };
   auto loop = [&](auto is_p) __attribute__((always_inline)) {
     for (int it = 0; it <= n_it; it += 6) {
@@ -465,22 +528,51 @@ size_t dkdv_partial_bytes(const AttnArgs& a, SplitPlan p) {
   return static_cast<size_t>(n_split) * a.pool.Hkv * keys * 2 * mf::D * sizeof(float);
 }
 
+// The dS spill takes 2 bytes per (query, attended key) pair of every 64-query tile and
+// 128-key block, and replaces the dQ pass's recomputation of S and dP (6 D of its 8 D
+// flops per pair) by a read of those bytes. It is used without a window (where every
+// tile of the chunk's rectangle is visited) while the workspace stays within
+// OOMB_DS_SPILL_MAX_MIB (default 32768 MiB; 0 turns the spill off), read at every call
+// like the split variables.
+size_t ds_spill_bytes(const AttnArgs& a) {
+  if (a.window > 0) return 0;
+  size_t cap = static_cast<size_t>(32768) << 20;
+  if (const char* v = getenv("OOMB_DS_SPILL_MAX_MIB")) {
+    const long long mib = atoll(v);
+    cap = mib > 0 ? static_cast<size_t>(mib) << 20 : 0;
+  }
+  const size_t nkb = (static_cast<size_t>(a.max_att_pages) * a.pool.P + mf::KPW - 1) / mf::KPW;
+  const size_t n_qt = (static_cast<size_t>(a.n_q) + mf::QTB - 1) / mf::QTB;
+  const size_t bytes = static_cast<size_t>(a.pool.Hq) * nkb * n_qt * 4 * mf::DS_REC * sizeof(uint16_t);
+  return bytes <= cap ? bytes : 0;
+}
+
 hipError_t launch_bwd_mfma(const AttnArgs& a, SplitPlan kv, float* part, SplitPlan dq,
-                           float* dq_part, hipStream_t s) {
-  // The dQ pass also computes Delta and stores it for the dK/dV pass.
-  hipError_t err = launch_dq_mfma(a, dq, dq_part, s);
-  if (err != hipSuccess) return err;
+                           float* dq_part, uint16_t* ds, hipStream_t s) {
+  hipError_t err;
+  if (ds == nullptr) {
+    // The dQ pass also computes Delta and stores it for the dK/dV pass.
+    if ((err = launch_dq_mfma(a, dq, dq_part, nullptr, s)) != hipSuccess) return err;
+  } else if ((err = launch_delta_mfma(a, s)) != hipSuccess) {
+    return err;
+  }
   const int nkb = (a.max_att_pages * a.pool.P + mf::KPW - 1) / mf::KPW;
   const int part_keys = a.max_att_pages * a.pool.P;
-  OOMB_LAUNCH("dkdv_mfma", mf::dkdv_mfma_kernel, dim3(a.pool.Hkv * plan_units(kv, nkb)),
-              dim3(64 * mf::DKV_WAVES), 0, s,
-              a, kv.n_ks, kv.whole, part, part_keys);
+  const dim3 grid(a.pool.Hkv * plan_units(kv, nkb));
+  if (ds == nullptr) {
+    OOMB_LAUNCH("dkdv_mfma", mf::dkdv_mfma_kernel<false>, grid, dim3(64 * mf::DKV_WAVES), 0, s,
+                a, kv.n_ks, kv.whole, part, part_keys, nullptr);
+  } else {
+    OOMB_LAUNCH("dkdv_mfma", mf::dkdv_mfma_kernel<true>, grid, dim3(64 * mf::DKV_WAVES), 0, s,
+                a, kv.n_ks, kv.whole, part, part_keys, ds);
+  }
   const int k_first = kv.whole * mf::KPW;  // keys of the blocks that ran whole are done
   if (kv.n_ks > 1 && k_first < part_keys) {
-    dim3 grid((part_keys - k_first + 3) / 4, a.pool.Hkv);
-    OOMB_LAUNCH("dkdv_merge", mf::dkdv_merge_kernel, grid, dim3(256), 0, s, a, kv.n_ks, part,
+    dim3 mgrid((part_keys - k_first + 3) / 4, a.pool.Hkv);
+    OOMB_LAUNCH("dkdv_merge", mf::dkdv_merge_kernel, mgrid, dim3(256), 0, s, a, kv.n_ks, part,
                 part_keys, k_first);
   }
+  if (ds != nullptr && (err = launch_dq_mfma(a, dq, dq_part, ds, s)) != hipSuccess) return err;
   return hipGetLastError();
 }
 

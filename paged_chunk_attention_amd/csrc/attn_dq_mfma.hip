@@ -256,6 +256,219 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(AttnArgs a, int n_ks, int
   *reinterpret_cast<f32x4*>(a.dq + h * a.dq_hs + static_cast<int64_t>(i) * a.dq_ts + c) = s;
 }
 
+// Delta_i = dO_i . O_i for the backward that spills dS, formed in the order the
+// recomputing dQ pass uses (each half of the row, 8-element groups 16 kk + 8 half .. +7
+// in element order by fused multiply-adds, then the two halves added), so that both
+// backward paths give the dK/dV pass the same Delta bits and so the same dK and dV.
+// Two lanes per row.
+__global__ __launch_bounds__(256) void delta_mfma_kernel(AttnArgs a) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = t >> 1;
+  const int half = static_cast<int>(t & 1);
+  const bool ok = row < static_cast<int64_t>(a.pool.Hq) * a.n_q;
+  const int h = ok ? static_cast<int>(row / a.n_q) : 0, i = ok ? static_cast<int>(row % a.n_q) : 0;
+  const uint16_t* dr = static_cast<const uint16_t*>(a.dout) + h * a.do_hs + static_cast<int64_t>(i) * a.do_ts;
+  const uint16_t* orow = static_cast<const uint16_t*>(a.o) + h * a.o_hs + static_cast<int64_t>(i) * a.o_ts;
+  float acc = 0.0f;
+  if (ok) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4 dv = *reinterpret_cast<const u32x4*>(dr + 16 * kk + 8 * half);
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(orow + 16 * kk + 8 * half);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = __builtin_fmaf(__uint_as_float(dv[w] << 16), __uint_as_float(ov[w] << 16), acc);
+        acc = __builtin_fmaf(__uint_as_float(dv[w] & 0xFFFF0000u), __uint_as_float(ov[w] & 0xFFFF0000u), acc);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  if (ok && half == 0) a.delta[row] = acc;
+}
+
+// ============================================================================ dQ from dS
+// When the dK/dV pass has spilled its dS tiles (see dkdv_mfma_kernel), dQ needs no
+// recomputation: dQ^T = scale K^T dS^T, one product per key block with K from the pool
+// and dS^T from the spill. The work units, key ranges and partials are those of
+// dq_mfma_kernel (256 queries of one head per workgroup, one workgroup per CU), over
+// stages of 64 keys. The spill holds each (64-query tile, 32-key group) as the very B
+// operands of this product (lane = query, eight keys), so they go from HBM straight
+// into registers, 16 bytes a lane, 1 KiB a wave-instruction, with no LDS round trip;
+// only K passes through LDS (a swizzled row-major tile, by DMA), for its transposed
+// fragments. Both arrive two stages ahead (K in triple buffers). This pass streams
+// the spill once, so HBM bandwidth bounds it.
+//
+// Wave w owns the 64-query tile jq = w % 4 and key half kh = w / 4 of every stage (the
+// key group 2 (b % 2) + kh of the spill): dQ^T of its 64 queries over all 128 d columns
+// (two query halves x four column blocks, 128 accumulators a lane), from 8 K fragments
+// and 4 dS fragments per stage for 16 products. The two key halves' sums are added
+// through LDS at the end.
+constexpr int DQS_KB = 64;  // keys per stage
+// Zero dS operands: the source of the loads of stages a tile does not see (fixed
+// operation counts; the values are never used).
+static __device__ __attribute__((aligned(16))) uint16_t g_zero_ops[4 * 512] = {};
+
+__global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_t* ds) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[DQS_KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[DQS_KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k2[DQS_KB * D];
+  __shared__ int s_page[PCAP];
+  constexpr int NT = 64 * DQ_WAVES;
+  // K rows by DMA issued from assembly (the compiler would otherwise wait for every
+  // DMA in flight before each LDS read). The compiler then counts only the dS loads in
+  // its own waits for them, so each such wait also covers up to two later K DMAs and
+  // half of the next stage's dS loads; the explicit waits below cover the K tiles.
+  using Stage = KeyStage<DQS_KB, DQ_WAVES, PCAP, true>;
+  static_assert(Stage::NI == 2, "stage instruction count");
+  constexpr int kStageOps = Stage::NI + 4;  // + four dS operand loads per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, col = lane & 31;
+  const int G = a.pool.Hq / a.pool.Hkv;
+  const int n_qt = (a.n_q + DQ_Q - 1) / DQ_Q;
+  const int n_qt64 = (a.n_q + QTB - 1) / QTB;
+  const int nkb = (a.max_att_pages * a.pool.P + KPW - 1) / KPW;  // the spill's key blocks
+  const HeadUnit hu = head_unit(blockIdx.x, gridDim.x, a.pool.Hkv);
+  const TileRange tr = tile_range(hu.unit, whole, n_ks);
+  const int g = hu.head, kr = tr.range, n_rng = tr.n_ranges;
+  const int hh = tr.tile % G, qt = n_qt - 1 - tr.tile / G;
+  const int h = g * G + hh;
+  const Keys km = make_keys(a, g);
+  const int q0 = qt * DQ_Q;
+  const int nblk = n_blocks(km, a.t0 + min(a.n_q, q0 + DQ_Q) - 1);  // stages of 64 keys
+  const int b0 = nblk * kr / n_rng, b1 = nblk * (kr + 1) / n_rng;
+
+  // This wave's 64-query tile and key half; the stages its queries see (those up to the
+  // tile's last query: the dK/dV pass visited this tile for each of their key blocks).
+  const int jq = wave & 3, kh = wave >> 2;
+  const int qt64 = 4 * qt + jq;
+  const int wq0 = QTB * qt64;
+  const int nblk_w = wq0 < a.n_q ? n_blocks(km, a.t0 + min(a.n_q, wq0 + QTB) - 1) : 0;
+  const uint16_t* ds_tile =
+      ds + (static_cast<int64_t>(h) * nkb * n_qt64 + (qt64 < n_qt64 ? qt64 : 0)) * (4 * DS_REC) + 8 * lane;
+
+  f32x16 acc[2][4];  // [query half][d block]: dQ^T over this wave's key halves
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  FragOffsets fo;
+  fo.init(lane);
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.pool.k_pool);
+  const int win0 = (b0 * DQS_KB) >> km.log2p;
+  Stage ks{km, s_page, win0, Stage::lane_offset(wave, lane)};
+  fill_pages<NT>(km, s_page, win0, tid);
+  wait_dma();
+  __syncthreads();
+
+  // Stage b: K rows into kt, and this wave's dS operands (four 16-byte loads) into bs.
+  // Every stage issues the same operations, also past the last one (b >= b1: zero
+  // sources, never used) and where this wave's tile does not see the stage (zero dS),
+  // so that both the explicit waits and the compiler's own count them exactly.
+  auto issue = [&](int b, uint16_t* kt, bf16x8 (&bs)[4]) __attribute__((always_inline)) {
+    if (b < b1) {
+      ks.issue_fixed(b, kpool, kt, wave, lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Stage::NI; ++i)
+        lds_dma16<true>(g_zero_rows + ks.lane_off, kt + 4 * (DQ_WAVES * i + wave) * D);
+    }
+    const bool ok = b < nblk_w && b < b1;
+    const uint16_t* rec = ds_tile + (static_cast<int64_t>(b >> 1) * n_qt64 * 4 + 2 * (b & 1) + kh) * DS_REC;
+    const uint16_t* src = ok ? rec : g_zero_ops + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bs[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + i * 512));
+    // The waits count a stage's memory operations in issue order: keep them here.
+    asm volatile("" ::: "memory");
+  };
+  auto compute = [&](const uint16_t* kt, const bf16x8 (&bs)[4]) __attribute__((always_inline)) {
+    FragOffsets o = fo;
+    o.opaque();
+    bf16x8 af[2][4];
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) af[sp][db] = tr_frag_at(kt, 32 * kh, sp, o, db);
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+      for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[us][db] = mfma(af[sp][db], bs[2 * us + sp], acc[us][db]);
+  };
+  // Stage b: once stage b has landed for everyone (and nobody reads stage b - 1 any
+  // more), stage b + 2 is issued into (kn, bn) and stage b computed from (kt, bt).
+  auto stage = [&](int b, const uint16_t* kt, const bf16x8 (&bt)[4], uint16_t* kn, bf16x8 (&bn)[4])
+      __attribute__((always_inline)) {
+    wait_vm<4 + kStageOps>();  // this wave's K rows of stage b (its dS and stage b + 1 may fly)
+    phase_barrier();           // ... everyone's
+    if (b + 2 < b1) {
+      const int last_e = ((b + 2) * DQS_KB + DQS_KB - 1) >> km.log2p;
+      if (last_e >= ks.win + PCAP) {  // uniform: slide the page window to stage b + 2
+        ks.win = ((b + 2) * DQS_KB) >> km.log2p;
+        fill_pages<NT>(km, s_page, ks.win, tid);
+        wait_dma();
+        __syncthreads();
+      }
+    }
+    issue(b + 2, kn, bn);
+    if (b < nblk_w && b < b1) compute(kt, bt);
+  };
+  bf16x8 bs0[4], bs1[4], bs2[4];
+  issue(b0, s_k0, bs0);
+  issue(b0 + 1, s_k1, bs1);
+  // Unrolled by three so that each third names its buffers statically; the stages past
+  // b1 that complete the last three are empty (no products), which keeps one path
+  // through the loop body and so the operand registers of each third fixed.
+  for (int b = b0; b < b1; b += 3) {
+    stage(b, s_k0, bs0, s_k2, bs2);
+    stage(b + 1, s_k1, bs1, s_k0, bs0);
+    stage(b + 2, s_k2, bs2, s_k1, bs1);
+  }
+
+  // The key halves' sums: the second half's waves hand theirs over through LDS (the K
+  // buffers are free now), one column block at a time.
+  float* xch = reinterpret_cast<float*>(jq < 2 ? s_k0 : s_k1) + (jq & 1) * (2 * 16 * 64);
+  wait_dma();
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    if (kh == 1) {
+#pragma unroll
+      for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(us * 16 + r) * 64 + lane] = acc[us][db][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[us][db][r] += xch[(us * 16 + r) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (kh != 0) return;
+
+#pragma unroll
+  for (int us = 0; us < 2; ++us) {
+    const int i = wq0 + 32 * us + col;
+    if (i >= a.n_q) continue;
+    float* drow = n_rng == 1 ? a.dq + h * a.dq_hs + static_cast<int64_t>(i) * a.dq_ts
+                            : part + ((static_cast<int64_t>(kr) * a.pool.Hq + h) * a.n_q + i) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ga = 0; ga < 4; ++ga) {
+        f32x4 w;
+#pragma unroll
+        for (int b2 = 0; b2 < 4; ++b2) w[b2] = acc[us][db][4 * ga + b2] * a.scale;
+        *reinterpret_cast<f32x4*>(drow + 32 * db + 8 * ga + 4 * h2) = w;
+      }
+  }
+}
+
 }  // namespace mf
 
 // Key ranges per query tile of the dQ pass, chosen for load balance: a tile's work is
@@ -284,16 +497,30 @@ SplitPlan dq_plan(const AttnArgs& a) {
   return mixed_plan(G * n_qt, a.pool.Hkv, smallest, nk);
 }
 
+hipError_t launch_delta_mfma(const AttnArgs& a, hipStream_t s) {
+  const int64_t lanes = 2 * static_cast<int64_t>(a.pool.Hq) * a.n_q;
+  OOMB_LAUNCH("delta_mfma", mf::delta_mfma_kernel, dim3(static_cast<unsigned>((lanes + 255) / 256)),
+              dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 size_t dq_partial_bytes(const AttnArgs& a, SplitPlan p) {
   if (p.n_ks <= 1) return 0;
   return static_cast<size_t>(p.n_ks) * a.pool.Hq * a.n_q * mf::D * sizeof(float);
 }
 
-hipError_t launch_dq_mfma(const AttnArgs& a, SplitPlan p, float* part, hipStream_t s) {
+hipError_t launch_dq_mfma(const AttnArgs& a, SplitPlan p, float* part, const uint16_t* ds,
+                          hipStream_t s) {
   const int n_qt = (a.n_q + mf::DQ_Q - 1) / mf::DQ_Q;
   const int G = a.pool.Hq / a.pool.Hkv;
-  OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, dim3(a.pool.Hkv * plan_units(p, G * n_qt)),
-              dim3(64 * mf::DQ_WAVES), 0, s, a, p.n_ks, p.whole, part);
+  const dim3 grid(a.pool.Hkv * plan_units(p, G * n_qt));
+  if (ds != nullptr) {
+    OOMB_LAUNCH("dqs_mfma", mf::dqs_mfma_kernel, grid, dim3(64 * mf::DQ_WAVES), 0, s, a, p.n_ks,
+                p.whole, part, ds);
+  } else {
+    OOMB_LAUNCH("dq_mfma", mf::dq_mfma_kernel, grid, dim3(64 * mf::DQ_WAVES), 0, s, a, p.n_ks,
+                p.whole, part);
+  }
   if (p.n_ks > 1) {
     const int64_t threads = static_cast<int64_t>(a.pool.Hq) * a.n_q * (mf::D / 4);
     OOMB_LAUNCH("dq_merge", mf::dq_merge_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),

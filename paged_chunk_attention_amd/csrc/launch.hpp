@@ -256,13 +256,22 @@ size_t fwd_partial_bytes(const AttnArgs& a, SplitPlan p);
 // `whole` blocks stay whole); `part` then holds dkdv_partial_bytes(a, plan) bytes of
 // fp32 partials. A dQ plan with n_ks > 1 cuts query tiles into key ranges; `dq_part`
 // then holds dq_partial_bytes(a, plan) bytes.
+// With ds (ds_spill_bytes(a) bytes) the dK/dV pass spills its bf16 dS tiles there and
+// the dQ pass reads them (Delta from launch_delta first); without, the dQ pass runs
+// first and recomputes S and dP.
 hipError_t launch_bwd_mfma(const AttnArgs& a, SplitPlan kv, float* part, SplitPlan dq,
-                           float* dq_part, hipStream_t s);
-// dQ pass of the matrix-core backward, launched first by launch_bwd_mfma; it also
-// computes Delta = rowsum(dO * O) and stores it in a.delta for the dK/dV pass.
-hipError_t launch_dq_mfma(const AttnArgs& a, SplitPlan p, float* part, hipStream_t s);
+                           float* dq_part, uint16_t* ds, hipStream_t s);
+// dQ pass of the matrix-core backward. Without ds it recomputes dS and also computes
+// Delta = rowsum(dO * O) into a.delta for the dK/dV pass (so it runs first); with ds it
+// reads the dK/dV pass's spilled dS (so it runs after that pass).
+hipError_t launch_dq_mfma(const AttnArgs& a, SplitPlan p, float* part, const uint16_t* ds,
+                          hipStream_t s);
 SplitPlan dkdv_plan(const AttnArgs& a);
 size_t dkdv_partial_bytes(const AttnArgs& a, SplitPlan p);
+// Workspace bytes of the dS spill for this call, or 0 when the spill is not used.
+size_t ds_spill_bytes(const AttnArgs& a);
+// Delta for the spilling backward, bit-identical to the one the recomputing dQ pass forms.
+hipError_t launch_delta_mfma(const AttnArgs& a, hipStream_t s);
 SplitPlan dq_plan(const AttnArgs& a);
 size_t dq_partial_bytes(const AttnArgs& a, SplitPlan p);
 // Delta_i = dO_i . O_i for the scalar backward (the matrix-core dQ pass forms its own).

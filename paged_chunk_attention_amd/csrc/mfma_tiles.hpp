@@ -49,6 +49,7 @@ constexpr int PCAP = 2048;    // attended page ids held in LDS at a time
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int KPW = 128;      // keys per workgroup in the dK/dV pass (32 per wavefront)
 constexpr int QTB = 64;       // queries per staged tile in the dK/dV pass
+constexpr int DS_REC = 4 * 64 * 8;  // bf16 of spilled dS per (64-query tile, 32 keys)
 
 // Whether attention row `row` (= h * n_q + i) belongs to a query tile (of `tileq`
 // queries) that a split plan cut into key ranges: its tile index in the KV head's

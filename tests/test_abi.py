@@ -190,8 +190,32 @@ def test_split_counts_at_the_workloads(lib, name, n_q, t0, sel_stride, splits):
     fwd = 0 if n_fwd == 1 else n_fwd * hq * n_q * (d + 2) * 4
     bwd = (a256(hq * n_q * 4) + a256(0 if n_kv == 1 else n_kv * hkv * keys * 2 * d * 4)
            + a256(0 if n_dq == 1 else n_dq * hq * n_q * d * 4))
+    # the bf16 dS spill: 2 bytes per pair of every (64-query tile, 128-key block)
+    spill = hq * -(-keys // 128) * -(-n_q // 64) * 64 * 128 * 2
     assert lib.oomb_fwd_workspace_bytes(ctypes.byref(p), n_q, t0, sel_stride, 0) == fwd, name
-    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), n_q, t0, sel_stride, 0) == bwd, name
+    assert lib.oomb_bwd_workspace_bytes(ctypes.byref(p), n_q, t0, sel_stride, 0) == bwd + spill, name
+
+
+def test_ds_spill_workspace(lib, monkeypatch):
+    """The backward spills dS (and its workspace holds it) only without a window and
+    within OOMB_DS_SPILL_MAX_MIB (default 32 GiB; 0 turns it off), read at every call."""
+    p = _pool()
+    size = lambda t0, w=0: lib.oomb_bwd_workspace_bytes(ctypes.byref(p), 4096, t0, -1, w)
+    spill = 28 * 32 * 64 * 64 * 128 * 2  # 4096 local keys: 32 blocks x 64 tiles
+    monkeypatch.setenv("OOMB_DS_SPILL_MAX_MIB", "0")
+    base, base_w = size(0), size(0, w=1024)  # Delta and the split partials
+    assert base < 2 ** 27 and base % 256 == 0
+    monkeypatch.delenv("OOMB_DS_SPILL_MAX_MIB")
+    assert size(0) == base + spill
+    assert size(0, w=1024) == base_w  # no spill with a window
+    monkeypatch.setenv("OOMB_DS_SPILL_MAX_MIB", str(spill >> 20))
+    assert size(0) == base + spill
+    monkeypatch.setenv("OOMB_DS_SPILL_MAX_MIB", str((spill >> 20) - 1))
+    assert size(0) == base
+    monkeypatch.delenv("OOMB_DS_SPILL_MAX_MIB")
+    # dense 128K spills 27.4 GiB, within the default; the dense 262,144-token chunk not
+    assert size(126976) > 27 * 2 ** 30
+    assert size(262144 - 4096) < 2 ** 30
 
 
 @pytest.mark.parametrize("name,n_q,t0,sel_stride,plan", [

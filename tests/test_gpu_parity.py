@@ -195,6 +195,53 @@ def test_backward_deterministic_run_twice():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(name="mfma_dense_ragged"),
+    dict(name="mfma_sparse_k5", chunk=333, total=2597 + 333, top_k=5, needles=3),
+    dict(name="mfma_window_slide", hq=4, hkv=1, page=16, chunk=256, total=16 * 8192 + 256),
+])
+def test_chunk_parity_mfma_recomputed_dq(kw, monkeypatch):
+    """With the dS spill turned off the dQ pass recomputes S and dP (the path of windowed
+    calls and of workspaces beyond the spill's limit): the same bars."""
+    monkeypatch.setenv("OOMB_DS_SPILL_MAX_MIB", "0")
+    run_chunk_parity(_w(**dict(kw, name=f"{kw['name']}_recompute")))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(name="spill_sparse", hq=8, hkv=2, chunk=300, total=2000, top_k=6),
+    dict(name="spill_dense_gqa7", hq=28, hkv=4, chunk=333, total=1700),
+])
+def test_ds_spill_matches_recompute(kw, monkeypatch):
+    """The backward with the dS spill and without: dK/dV bit for bit (the dK/dV pass does
+    the same arithmetic, the spill only stores its dS), dQ within the bf16 bar of each
+    other (the spilled dS is formed from the fp16 P the dK/dV pass exchanges, the
+    recomputed one from an fp32 P)."""
+    w = _w(**kw)
+    x = wl.make_inputs(w)
+    table = x["table"].to(DEV)
+    pool = pca.PagedPool(w.pool_pages, w.page, w.d, w.hq, w.hkv, w.dtype, DEV)
+    log(f"[case {w.name}] spill on / off")
+    pca.oomb_kv_append(pool, table, x["k"].to(DEV), x["v"].to(DEV), 0)
+    pca.oomb_page_summarize(pool, table, 0, w.pages_per_head, w.total)
+    q, do = x["q"].to(DEV), x["do"].to(DEV)
+    sel = cnt = None
+    if w.top_k is not None:
+        sel, cnt = pca.oomb_select_pages(pool, table, q, w.t0, w.top_k)
+    o, lse = pca.oomb_paged_chunk_attn_fwd(pool, table, q, w.t0, sel, cnt)
+    res = []
+    for limit in (None, "0"):
+        if limit is None:
+            monkeypatch.delenv("OOMB_DS_SPILL_MAX_MIB", raising=False)
+        else:
+            monkeypatch.setenv("OOMB_DS_SPILL_MAX_MIB", limit)
+        pool.zero_grad()
+        dq = pca.oomb_paged_chunk_attn_bwd(pool, table, table, q, w.t0, sel, cnt, o, do, lse)
+        torch.cuda.synchronize()
+        res.append((dq.cpu(), pool.dk.cpu(), pool.dv.cpu()))
+    assert torch.equal(res[0][1], res[1][1]) and torch.equal(res[0][2], res[1][2])
+    compare("dQ spill vs recompute", res[0][0], res[1][0].double(), w.dtype)
+
+
 def test_strided_views_match_contiguous():
     """[C, H, D] storage (token-major) gives the same results as [H, C, D]."""
     import paged_chunk_attention_amd as pca
