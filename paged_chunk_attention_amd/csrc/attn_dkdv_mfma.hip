@@ -31,18 +31,16 @@ namespace mf {
 // about 1 elsewhere (it is exp(S - LSE) with the forward's LSE), which fp16 holds.
 //
 // With SPILL the D wave also writes every dS tile it forms to ds, for the dQ pass to use
-// instead of recomputing S and dP. The dQ product contracts over keys, so it wants dS
-// with a lane per query and keys along the operand, the transpose of what the D wave
-// holds (a lane per key). Two products with 0/1 matrices transpose a tile exactly on
-// the matrix core: with A = the D wave's dS^T operand of one 32-query half (32 keys x 16
-// queries, twice) and B = the selection of those queries, C = dS^T lands in C layout,
-// lane = query, register r = key 8 (r / 4) + 4 h2 + r % 4, every value a single bf16
-// times 1 (exact). Packed to bf16 that is the B operand of dQ^T += K^T dS^T for k-step
-// sp = r / 8, in the row order of the transposed K fragment. Per (query head, key
-// block, 64-query tile, key group) the record block of DS_REC values is [us][sp][lane][8]
-// (query half us, k-step sp): four 16-byte stores per lane and tile, each a contiguous
-// 1 KiB. Masked pairs store exact zeros (P = 0); the tiles the pass never visits (query
-// tiles wholly before a chunk key block) are never read.
+// instead of recomputing S and dP: its bf16 dS^T operands as they are, per (query head,
+// key block, 64-query tile, key group) one record block of DS_REC values, [pack p =
+// 2 us + s][lane][8], where lane (h2, col) holds key 32 kg + col and element j of pack
+// (us, s) is query row 32 us + 16 s + 4 h2 + 8 (j / 4) + j % 4 of the tile. Four 16-byte
+// stores per lane and tile, each a contiguous 1 KiB. The dQ product contracts over keys
+// and so wants the transpose; the dQ pass forms it with transposing LDS reads, which
+// costs it less than the two extra products a tile would cost here (measured: this pass
+// 2.4% faster at dense 128K, the dQ pass 4% slower, the backward 0.8% faster). Masked
+// pairs store exact zeros (P = 0); the tiles the pass never visits (query tiles wholly
+// before a chunk key block) are never read.
 //
 // The D wave never waits for its stores: with SPILL the P waves stage both the Q and
 // the dO tiles (and load the rows' LSE and Delta), so a D wave issues no load in the
@@ -316,29 +314,11 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
         const int hq = g * G + u_prev / tph, qt = qt0 + u_prev % tph;
         uint16_t* rec = ds + ((((static_cast<int64_t>(hq) * nkb + kb) * n_qt + qt) * 4 + kg) * DS_REC) +
                         8 * lane;
-        // The 0/1 operands: element e of lane (h2, j) stands for query 16 s + 4 h2 +
-        // 8 (e / 4) + e % 4 of the half (the k order of the dS^T operand) and is 1 where
-        // that query is column j.
-        bf16x8 sel01[2];
 #pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          float e01[8];
+        for (int us = 0; us < 2; ++us)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) e01[e] = (16 * sh + 4 * h2 + 8 * (e >> 2) + (e & 3)) == col ? 1.0f : 0.0f;
-          sel01[sh] = pack8(e01);
-        }
-#pragma unroll
-        for (int us = 0; us < 2; ++us) {
-          f32x16 t = mfma(dsb[us][0], sel01[0], f32x16{});
-          t = mfma(dsb[us][1], sel01[1], t);
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp) {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = t[8 * sp + j];
-            *reinterpret_cast<u32x4*>(rec + (2 * us + sp) * 512) = __builtin_bit_cast(u32x4, pack8(v));
-          }
-        }
+          for (int sh = 0; sh < 2; ++sh)
+            *reinterpret_cast<u32x4*>(rec + (2 * us + sh) * 512) = __builtin_bit_cast(u32x4, dsb[us][sh]);
       }
       // dK += dS^T Q (the scale is applied once, at the end).
       bf16x8 ft = tr_frag_at(qp, 0, 0, o, 0);

@@ -291,37 +291,38 @@ __global__ __launch_bounds__(256) void delta_mfma_kernel(AttnArgs a) {
 // recomputation: dQ^T = scale K^T dS^T, one product per key block with K from the pool
 // and dS^T from the spill. The work units, key ranges and partials are those of
 // dq_mfma_kernel (256 queries of one head per workgroup, one workgroup per CU), over
-// stages of 64 keys. The spill holds each (64-query tile, 32-key group) as the very B
-// operands of this product (lane = query, eight keys), so they go from HBM straight
-// into registers, 16 bytes a lane, 1 KiB a wave-instruction, with no LDS round trip;
-// only K passes through LDS (a swizzled row-major tile, by DMA), for its transposed
-// fragments. Both arrive two stages ahead (K in triple buffers). This pass streams
-// the spill once, so HBM bandwidth bounds it.
+// stages of 64 keys: K rows (a swizzled row-major tile) and the spilled record blocks
+// arrive by DMA two stages ahead, into triple buffers. This pass streams the spill
+// once, so HBM bandwidth bounds it.
 //
 // Wave w owns the 64-query tile jq = w % 4 and key half kh = w / 4 of every stage (the
 // key group 2 (b % 2) + kh of the spill): dQ^T of its 64 queries over all 128 d columns
-// (two query halves x four column blocks, 128 accumulators a lane), from 8 K fragments
-// and 4 dS fragments per stage for 16 products. The two key halves' sums are added
-// through LDS at the end.
+// (two query halves x four column blocks, 128 accumulators a lane), from 8 transposed K
+// fragments and 4 dS^T fragments per stage for 16 products. It stages its own record
+// block (4 KiB), in which a lane holds one key and runs of four consecutive queries
+// (8 bytes): ds_read_b64_tr_b16 gathers exactly the B operand (a lane per query, keys
+// along it) from those runs, source lane 4k + m reading key k's run 4m .. 4m + 3, in the
+// key order of the transposed K fragment. Records land in LDS with their lane index
+// XORed by 4 ((l / 32) | 2 (p % 2)), which makes every half-wave of those reads
+// conflict-free. The two key halves' sums are added through LDS at the end.
 constexpr int DQS_KB = 64;  // keys per stage
-// Zero dS operands: the source of the loads of stages a tile does not see (fixed
-// operation counts; the values are never used).
-static __device__ __attribute__((aligned(16))) uint16_t g_zero_ops[4 * 512] = {};
+
+// LDS slot of spilled record lane l in pack p (an involution: bit 5 is kept).
+__device__ __forceinline__ int ds_slot(int p, int l) { return l ^ (4 * ((l >> 5) | ((p & 1) << 1))); }
 
 __global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_t* ds) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[DQS_KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k1[DQS_KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_k2[DQS_KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_s0[DQ_WAVES * DS_REC];
+  __shared__ __attribute__((aligned(16))) uint16_t s_s1[DQ_WAVES * DS_REC];
+  __shared__ __attribute__((aligned(16))) uint16_t s_s2[DQ_WAVES * DS_REC];
   __shared__ int s_page[PCAP];
   constexpr int NT = 64 * DQ_WAVES;
-  // K rows by DMA issued from assembly (the compiler would otherwise wait for every
-  // DMA in flight before each LDS read). The compiler then counts only the dS loads in
-  // its own waits for them, so each such wait also covers up to two later K DMAs and
-  // half of the next stage's dS loads; the explicit waits below cover the K tiles.
-  using Stage = KeyStage<DQS_KB, DQ_WAVES, PCAP, true>;
+  using Stage = KeyStage<DQS_KB, DQ_WAVES, PCAP, true>;  // K rows by DMA from assembly
   static_assert(Stage::NI == 2, "stage instruction count");
-  constexpr int kStageOps = Stage::NI + 4;  // + four dS operand loads per wave
+  constexpr int kStageOps = Stage::NI + 4;  // + the wave's four dS record rows
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, col = lane & 31;
   const int G = a.pool.Hq / a.pool.Hkv;
@@ -344,8 +345,15 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
   const int qt64 = 4 * qt + jq;
   const int wq0 = QTB * qt64;
   const int nblk_w = wq0 < a.n_q ? n_blocks(km, a.t0 + min(a.n_q, wq0 + QTB) - 1) : 0;
-  const uint16_t* ds_tile =
-      ds + (static_cast<int64_t>(h) * nkb * n_qt64 + (qt64 < n_qt64 ? qt64 : 0)) * (4 * DS_REC) + 8 * lane;
+  const uint16_t* ds_tile = ds + (static_cast<int64_t>(h) * nkb * n_qt64 + (qt64 < n_qt64 ? qt64 : 0)) * (4 * DS_REC);
+  // DMA source offsets of this lane's slot in even and odd packs
+  const int src_even = 8 * ds_slot(0, lane), src_odd = 8 * ds_slot(1, lane);
+  // dS^T operand reads (see above): this lane's offsets for the two key quartets of a
+  // k-step of the first query half
+  const int qh = (lane >> 4) & 1, kq = (lane & 15) >> 2, m = lane & 3;
+  int boff[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) boff[r] = qh * 512 + 8 * ds_slot(qh, 32 * (m & 1) + 4 * h2 + kq + 8 * r) + 4 * (m >> 1);
 
   f32x16 acc[2][4];  // [query half][d block]: dQ^T over this wave's key halves
 #pragma unroll
@@ -362,11 +370,11 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
   wait_dma();
   __syncthreads();
 
-  // Stage b: K rows into kt, and this wave's dS operands (four 16-byte loads) into bs.
+  // Stage b: K rows into kt, and this wave's dS record block into its 4 KiB of st.
   // Every stage issues the same operations, also past the last one (b >= b1: zero
-  // sources, never used) and where this wave's tile does not see the stage (zero dS),
-  // so that both the explicit waits and the compiler's own count them exactly.
-  auto issue = [&](int b, uint16_t* kt, bf16x8 (&bs)[4]) __attribute__((always_inline)) {
+  // sources, never used) and where this wave's tile does not see the stage, so that
+  // the waits count them exactly.
+  auto issue = [&](int b, uint16_t* kt, uint16_t* st) __attribute__((always_inline)) {
     if (b < b1) {
       ks.issue_fixed(b, kpool, kt, wave, lane);
     } else {
@@ -376,33 +384,42 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
     }
     const bool ok = b < nblk_w && b < b1;
     const uint16_t* rec = ds_tile + (static_cast<int64_t>(b >> 1) * n_qt64 * 4 + 2 * (b & 1) + kh) * DS_REC;
-    const uint16_t* src = ok ? rec : g_zero_ops + 8 * lane;
+    uint16_t* dst = st + wave * DS_REC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bs[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + i * 512));
-    // The waits count a stage's memory operations in issue order: keep them here.
-    asm volatile("" ::: "memory");
+    for (int p = 0; p < 4; ++p)
+      lds_dma16<true>(ok ? rec + p * 512 + ((p & 1) ? src_odd : src_even) : g_zero_rows + 8 * lane,
+                      dst + p * 512);
   };
-  auto compute = [&](const uint16_t* kt, const bf16x8 (&bs)[4]) __attribute__((always_inline)) {
+  auto compute = [&](const uint16_t* kt, const uint16_t* st) __attribute__((always_inline)) {
     FragOffsets o = fo;
     o.opaque();
-    bf16x8 af[2][4];
+    const uint16_t* sb = st + wave * DS_REC;
+    bf16x8 af[2][4], bf[2][2];
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp)
+    for (int sp = 0; sp < 2; ++sp) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) af[sp][db] = tr_frag_at(kt, 32 * kh, sp, o, db);
+#pragma unroll
+      for (int us = 0; us < 2; ++us) {
+        const uint16_t* base = sb + us * 1024 + sp * 128;
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + boff[0]));
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + boff[1]));
+        bf[us][sp] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
       for (int us = 0; us < 2; ++us)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) acc[us][db] = mfma(af[sp][db], bs[2 * us + sp], acc[us][db]);
+        for (int db = 0; db < 4; ++db) acc[us][db] = mfma(af[sp][db], bf[us][sp], acc[us][db]);
   };
   // Stage b: once stage b has landed for everyone (and nobody reads stage b - 1 any
-  // more), stage b + 2 is issued into (kn, bn) and stage b computed from (kt, bt).
-  auto stage = [&](int b, const uint16_t* kt, const bf16x8 (&bt)[4], uint16_t* kn, bf16x8 (&bn)[4])
+  // more), stage b + 2 is issued into (kn, sn) and stage b computed from (kt, st).
+  auto stage = [&](int b, const uint16_t* kt, const uint16_t* st, uint16_t* kn, uint16_t* sn)
       __attribute__((always_inline)) {
-    wait_vm<4 + kStageOps>();  // this wave's K rows of stage b (its dS and stage b + 1 may fly)
-    phase_barrier();           // ... everyone's
+    wait_vm<kStageOps>();  // this wave's part of stage b (stage b + 1 may stay in flight)
+    phase_barrier();       // ... everyone's
     if (b + 2 < b1) {
       const int last_e = ((b + 2) * DQS_KB + DQS_KB - 1) >> km.log2p;
       if (last_e >= ks.win + PCAP) {  // uniform: slide the page window to stage b + 2
@@ -412,19 +429,17 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
         __syncthreads();
       }
     }
-    issue(b + 2, kn, bn);
-    if (b < nblk_w && b < b1) compute(kt, bt);
+    issue(b + 2, kn, sn);
+    if (b < nblk_w && b < b1) compute(kt, st);
   };
-  bf16x8 bs0[4], bs1[4], bs2[4];
-  issue(b0, s_k0, bs0);
-  issue(b0 + 1, s_k1, bs1);
+  issue(b0, s_k0, s_s0);
+  issue(b0 + 1, s_k1, s_s1);
   // Unrolled by three so that each third names its buffers statically; the stages past
-  // b1 that complete the last three are empty (no products), which keeps one path
-  // through the loop body and so the operand registers of each third fixed.
+  // b1 that complete the last three are empty (no products).
   for (int b = b0; b < b1; b += 3) {
-    stage(b, s_k0, bs0, s_k2, bs2);
-    stage(b + 1, s_k1, bs1, s_k0, bs0);
-    stage(b + 2, s_k2, bs2, s_k1, bs1);
+    stage(b, s_k0, s_s0, s_k2, s_s2);
+    stage(b + 1, s_k1, s_s1, s_k0, s_s0);
+    stage(b + 2, s_k2, s_s2, s_k1, s_s1);
   }
 
   // The key halves' sums: the second half's waves hand theirs over through LDS (the K
