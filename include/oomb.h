@@ -254,7 +254,15 @@ size_t oomb_fwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
  * n_q queries after t0 prior tokens, with at most sel_stride selected prior pages
  * per KV head (sel_stride < 0: dense, every prior page). It holds Delta and, when
  * the dK/dV pass is split over the query stream or the dQ pass over key ranges (so
- * that the work spreads evenly over the GPU), their fp32 partials.
+ * that the work spreads evenly over the GPU), their fp32 partials; and, on the
+ * matrix-core path without a window, the bf16 dS of every (64-query tile, 128-key
+ * block) the key pass visits: Hq * ceil(keys / 128) * ceil(n_q / 64) * 16 KiB, with
+ * keys = (selected + local pages) * page_size. The dQ pass then reads dS instead of
+ * recomputing it (27.4 GiB for a 4096-query chunk over a 128K-token dense context,
+ * 2.6 GiB over 64 selected pages). That part is included only while it stays within
+ * the environment variable OOMB_DS_SPILL_MAX_MIB (MiB, default 32768; 0 = never),
+ * read at every call like the split variables: the backward then recomputes dS in
+ * the dQ pass instead, with the same dK/dV bits and dQ within rounding.
  * Returns 0 for invalid arguments. */
 size_t oomb_bwd_workspace_bytes(const oomb_pool* pool, int32_t n_q, int64_t t0,
                                 int64_t sel_stride, int32_t window);

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.oomb_abi_version() == 10
+    assert lib.oomb_abi_version() == 11
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
                        (3, b"HIP launch failure"), (4, b"workspace missing or too small")]:
         assert lib.oomb_status_string(code) == text
