@@ -841,6 +841,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip timing one chunk-recurrent attention layer (65,536 tokens)")
+    ap.add_argument("--no-selectors", action="store_true",
+                    help="skip the selector-variant leg (mean-key and per-tile selection)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the CPU-offload measurements (sparse workloads)")
     ap.add_argument("--offload-layers", type=int, default=4,
@@ -981,7 +983,7 @@ def main():
                 "unit": "GB/s", "frac": None, "traffic": None, "ms_per_launch": dom_ms}
 
     selector = None
-    if sparse:
+    if sparse and not args.no_selectors:
         selector = mean_selector_leg(pca, torch, w, pool, table, q, sel, count, x["needles"])
         hbm["page_summarize_mean"] = selector.pop("page_summarize_mean")
         hbm["select_pages_mean"] = selector.pop("select_pages_mean")
