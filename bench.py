@@ -90,6 +90,9 @@ def measured_traffic(workload: str, kernel: str):
     if fields.get("sha") != sha:
         return None
     rec = fields.get(kernel + "_kernel") or fields.get(kernel)
+    if rec is None:  # a template instance (the only one the profiled step ran)
+        inst = [k for k in fields if k.startswith(kernel + "_kernel<")]
+        rec = fields[inst[0]] if len(inst) == 1 else None
     return None if rec is None else {"read_bytes": rec[0], "write_bytes": rec[1],
                                      "bytes": rec[0] + rec[1]}
 
