@@ -44,9 +44,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # credited with dQ only: dq_mfma recomputes S and dP, dqs_mfma reads the dS the dK/dV
 # pass spilled.
 FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 2, "dqs_mfma": 2}
-# what each pass executes on the matrix cores (the forward also forms its row sums there:
-# one ones-operand product per four PV products)
-HW_FLOP_PER_PAIR_D = {"fwd_mfma": 4.5, "dkdv_mfma": 8, "dq_mfma": 6, "dqs_mfma": 2}
+# what each pass executes on the matrix cores
+HW_FLOP_PER_PAIR_D = {"fwd_mfma": 4, "dkdv_mfma": 8, "dq_mfma": 6, "dqs_mfma": 2}
 
 
 def spill_read_bytes(w, counts):

@@ -93,13 +93,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
   f32x16 ot[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) ot[db] = f32x16{};
-  float m_run = -__builtin_inff();
-  // Row sums of P on the matrix core: an all-ones A operand times each P^T step gives
-  // every row of lsum the column (query) sum of the bf16 P that also weights V, so the
-  // softmax phase does no additions (the vector ALU is the scarcer unit: two waves share
-  // its issue port, packed fp32 arithmetic is not used).
-  f32x16 lsum = f32x16{};
-  const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x16 st[2];     // S^T of the block last multiplied: from its M phase to its V phase
   bf16x8 pb[2][2];  // P^T of the block last normalised: from its V phase to the next M phase
 #pragma unroll
@@ -131,11 +125,10 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
   wait_dma();
   __syncthreads();
 
-  // Both products of an M phase as one software pipeline of eight steps: four PV steps
-  // (one k-step of one 32-key half each: four MFMAs and the row-sum product) then four
-  // S steps (k-steps 2i and 2i + 1 of both halves, alternating halves so that
-  // consecutive MFMAs are independent). The fragments of step i + 1 are read from LDS
-  // while step i multiplies.
+  // Both products of an M phase as one software pipeline of eight steps of four MFMAs:
+  // four PV steps (one k-step of one 32-key half each) then four S steps (k-steps 2i and
+  // 2i + 1 of both halves, alternating halves so that consecutive MFMAs are
+  // independent). The fragments of step i + 1 are read from LDS while step i multiplies.
   auto mul_pv_s = [&](const uint16_t* vt, const uint16_t* kt) __attribute__((always_inline)) {
     FragOffsets o = fo;
     o.opaque();
@@ -155,7 +148,6 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
       if (i < 4) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) ot[db] = mfma(f[db], pb[i >> 1][i & 1], ot[db]);
-        lsum = mfma(ones, pb[i >> 1][i & 1], lsum);
       } else {
         const int kk = 2 * (i - 4);
         if (i == 4) {
@@ -206,11 +198,12 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
     if (__any(grow)) {
       const float alpha = grow ? fast_exp2(m_run - mx) : 1.0f;
       if (grow) m_run = mx;
-      lsum *= alpha;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) ot[db] *= alpha;
     }
     const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // partial row sums (short dependency chains)
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -219,9 +212,11 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           p[j] = fast_exp2(__builtin_fmaf(st[sub][8 * s + j], c2, -mref));
+          ls[j & 3] += p[j];
         }
         pb[sub][s] = pack8(p);
       }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
   // Phase t, j = t / 2. DMA duties, always in the wave's V phase: at even t the second
@@ -306,7 +301,7 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
   wait_dma();  // no DMA may outlive the workgroup's LDS
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2; or this key range's partial.
-  const float lt = lsum[0];  // every row holds the sum over all keys
+  const float lt = add_halves(l_run);
   if (n_rng > 1) {
     if (i < a.n_q) {
       const int64_t row = (static_cast<int64_t>(krange) * a.pool.Hq + h) * a.n_q + i;
