@@ -129,6 +129,15 @@ def test_chunk_parity_mfma_window_fixed_splits(n, monkeypatch):
     dict(name="f32_d64_window", hq=2, hkv=1, d=64, page=16, chunk=64, total=1024, window=40,
          dtype=torch.float32),
     dict(name="bf16_d64_window", hq=4, hkv=1, d=64, page=64, chunk=100, total=300, window=150),
+    # the largest page size, a ragged chunk, rows whose keys take several rounds of the
+    # workgroup's four waves (64 keys each)
+    dict(name="f32_d128_p256_ragged", hq=2, hkv=1, d=128, page=256, chunk=77, total=77 + 1500,
+         dtype=torch.float32),
+    # a one-query chunk: one workgroup per head, two of its four waves without keys
+    dict(name="f32_d64_one_query", hq=2, hkv=1, d=64, page=16, chunk=1, total=1 + 100,
+         dtype=torch.float32),
+    dict(name="bf16_d64_p256_sparse", hq=6, hkv=2, d=64, page=256, chunk=130, total=130 + 2600,
+         top_k=3),
 ])
 def test_chunk_parity_scalar(kw):
     run_chunk_parity(_w(**kw))
