@@ -35,6 +35,10 @@ def _w(**kw):
     dict(name="mfma_single_query", hq=4, hkv=2, chunk=1, total=777),
     dict(name="mfma_k0_local_only", hq=4, hkv=2, chunk=128, total=1024, top_k=0),
     dict(name="mfma_k_exceeds", hq=4, hkv=2, chunk=64, total=640, top_k=50),
+    # pages of 64 (a key block of 64 is one page) and 256 (a page spans four key blocks)
+    dict(name="mfma_page64_dense", hq=4, hkv=2, page=64, chunk=160, total=160 + 900),
+    dict(name="mfma_page256_sparse", hq=8, hkv=2, page=256, chunk=300, total=300 + 2600, top_k=4),
+    dict(name="mfma_no_gqa", hq=4, hkv=4, chunk=200, total=200 + 900, top_k=3),  # G = 1
 ])
 def test_chunk_parity_mfma(kw):
     run_chunk_parity(_w(**kw))
