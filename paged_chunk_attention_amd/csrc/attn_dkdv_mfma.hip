@@ -318,7 +318,9 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
         for (int us = 0; us < 2; ++us)
 #pragma unroll
           for (int sh = 0; sh < 2; ++sh)
-            *reinterpret_cast<u32x4*>(rec + (2 * us + sh) * 512) = __builtin_bit_cast(u32x4, dsb[us][sh]);
+            // non-temporal: the records are read once, by the dQ pass after this one
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, dsb[us][sh]),
+                                        reinterpret_cast<u32x4*>(rec + (2 * us + sh) * 512));
       }
       // dK += dS^T Q (the scale is applied once, at the end).
       bf16x8 ft = tr_frag_at(qp, 0, 0, o, 0);
