@@ -215,8 +215,8 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
     // Some pair of this tile hidden for this lane's key (in its future, or past the end
     // of a window: q - kpos >= window, written so that kpos = INT_MAX cannot overflow)?
     const bool wmask = __any(kpos > a.t0 + q0 || a.t0 + q0 + QTB - 1 - kpos >= wlim);
-    FragOffsets o = fo;
-    o.opaque();
+    fo.opaque();
+    const FragOffsets& o = fo;
     // S = Q K^T for both 32-query halves, the two chains interleaved, fragments read one
     // step ahead.
     f32x16 sa[2] = {f32x16{}, f32x16{}};
@@ -287,8 +287,8 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
   // tile dt, if any.
   auto d_tile = [&](bool prev, const uint16_t* qp, const float* delp, int xp, bool cur,
                     const uint16_t* dt, int u_prev) __attribute__((always_inline)) {
-    FragOffsets o = fo;
-    o.opaque();
+    fo.opaque();
+    const FragOffsets& o = fo;
     __builtin_amdgcn_s_setprio(1);
     if (prev) {
       bf16x8 dsb[2][2];

@@ -47,7 +47,7 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_v1[DQ_KB * D];
   __shared__ int s_page[PCAP];
   constexpr int NT = 64 * DQ_WAVES;
-  using Stage = KeyStage<DQ_KB, DQ_WAVES, PCAP, true>;  // DMA from assembly
+  using Stage = KeyStage<DQ_KB, DQ_WAVES, PCAP>;
   // the wave index is uniform: keep it (and the LDS addresses built from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, col = lane & 31;
@@ -158,8 +158,8 @@ void dq_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part) {
       }
     }
     if (b < nblk_w && b >= blo_w) {
-      FragOffsets o = fo;
-      o.opaque();
+      fo.opaque();
+      const FragOffsets& o = fo;
       const bool mask = b * DQ_KB + DQ_KB - 1 > klim_w0 || b * DQ_KB < klo_wl;
 #pragma unroll
       for (int sub = 0; sub < DQ_KB / 32; ++sub) {
@@ -320,7 +320,7 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
   __shared__ __attribute__((aligned(16))) uint16_t s_s2[DQ_WAVES * DS_REC];
   __shared__ int s_page[PCAP];
   constexpr int NT = 64 * DQ_WAVES;
-  using Stage = KeyStage<DQS_KB, DQ_WAVES, PCAP, true>;  // K rows by DMA from assembly
+  using Stage = KeyStage<DQS_KB, DQ_WAVES, PCAP>;  // K rows
   static_assert(Stage::NI == 2, "stage instruction count");
   constexpr int kStageOps = Stage::NI + 4;  // + the wave's four dS record rows
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -391,8 +391,8 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
                       dst + p * 512);
   };
   auto compute = [&](const uint16_t* kt, const uint16_t* st) __attribute__((always_inline)) {
-    FragOffsets o = fo;
-    o.opaque();
+    fo.opaque();
+    const FragOffsets& o = fo;
     const uint16_t* sb = st + wave * DS_REC;
     bf16x8 af[2][4], bf[2][2];
 #pragma unroll

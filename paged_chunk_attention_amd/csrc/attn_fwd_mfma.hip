@@ -130,8 +130,8 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
   // 2i + 1 of both halves, alternating halves so that consecutive MFMAs are
   // independent). The fragments of step i + 1 are read from LDS while step i multiplies.
   auto mul_pv_s = [&](const uint16_t* vt, const uint16_t* kt) __attribute__((always_inline)) {
-    FragOffsets o = fo;
-    o.opaque();
+    fo.opaque();
+    const FragOffsets& o = fo;
     auto load = [&](int i, bf16x8 (&f)[4]) __attribute__((always_inline)) {
       if (i < 4) {
 #pragma unroll

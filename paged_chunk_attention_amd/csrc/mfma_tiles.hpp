@@ -118,6 +118,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* t, int r0, int c0, int
 // 16 values, rather than one address per fragment per buffer, keeps register use flat
 // however many LDS buffers a kernel reads; opaque() makes the compiler re-add the buffer
 // base at each use instead of keeping one address register per buffer and fragment.
+// Kernels apply it to their one copy in place (a copy made opaque costs 16 moves per use).
 struct FragOffsets {
   int rf[8];  // row fragment, k-step kk
   int tr[8];  // transposed fragment, column block db: [2 db] rows +0, [2 db + 1] rows +8
@@ -262,8 +263,7 @@ __device__ __forceinline__ int first_block(const Keys& k, int qpos) {
 // filled. The compiler's own vmcnt waits stay correct: loads retire in issue order, so
 // untracked DMAs can only make them wait longer. M0 (the LDS base) is an input operand,
 // so the compiler knows it is set; the nop is the one wait state an LDS DMA needs after
-// an M0 write. (Measured: 1-2% faster in the dQ and dK/dV passes; 3% slower in the
-// forward, whose phases the compiler schedules better around the builtin.)
+// an M0 write. (Measured: 1-2% faster in the dQ and dK/dV passes.)
 template <bool ASM = false>
 __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* ldst) {
   if constexpr (ASM) {
@@ -273,6 +273,15 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* ldst) 
   } else {
     __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
   }
+}
+// As lds_dma16<true>, in the instruction's scalar-base form: a wave-uniform 64-bit base
+// in scalar registers plus a per-lane 32-bit byte offset. A wave whose rows share one base
+// then needs no per-lane 64-bit address arithmetic (vector ALU work that the forward's
+// softmax phases compete for).
+__device__ __forceinline__ void lds_dma16_s(const uint16_t* gbase, uint32_t off_bytes, uint16_t* ldst) {
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint16_t*)ldst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off_bytes), "s"(gbase), "{m0}"(base));
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -329,7 +338,7 @@ static __device__ __attribute__((aligned(16))) uint16_t g_zero_rows[4 * D] = {};
 // gives a uniform page base, and lane L adds a fixed offset, row L/16 of the four plus
 // the logical column whose 16 bytes land in its physical slot. With NW a multiple of 4,
 // swz(r) = 4 (L/16) + (w % 4) for every instruction, so that offset is one register.
-template <int ROWS, int NW, int CAP = PCAP, bool ASM = false>
+template <int ROWS, int NW, int CAP = PCAP>
 struct KeyStage {
   static_assert(NW % 4 == 0 && ROWS % (4 * NW) == 0, "rows per wave must tile the stage");
   static constexpr int NI = ROWS / (4 * NW);
@@ -352,26 +361,34 @@ struct KeyStage {
   __device__ __forceinline__ void read_pages(int st, int wave, int (&ph)[NI]) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      // branch-free: the read index is clamped into the window, the result discarded
-      // for rows past the attended keys
+      // branch-free: the read index is clamped into the window; for rows past the
+      // attended keys the id is read but never used (in_seq fails for them)
       const int a = st * ROWS + 4 * (NW * i + wave);
       const int e = min(a >> k.log2p, k.n_entries - 1) - win;
-      const int v = spage[max(0, min(e, CAP - 1))];
-      ph[i] = a < k.n_keys ? v : -1;
+      ph[i] = spage[max(0, min(e, CAP - 1))];
     }
   }
   __device__ __forceinline__ void dma_fixed(int st, const uint16_t* pool, uint16_t* t, int wave,
                                             int lane, const int (&ph)[NI]) const {
-    int lo = lane_off;
-    asm volatile("" : "+v"(lo));
+    const uint32_t lob = 2u * static_cast<uint32_t>(lane_off);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r0 = 4 * (NW * i + wave);
       const int a = st * ROWS + r0;
       const int p = __builtin_amdgcn_readfirstlane(ph[i]);
       const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
-      const bool ok = (p >= 0) & k.in_seq(a + (lane >> 4));
-      lds_dma16<ASM>((ok ? pool + base : g_zero_rows) + lo, t + r0 * D);
+      // The rows of the sequence are a prefix of the attended keys (in_seq(x) implies
+      // in_seq(y) for y < x), so rows a .. a + 3 all exist exactly when row a + 3 does.
+      // That is the rule (one branch per wave): the page base is then uniform. Otherwise
+      // (the sequence's last rows, an invalid page) each lane picks its row or a zero row.
+      if ((p >= 0) & k.in_seq(a + 3)) {
+        lds_dma16_s(pool + base, lob, t + r0 * D);
+      } else {
+        int lo = lane_off, row = lane >> 4;
+        asm volatile("" : "+v"(lo), "+v"(row));  // keep the per-lane work in this branch
+        const bool ok = (p >= 0) & k.in_seq(a + row);
+        lds_dma16<true>((ok ? pool + base : g_zero_rows) + lo, t + r0 * D);
+      }
     }
   }
   __device__ __forceinline__ void issue_fixed(int st, const uint16_t* pool, uint16_t* t, int wave,
