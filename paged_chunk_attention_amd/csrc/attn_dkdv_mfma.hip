@@ -159,7 +159,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r0 = 16 * i + 4 * kg;
-        lds_dma16<true>(src + static_cast<int64_t>(q0 + r0) * ts + lo, dst + r0 * D);
+        lds_dma16(src + static_cast<int64_t>(q0 + r0) * ts + lo, dst + r0 * D);
       }
     } else {
       // The last, partial tile: rows past the end reload the last row. Their data is
@@ -168,7 +168,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
       for (int i = 0; i < 4; ++i) {
         const int r0 = 16 * i + 4 * kg;
         const int qi = min(q0 + r0 + (lane >> 4), a.n_q - 1);
-        lds_dma16<true>(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
+        lds_dma16(src + static_cast<int64_t>(qi) * ts + c8, dst + r0 * D);
       }
     }
   };

@@ -380,14 +380,14 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
     } else {
 #pragma unroll
       for (int i = 0; i < Stage::NI; ++i)
-        lds_dma16<true>(g_zero_rows + ks.lane_off, kt + 4 * (DQ_WAVES * i + wave) * D);
+        lds_dma16(g_zero_rows + ks.lane_off, kt + 4 * (DQ_WAVES * i + wave) * D);
     }
     const bool ok = b < nblk_w && b < b1;
     const uint16_t* rec = ds_tile + (static_cast<int64_t>(b >> 1) * n_qt64 * 4 + 2 * (b & 1) + kh) * DS_REC;
     uint16_t* dst = st + wave * DS_REC;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-      lds_dma16<true>(ok ? rec + p * 512 + ((p & 1) ? src_odd : src_even) : g_zero_rows + 8 * lane,
+      lds_dma16(ok ? rec + p * 512 + ((p & 1) ? src_odd : src_even) : g_zero_rows + 8 * lane,
                       dst + p * 512);
   };
   auto compute = [&](const uint16_t* kt, const uint16_t* st) __attribute__((always_inline)) {

@@ -253,28 +253,23 @@ __device__ __forceinline__ int first_block(const Keys& k, int qpos) {
 // this row order swz(r) = 4(L/16) + w is the same for all four instructions of a lane,
 // so one column offset serves them all.
 //
-// With ASM the instruction is issued from inline assembly rather than through the
-// compiler's builtin. The compiler models the builtin as a flat access that may touch
-// LDS, and while one is outstanding it waits for every pending LDS read (lgkmcnt(0))
-// wherever a single fragment is needed; issued from assembly, the LDS reads keep their
-// exact in-order counts. The compiler then does not know of the DMA at all, which is
-// sound because every caller waits for its DMAs explicitly (vmcnt, then a barrier)
-// before anything reads the buffer, and no code touches a buffer while it is being
-// filled. The compiler's own vmcnt waits stay correct: loads retire in issue order, so
-// untracked DMAs can only make them wait longer. M0 (the LDS base) is an input operand,
-// so the compiler knows it is set; the nop is the one wait state an LDS DMA needs after
-// an M0 write. (Measured: 1-2% faster in the dQ and dK/dV passes.)
-template <bool ASM = false>
+// The instruction is issued from inline assembly rather than through the compiler's
+// builtin. The compiler models the builtin as a flat access that may touch LDS, and while
+// one is outstanding it waits for every pending LDS read (lgkmcnt(0)) wherever a single
+// fragment is needed; issued from assembly, the LDS reads keep their exact in-order
+// counts. The compiler then does not know of the DMA at all, which is sound because every
+// caller waits for its DMAs explicitly (vmcnt, then a barrier) before anything reads the
+// buffer, and no code touches a buffer while it is being filled. The compiler's own
+// vmcnt waits stay correct: loads retire in issue order, so untracked DMAs can only make
+// them wait longer. M0 (the LDS base) is an input operand, so the compiler knows it is
+// set; the nop is the one wait state an LDS DMA needs after an M0 write. (Measured: 1-2%
+// faster than the builtin in the dQ and dK/dV passes.)
 __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* ldst) {
-  if constexpr (ASM) {
-    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) uint16_t*)ldst));
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(base));
-  } else {
-    __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
-  }
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint16_t*)ldst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(base));
 }
-// As lds_dma16<true>, in the instruction's scalar-base form: a wave-uniform 64-bit base
+// As lds_dma16, in the instruction's scalar-base form: a wave-uniform 64-bit base
 // in scalar registers plus a per-lane 32-bit byte offset. A wave whose rows share one base
 // then needs no per-lane 64-bit address arithmetic (vector ALU work that the forward's
 // softmax phases compete for).
@@ -387,7 +382,7 @@ struct KeyStage {
         int lo = lane_off, row = lane >> 4;
         asm volatile("" : "+v"(lo), "+v"(row));  // keep the per-lane work in this branch
         const bool ok = (p >= 0) & k.in_seq(a + row);
-        lds_dma16<true>((ok ? pool + base : g_zero_rows) + lo, t + r0 * D);
+        lds_dma16((ok ? pool + base : g_zero_rows) + lo, t + r0 * D);
       }
     }
   }
