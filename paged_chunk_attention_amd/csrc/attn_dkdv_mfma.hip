@@ -22,10 +22,12 @@ namespace mf {
 // Each wave carries half of the state of one owner of 32 keys, so two fit on a SIMD,
 // and the hardware overlaps one wave's softmax arithmetic with the other's products.
 // The D wave's order (dS and dK of the previous tile, then dP of this one) puts its
-// 32 products under the P wave's softmax, and it runs its tile at raised wave
+// 32 products under the P wave's softmax. Without SPILL it runs its tile at raised wave
 // priority, so that the SIMD's arbiter feeds the matrix core first whenever both waves
 // are ready (measured 4-5% faster than equal priorities; raising the P wave's products
-// too gained less). Query tiles arrive by DMA one tile ahead: Q in three buffers (the
+// too gained less). With SPILL the waves keep equal priorities: there the raised D wave
+// measured 3-4% slower, its products delaying the P wave's S chain, which the softmax
+// and dV wait for. Query tiles arrive by DMA one tile ahead: Q in three buffers (the
 // D wave still reads the previous tile's), dO in two; the buffers' roles are static in
 // each sixth of the unrolled loop. P has to be exactly 0 for masked pairs and at most
 // about 1 elsewhere (it is exp(S - LSE) with the forward's LSE), which fp16 holds.
@@ -289,7 +291,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
                     const uint16_t* dt, int u_prev) __attribute__((always_inline)) {
     fo.opaque();
     const FragOffsets& o = fo;
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!SPILL) __builtin_amdgcn_s_setprio(1);
     if (prev) {
       bf16x8 dsb[2][2];
 #pragma unroll
@@ -350,7 +352,7 @@ void dkdv_mfma_kernel(AttnArgs a, int n_split, int whole, float* part, int part_
         fd = nd;
       }
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!SPILL) __builtin_amdgcn_s_setprio(0);
   };
 
   // Iteration it (0 .. n_it): DMA of tile it + 1 into set (qn, dn, lsen, deln); the P
