@@ -254,19 +254,19 @@ void fwd_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, float* part_m
     if constexpr (decltype(is_m)::value) {
       const int b = (u >> 1) - 1;  // M(b): PV of block b, S of block b + 1
       if (u >= 0) {
+        // The M phase, the longer of the two, issues at raised priority. (While the DMA
+        // duty cost a V phase more cycles than the products, raising the softmax instead
+        // was faster.)
+        __builtin_amdgcn_s_setprio(1);
         // M(-1) multiplies the zero P^T by the zero-filled V buffer (adds exact zeros);
         // M(nblk_w - 1) computes an S^T no softmax will read. Before this wave's first
         // block (a window) P^T is still zero: M(blo_w - 1) only computes S^T of blo_w.
         if (b < nblk_w && b + 1 >= blo_w) mul_pv_s(vr, kr);
+        __builtin_amdgcn_s_setprio(0);
       }
     } else {
-      // The softmax issues at raised priority: its dependent vector chain, not the
-      // products (which queue in the matrix core anyway), is what the SIMD's other wave
-      // should not delay. (Measured 1-2% faster than raising the M phase instead.)
       const int b = u >> 1;
-      __builtin_amdgcn_s_setprio(1);
       if (u >= 0 && b < nblk_w && b >= blo_w) softmax(b);
-      __builtin_amdgcn_s_setprio(0);
     }
     if (dma) {
       __builtin_amdgcn_sched_barrier(0);

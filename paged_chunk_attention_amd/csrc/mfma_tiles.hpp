@@ -353,7 +353,18 @@ struct KeyStage {
   // finite, since a masked P of 0 still multiplies them). A fixed count per call lets
   // the caller wait for all but its most recent batches with vmcnt(n). Split in two so
   // that the page-id reads (LDS) can be issued well before the DMA needs them.
+  static constexpr int LOG2_ROWS = ROWS == 64 ? 6 : ROWS == 128 ? 7 : ROWS == 256 ? 8 : 30;
+  // With pages of at least ROWS tokens every stage (ROWS-aligned) lies in one page: one
+  // page id, one validity test and one base then serve all NI instructions. A wave issues
+  // its instructions one at a time, so this per-stage work (about 30 scalar instructions
+  // per DMA instruction otherwise) is time the wave's softmax waits behind.
+  __device__ __forceinline__ bool one_page() const { return k.log2p >= LOG2_ROWS; }
   __device__ __forceinline__ void read_pages(int st, int wave, int (&ph)[NI]) const {
+    if (one_page()) {  // uniform; dma_fixed then reads ph[0] only
+      const int e = min((st * ROWS) >> k.log2p, k.n_entries - 1) - win;
+      ph[0] = spage[max(0, min(e, CAP - 1))];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       // branch-free: the read index is clamped into the window; for rows past the
@@ -366,16 +377,41 @@ struct KeyStage {
   __device__ __forceinline__ void dma_fixed(int st, const uint16_t* pool, uint16_t* t, int wave,
                                             int lane, const int (&ph)[NI]) const {
     const uint32_t lob = 2u * static_cast<uint32_t>(lane_off);
+    if (one_page()) {
+      const int a0 = st * ROWS;
+      const int p = __builtin_amdgcn_readfirstlane(ph[0]);
+      const uint16_t* base =
+          pool + ((static_cast<int64_t>(p) << k.log2p) + (a0 & ((1 << k.log2p) - 1))) * D;
+      // The rows of the sequence are a prefix of the attended keys (in_seq(x) implies
+      // in_seq(y) for y < x), so the whole stage exists exactly when its last row does:
+      // then every instruction takes the uniform base. Otherwise (the sequence's last
+      // stage, an invalid page) each lane picks its row or a zero row.
+      if ((p >= 0) & k.in_seq(a0 + ROWS - 1)) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int r0 = 4 * (NW * i + wave);
+          lds_dma16_s(base + r0 * D, lob, t + r0 * D);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int r0 = 4 * (NW * i + wave);
+          int lo = lane_off, row = lane >> 4;
+          asm volatile("" : "+v"(lo), "+v"(row));  // keep the per-lane work in this branch
+          const bool ok = (p >= 0) & k.in_seq(a0 + r0 + row);
+          lds_dma16((ok ? base + r0 * D : g_zero_rows) + lo, t + r0 * D);
+        }
+      }
+      return;
+    }
+    // Smaller pages: each instruction's four rows (4-aligned) still share a page.
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r0 = 4 * (NW * i + wave);
       const int a = st * ROWS + r0;
       const int p = __builtin_amdgcn_readfirstlane(ph[i]);
       const int64_t base = ((static_cast<int64_t>(p) << k.log2p) + (a & ((1 << k.log2p) - 1))) * D;
-      // The rows of the sequence are a prefix of the attended keys (in_seq(x) implies
-      // in_seq(y) for y < x), so rows a .. a + 3 all exist exactly when row a + 3 does.
-      // That is the rule (one branch per wave): the page base is then uniform. Otherwise
-      // (the sequence's last rows, an invalid page) each lane picks its row or a zero row.
+      // Rows a .. a + 3 all exist exactly when row a + 3 does (the prefix rule above).
       if ((p >= 0) & k.in_seq(a + 3)) {
         lds_dma16_s(pool + base, lob, t + r0 * D);
       } else {
