@@ -385,10 +385,14 @@ void dqs_mfma_kernel(AttnArgs a, int n_ks, int whole, float* part, const uint16_
     const bool ok = b < nblk_w && b < b1;
     const uint16_t* rec = ds_tile + (static_cast<int64_t>(b >> 1) * n_qt64 * 4 + 2 * (b & 1) + kh) * DS_REC;
     uint16_t* dst = st + wave * DS_REC;
+    if (ok) {  // uniform: one base per 512-value part, the lane's offset in the instruction
+      const uint32_t lo_e = 2u * static_cast<uint32_t>(src_even), lo_o = 2u * static_cast<uint32_t>(src_odd);
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      lds_dma16(ok ? rec + p * 512 + ((p & 1) ? src_odd : src_even) : g_zero_rows + 8 * lane,
-                      dst + p * 512);
+      for (int p = 0; p < 4; ++p) lds_dma16_s(rec + p * 512, (p & 1) ? lo_o : lo_e, dst + p * 512);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) lds_dma16(g_zero_rows + 8 * lane, dst + p * 512);
+    }
   };
   auto compute = [&](const uint16_t* kt, const uint16_t* st) __attribute__((always_inline)) {
     fo.opaque();
