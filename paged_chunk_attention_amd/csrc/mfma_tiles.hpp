@@ -272,7 +272,9 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* gsrc, uint16_t* ldst) 
 // As lds_dma16, in the instruction's scalar-base form: a wave-uniform 64-bit base
 // in scalar registers plus a per-lane 32-bit byte offset. A wave whose rows share one base
 // then needs no per-lane 64-bit address arithmetic (vector ALU work that the forward's
-// softmax phases compete for).
+// softmax phases compete for). gbase must be the same in every lane of the wave: the
+// operand is bound to scalar registers, so a per-lane value would silently be read from
+// one lane. Every caller derives it from wave-uniform indices and readfirstlane'd ids.
 __device__ __forceinline__ void lds_dma16_s(const uint16_t* gbase, uint32_t off_bytes, uint16_t* ldst) {
   const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) uint16_t*)ldst));
@@ -346,6 +348,14 @@ struct KeyStage {
     return (lane >> 4) * D + 8 * ((lane & 15) ^ (((lane >> 4) << 2) | (wave & 3)));
   }
 
+  // With pages of at least ROWS tokens every stage (ROWS-aligned) lies in one page: one
+  // page id, one validity test and one base then serve all NI instructions. A wave issues
+  // its instructions one at a time, so this per-stage work (about 30 scalar instructions
+  // per DMA instruction otherwise) is time the wave's softmax waits behind. (Stage sizes
+  // other than 64, 128 and 256 rows always take the per-instruction path.)
+  static constexpr int LOG2_ROWS = ROWS == 64 ? 6 : ROWS == 128 ? 7 : ROWS == 256 ? 8 : 30;
+  __device__ __forceinline__ bool one_page() const { return k.log2p >= LOG2_ROWS; }
+
   // DMA the rows of stage st (attended keys st*ROWS ..) of one pool (K or V) into t.
   // Every wave issues exactly NI DMA instructions with all lanes active, whatever the
   // rows: a lane whose row does not exist, lies past the end of the sequence or has an
@@ -353,12 +363,6 @@ struct KeyStage {
   // finite, since a masked P of 0 still multiplies them). A fixed count per call lets
   // the caller wait for all but its most recent batches with vmcnt(n). Split in two so
   // that the page-id reads (LDS) can be issued well before the DMA needs them.
-  static constexpr int LOG2_ROWS = ROWS == 64 ? 6 : ROWS == 128 ? 7 : ROWS == 256 ? 8 : 30;
-  // With pages of at least ROWS tokens every stage (ROWS-aligned) lies in one page: one
-  // page id, one validity test and one base then serve all NI instructions. A wave issues
-  // its instructions one at a time, so this per-stage work (about 30 scalar instructions
-  // per DMA instruction otherwise) is time the wave's softmax waits behind.
-  __device__ __forceinline__ bool one_page() const { return k.log2p >= LOG2_ROWS; }
   __device__ __forceinline__ void read_pages(int st, int wave, int (&ph)[NI]) const {
     if (one_page()) {  // uniform; dma_fixed then reads ph[0] only
       const int e = min((st * ROWS) >> k.log2p, k.n_entries - 1) - win;
