@@ -82,6 +82,19 @@ def test_padding_rows_come_from_zeros(kw):
     run_chunk_parity(w, x)
 
 
+def test_padding_rows_come_from_zeros_recomputing_dq(monkeypatch):
+    """The same NaN sentinel with the dS spill off, so the dQ pass recomputes S and dP and
+    stages its own blocks of 128 keys (one page id per block with pages of 128; the block
+    holding the sequence's end takes the per-row path): its padding rows come from zeros
+    too."""
+    monkeypatch.setenv("OOMB_DS_SPILL_MAX_MIB", "0")
+    w = _w(name="mfma_nan_page0_recompute", chunk=333, total=2597 + 333, top_k=5, needles=3)
+    x = wl.make_inputs(w)
+    x["table"] = x["table"] + 1
+    x["gtable"] = x["gtable"] + 1
+    run_chunk_parity(w, x)
+
+
 @pytest.mark.parametrize("n,whole", [(3, 5), (2, 13), (4, 14)])
 @pytest.mark.parametrize("kw", [
     dict(name="mfma_gqa7_mixed_sparse", hq=28, hkv=4, chunk=333, total=2597 + 333, top_k=5, needles=3),
