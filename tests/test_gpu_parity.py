@@ -69,6 +69,8 @@ def test_chunk_parity_mfma_fixed_splits(kw, n, monkeypatch):
 @pytest.mark.parametrize("kw", [
     dict(name="mfma_nan_page0_dense"),
     dict(name="mfma_nan_page0_sparse", chunk=333, total=2597 + 333, top_k=5, needles=3),
+    # pages of 16: every staging instruction reads its own page id (the per-instruction path)
+    dict(name="mfma_nan_page0_p16", hq=4, hkv=2, page=16, chunk=200, total=900, top_k=6),
 ])
 def test_padding_rows_come_from_zeros(kw):
     """Physical page 0 is never mapped and holds NaN: the rows staged for block tails,
